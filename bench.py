@@ -1,0 +1,291 @@
+"""Benchmark: Q4_K GEMV weight GB/s and % of HBM roofline at batch 1 on the
+Qwen3.5-9B-shaped FFN and untied lm_head (shapes from issue #3346,
+size_variants.9b: d = 4096, intermediate = 12288, V = 248320).
+
+One step is one pass of the decode hot path over resident weights:
+    h      = silu(W_gate x) * (W_up x)   q4k_fused_swiglu  2 x [12288, 4096]
+    y      = W_down h                    q4k_gemv          [4096, 12288]
+    logits = W_lm_head y                 q4k_gemv          [248320, 4096]
+657 MB of Q4_K weights per step (more than the 256 MB Infinity Cache, so
+every step streams its weights from HBM).  Inputs are seeded synthetic data of
+the pages' value distributions (q4_dequant_gemv_amd/inputs.py).
+
+Prints ONE JSON line.  `roofline` covers the dominant kernel (the lm_head
+GEMV): algorithmic bytes per launch / mean launch time, both from HIP events
+recorded on the launch stream over the timed region.  `traffic` comes from the
+committed rocprofv3 counter summary (profiles/traffic_lm_head_9b.json) when it
+was taken from the kernel sources as they are now, else null.  `cpu_baseline`
+times the CPU oracle on one full step.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "Q4_K GEMV weight GB/s and % HBM roofline at batch 1 (9B lm_head/FFN)"
+KERNEL_SOURCES = ["q4k_device.h", "q4k_int_dot.h", "gemv.hip", "api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "q4_dequant_gemv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(launch_weight_bytes: int):
+    path = os.path.join(ROOT, "profiles", "traffic_lm_head_9b.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time every kernel at every config shape (table on stderr)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this path runs on one GPU; multi-GPU runs are not part of this benchmark "
+              "(rows shard across GPUs without communication, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from q4_dequant_gemv_amd import inputs, q4k
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q4k.lib()
+
+    log("[bench] generating inputs")
+    shapes = {nm: inputs.SHAPES[nm] for nm in ("gate_9b", "up_9b", "down_9b", "lm_head_9b")}
+    host = {
+        "gate_9b": inputs.make_q4k(*shapes["gate_9b"], config_id=2, tensor_id=0),
+        "up_9b": inputs.make_q4k(*shapes["up_9b"], config_id=2, tensor_id=1),
+        "down_9b": inputs.make_q4k(*shapes["down_9b"], config_id=2, tensor_id=2),
+        "lm_head_9b": inputs.make_q4k(*shapes["lm_head_9b"], config_id=3, tensor_id=0),
+    }
+    x_host = inputs.make_x(1, 4096, config_id=2, tensor_id=100)[0]
+    W = {nm: torch.from_numpy(a.reshape(-1)).to(dev) for nm, a in host.items()}
+    x = torch.from_numpy(x_host).to(dev)
+    h = torch.empty(12288, dtype=torch.float32, device=dev)
+    y = torch.empty(4096, dtype=torch.float32, device=dev)
+    logits = torch.empty(248320, dtype=torch.float32, device=dev)
+    wbytes = {nm: a.nbytes for nm, a in host.items()}
+    step_weight_bytes = sum(wbytes.values())
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        q4k.fused_swiglu(W["gate_9b"], W["up_9b"], x, h=h, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        q4k.gemv(W["down_9b"], h, y=y, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        q4k.gemv(W["lm_head_9b"], y, y=logits, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    per = {"fused_swiglu": [], "gemv_down": [], "gemv_lm_head": []}
+    for e in evs:
+        per["fused_swiglu"].append(e[0].elapsed_time(e[1]))
+        per["gemv_down"].append(e[1].elapsed_time(e[2]))
+        per["gemv_lm_head"].append(e[2].elapsed_time(e[3]))
+    kernel_bytes = {
+        "fused_swiglu": wbytes["gate_9b"] + wbytes["up_9b"] + 4 * 4096 + 4 * 12288,
+        "gemv_down": wbytes["down_9b"] + 4 * 12288 + 4 * 4096,
+        "gemv_lm_head": wbytes["lm_head_9b"] + 4 * 4096 + 4 * 248320,
+    }
+    kernels = {}
+    for nm, ts in per.items():
+        mean_ms = float(np.mean(ts))
+        kernels[nm] = {"mean_us": round(mean_ms * 1e3, 3), "median_us": round(float(np.median(ts)) * 1e3, 3),
+                       "GB/s": round(kernel_bytes[nm] / (mean_ms * 1e-3) / 1e9, 1),
+                       "frac_hbm_peak": round(kernel_bytes[nm] / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    value = step_weight_bytes / (ms_per_step * 1e-3) / 1e9
+    lm = kernels["gemv_lm_head"]
+    achieved = kernel_bytes["gemv_lm_head"] / (float(np.mean(per["gemv_lm_head"])) * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(wbytes["lm_head_9b"]),
+                "kernel": "q4k_gemv lm_head 248320x4096", "bytes_per_launch": kernel_bytes["gemv_lm_head"]}
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s; per kernel {kernels}; host wall {wall:.3f}s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        cores = len(os.sched_getaffinity(0))
+        threads = max(1, min(cores, 64))
+        log(f"[bench] cpu baseline: oracle on full steps for >= 10 s, {threads} threads")
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            ref_h = oracle.fused_swiglu(host["gate_9b"], host["up_9b"], x_host, threads=threads)["h"]
+            ref_y = oracle.gemv(host["down_9b"], ref_h.astype(np.float32), threads=threads)[0]
+            oracle.gemv(host["lm_head_9b"], ref_y.astype(np.float32), threads=threads)
+            reps += 1
+            cpu_s = time.perf_counter() - t0
+            if cpu_s >= 10.0 or reps >= 200:
+                break
+        cpu = {"value": round(reps * step_weight_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{reps} full steps (gate+up SwiGLU, down, lm_head: all rows, 657 MB of Q4_K each), "
+                         f"{cpu_s:.1f} s on {threads} host threads"}
+
+    if args.sweep:
+        sweep(q4k, inputs, torch, np, dev)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "qwen3.5-9b-shaped decode FFN + lm_head at batch 1: fused gate+up SwiGLU "
+                        "(2 x 12288x4096), down (4096x12288), untied lm_head (248320x4096), Q4_K weights, f32 activations",
+            "weight_bytes_per_step": step_weight_bytes,
+            "frac_hbm_peak_step": round(value / HBM_PEAK_GBS, 4),
+            "kernels": kernels,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def time_call(fn, torch, reps=50, warm=5):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    s = torch.cuda.current_stream()
+    for a, b in evs:
+        a.record(s)
+        fn()
+        b.record(s)
+    torch.cuda.synchronize()
+    import numpy as np
+
+    return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e-3
+
+
+def sweep(q4k, inputs, torch, np, dev):
+    """Every kernel at every config shape; weights rotated over >= 512 MiB of
+    copies so repeated calls do not hit the Infinity Cache."""
+    log("[sweep] kernel  shape  m  us  GB/s(weights)  frac")
+
+    def copies(nbytes):
+        return max(1, -(-(512 << 20) // nbytes))
+
+    def gemv_case(name, n, k):
+        w0 = inputs.make_q4k(n, k, config_id=7, tensor_id=1).reshape(-1)
+        ws = [torch.from_numpy(w0).to(dev) for _ in range(copies(w0.nbytes))]
+        x = torch.from_numpy(inputs.make_x(1, k, config_id=7)[0]).to(dev)
+        y = torch.empty(n, dtype=torch.float32, device=dev)
+        it = iter(range(10 ** 9))
+        t = time_call(lambda: q4k.gemv(ws[next(it) % len(ws)], x, y=y), torch)
+        log(f"[sweep] gemv {name} {n}x{k} m=1 {t * 1e6:.2f} {w0.nbytes / t / 1e9:.1f} {w0.nbytes / t / 8e12:.3f}")
+        del ws
+
+    for name in ("square_1k", "q_proj_0p8b", "out_proj_0p8b", "lm_head_0p8b", "down_9b", "gate_9b", "lm_head_9b"):
+        gemv_case(name, *inputs.SHAPES[name])
+    n, k = inputs.SHAPES["gate_9b"]
+    g0 = inputs.make_q4k(n, k, config_id=7, tensor_id=2).reshape(-1)
+    c = copies(2 * g0.nbytes)
+    gs = [torch.from_numpy(g0).to(dev) for _ in range(c)]
+    us = [torch.from_numpy(g0).to(dev) for _ in range(c)]
+    x = torch.from_numpy(inputs.make_x(1, k, config_id=7)[0]).to(dev)
+    hh = torch.empty(n, dtype=torch.float32, device=dev)
+    it = iter(range(10 ** 9))
+
+    def sw():
+        i = next(it) % c
+        q4k.fused_swiglu(gs[i], us[i], x, h=hh)
+
+    t = time_call(sw, torch)
+    log(f"[sweep] swiglu gate+up {n}x{k} m=1 {t * 1e6:.2f} {2 * g0.nbytes / t / 1e9:.1f} {2 * g0.nbytes / t / 8e12:.3f}")
+    del gs, us
+    for name in ("gate_9b", "down_9b"):
+        n, k = inputs.SHAPES[name]
+        w0 = inputs.make_q4k(n, k, config_id=7, tensor_id=3).reshape(-1)
+        ws = [torch.from_numpy(w0).to(dev) for _ in range(copies(w0.nbytes))]
+        for m in (1, 4, 16, 32, 64):
+            xs = torch.from_numpy(inputs.make_x(m, k, config_id=7)).to(dev)
+            yy = torch.empty((m, n), dtype=torch.float32, device=dev)
+            it2 = iter(range(10 ** 9))
+            t = time_call(lambda: q4k.gemv_batched(ws[next(it2) % len(ws)], xs, y=yy), torch)
+            tflops = 2.0 * m * n * k / t / 1e12
+            log(f"[sweep] batched {name} {n}x{k} m={m} {t * 1e6:.2f} {w0.nbytes / t / 1e9:.1f} "
+                f"{w0.nbytes / t / 8e12:.3f} ({tflops:.1f} TFLOP/s)")
+        del ws
+    n, k = inputs.SHAPES["lm_head_0p8b"]
+    w0 = inputs.make_q4k(n, k, config_id=7, tensor_id=4).reshape(-1)
+    ws = [torch.from_numpy(w0).to(dev) for _ in range(copies(w0.nbytes))]
+    out = torch.empty((n, k), dtype=torch.float32, device=dev)
+    it3 = iter(range(10 ** 9))
+    t = time_call(lambda: q4k.dequant(ws[next(it3) % len(ws)], k, out=out), torch, reps=20)
+    tot = w0.nbytes + out.numel() * 4
+    log(f"[sweep] dequant {n}x{k} {t * 1e6:.2f} {tot / t / 1e9:.1f} (read+write) {tot / t / 8e12:.3f}")
+
+
+if __name__ == "__main__":
+    main()

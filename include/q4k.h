@@ -1,0 +1,119 @@
+/*
+ * q4k.h -- C ABI of libq4k.so: fused Q4_K dequantize-and-multiply on MI355X
+ * (gfx950), hand-written HIP kernels.
+ *
+ * The operation.  "Struct WgslForwardPass" (trueno docs), upload_q4k_weight:
+ * weights stay as raw Q4K bytes and are multiplied by a fused dequant+GEMV on
+ * the GPU.  "qualia_core_db/inference/cuda_lane/mod.rs" names the entry points
+ * this ABI mirrors (try_q4k_soa_gemv, try_q4k_soa_fused_swiglu) and, under
+ * "Honest limits", the fallback they replace: dequantize once to dense f32.
+ *
+ * Weight format.  A Q4_K matrix W of n rows and k columns (k % 256 == 0) is
+ * n * (k/256) super-blocks of 144 bytes, row-major: row r occupies bytes
+ * [r*(k/256)*144, (r+1)*(k/256)*144) and its super-block b covers columns
+ * [256b, 256b+256) ("@simulatte/doppler 0.1.7 -> 0.1.8", matmul.d.ts,
+ * MatmulOptions.transposeB: B is [N,K], row-major).  A super-block is
+ *     bytes 0-1   d      IEEE binary16, little-endian
+ *     bytes 2-3   dmin   IEEE binary16, little-endian
+ *     bytes 4-15  eight six-bit scales sc_j and eight six-bit mins m_j
+ *     bytes 16-143 256 four-bit codes q (byte 32g+l: low nibble is weight
+ *                  64g+l, high nibble weight 64g+32+l)
+ * and weight e of sub-block j = e/32 is  w = d*sc_j*q - dmin*m_j  (the GGUF
+ * Q4_K layout; the pages' model files are Q4_K_M GGUF files, issue #3346).
+ *
+ * Conventions shared by every entry point:
+ *  - All pointers except `stream` are DEVICE pointers owned by the caller.
+ *    The library never allocates, frees or synchronises; every call only
+ *    enqueues kernels on `stream` (a hipStream_t passed as void*; NULL means
+ *    the null stream) and returns.  Results are ready when the stream is.
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is launched and the status says why.  Launch failures are
+ *    reported as Q4K_ERR_LAUNCH.
+ *  - w must be 16-byte aligned; x, y, h must be 4-byte aligned and the
+ *    dequant output 16-byte aligned.  Outputs
+ *    must not overlap any input.  Sub-ranges of rows are passed by pointer
+ *    offsets (w + r0*(k/256)*144, y + r0), which keep 16-byte alignment.
+ *  - n == 0 or m == 0 is an empty call: Q4K_OK, nothing launched.  k == 0 is
+ *    a valid empty sum: outputs are written as 0 (dequant writes nothing).
+ *  - Activations and outputs are f32.  The products use the factored form
+ *    sum_j [d*sc_j * sum_{e in j} q_e x_e - dmin*m_j * sum_{e in j} x_e]
+ *    in f32; each result satisfies |y - y_exact| <= 2e-4 * sum_k |w_k x_k|
+ *    for finite inputs (non-finite x gives NaN in the affected outputs).
+ *  - Calls are stateless and may be made from several host threads.
+ */
+#ifndef Q4K_H
+#define Q4K_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define Q4K_API __attribute__((visibility("default")))
+#else
+#define Q4K_API
+#endif
+
+typedef enum {
+    Q4K_OK = 0,
+    Q4K_ERR_INVALID_ARG = 1,       /* null pointer, negative size, overlap, size overflow */
+    Q4K_ERR_UNSUPPORTED_SHAPE = 2, /* k % 256 != 0 */
+    Q4K_ERR_MISALIGNED = 3,        /* w not 16-B aligned, or x/y not 4-B aligned */
+    Q4K_ERR_LAUNCH = 4             /* the HIP runtime refused a launch */
+} q4k_status;
+
+/* Bytes of one Q4_K super-block and weights per super-block. */
+#define Q4K_BLOCK_BYTES 144
+#define Q4K_BLOCK_WEIGHTS 256
+
+/*
+ * Batch-1 GEMV (the decode case: "@simulatte/doppler 0.1.7 -> 0.1.8",
+ * matmul-selection.js, resolveMatmulPhase treats M == 1 as decode and
+ * selectQ4KFusedVariant picks the fused Q4K variant for it).
+ *   w : Q4_K matrix [n, k] (n*(k/256)*144 bytes)
+ *   x : f32 [k]
+ *   y : f32 [n], written: y[r] = sum_c W[r,c] x[c]
+ */
+Q4K_API q4k_status q4k_gemv(const void *w, const float *x, float *y, int64_t n, int64_t k, void *stream);
+
+/*
+ * Skinny GEMM over the same weights for m tokens (selectQ4KFusedVariant's
+ * non-M1 variant; "Module qwen3_attention" names a W4A16 batched path).
+ *   x : f32 [m, k] row-major (token-major), y : f32 [m, n] row-major:
+ *   y[t, r] = sum_c W[r,c] x[t,c].
+ * m < 16 runs on the vector ALUs (each weight decoded once, used m times);
+ * m >= 16 decodes tiles of weights into f16 operands for the matrix cores.
+ */
+Q4K_API q4k_status q4k_gemv_batched(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
+                            void *stream);
+
+/*
+ * Fused gate/up GEMV with SwiGLU ("qualia_core_db/inference/cuda_lane/mod.rs",
+ * try_q4k_soa_fused_swiglu; "Struct WgslForwardPass", silu_mul_shader):
+ *   w_gate, w_up : two separate Q4_K matrices [n, k]
+ *   x : f32 [k]; h : f32 [n], written: h[r] = silu(g[r]) * u[r] with
+ *   g = W_gate x, u = W_up x, silu(t) = t / (1 + exp(-t)).
+ */
+Q4K_API q4k_status q4k_fused_swiglu(const void *w_gate, const void *w_up, const float *x, float *h, int64_t n,
+                            int64_t k, void *stream);
+
+/*
+ * Dequantize to dense f32 (the "dequantize once to dense f32" fallback of the
+ * cuda_lane module docs), bit-exact: out[r, c] = f32(f32(d*sc)*q - f32(dmin*m)).
+ *   out : f32 [n, k] row-major.
+ */
+Q4K_API q4k_status q4k_dequant(const void *w, float *out, int64_t n, int64_t k, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+Q4K_API const char *q4k_status_string(q4k_status s);
+
+/* ABI version of this header (major*100 + minor). */
+Q4K_API int q4k_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4K_H */

@@ -1,0 +1,148 @@
+// C ABI of libq4k.so (declared in include/q4k.h): host-side validation, then
+// dispatch to the kernels on the caller's stream.  Validation follows the
+// fail-before-dispatch practice of resolveMatmulOverride / failOrWarn in
+// "@simulatte/doppler 0.1.7 -> 0.1.8" (matmul-selection.js): a bad argument is
+// reported before anything is enqueued.
+#include <stdint.h>
+
+#include <atomic>
+
+#include "../../include/q4k.h"
+#include "launch.h"
+
+namespace q4k {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+__global__ void fill_zero_kernel(float *__restrict__ y, int64_t count) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride) y[i] = 0.0f;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap (byte ranges, both non-empty).
+bool overlap(const void *a, uint64_t na, const void *b, uint64_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a);
+    const uintptr_t pb = reinterpret_cast<uintptr_t>(b);
+    if (na == 0 || nb == 0) return false;
+    return pa < pb + nb && pb < pa + na;
+}
+
+// Largest element count accepted for any one tensor: keeps every byte offset
+// inside int64 with room to spare.
+constexpr int64_t kMaxElems = int64_t(1) << 56;
+
+// Checks the sizes shared by every entry point and returns the weight bytes.
+q4k_status check_shape(int64_t n, int64_t k, uint64_t *w_bytes) {
+    if (n < 0 || k < 0) return Q4K_ERR_INVALID_ARG;
+    if (k % Q4K_BLOCK_WEIGHTS != 0) return Q4K_ERR_UNSUPPORTED_SHAPE;
+    if (k > 0 && n > kMaxElems / k) return Q4K_ERR_INVALID_ARG;
+    *w_bytes = static_cast<uint64_t>(n) * static_cast<uint64_t>(k / Q4K_BLOCK_WEIGHTS) * Q4K_BLOCK_BYTES;
+    return Q4K_OK;
+}
+
+q4k_status from_hip(hipError_t e) { return e == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH; }
+
+}  // namespace
+
+int device_cu_count() {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+    cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream) {
+    if (count == 0) return hipSuccess;
+    const int64_t need = (count + 255) / 256;
+    const int grid = static_cast<int>(need < 4096 ? need : 4096);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, stream, y, count);
+    return hipGetLastError();
+}
+
+}  // namespace q4k
+
+using q4k::aligned;
+using q4k::check_shape;
+using q4k::from_hip;
+using q4k::overlap;
+
+extern "C" {
+
+q4k_status q4k_gemv(const void *w, const float *x, float *y, int64_t n, int64_t k, void *stream) {
+    uint64_t wb = 0;
+    const q4k_status s = check_shape(n, k, &wb);
+    if (s != Q4K_OK) return s;
+    if (n == 0) return Q4K_OK;
+    if (y == nullptr || (k > 0 && (w == nullptr || x == nullptr))) return Q4K_ERR_INVALID_ARG;
+    if (!aligned(w, 16) || !aligned(x, 4) || !aligned(y, 4)) return Q4K_ERR_MISALIGNED;
+    const uint64_t yb = static_cast<uint64_t>(n) * 4, xb = static_cast<uint64_t>(k) * 4;
+    if (overlap(y, yb, w, wb) || overlap(y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
+    return from_hip(q4k::launch_gemv(static_cast<const uint8_t *>(w), nullptr, x, y, n, k,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+q4k_status q4k_gemv_batched(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
+                            void *stream) {
+    uint64_t wb = 0;
+    const q4k_status s = check_shape(n, k, &wb);
+    if (s != Q4K_OK) return s;
+    if (m < 0) return Q4K_ERR_INVALID_ARG;
+    if (m > 0 && (n > q4k::kMaxElems / m || (k > 0 && m > q4k::kMaxElems / k))) return Q4K_ERR_INVALID_ARG;
+    if (n == 0 || m == 0) return Q4K_OK;
+    if (y == nullptr || (k > 0 && (w == nullptr || x == nullptr))) return Q4K_ERR_INVALID_ARG;
+    if (!aligned(w, 16) || !aligned(x, 4) || !aligned(y, 4)) return Q4K_ERR_MISALIGNED;
+    const uint64_t yb = static_cast<uint64_t>(m) * n * 4, xb = static_cast<uint64_t>(m) * k * 4;
+    if (overlap(y, yb, w, wb) || overlap(y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
+    return from_hip(q4k::launch_gemv_batched(static_cast<const uint8_t *>(w), x, y, m, n, k,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+q4k_status q4k_fused_swiglu(const void *w_gate, const void *w_up, const float *x, float *h, int64_t n, int64_t k,
+                            void *stream) {
+    uint64_t wb = 0;
+    const q4k_status s = check_shape(n, k, &wb);
+    if (s != Q4K_OK) return s;
+    if (n == 0) return Q4K_OK;
+    if (h == nullptr || (k > 0 && (w_gate == nullptr || w_up == nullptr || x == nullptr))) return Q4K_ERR_INVALID_ARG;
+    if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(x, 4) || !aligned(h, 4)) return Q4K_ERR_MISALIGNED;
+    const uint64_t hb = static_cast<uint64_t>(n) * 4, xb = static_cast<uint64_t>(k) * 4;
+    if (overlap(h, hb, w_gate, wb) || overlap(h, hb, w_up, wb) || overlap(h, hb, x, xb)) return Q4K_ERR_INVALID_ARG;
+    return from_hip(q4k::launch_gemv(static_cast<const uint8_t *>(w_gate), static_cast<const uint8_t *>(w_up), x,
+                                     h, n, k, static_cast<hipStream_t>(stream)));
+}
+
+q4k_status q4k_dequant(const void *w, float *out, int64_t n, int64_t k, void *stream) {
+    uint64_t wb = 0;
+    const q4k_status s = check_shape(n, k, &wb);
+    if (s != Q4K_OK) return s;
+    if (n == 0 || k == 0) return Q4K_OK;
+    if (w == nullptr || out == nullptr) return Q4K_ERR_INVALID_ARG;
+    if (!aligned(w, 16) || !aligned(out, 16)) return Q4K_ERR_MISALIGNED;
+    const uint64_t ob = static_cast<uint64_t>(n) * k * 4;
+    if (overlap(out, ob, w, wb)) return Q4K_ERR_INVALID_ARG;
+    return from_hip(q4k::launch_dequant(static_cast<const uint8_t *>(w), out, n, k, static_cast<hipStream_t>(stream)));
+}
+
+const char *q4k_status_string(q4k_status s) {
+    switch (s) {
+        case Q4K_OK: return "ok";
+        case Q4K_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size, overlapping buffers or size overflow)";
+        case Q4K_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (k must be a multiple of 256)";
+        case Q4K_ERR_MISALIGNED: return "misaligned pointer (w needs 16-byte alignment, activations/outputs 4-byte; dequant output 16-byte)";
+        case Q4K_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int q4k_abi_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+"""Python binding of libq4k.so (C ABI in include/q4k.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+HIP stream becomes the ``stream`` argument, and any status other than
+``Q4K_OK`` raises ``Q4KError``.  Every step of the computation runs in the
+library's HIP kernels; there is no CPU path.  The library must have been built
+(``python -m q4_dequant_gemv_amd.build`` or ``__graft_entry__.build()``); if it
+is missing, loading raises instead of falling back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libq4k.so")
+
+BLOCK_BYTES = 144
+BLOCK_WEIGHTS = 256
+
+STATUS = {0: "Q4K_OK", 1: "Q4K_ERR_INVALID_ARG", 2: "Q4K_ERR_UNSUPPORTED_SHAPE", 3: "Q4K_ERR_MISALIGNED",
+          4: "Q4K_ERR_LAUNCH"}
+
+# exported symbols, in the order include/q4k.h declares them
+EXPORTS = ("q4k_gemv", "q4k_gemv_batched", "q4k_fused_swiglu", "q4k_dequant", "q4k_status_string",
+           "q4k_abi_version")
+
+
+class Q4KError(RuntimeError):
+    def __init__(self, status: int, call: str, detail: str):
+        super().__init__(f"{call}: {STATUS.get(status, status)} ({detail})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libq4k.so with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m q4_dequant_gemv_amd.build` first")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.q4k_gemv.argtypes = [p, p, p, i64, i64, p]
+        L.q4k_gemv_batched.argtypes = [p, p, p, i64, i64, i64, p]
+        L.q4k_fused_swiglu.argtypes = [p, p, p, p, i64, i64, p]
+        L.q4k_dequant.argtypes = [p, p, i64, i64, p]
+        for f in (L.q4k_gemv, L.q4k_gemv_batched, L.q4k_fused_swiglu, L.q4k_dequant):
+            f.restype = st
+        L.q4k_status_string.argtypes = [st]
+        L.q4k_status_string.restype = ctypes.c_char_p
+        L.q4k_abi_version.argtypes = []
+        L.q4k_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().q4k_status_string(status).decode()
+
+
+def _check(status: int, call: str) -> None:
+    if status != 0:
+        raise Q4KError(status, call, status_string(status))
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name, dtype):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def rows_of(w, k: int) -> int:
+    if k % BLOCK_WEIGHTS != 0:
+        raise ValueError(f"k={k} is not a multiple of {BLOCK_WEIGHTS}")
+    rb = (k // BLOCK_WEIGHTS) * BLOCK_BYTES
+    if rb == 0:
+        raise ValueError("k must be positive to infer the row count; pass n")
+    if w.numel() % rb != 0:
+        raise ValueError(f"weight tensor of {w.numel()} bytes is not a whole number of {rb}-byte rows")
+    return w.numel() // rb
+
+
+def gemv(w, x, y=None, n: int | None = None, stream=None):
+    """y[r] = sum_c W[r,c] x[c] for a Q4_K matrix ``w`` (uint8) and f32 ``x`` [k]."""
+    import torch
+
+    k = x.numel()
+    n = rows_of(w, k) if n is None else n
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=x.device)
+    _check(lib().q4k_gemv(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float32), _dev(y, "y", torch.float32),
+                          n, k, _stream(stream)), "q4k_gemv")
+    return y
+
+
+def gemv_batched(w, x, y=None, n: int | None = None, stream=None):
+    """y[t, r] = sum_c W[r,c] x[t,c]; ``x`` f32 [m, k] -> ``y`` f32 [m, n]."""
+    import torch
+
+    if x.dim() != 2:
+        raise ValueError("x must be [m, k]")
+    m, k = x.shape
+    n = rows_of(w, k) if n is None else n
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _check(lib().q4k_gemv_batched(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float32),
+                                  _dev(y, "y", torch.float32), m, n, k, _stream(stream)), "q4k_gemv_batched")
+    return y
+
+
+def fused_swiglu(w_gate, w_up, x, h=None, n: int | None = None, stream=None):
+    """h[r] = silu((W_gate x)[r]) * (W_up x)[r]."""
+    import torch
+
+    k = x.numel()
+    n = rows_of(w_gate, k) if n is None else n
+    if h is None:
+        h = torch.empty(n, dtype=torch.float32, device=x.device)
+    _check(lib().q4k_fused_swiglu(_dev(w_gate, "w_gate", torch.uint8), _dev(w_up, "w_up", torch.uint8),
+                                  _dev(x, "x", torch.float32), _dev(h, "h", torch.float32), n, k,
+                                  _stream(stream)), "q4k_fused_swiglu")
+    return h
+
+
+def dequant(w, k: int, out=None, n: int | None = None, stream=None):
+    """W as dense f32 [n, k], bit-exact."""
+    import torch
+
+    n = rows_of(w, k) if n is None else n
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=w.device)
+    _check(lib().q4k_dequant(_dev(w, "w", torch.uint8), _dev(out, "out", torch.float32), n, k, _stream(stream)),
+           "q4k_dequant")
+    return out

@@ -18,3 +18,16 @@ def oracle_mod():
 
     oracle.build(force=False)
     return oracle
+
+
+@pytest.hookimpl(trylast=True)
+def pytest_collection_modifyitems(config, items):
+    gpu_items = [it for it in items if "gpu" in it.keywords]
+    if not gpu_items:
+        return
+    import torch
+
+    if not torch.cuda.is_available():
+        skip = pytest.mark.skip(reason="no GPU visible (run on an MI355X with -m gpu)")
+        for it in gpu_items:
+            it.add_marker(skip)

@@ -1,0 +1,296 @@
+"""GPU parity: every entry point of libq4k.so (called through the C ABI via
+the thin binding) against the CPU oracle on the same seeded inputs.
+
+  * q4k_dequant: bitwise equal to the oracle's f32 dequant.
+  * q4k_gemv / q4k_gemv_batched: every output within 2e-4 * sum_k |w_k x_k|.
+  * q4k_fused_swiglu: within the bound derived from the GEMV bound.
+
+Small shapes are compared whole; the full-size matrices of the Qwen3.5
+shapes (issue #3346) are run whole on the GPU in the same launch
+configuration the benchmark times, and compared on sampled rows that the
+oracle computes one by one.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import THREADS, check_bound, check_swiglu_bound, to_dev, to_host
+from q4_dequant_gemv_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q4k():
+    import torch
+
+    from q4_dequant_gemv_amd import q4k as mod
+
+    torch.cuda.init()
+    mod.lib()
+    oracle.build(force=False)
+    return mod
+
+
+def _sample_rows(n, count, seed):
+    g = np.random.default_rng(seed)
+    edge = np.r_[0:min(n, 64), max(0, n - 64):n]
+    pick = g.choice(n, size=min(n, count), replace=False)
+    return np.unique(np.r_[edge, pick]).astype(np.int64)
+
+
+def _report(name, worst):
+    print(f"[parity] {name}: worst |err|/sum|wx| = {worst:.3e}", flush=True)
+
+
+# ------------------------------------------------------------------ dequant
+@pytest.mark.parametrize("n,k", [(1024, 1024), (4096, 1024), (1024, 2048), (37, 256), (3, 12288), (5, 20480)])
+def test_dequant_bit_exact(q4k, n, k):
+    w = inputs.make_q4k(n, k, config_id=90, tensor_id=k)
+    got = to_host(q4k.dequant(to_dev(w), k))
+    want = oracle.dequant(w, k, threads=THREADS)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_dequant_every_f16_pattern(q4k):
+    """d and dmin take all 65,536 binary16 patterns (subnormals, inf, NaN)."""
+    nb = 65536
+    g = np.random.default_rng(21)
+    qs = g.integers(0, 256, size=(nb, 128), dtype=np.uint8)
+    sc = g.integers(0, 256, size=(nb, 12), dtype=np.uint8)
+    bits = np.arange(nb, dtype=np.uint32).astype(np.uint16)
+    w = inputs.assemble_blocks(qs, sc, bits.view(np.float16), np.roll(bits, 12345).view(np.float16))
+    got = to_host(q4k.dequant(to_dev(w.reshape(-1)), 256))
+    want = oracle.dequant(w.reshape(-1), 256, threads=THREADS)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
+def test_dequant_row_chunks_of_lm_head_0p8b(q4k):
+    """Rows of the 0.8B lm_head (248320 x 1024) through pointer offsets."""
+    import torch
+
+    n, k = inputs.SHAPES["lm_head_0p8b"]
+    w = inputs.make_q4k(n, k, config_id=1, tensor_id=3)
+    wd = to_dev(w.reshape(-1))
+    rb = inputs.row_bytes(k)
+    for r0, cnt in ((0, 512), (123_457, 300), (n - 777, 777)):
+        out = torch.empty((cnt, k), dtype=torch.float32, device="cuda")
+        q4k.dequant(wd[r0 * rb:(r0 + cnt) * rb], k, out=out)
+        want = oracle.dequant(w[r0:r0 + cnt], k, threads=THREADS)
+        np.testing.assert_array_equal(to_host(out).view(np.uint32), want.view(np.uint32))
+
+
+# --------------------------------------------------------------------- gemv
+def _gemv_case(q4k, w, x, rows=None):
+    y = to_host(q4k.gemv(to_dev(w.reshape(-1)), to_dev(x)))
+    if rows is None:
+        yr, ar = oracle.gemv(w, x, threads=THREADS)
+        return y, yr, ar
+    yr, ar = oracle.gemv(w[rows], x, threads=THREADS)
+    return y[rows], yr, ar
+
+
+def test_gemv_square_1k(q4k):
+    """1024 x 1024, seed 0: the small case, compared whole."""
+    n, k = inputs.SHAPES["square_1k"]
+    w = inputs.make_q4k(n, k, config_id=0, tensor_id=0)
+    x = inputs.make_x(1, k, config_id=0)[0]
+    _report("square_1k", check_bound(*_gemv_case(q4k, w, x), "square_1k"))
+
+
+@pytest.mark.parametrize("name,tid", [("q_proj_0p8b", 1), ("out_proj_0p8b", 2)])
+def test_gemv_0p8b_projections(q4k, name, tid):
+    n, k = inputs.SHAPES[name]
+    w = inputs.make_q4k(n, k, config_id=1, tensor_id=tid)
+    x = inputs.make_x(1, k, config_id=1, tensor_id=100 + tid)[0]
+    _report(name, check_bound(*_gemv_case(q4k, w, x), name))
+
+
+@pytest.mark.parametrize("name,cfg,tid", [("lm_head_0p8b", 1, 3), ("lm_head_9b", 3, 0), ("down_9b", 2, 2)])
+def test_gemv_full_size_sampled(q4k, name, cfg, tid):
+    n, k = inputs.SHAPES[name]
+    w = inputs.make_q4k(n, k, config_id=cfg, tensor_id=tid)
+    x = inputs.make_x(1, k, config_id=cfg, tensor_id=100 + tid)[0]
+    rows = _sample_rows(n, 3000, seed=cfg)
+    _report(name, check_bound(*_gemv_case(q4k, w, x, rows), name))
+
+
+@pytest.mark.parametrize("n,k", [(1, 256), (3, 256), (5, 512), (7, 768), (4097, 1024), (33, 2304), (129, 8192),
+                                 (65, 12288), (17, 16384), (9, 20480), (300, 3072)])
+def test_gemv_edge_shapes(q4k, n, k):
+    w = inputs.make_q4k(n, k, config_id=91, tensor_id=k)
+    x = inputs.make_x(1, k, config_id=91, tensor_id=k)[0]
+    _report(f"gemv {n}x{k}", check_bound(*_gemv_case(q4k, w, x), f"gemv {n}x{k}"))
+
+
+def test_gemv_row_subrange_matches_whole(q4k):
+    """A row range passed by pointer offsets gives the same bits as the whole call."""
+    import torch
+
+    n, k = 1000, 4096
+    w = inputs.make_q4k(n, k, config_id=92, tensor_id=0)
+    x = to_dev(inputs.make_x(1, k, config_id=92)[0])
+    wd = to_dev(w.reshape(-1))
+    full = to_host(q4k.gemv(wd, x))
+    rb = inputs.row_bytes(k)
+    part = torch.empty(300, dtype=torch.float32, device="cuda")
+    q4k.gemv(wd[517 * rb:817 * rb], x, y=part)
+    np.testing.assert_array_equal(to_host(part), full[517:817])
+
+
+def test_gemv_special_values(q4k):
+    n, k = 64, 1024
+    x = inputs.make_x(1, k, config_id=93)[0]
+    # all-zero nibbles: every weight is -dmin*m
+    w = inputs.make_q4k(n, k, config_id=93, tensor_id=1).reshape(-1, 144)
+    w[:, 16:] = 0
+    _report("zero codes", check_bound(*_gemv_case(q4k, w.reshape(n, -1), x), "zero codes"))
+    # x == 0 gives exactly 0
+    w = inputs.make_q4k(n, k, config_id=93, tensor_id=2)
+    y = to_host(q4k.gemv(to_dev(w.reshape(-1)), to_dev(np.zeros(k, np.float32))))
+    assert np.all(y == 0)
+    # every weight exactly zero through cancellation: q = 1, sc = m, d = dmin
+    blocks = inputs.make_q4k(n, k, config_id=93, tensor_id=3).reshape(-1, 144).copy()
+    blocks[:, 16:] = 0x11
+    blocks[:, 2:4] = blocks[:, 0:2]
+    from independent_decoder import pack_scales
+
+    rng = np.random.default_rng(5)
+    for b in blocks:
+        v = list(rng.integers(1, 64, 8))
+        b[4:16] = np.frombuffer(pack_scales(v, v), np.uint8)
+    assert np.all(oracle.dequant(blocks.reshape(-1), k) == 0)
+    y = to_host(q4k.gemv(to_dev(blocks.reshape(-1)), to_dev(x)))
+    assert np.all(y == 0)
+    # partial cancellation: a few sub-blocks cancel, the rest do not
+    blocks = inputs.make_q4k(n, k, config_id=93, tensor_id=4).reshape(-1, 144).copy()
+    blocks[::3, 16:48] = 0x11
+    _report("partial cancel", check_bound(*_gemv_case(q4k, blocks.reshape(n, -1), x), "partial cancel"))
+    # activations spanning 16 binades (outlier channels), and tiny / huge scales
+    xs = (x * np.exp2(np.random.default_rng(6).integers(-8, 9, k))).astype(np.float32)
+    _report("wide x", check_bound(*_gemv_case(q4k, w, xs), "wide x"))
+    for s in (1e-30, 1e25):
+        xs = (x * np.float32(s)).astype(np.float32)
+        _report(f"x*{s}", check_bound(*_gemv_case(q4k, w, xs), f"x*{s}"))
+    # weights with arbitrary finite f16 d, dmin (subnormals included)
+    wb = inputs.make_q4k(n, k, config_id=93, tensor_id=5).reshape(-1, 144).copy()
+    bits = np.random.default_rng(7).integers(0, 0x7800, size=(wb.shape[0], 2), dtype=np.uint16)
+    wb[:, 0:4] = bits.view(np.uint8).reshape(-1, 4)
+    _report("f16 range", check_bound(*_gemv_case(q4k, wb.reshape(n, -1), x), "f16 range"))
+    # a non-finite activation poisons every output (each row reads all of x)
+    xn = x.copy()
+    xn[77] = np.nan
+    y = to_host(q4k.gemv(to_dev(w.reshape(-1)), to_dev(xn)))
+    assert np.all(np.isnan(y))
+
+
+def test_gemv_k_zero_writes_zeros(q4k):
+    import torch
+
+    y = torch.full((10,), 5.0, device="cuda")
+    q4k.gemv(torch.empty(0, dtype=torch.uint8, device="cuda"), torch.empty(0, device="cuda"), y=y, n=10)
+    assert np.all(to_host(y) == 0)
+
+
+def test_gemv_on_side_stream_and_deterministic(q4k):
+    import torch
+
+    n, k = 2048, 4096
+    w = to_dev(inputs.make_q4k(n, k, config_id=94, tensor_id=0).reshape(-1))
+    x = to_dev(inputs.make_x(1, k, config_id=94)[0])
+    base = to_host(q4k.gemv(w, x))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        again = q4k.gemv(w, x)
+    s.synchronize()
+    np.testing.assert_array_equal(to_host(again), base)
+    for _ in range(3):
+        np.testing.assert_array_equal(to_host(q4k.gemv(w, x)), base)
+
+
+# ------------------------------------------------------------------- swiglu
+def test_swiglu_ffn_9b(q4k):
+    """Gate and up of the 9B FFN (12288 x 4096 each), whole on the GPU."""
+    n, k = inputs.SHAPES["gate_9b"]
+    wg = inputs.make_q4k(n, k, config_id=2, tensor_id=0)
+    wu = inputs.make_q4k(n, k, config_id=2, tensor_id=1)
+    x = inputs.make_x(1, k, config_id=2, tensor_id=100)[0]
+    h = to_host(q4k.fused_swiglu(to_dev(wg.reshape(-1)), to_dev(wu.reshape(-1)), to_dev(x)))
+    rows = _sample_rows(n, 4000, seed=2)
+    ref = oracle.fused_swiglu(wg[rows], wu[rows], x, threads=THREADS)
+    _report("swiglu 9b", check_swiglu_bound(h[rows], ref, "swiglu 9b"))
+
+
+@pytest.mark.parametrize("n,k", [(1, 256), (77, 1024), (300, 2048), (65, 12288), (9, 16384)])
+def test_swiglu_shapes(q4k, n, k):
+    wg = inputs.make_q4k(n, k, config_id=95, tensor_id=2 * k)
+    wu = inputs.make_q4k(n, k, config_id=95, tensor_id=2 * k + 1)
+    x = inputs.make_x(1, k, config_id=95, tensor_id=k)[0]
+    h = to_host(q4k.fused_swiglu(to_dev(wg.reshape(-1)), to_dev(wu.reshape(-1)), to_dev(x)))
+    ref = oracle.fused_swiglu(wg, wu, x, threads=THREADS)
+    _report(f"swiglu {n}x{k}", check_swiglu_bound(h, ref, f"swiglu {n}x{k}"))
+
+
+# ------------------------------------------------------------------ batched
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 15, 16, 17, 31, 32, 33, 48, 63, 64, 65, 100])
+def test_batched_small(q4k, m):
+    n, k = 200, 2048
+    w = inputs.make_q4k(n, k, config_id=96, tensor_id=0)
+    xs = inputs.make_x(m, k, config_id=96, tensor_id=m)
+    y = to_host(q4k.gemv_batched(to_dev(w.reshape(-1)), to_dev(xs)))
+    yr, ar = oracle.gemv_batched(w, xs, threads=THREADS)
+    _report(f"batched m={m}", check_bound(y, yr, ar, f"batched m={m} {n}x{k}"))
+
+
+@pytest.mark.parametrize("m,n,k", [(4, 70, 12288), (16, 70, 12288), (64, 70, 12288), (3, 10, 256), (20, 10, 256),
+                                   (7, 129, 20480), (40, 129, 1280)])
+def test_batched_shapes(q4k, m, n, k):
+    w = inputs.make_q4k(n, k, config_id=97, tensor_id=k)
+    xs = inputs.make_x(m, k, config_id=97, tensor_id=m)
+    y = to_host(q4k.gemv_batched(to_dev(w.reshape(-1)), to_dev(xs)))
+    yr, ar = oracle.gemv_batched(w, xs, threads=THREADS)
+    _report(f"batched m={m} {n}x{k}", check_bound(y, yr, ar, f"batched m={m} {n}x{k}"))
+
+
+@pytest.mark.parametrize("name,tid", [("gate_9b", 0), ("down_9b", 2)])
+@pytest.mark.parametrize("m", [1, 4, 16, 32, 64])
+def test_batched_ffn_9b_sampled(q4k, name, tid, m):
+    n, k = inputs.SHAPES[name]
+    w = inputs.make_q4k(n, k, config_id=4, tensor_id=tid)
+    xs = inputs.make_x(m, k, config_id=4, tensor_id=100 + m)
+    y = to_host(q4k.gemv_batched(to_dev(w.reshape(-1)), to_dev(xs)))
+    rows = _sample_rows(n, 600, seed=m)
+    yr, ar = oracle.gemv_batched(w[rows], xs, threads=THREADS)
+    _report(f"batched 9b {name} m={m}", check_bound(y[:, rows], yr, ar, f"batched {name} m={m}"))
+
+
+def test_batched_special_values(q4k):
+    n, k = 64, 1024
+    w = inputs.make_q4k(n, k, config_id=98, tensor_id=0)
+    for m in (4, 16):
+        xs = inputs.make_x(m, k, config_id=98, tensor_id=m)
+        xs[1] = 0.0
+        xs[2] *= np.float32(1e-30)
+        xs[3] = (xs[3] * np.exp2(np.random.default_rng(m).integers(-8, 9, k))).astype(np.float32)
+        y = to_host(q4k.gemv_batched(to_dev(w.reshape(-1)), to_dev(xs)))
+        assert np.all(y[1] == 0)
+        yr, ar = oracle.gemv_batched(w, xs, threads=THREADS)
+        _report(f"batched special m={m}", check_bound(y, yr, ar, f"batched special m={m}"))
+        xs[0, 5] = np.inf
+        y = to_host(q4k.gemv_batched(to_dev(w.reshape(-1)), to_dev(xs)))
+        assert np.all(np.isnan(y[0])) and np.all(np.isfinite(y[1:]))
+
+
+def test_batched_deterministic(q4k):
+    n, k = 512, 4096
+    w = to_dev(inputs.make_q4k(n, k, config_id=99, tensor_id=0).reshape(-1))
+    for m in (4, 32):
+        xs = to_dev(inputs.make_x(m, k, config_id=99, tensor_id=m))
+        a = to_host(q4k.gemv_batched(w, xs))
+        b = to_host(q4k.gemv_batched(w, xs))
+        np.testing.assert_array_equal(a, b)
