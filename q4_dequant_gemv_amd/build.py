@@ -2,6 +2,7 @@
 
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -22,23 +23,26 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source (in parallel) and link libq4k.so in place."""
-    objdir = os.path.join(HERE, "_build")
+def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
+    """Compile every source (in parallel) and link libq4k.so in place.
+
+    ``out`` and ``extra_flags`` (e.g. -D launch-shape macros) let a variant be
+    built next to the default library for comparison."""
+    objdir = os.path.join(HERE, "_build", hashlib.sha1(" ".join(extra_flags).encode()).hexdigest()[:8])
     os.makedirs(objdir, exist_ok=True)
     procs = []
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = ["hipcc", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ["hipcc", *FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     failed = []
     for src, p in procs:
-        out, _ = p.communicate()
-        text = out.decode(errors="replace")
+        log, _ = p.communicate()
+        text = log.decode(errors="replace")
         # the host pass does not know the device-only feature flag
         lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln]
         if lines:
@@ -47,10 +51,10 @@ def build(verbose: bool = False) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     subprocess.check_call(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

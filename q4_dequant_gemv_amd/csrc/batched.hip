@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void batched_valu_kernel(const uint8_t *__rest
                 const uint4 qa = load_stream16(blk + 16 + 32 * grp);
                 const uint4 qb = load_stream16(blk + 32 + 32 * grp);
                 GroupCodes c;
-                decode_group(hdr, qa, qb, grp, c);
+                decode_group(hdr, qa, qb, pair_select(grp), c);
 #pragma unroll
                 for (int t = 0; t < M; ++t) acc[p][t] += xg[t][sub].scale * group_dot(c, xg[t][sub]);
             }

@@ -44,75 +44,153 @@
 
 namespace q4k {
 
-// LPR lanes per row (power of two, <= 64), G groups per lane; SWIGLU reads a
-// second matrix `wu` of the same shape and writes silu(W x) * (Wu x).
-template <int LPR, int G, bool SWIGLU, int BLOCK, int MIN_WAVES>
+// One iteration's weight bytes for one lane: per matrix and per owned group,
+// the super-block header and the group's 32 code bytes.
+template <int G, int NMAT>
+struct RowLoads {
+    uint4 hdr[NMAT][G];
+    uint4 qa[NMAT][G];
+    uint4 qb[NMAT][G];
+};
+
+// LPR lanes per row (power of two, <= 64), G groups per lane.  SWIGLU reads a
+// second matrix `wu` of the same shape and writes silu(W x) * (Wu x).  XREG
+// keeps the lane's activation limbs in registers for the whole kernel (G == 1);
+// otherwise they are re-read from LDS for every row.
+//
+// Each wave walks its rows with two register buffers: the loads of the next
+// row are in flight while the current row is decoded, multiplied and reduced,
+// and the first row's loads are issued before the activations are prepared.
+template <int LPR, int G, bool SWIGLU, bool XREG, int BLOCK, int MIN_WAVES>
 __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const uint8_t *__restrict__ w,
-                                                                const uint8_t *__restrict__ wu,
-                                                                const float *__restrict__ x, float *__restrict__ y,
-                                                                int64_t n, int ngroups, int64_t row_bytes) {
+                                                                const uint8_t *__restrict__ wu, const float *x,
+                                                                float *__restrict__ y, int64_t n, int ngroups,
+                                                                int64_t row_bytes) {
     static_assert(G == 1 || LPR == 64, "several groups per lane only with a full wave per row");
+    static_assert(!XREG || G == 1, "activation limbs held in registers for one group per lane");
+    constexpr int NMAT = SWIGLU ? 2 : 1;
     constexpr int kRowsPerWave = kWave / LPR;
     constexpr int kWavesPerBlock = BLOCK / kWave;
     extern __shared__ __align__(16) unsigned char smem[];
     XGroup *xg = reinterpret_cast<XGroup *>(smem);
 
-    prepare_x<BLOCK>(x, ngroups, xg);
-    __syncthreads();
-
     const int lane = threadIdx.x & (kWave - 1);
     const int sub = lane % LPR;
     const int slot = lane / LPR;
-
-    XRegs xr[G];
-    int grp[G];
-    int boff[G];
+    // Byte offsets of this lane's loads inside one wave iteration (rows
+    // it*kRowsPerWave .. +kRowsPerWave-1), fixed for the whole kernel.  The
+    // iteration's base address is wave-uniform (scalar registers), so the loop
+    // rewrites no per-lane address registers while earlier loads are in flight.
+    // Lanes past the row's last group (K/64 not a power of two) load group 0
+    // again and ignore it.
+    uint32_t off_hdr[G], off_qa[G];
+    PairSelect psel[G];
     bool gok[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const int j = sub + LPR * g;
         gok[g] = j < ngroups;
-        load_xregs(xg[gok[g] ? j : 0], xr[g]);
-        grp[g] = j & 3;
-        boff[g] = (j >> 2) * kBlockBytes;
+        const int jj = gok[g] ? j : 0;
+        psel[g] = pair_select(jj & 3);
+        off_hdr[g] = static_cast<uint32_t>(slot * row_bytes + (jj >> 2) * kBlockBytes);
+        off_qa[g] = off_hdr[g] + 16u + 32u * static_cast<uint32_t>(jj & 3);
     }
+    const uint8_t *mats[2] = {w, wu};
+    // Loop control is 32-bit and scalar (the host keeps the iteration count
+    // below 2^31): gfx9 has no 64-bit scalar compare, and a vector compare in
+    // the loop would borrow registers that earlier memory operations still own.
+    const int iter_bytes = kRowsPerWave * static_cast<int>(row_bytes);
+    const int niters = static_cast<int>((n + kRowsPerWave - 1) / kRowsPerWave);
+    const int tail_bytes = static_cast<int>(n - static_cast<int64_t>(niters - 1) * kRowsPerWave) *
+                           static_cast<int>(row_bytes);
 
-    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
-    const int64_t niters = (n + kRowsPerWave - 1) / kRowsPerWave;
-    for (int64_t it = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6); it < niters;
-         it += nwaves) {
-        const int64_t row = it * kRowsPerWave + slot;
-        const bool rok = row < n;
-        float acc = 0.0f, accu = 0.0f;
+    // Loads of one iteration: unconditional, from a descriptor based at the
+    // iteration's first row; rows past n read as zeros and are not stored.
+    auto issue = [&](auto &b, int it) {
+        const int64_t base = static_cast<int64_t>(it) * iter_bytes;
+        const int left = niters - it;
+        const int nrec = left > 1 ? iter_bytes : (left == 1 ? tail_bytes : 0);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (rok && gok[g]) {
-                const uint8_t *blk = w + row * row_bytes + boff[g];
-                const uint4 hdr = load_stream16(blk);
-                const uint4 qa = load_stream16(blk + 16 + 32 * grp[g]);
-                const uint4 qb = load_stream16(blk + 32 + 32 * grp[g]);
-                GroupCodes c;
-                decode_group(hdr, qa, qb, grp[g], c);
-                acc += xr[g].scale * group_dot(c, xr[g]);
-                if constexpr (SWIGLU) {
-                    const uint8_t *blku = wu + row * row_bytes + boff[g];
-                    const uint4 hdru = load_stream16(blku);
-                    const uint4 qau = load_stream16(blku + 16 + 32 * grp[g]);
-                    const uint4 qbu = load_stream16(blku + 32 + 32 * grp[g]);
-                    GroupCodes cu;
-                    decode_group(hdru, qau, qbu, grp[g], cu);
-                    accu += xr[g].scale * group_dot(cu, xr[g]);
-                }
+        for (int mt = 0; mt < NMAT; ++mt) {
+            const __amdgpu_buffer_rsrc_t r = stream_rsrc(mats[mt] + base, nrec);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                b.hdr[mt][g] = buffer_load16(r, off_hdr[g]);
+                b.qa[mt][g] = buffer_load16(r, off_qa[g]);
+                b.qb[mt][g] = buffer_load16(r, off_qa[g] + 16u);
             }
         }
-        acc = group_sum<LPR>(acc);
-        if constexpr (SWIGLU) accu = group_sum<LPR>(accu);
+    };
+
+    const int nwaves = static_cast<int>(gridDim.x) * kWavesPerBlock;
+    const int it0 = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWavesPerBlock +
+                                                   static_cast<int>(threadIdx.x >> 6));
+
+    // activations first, then the first row's weights: waiting for the
+    // activations (in issue order) then leaves the weight loads in flight
+    constexpr int kXChunks = (64 * G * 16 + BLOCK - 1) / BLOCK;
+    const XLoaded<kXChunks> xl = load_x<BLOCK, kXChunks>(x, ngroups);
+    // keep the activation loads ahead of the weight loads (an empty asm with a
+    // memory clobber: no instruction, only an ordering point for the compiler;
+    // x is deliberately not __restrict__ so its loads cannot move across it)
+    asm volatile("" ::: "memory");
+    RowLoads<G, NMAT> bufa;
+    RowLoads<G, XREG ? NMAT : 1> bufb;
+    issue(bufa, it0);
+
+    prepare_x<BLOCK, kXChunks>(xl, ngroups, xg);
+    __syncthreads();
+
+    XRegs xr[XREG ? 1 : 1];
+    if constexpr (XREG) load_xregs(xg[gok[0] ? sub : 0], xr[0]);
+
+    auto process = [&](const auto &b, int it) {
+        const int64_t row = static_cast<int64_t>(it) * kRowsPerWave + slot;
+        const bool rok = row < n;
+        float acc[NMAT];
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt) {
+            acc[mt] = 0.0f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (rok && gok[g]) {
+                    GroupCodes c;
+                    decode_group(b.hdr[mt][g], b.qa[mt][g], b.qb[mt][g], psel[g], c);
+                    if constexpr (XREG) {
+                        acc[mt] += xr[0].scale * group_dot(c, xr[0]);
+                    } else {
+                        const XGroup &xs = xg[sub + LPR * g];
+                        acc[mt] += xs.scale * group_dot(c, xs);
+                    }
+                }
+            }
+            acc[mt] = lane_group_sum<LPR>(acc[mt]);
+        }
         if (sub == 0 && rok) {
             if constexpr (SWIGLU) {
-                y[row] = silu(acc) * accu;
+                y[row] = silu(acc[0]) * acc[1];
             } else {
-                y[row] = acc;
+                y[row] = acc[0];
             }
+        }
+    };
+
+    // The loads are never inside a branch: at a control-flow join the wait
+    // counters would have to assume the fewest loads in flight and drain the
+    // prefetch.  Iterations past the end load nothing (0-byte descriptor).
+    if constexpr (XREG) {
+        for (int it = it0; it < niters; it += 2 * nwaves) {
+            issue(bufb, it + nwaves);
+            process(bufa, it);
+            if (it + nwaves >= niters) break;
+            issue(bufa, it + 2 * nwaves);
+            process(bufb, it + nwaves);
+        }
+    } else {
+        // G groups per lane already put G*48 bytes per lane in flight per row
+        for (int it = it0; it < niters; it += nwaves) {
+            if (it != it0) issue(bufa, it);
+            process(bufa, it);
         }
     }
 }
@@ -174,22 +252,20 @@ int resident_blocks_per_cu(Kernel kern, int block, size_t lds, std::atomic<int> 
     return nb;
 }
 
-template <int LPR, int G, bool SWIGLU>
+template <int LPR, int G, bool SWIGLU, bool XREG, int BLOCK, int MIN_WAVES>
 hipError_t launch_fast(const uint8_t *w, const uint8_t *wu, const float *x, float *y, int64_t n, int64_t k,
                        hipStream_t stream) {
-    constexpr int kBlock = (G == 1) ? 512 : 256;
-    constexpr int kMinWaves = (G == 1) ? 4 : 2;
-    auto kern = gemv_kernel<LPR, G, SWIGLU, kBlock, kMinWaves>;
+    auto kern = gemv_kernel<LPR, G, SWIGLU, XREG, BLOCK, MIN_WAVES>;
     const int ngroups = static_cast<int>(k / 64);
     const size_t lds = static_cast<size_t>(ngroups) * sizeof(XGroup);
     static std::atomic<int> cache[kMaxDevices];
-    const int per_cu = resident_blocks_per_cu(kern, kBlock, lds, cache);
+    const int per_cu = resident_blocks_per_cu(kern, BLOCK, lds, cache);
     constexpr int kRowsPerWave = kWave / LPR;
     const int64_t niters = (n + kRowsPerWave - 1) / kRowsPerWave;
-    const int64_t need = (niters + kBlock / kWave - 1) / (kBlock / kWave);
+    const int64_t need = (niters + BLOCK / kWave - 1) / (BLOCK / kWave);
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
     const int grid = static_cast<int>(need < cap ? need : cap);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), lds, stream, w, wu, x, y, n, ngroups,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, w, wu, x, y, n, ngroups,
                        (k / kBlockWeights) * kBlockBytes);
     return hipGetLastError();
 }
@@ -205,18 +281,70 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const float *x, f
     return hipGetLastError();
 }
 
+// Launch shapes: threads per block and minimum resident waves per SIMD (the
+// register budget).  Streams of several MB run best as one 1024-thread block
+// per CU (4 waves per SIMD; more resident waves measured slower); small
+// matrices, which finish in a few microseconds, start faster with 256-thread
+// blocks (less activation preparation per block, more blocks).
+#ifndef Q4K_LARGE_BLOCK
+#define Q4K_LARGE_BLOCK 1024
+#endif
+#ifndef Q4K_LARGE_MINW
+#define Q4K_LARGE_MINW 4
+#endif
+#ifndef Q4K_SMALL_BLOCK
+#define Q4K_SMALL_BLOCK 256
+#endif
+#ifndef Q4K_SMALL_MINW
+#define Q4K_SMALL_MINW 3
+#endif
+#ifndef Q4K_SWIGLU_BLOCK
+#define Q4K_SWIGLU_BLOCK 512
+#endif
+#ifndef Q4K_SWIGLU_MINW
+#define Q4K_SWIGLU_MINW 2
+#endif
+#ifndef Q4K_BIGK_BLOCK
+#define Q4K_BIGK_BLOCK 1024
+#endif
+#ifndef Q4K_BIGK_MINW
+#define Q4K_BIGK_MINW 4
+#endif
+// matrices below this many bytes use the small launch shape
+#ifndef Q4K_SMALL_BYTES
+#define Q4K_SMALL_BYTES (8 << 20)
+#endif
+
+template <int LPR, bool SWIGLU>
+hipError_t dispatch_regx(const uint8_t *w, const uint8_t *wu, const float *x, float *y, int64_t n, int64_t k,
+                         hipStream_t stream) {
+    if constexpr (SWIGLU) {
+        return launch_fast<LPR, 1, true, true, Q4K_SWIGLU_BLOCK, Q4K_SWIGLU_MINW>(w, wu, x, y, n, k, stream);
+    } else {
+        const int64_t bytes = n * (k / kBlockWeights) * kBlockBytes;
+        if (bytes < Q4K_SMALL_BYTES) {
+            return launch_fast<LPR, 1, false, true, Q4K_SMALL_BLOCK, Q4K_SMALL_MINW>(w, wu, x, y, n, k, stream);
+        }
+        return launch_fast<LPR, 1, false, true, Q4K_LARGE_BLOCK, Q4K_LARGE_MINW>(w, wu, x, y, n, k, stream);
+    }
+}
+
 template <bool SWIGLU>
 hipError_t dispatch(const uint8_t *w, const uint8_t *wu, const float *x, float *y, int64_t n, int64_t k,
                     hipStream_t stream) {
     const int64_t ngroups = k / 64;
-    if (ngroups <= 4) return launch_fast<4, 1, SWIGLU>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 8) return launch_fast<8, 1, SWIGLU>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 16) return launch_fast<16, 1, SWIGLU>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 32) return launch_fast<32, 1, SWIGLU>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 64) return launch_fast<64, 1, SWIGLU>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 128) return launch_fast<64, 2, SWIGLU>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 192) return launch_fast<64, 3, SWIGLU>(w, wu, x, y, n, k, stream);
-    // beyond K = 12288 the per-lane activations no longer fit in registers
+    if (ngroups <= 4) return dispatch_regx<4, SWIGLU>(w, wu, x, y, n, k, stream);
+    if (ngroups <= 8) return dispatch_regx<8, SWIGLU>(w, wu, x, y, n, k, stream);
+    if (ngroups <= 16) return dispatch_regx<16, SWIGLU>(w, wu, x, y, n, k, stream);
+    if (ngroups <= 32) return dispatch_regx<32, SWIGLU>(w, wu, x, y, n, k, stream);
+    if (ngroups <= 64) return dispatch_regx<64, SWIGLU>(w, wu, x, y, n, k, stream);
+    // two matrices' row buffers need twice the registers
+    constexpr int BB = Q4K_BIGK_BLOCK;
+    constexpr int BMW = SWIGLU ? 2 : Q4K_BIGK_MINW;
+    constexpr int BBS = SWIGLU ? (BB > 512 ? 512 : BB) : BB;
+    if (ngroups <= 128) return launch_fast<64, 2, SWIGLU, false, BBS, BMW>(w, wu, x, y, n, k, stream);
+    if (ngroups <= 192) return launch_fast<64, 3, SWIGLU, false, BBS, BMW>(w, wu, x, y, n, k, stream);
+    // beyond K = 12288 the per-row register buffers no longer fit
     return launch_generic<SWIGLU>(w, wu, x, y, n, k, stream);
 }
 

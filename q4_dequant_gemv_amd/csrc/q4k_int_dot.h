@@ -35,19 +35,49 @@ static_assert(sizeof(XGroup) == 208, "XGroup layout");
 // Converts x[0 .. 64*ngroups) into XGroups, 16 threads per group, 4
 // activations per thread.  BLOCK is a multiple of 64, so the 16 threads of a
 // group are 16 aligned lanes of one wave and are either all active or all not.
-template <int BLOCK>
-__device__ __forceinline__ void prepare_x(const float *__restrict__ x, int ngroups, XGroup *__restrict__ xg) {
+// Converts x[0 .. 64*ngroups) into XGroups, 16 threads per group, 4
+// activations per thread.  BLOCK is a multiple of 64, so the 16 threads of a
+// group are 16 aligned lanes of one wave and are either all active or all not.
+// The activations are loaded first (load_x) so that a kernel can issue them
+// ahead of its weight loads: waits are counted in issue order, so waiting for
+// the activations then leaves the weight loads in flight.  NCH covers
+// ngroups*16 <= NCH*BLOCK.
+template <int NCH>
+struct XLoaded {
+    float v[NCH][4];
+};
+
+template <int BLOCK, int NCH>
+__device__ __forceinline__ XLoaded<NCH> load_x(const float *x, int ngroups) {
+    XLoaded<NCH> f;
     const int total = ngroups * 16;
-    for (int it = threadIdx.x; it < total; it += BLOCK) {
+    // every load is issued (items past the end re-read item 0) so that no
+    // load sits in a branch; the unused values are dropped afterwards
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int it = static_cast<int>(threadIdx.x) + c * BLOCK;
+        const float *p = x + 4 * (it < total ? it : 0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) f.v[c][b] = p[b];
+    }
+    return f;
+}
+
+template <int BLOCK, int NCH>
+__device__ __forceinline__ void prepare_x(const XLoaded<NCH> &f, int ngroups, XGroup *__restrict__ xg) {
+    const int total = ngroups * 16;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int it = static_cast<int>(threadIdx.x) + c * BLOCK;
+        if (it >= total) break;
         const int j = it >> 4;
         const int half = (it >> 3) & 1;
         const int i = it & 7;
-        const float *p = x + 64 * j + 32 * half + 4 * i;
         float v[4];
         float amax = 0.0f;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            v[b] = p[b];
+            v[b] = f.v[c][b];
             float a = fabsf(v[b]);
             a = (a <= FLT_MAX) ? a : INFINITY;  // NaN counts as non-finite
             amax = fmaxf(amax, a);
@@ -87,6 +117,16 @@ __device__ __forceinline__ void prepare_x(const float *__restrict__ x, int ngrou
     }
 }
 
+// The general form for any number of groups (loads inside the loop).
+template <int BLOCK>
+__device__ __forceinline__ void prepare_x(const float *__restrict__ x, int ngroups, XGroup *__restrict__ xg) {
+    const int total = ngroups * 16;
+    for (int base = 0; base < total; base += BLOCK) {
+        const XLoaded<1> f = load_x<BLOCK, 1>(x + 4 * base, (total - base + 15) / 16);
+        prepare_x<BLOCK, 1>(f, (total - base + 15) / 16, xg + base / 16);
+    }
+}
+
 // Per-lane register copy of one XGroup.
 struct XRegs {
     uint32_t limb[2][3][8];
@@ -115,17 +155,16 @@ struct GroupCodes {
     float dl0, ml0, dl1, ml1;
 };
 
-__device__ __forceinline__ void decode_group(const uint4 &hdr, const uint4 &qa, const uint4 &qb, int grp,
-                                             GroupCodes &c) {
+__device__ __forceinline__ void decode_group(const uint4 &hdr, const uint4 &qa, const uint4 &qb,
+                                             const PairSelect &ps, GroupCodes &c) {
     const float d = half_bits_to_float(hdr.x);
     const float dmin = half_bits_to_float(hdr.x >> 16);
-    int sc0, m0, sc1, m1;
-    scale_min(hdr.y, hdr.z, hdr.w, 2 * grp, sc0, m0);
-    scale_min(hdr.y, hdr.z, hdr.w, 2 * grp + 1, sc1, m1);
-    c.dl0 = d * static_cast<float>(sc0);
-    c.ml0 = dmin * static_cast<float>(m0);
-    c.dl1 = d * static_cast<float>(sc1);
-    c.ml1 = dmin * static_cast<float>(m1);
+    uint32_t scp, mp;
+    scale_min_pair(hdr.y, hdr.z, hdr.w, ps, scp, mp);
+    c.dl0 = d * static_cast<float>(scp & 0xffu);
+    c.ml0 = dmin * static_cast<float>(mp & 0xffu);
+    c.dl1 = d * static_cast<float>((scp >> 8) & 0xffu);
+    c.ml1 = dmin * static_cast<float>((mp >> 8) & 0xffu);
     const uint32_t q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
