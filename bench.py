@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--sweep", action="store_true",
                     help="also time every kernel at every config shape (table on stderr)")
+    ap.add_argument("--case", default=None,
+                    help="only run one kernel in a loop, for profilers: gemv:NAME, swiglu:NAME, "
+                         "dequant:NAME or batched:M:NAME with NAME a shape of inputs.SHAPES")
     return ap.parse_args()
 
 
@@ -86,6 +89,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     q4k.lib()
+    if args.case:
+        run_case(args.case, args.steps, args.warmup, q4k, inputs, torch, np, dev)
+        return
 
     log("[bench] generating inputs")
     shapes = {nm: inputs.SHAPES[nm] for nm in ("gate_9b", "up_9b", "down_9b", "lm_head_9b")}
@@ -226,6 +232,46 @@ def time_call(fn, torch, reps=50, warm=5):
     import numpy as np
 
     return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e-3
+
+
+def run_case(case, steps, warmup, q4k, inputs, torch, np, dev):
+    """One kernel at one shape, rotated over >= 512 MiB of weight copies."""
+    parts = case.split(":")
+    kind, name = parts[0], parts[-1]
+    m = int(parts[1]) if kind == "batched" else 1
+    n, k = inputs.SHAPES[name]
+    w0 = inputs.make_q4k(n, k, config_id=7, tensor_id=1).reshape(-1)
+    mats = 2 if kind == "swiglu" else 1
+    copies = max(1, -(-(512 << 20) // (mats * w0.nbytes)))
+    ws = [torch.from_numpy(w0).to(dev) for _ in range(copies * mats)]
+    xs = torch.from_numpy(inputs.make_x(m, k, config_id=7)).to(dev)
+    out = torch.empty((n, k) if kind == "dequant" else (m, n), dtype=torch.float32, device=dev)
+
+    def call(i):
+        c = i % copies
+        if kind == "gemv":
+            q4k.gemv(ws[c], xs[0], y=out[0])
+        elif kind == "swiglu":
+            q4k.fused_swiglu(ws[2 * c], ws[2 * c + 1], xs[0], h=out[0])
+        elif kind == "batched":
+            q4k.gemv_batched(ws[c], xs, y=out)
+        elif kind == "dequant":
+            q4k.dequant(ws[c], k, out=out)
+        else:
+            raise SystemExit(f"unknown case kind {kind}")
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        call(i)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / steps * 1e-3
+    nbytes = mats * w0.nbytes + (out.numel() * 4 if kind == "dequant" else 0)
+    log(f"[case] {case}: {t * 1e6:.2f} us per call (host-enqueued back to back), {nbytes / t / 1e9:.1f} GB/s")
 
 
 def sweep(q4k, inputs, torch, np, dev):

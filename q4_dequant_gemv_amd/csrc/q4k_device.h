@@ -183,4 +183,30 @@ __device__ __forceinline__ float lane_group_sum(float v) {
     return v;
 }
 
+// Maximum over aligned groups of W lanes (same lane pairings as lane_group_sum).
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+    const int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true);
+    return fmaxf(__builtin_bit_cast(float, moved), v);
+}
+
+__device__ __forceinline__ float swap16_max(float v) {
+    const unsigned u = __float_as_uint(v);
+    const auto s = __builtin_amdgcn_permlane16_swap(u, opaque_copy(u), false, false);
+    const unsigned r0 = s[0];
+    const unsigned r1 = opaque_copy(s[1]);
+    return fmaxf(__uint_as_float(r0), __uint_as_float(r1));
+}
+
+template <int W>
+__device__ __forceinline__ float lane_group_max(float v) {
+    static_assert(W == 4 || W == 8 || W == 16 || W == 32, "group width");
+    if constexpr (W >= 32) v = swap16_max(v);
+    v = dpp_max<0xb1>(v);
+    v = dpp_max<0x4e>(v);
+    if constexpr (W >= 8) v = dpp_max<0x141>(v);
+    if constexpr (W >= 16) v = dpp_max<0x140>(v);
+    return v;
+}
+
 }  // namespace q4k

@@ -286,11 +286,21 @@ def test_batched_special_values(q4k):
         assert np.all(np.isnan(y[0])) and np.all(np.isfinite(y[1:]))
 
 
-def test_batched_deterministic(q4k):
+def test_batched_run_to_run(q4k):
+    """m < 16 is bitwise reproducible; m >= 16 adds K slices with f32 atomics,
+    so the summation order (and the last bits) may change between runs while
+    every run stays inside the bound."""
     n, k = 512, 4096
-    w = to_dev(inputs.make_q4k(n, k, config_id=99, tensor_id=0).reshape(-1))
+    wh = inputs.make_q4k(n, k, config_id=99, tensor_id=0)
+    w = to_dev(wh.reshape(-1))
     for m in (4, 32):
-        xs = to_dev(inputs.make_x(m, k, config_id=99, tensor_id=m))
+        xh = inputs.make_x(m, k, config_id=99, tensor_id=m)
+        xs = to_dev(xh)
         a = to_host(q4k.gemv_batched(w, xs))
         b = to_host(q4k.gemv_batched(w, xs))
-        np.testing.assert_array_equal(a, b)
+        if m < 16:
+            np.testing.assert_array_equal(a, b)
+        else:
+            yr, ar = oracle.gemv_batched(wh, xh, threads=THREADS)
+            check_bound(a, yr, ar, f"run 1 m={m}")
+            check_bound(b, yr, ar, f"run 2 m={m}")
