@@ -235,7 +235,24 @@ def time_call(fn, torch, reps=50, warm=5):
 
 
 def run_case(case, steps, warmup, q4k, inputs, torch, np, dev):
-    """One kernel at one shape, rotated over >= 512 MiB of weight copies."""
+    """One kernel at one shape, rotated over >= 512 MiB of weight copies.
+    `copy` instead runs a plain 512 MiB device-to-device copy (the reference
+    kernel that calibrates the profiler's byte counters)."""
+    if case == "copy":
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) / steps * 1e-3
+        log(f"[case] copy 512 MiB: {t * 1e6:.1f} us per copy, {2 * src.numel() / t / 1e9:.1f} GB/s read+write")
+        return
     parts = case.split(":")
     kind, name = parts[0], parts[-1]
     m = int(parts[1]) if kind == "batched" else 1
