@@ -10,9 +10,10 @@ One step is one pass of the decode hot path over resident weights:
 every step streams its weights from HBM).  Inputs are seeded synthetic data of
 the pages' value distributions (q4_dequant_gemv_amd/inputs.py).
 
-Prints ONE JSON line.  `roofline` covers the dominant kernel (the lm_head
-GEMV): algorithmic bytes per launch / mean launch time, both from HIP events
-recorded on the launch stream over the timed region.  `traffic` comes from the
+Prints ONE JSON line.  `value` is step weight bytes / mean step time over K
+steps bracketed by HIP events on the launch stream.  `roofline` covers the
+dominant kernel (the lm_head GEMV): algorithmic bytes per launch / mean launch
+time over K back-to-back launches, again between events on the launch stream.  `traffic` comes from the
 committed rocprofv3 counter summary (profiles/traffic_lm_head_9b.json) when it
 was taken from the kernel sources as they are now, else null.  `cpu_baseline`
 times the CPU oracle on one full step.
@@ -111,61 +112,92 @@ def main():
     step_weight_bytes = sum(wbytes.values())
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
         q4k.fused_swiglu(W["gate_9b"], W["up_9b"], x, h=h, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
         q4k.gemv(W["down_9b"], h, y=y, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
         q4k.gemv(W["lm_head_9b"], y, y=logits, stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
 
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
+    # Timed region 1: K whole steps, bracketed by two events on the launch
+    # stream (no events between the kernels: each one costs microseconds).
     log(f"[bench] timing {args.steps} steps")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
+    for _ in range(args.steps):
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-    per = {"fused_swiglu": [], "gemv_down": [], "gemv_lm_head": []}
-    for e in evs:
-        per["fused_swiglu"].append(e[0].elapsed_time(e[1]))
-        per["gemv_down"].append(e[1].elapsed_time(e[2]))
-        per["gemv_lm_head"].append(e[2].elapsed_time(e[3]))
+    ms_per_step = start.elapsed_time(end) / args.steps
+    value = step_weight_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # Timed region 2, per kernel: K launches of that kernel alone, back to
+    # back on the launch stream between two events.  The FFN matrices (85 MB
+    # together) would stay in the 256 MB Infinity Cache when repeated, so
+    # those launches rotate over copies totalling >= 512 MiB, as in the step
+    # where the lm_head evicts them; the lm_head (572 MB) streams from HBM.
     kernel_bytes = {
         "fused_swiglu": wbytes["gate_9b"] + wbytes["up_9b"] + 4 * 4096 + 4 * 12288,
         "gemv_down": wbytes["down_9b"] + 4 * 12288 + 4 * 4096,
         "gemv_lm_head": wbytes["lm_head_9b"] + 4 * 4096 + 4 * 248320,
     }
+
+    def rotated(names):
+        """The resident weights plus enough copies to total >= 512 MiB."""
+        n_copies = max(1, -(-(512 << 20) // sum(wbytes[nm] for nm in names)))
+        return [[W[nm] for nm in names]] + [[W[nm].clone() for nm in names] for _ in range(n_copies - 1)]
+
+    sets_sw = rotated(["gate_9b", "up_9b"])
+    sets_dn = rotated(["down_9b"])
+    launches = {
+        "fused_swiglu": lambda i: q4k.fused_swiglu(*sets_sw[i % len(sets_sw)], x, h=h, stream=stream),
+        "gemv_down": lambda i: q4k.gemv(sets_dn[i % len(sets_dn)][0], h, y=y, stream=stream),
+        "gemv_lm_head": lambda i: q4k.gemv(W["lm_head_9b"], y, y=logits, stream=stream),
+    }
     kernels = {}
-    for nm, ts in per.items():
-        mean_ms = float(np.mean(ts))
-        kernels[nm] = {"mean_us": round(mean_ms * 1e3, 3), "median_us": round(float(np.median(ts)) * 1e3, 3),
-                       "GB/s": round(kernel_bytes[nm] / (mean_ms * 1e-3) / 1e9, 1),
-                       "frac_hbm_peak": round(kernel_bytes[nm] / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    value = step_weight_bytes / (ms_per_step * 1e-3) / 1e9
-    lm = kernels["gemv_lm_head"]
-    achieved = kernel_bytes["gemv_lm_head"] / (float(np.mean(per["gemv_lm_head"])) * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+    for nm, fn in launches.items():
+        for i in range(args.warmup):
+            fn(i)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        mean_s = a.elapsed_time(b) / args.steps * 1e-3
+        gbs = kernel_bytes[nm] / mean_s / 1e9
+        kernels[nm] = {"mean_us": round(mean_s * 1e6, 3), "GB/s": round(gbs, 1),
+                       "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "calls_per_s": round(1.0 / mean_s, 1)}
+    del sets_sw, sets_dn
+    achieved = kernels["gemv_lm_head"]["GB/s"]
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(wbytes["lm_head_9b"]),
                 "kernel": "q4k_gemv lm_head 248320x4096", "bytes_per_launch": kernel_bytes["gemv_lm_head"]}
-    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s; per kernel {kernels}; host wall {wall:.3f}s")
+
+    # Context only: a plain read-only stream (a sum over 1 GiB) on this part.
+    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    big.sum()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(20):
+        big.sum()
+    b.record(stream)
+    torch.cuda.synchronize()
+    stream_ceiling = big.numel() * 4 / (a.elapsed_time(b) / 20 * 1e-3) / 1e9
+    del big
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s; per kernel {kernels}; "
+        f"read-only stream {stream_ceiling:.0f} GB/s; host wall {wall:.3f}s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -211,6 +243,7 @@ def main():
             "weight_bytes_per_step": step_weight_bytes,
             "frac_hbm_peak_step": round(value / HBM_PEAK_GBS, 4),
             "kernels": kernels,
+            "read_only_stream_GBps": round(stream_ceiling, 1),
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -7,7 +7,7 @@
 
 #include <atomic>
 
-#include "../../include/q4k.h"
+#include "q4k.h"
 #include "launch.h"
 
 namespace q4k {

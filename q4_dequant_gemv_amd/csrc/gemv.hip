@@ -10,9 +10,10 @@
 // kernel is an HBM stream: each lane owns one 64-weight group (the code bytes
 // of a sub-block pair, 32 contiguous bytes) of a row, plus the super-block's
 // 16-byte header, and a row of K weights is covered by LPR = K/64 lanes (16,
-// 32 or 64 at K = 1024, 2048, 4096; a lane owns G groups when K/64 > 64).
-// Rows are handed to waves round-robin by a persistent grid sized to the
-// resident capacity.
+// 32 or 64 at K = 1024, 2048, 4096).  Rows are handed to waves round-robin by
+// a persistent grid sized to the resident capacity.  Wider rows (K = 8192 to
+// 16384) are split over S = K/4096 waves of one workgroup, each holding its
+// slice of the activations in registers; their partial row sums meet in LDS.
 //
 // Arithmetic per weight has to stay near one vector instruction, so the dot
 // product is done in integers: each 64-activation group is converted once per
@@ -30,9 +31,9 @@
 // 2e-4 * sum|w x| bound unless, within one 64-activation group, the largest
 // |x| exceeds the |w|-weighted typical |x| by several hundred times.
 //
-// Row partial sums are reduced across the LPR lanes of the row with
-// cross-lane shuffles; the workgroup's activations are staged once in LDS and
-// then held in registers for the whole row stream.
+// Row partial sums are reduced across the LPR lanes of the row with DPP and
+// permlane swaps (no LDS); the workgroup's activations are converted once into
+// LDS and then held in registers for the whole row stream.
 #include <float.h>
 #include <math.h>
 
@@ -44,30 +45,79 @@
 
 namespace q4k {
 
-// One iteration's weight bytes for one lane: per matrix and per owned group,
-// the super-block header and the group's 32 code bytes.
-template <int G, int NMAT>
+// One row's weight bytes for one lane (its 64-weight group), per matrix: the
+// super-block header and the group's 32 code bytes.
+template <int NMAT>
 struct RowLoads {
-    uint4 hdr[NMAT][G];
-    uint4 qa[NMAT][G];
-    uint4 qb[NMAT][G];
+    uint4 hdr[NMAT];
+    uint4 qa[NMAT];
+    uint4 qb[NMAT];
 };
 
-// LPR lanes per row (power of two, <= 64), G groups per lane.  SWIGLU reads a
-// second matrix `wu` of the same shape and writes silu(W x) * (Wu x).  XREG
-// keeps the lane's activation limbs in registers for the whole kernel (G == 1);
-// otherwise they are re-read from LDS for every row.
-//
-// Each wave walks its rows with two register buffers: the loads of the next
-// row are in flight while the current row is decoded, multiplied and reduced,
-// and the first row's loads are issued before the activations are prepared.
-template <int LPR, int G, bool SWIGLU, bool XREG, int BLOCK, int MIN_WAVES>
+// Where a lane's group sits inside a row (fixed for the whole kernel).  Lanes
+// past the row's last group (K/64 not a power of two) read group 0 again and
+// drop it.
+struct LaneGroup {
+    uint32_t off_hdr;  // byte offset of the super-block header
+    uint32_t off_qa;   // byte offset of the group's first 16 code bytes
+    PairSelect ps;
+    int j;             // group index (clamped)
+    bool ok;           // the group exists
+};
+
+__device__ __forceinline__ LaneGroup lane_group(int j, int ngroups, uint32_t row_off) {
+    LaneGroup g;
+    g.ok = j < ngroups;
+    g.j = g.ok ? j : 0;
+    g.ps = pair_select(g.j & 3);
+    g.off_hdr = row_off + static_cast<uint32_t>(g.j >> 2) * kBlockBytes;
+    g.off_qa = g.off_hdr + 16u + 32u * static_cast<uint32_t>(g.j & 3);
+    return g;
+}
+
+// Issues one row's loads from descriptors based at `base` (wave-uniform) that
+// cover `nrec` bytes: loads at or past nrec return zeros, so a row past the
+// end costs no memory traffic and needs no branch.
+template <int NMAT>
+__device__ __forceinline__ void issue_row(RowLoads<NMAT> &b, const uint8_t *w, const uint8_t *wu, int64_t base,
+                                          int nrec, const LaneGroup &g) {
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+        const __amdgpu_buffer_rsrc_t r = stream_rsrc((mt == 0 ? w : wu) + base, nrec);
+        b.hdr[mt] = buffer_load16(r, g.off_hdr);
+        b.qa[mt] = buffer_load16(r, g.off_qa);
+        b.qb[mt] = buffer_load16(r, g.off_qa + 16u);
+    }
+}
+
+// The lane's share of the row, per matrix: sum over its group of w * x.
+template <int NMAT>
+__device__ __forceinline__ void lane_dot(const RowLoads<NMAT> &b, const LaneGroup &g, const XRegs &xr, bool active,
+                                         float (&acc)[NMAT]) {
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+        acc[mt] = 0.0f;
+        if (active) {
+            GroupCodes c;
+            decode_group(b.hdr[mt], b.qa[mt], b.qb[mt], g.ps, c);
+            acc[mt] = xr.scale * group_dot(c, xr);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- K <= 4096
+// LPR lanes per row (power of two, <= 64; LPR >= K/64), 64/LPR rows per wave
+// iteration.  SWIGLU reads a second matrix `wu` of the same shape and writes
+// silu(W x) * (Wu x).  Each wave rotates NB register buffers: while one row is
+// decoded, multiplied and reduced, the next NB-1 rows' loads are in flight;
+// the first rows are issued before the activations are prepared.  Wave
+// iterations are dealt round-robin over the persistent grid.
+template <int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES>
 __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const uint8_t *__restrict__ w,
                                                                 const uint8_t *__restrict__ wu, const float *x,
                                                                 float *__restrict__ y, int64_t n, int ngroups,
                                                                 int64_t row_bytes) {
-    static_assert(G == 1 || LPR == 64, "several groups per lane only with a full wave per row");
-    static_assert(!XREG || G == 1, "activation limbs held in registers for one group per lane");
+    static_assert(NB >= 2, "at least one row in flight");
     constexpr int NMAT = SWIGLU ? 2 : 1;
     constexpr int kRowsPerWave = kWave / LPR;
     constexpr int kWavesPerBlock = BLOCK / kWave;
@@ -77,25 +127,11 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const uint8_t *_
     const int lane = threadIdx.x & (kWave - 1);
     const int sub = lane % LPR;
     const int slot = lane / LPR;
-    // Byte offsets of this lane's loads inside one wave iteration (rows
-    // it*kRowsPerWave .. +kRowsPerWave-1), fixed for the whole kernel.  The
-    // iteration's base address is wave-uniform (scalar registers), so the loop
-    // rewrites no per-lane address registers while earlier loads are in flight.
-    // Lanes past the row's last group (K/64 not a power of two) load group 0
-    // again and ignore it.
-    uint32_t off_hdr[G], off_qa[G];
-    PairSelect psel[G];
-    bool gok[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int j = sub + LPR * g;
-        gok[g] = j < ngroups;
-        const int jj = gok[g] ? j : 0;
-        psel[g] = pair_select(jj & 3);
-        off_hdr[g] = static_cast<uint32_t>(slot * row_bytes + (jj >> 2) * kBlockBytes);
-        off_qa[g] = off_hdr[g] + 16u + 32u * static_cast<uint32_t>(jj & 3);
-    }
-    const uint8_t *mats[2] = {w, wu};
+    // byte offsets inside one wave iteration (rows it*kRowsPerWave ..
+    // +kRowsPerWave-1): the iteration's base address is wave-uniform (scalar
+    // registers), so the loop rewrites no per-lane address registers while
+    // earlier loads are in flight
+    const LaneGroup g = lane_group(sub, ngroups, static_cast<uint32_t>(slot * row_bytes));
     // Loop control is 32-bit and scalar (the host keeps the iteration count
     // below 2^31): gfx9 has no 64-bit scalar compare, and a vector compare in
     // the loop would borrow registers that earlier memory operations still own.
@@ -103,94 +139,143 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const uint8_t *_
     const int niters = static_cast<int>((n + kRowsPerWave - 1) / kRowsPerWave);
     const int tail_bytes = static_cast<int>(n - static_cast<int64_t>(niters - 1) * kRowsPerWave) *
                            static_cast<int>(row_bytes);
-
-    // Loads of one iteration: unconditional, from a descriptor based at the
-    // iteration's first row; rows past n read as zeros and are not stored.
-    auto issue = [&](auto &b, int it) {
-        const int64_t base = static_cast<int64_t>(it) * iter_bytes;
+    auto issue = [&](RowLoads<NMAT> &b, int it) {
         const int left = niters - it;
-        const int nrec = left > 1 ? iter_bytes : (left == 1 ? tail_bytes : 0);
-#pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt) {
-            const __amdgpu_buffer_rsrc_t r = stream_rsrc(mats[mt] + base, nrec);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                b.hdr[mt][g] = buffer_load16(r, off_hdr[g]);
-                b.qa[mt][g] = buffer_load16(r, off_qa[g]);
-                b.qb[mt][g] = buffer_load16(r, off_qa[g] + 16u);
-            }
-        }
+        issue_row(b, w, wu, static_cast<int64_t>(it) * iter_bytes,
+                  left > 1 ? iter_bytes : (left == 1 ? tail_bytes : 0), g);
     };
 
     const int nwaves = static_cast<int>(gridDim.x) * kWavesPerBlock;
     const int it0 = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWavesPerBlock +
                                                    static_cast<int>(threadIdx.x >> 6));
 
-    // activations first, then the first row's weights: waiting for the
+    // activations first, then the first rows' weights: waiting for the
     // activations (in issue order) then leaves the weight loads in flight
-    constexpr int kXChunks = (64 * G * 16 + BLOCK - 1) / BLOCK;
+    constexpr int kXChunks = (LPR * 16 + BLOCK - 1) / BLOCK;
     const XLoaded<kXChunks> xl = load_x<BLOCK, kXChunks>(x, ngroups);
     // keep the activation loads ahead of the weight loads (an empty asm with a
     // memory clobber: no instruction, only an ordering point for the compiler;
     // x is deliberately not __restrict__ so its loads cannot move across it)
     asm volatile("" ::: "memory");
-    RowLoads<G, NMAT> bufa;
-    RowLoads<G, XREG ? NMAT : 1> bufb;
-    issue(bufa, it0);
+    RowLoads<NMAT> buf[NB];
+#pragma unroll
+    for (int b = 0; b + 1 < NB; ++b) issue(buf[b], it0 + b * nwaves);
 
     prepare_x<BLOCK, kXChunks>(xl, ngroups, xg);
     __syncthreads();
-
-    XRegs xr[XREG ? 1 : 1];
-    if constexpr (XREG) load_xregs(xg[gok[0] ? sub : 0], xr[0]);
-
-    auto process = [&](const auto &b, int it) {
-        const int64_t row = static_cast<int64_t>(it) * kRowsPerWave + slot;
-        const bool rok = row < n;
-        float acc[NMAT];
-#pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt) {
-            acc[mt] = 0.0f;
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                if (rok && gok[g]) {
-                    GroupCodes c;
-                    decode_group(b.hdr[mt][g], b.qa[mt][g], b.qb[mt][g], psel[g], c);
-                    if constexpr (XREG) {
-                        acc[mt] += xr[0].scale * group_dot(c, xr[0]);
-                    } else {
-                        const XGroup &xs = xg[sub + LPR * g];
-                        acc[mt] += xs.scale * group_dot(c, xs);
-                    }
-                }
-            }
-            acc[mt] = lane_group_sum<LPR>(acc[mt]);
-        }
-        if (sub == 0 && rok) {
-            if constexpr (SWIGLU) {
-                y[row] = silu(acc[0]) * acc[1];
-            } else {
-                y[row] = acc[0];
-            }
-        }
-    };
+    XRegs xr;
+    load_xregs(xg[g.j], xr);
 
     // The loads are never inside a branch: at a control-flow join the wait
     // counters would have to assume the fewest loads in flight and drain the
     // prefetch.  Iterations past the end load nothing (0-byte descriptor).
-    if constexpr (XREG) {
-        for (int it = it0; it < niters; it += 2 * nwaves) {
-            issue(bufb, it + nwaves);
-            process(bufa, it);
-            if (it + nwaves >= niters) break;
-            issue(bufa, it + 2 * nwaves);
-            process(bufb, it + nwaves);
+    for (int it = it0; it < niters; it += NB * nwaves) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int cur = it + b * nwaves;
+            issue(buf[(b + NB - 1) % NB], cur + (NB - 1) * nwaves);
+            const int64_t row = static_cast<int64_t>(cur) * kRowsPerWave + slot;
+            const bool rok = row < n;
+            float acc[NMAT];
+            lane_dot(buf[b], g, xr, rok && g.ok, acc);
+#pragma unroll
+            for (int mt = 0; mt < NMAT; ++mt) acc[mt] = lane_group_sum<LPR>(acc[mt]);
+            if (sub == 0 && rok) y[row] = SWIGLU ? silu(acc[0]) * acc[1] : acc[0];
+            if (cur + nwaves >= niters) break;
         }
-    } else {
-        // G groups per lane already put G*48 bytes per lane in flight per row
-        for (int it = it0; it < niters; it += nwaves) {
-            if (it != it0) issue(bufa, it);
-            process(bufa, it);
+    }
+}
+
+// ------------------------------------------------------ 4096 < K <= 16384
+// A row is split over S waves of the workgroup (S * 64 groups, wave s owns
+// groups 64s .. 64s+63, one per lane, with its activation slice in registers);
+// the workgroup streams R rows per block iteration, one per group of S waves.
+// Each wave reduces its slice across its lanes and leaves the partial sum in
+// LDS; every kFlush iterations (and at the end) a barrier, then one thread per
+// row adds the S partials in slice order and stores the result, so the result
+// does not depend on timing.  The partial buffer has two halves, so the next
+// stretch of iterations writes while the last one is read.
+constexpr int kFlush = 8;
+
+template <int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
+__global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const uint8_t *__restrict__ w,
+                                                                           const uint8_t *__restrict__ wu,
+                                                                           const float *x, float *__restrict__ y,
+                                                                           int64_t n, int ngroups,
+                                                                           int64_t row_bytes) {
+    constexpr int BLOCK = 64 * S * R;
+    constexpr int NMAT = SWIGLU ? 2 : 1;
+    extern __shared__ __align__(16) unsigned char smem[];
+    XGroup *xg = reinterpret_cast<XGroup *>(smem);
+    float *part = reinterpret_cast<float *>(smem + static_cast<size_t>(ngroups) * sizeof(XGroup));  // [2][kFlush][R][S][NMAT]
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int slice = wave % S;
+    const int rslot = wave / S;
+    const LaneGroup g = lane_group(slice * kWave + lane, ngroups, 0u);
+    // block iterations b = blockIdx.x + c * gridDim.x cover rows b*R .. b*R+R-1;
+    // the host keeps gridDim.x <= the number of block iterations
+    const int64_t nbi = (n + R - 1) / R;
+    const int my_iters = static_cast<int>((nbi - 1 - blockIdx.x) / gridDim.x) + 1;
+    auto row_of = [&](int c, int r) -> int64_t {
+        return (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(c) * gridDim.x) * R + r;
+    };
+    auto issue = [&](RowLoads<NMAT> &b, int c) {
+        const int64_t row = row_of(c, rslot);
+        const bool live = c < my_iters && row < n;
+        issue_row(b, w, wu, live ? row * row_bytes : 0, live ? static_cast<int>(row_bytes) : 0, g);
+    };
+
+    constexpr int kXChunks = (S * kWave * 16 + BLOCK - 1) / BLOCK;
+    const XLoaded<kXChunks> xl = load_x<BLOCK, kXChunks>(x, ngroups);
+    asm volatile("" ::: "memory");
+    RowLoads<NMAT> buf[NB];
+#pragma unroll
+    for (int b = 0; b + 1 < NB; ++b) issue(buf[b], b);
+
+    prepare_x<BLOCK, kXChunks>(xl, ngroups, xg);
+    __syncthreads();
+    XRegs xr;
+    load_xregs(xg[g.j], xr);
+
+    for (int c = 0; c < my_iters; c += NB) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int cur = c + b;
+            issue(buf[(b + NB - 1) % NB], cur + NB - 1);
+            float acc[NMAT];
+            lane_dot(buf[b], g, xr, g.ok, acc);
+            const int d = cur % kFlush;
+            const int half = (cur / kFlush) & 1;
+            float *pp = part + (((half * kFlush + d) * R + rslot) * S + slice) * NMAT;
+#pragma unroll
+            for (int mt = 0; mt < NMAT; ++mt) {
+                acc[mt] = lane_group_sum<kWave>(acc[mt]);
+                if (lane == 0) pp[mt] = acc[mt];
+            }
+            if (d == kFlush - 1 || cur + 1 == my_iters) {
+                __syncthreads();
+                const int t = static_cast<int>(threadIdx.x);
+                if (t < (d + 1) * R) {
+                    const int dd = t / R;
+                    const int r = t % R;
+                    const int64_t row = row_of(cur - d + dd, r);
+                    if (row < n) {
+                        const float *q = part + ((half * kFlush + dd) * R + r) * S * NMAT;
+                        float sum[NMAT];
+#pragma unroll
+                        for (int mt = 0; mt < NMAT; ++mt) sum[mt] = q[mt];
+#pragma unroll
+                        for (int s = 1; s < S; ++s) {
+#pragma unroll
+                            for (int mt = 0; mt < NMAT; ++mt) sum[mt] += q[s * NMAT + mt];
+                        }
+                        y[row] = SWIGLU ? silu(sum[0]) * sum[1] : sum[0];
+                    }
+                }
+            }
+            if (cur + 1 >= my_iters) break;
         }
     }
 }
@@ -252,10 +337,10 @@ int resident_blocks_per_cu(Kernel kern, int block, size_t lds, std::atomic<int> 
     return nb;
 }
 
-template <int LPR, int G, bool SWIGLU, bool XREG, int BLOCK, int MIN_WAVES>
+template <int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES>
 hipError_t launch_fast(const uint8_t *w, const uint8_t *wu, const float *x, float *y, int64_t n, int64_t k,
                        hipStream_t stream) {
-    auto kern = gemv_kernel<LPR, G, SWIGLU, XREG, BLOCK, MIN_WAVES>;
+    auto kern = gemv_kernel<LPR, SWIGLU, NB, BLOCK, MIN_WAVES>;
     const int ngroups = static_cast<int>(k / 64);
     const size_t lds = static_cast<size_t>(ngroups) * sizeof(XGroup);
     static std::atomic<int> cache[kMaxDevices];
@@ -263,6 +348,24 @@ hipError_t launch_fast(const uint8_t *w, const uint8_t *wu, const float *x, floa
     constexpr int kRowsPerWave = kWave / LPR;
     const int64_t niters = (n + kRowsPerWave - 1) / kRowsPerWave;
     const int64_t need = (niters + BLOCK / kWave - 1) / (BLOCK / kWave);
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
+    const int grid = static_cast<int>(need < cap ? need : cap);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, w, wu, x, y, n, ngroups,
+                       (k / kBlockWeights) * kBlockBytes);
+    return hipGetLastError();
+}
+
+template <int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
+hipError_t launch_split(const uint8_t *w, const uint8_t *wu, const float *x, float *y, int64_t n, int64_t k,
+                        hipStream_t stream) {
+    auto kern = gemv_split_kernel<S, R, SWIGLU, NB, MIN_WAVES>;
+    constexpr int BLOCK = 64 * S * R;
+    const int ngroups = static_cast<int>(k / 64);
+    const size_t lds = static_cast<size_t>(ngroups) * sizeof(XGroup) +
+                       sizeof(float) * 2 * kFlush * R * S * (SWIGLU ? 2 : 1);
+    static std::atomic<int> cache[kMaxDevices];
+    const int per_cu = resident_blocks_per_cu(kern, BLOCK, lds, cache);
+    const int64_t need = (n + R - 1) / R;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
     const int grid = static_cast<int>(need < cap ? need : cap);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, w, wu, x, y, n, ngroups,
@@ -281,16 +384,20 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const float *x, f
     return hipGetLastError();
 }
 
-// Launch shapes: threads per block and minimum resident waves per SIMD (the
-// register budget).  Streams of several MB run best as one 1024-thread block
-// per CU (4 waves per SIMD; more resident waves measured slower); small
-// matrices, which finish in a few microseconds, start faster with 256-thread
-// blocks (less activation preparation per block, more blocks).
+// Launch shapes: threads per block, minimum resident waves per SIMD (the
+// register budget) and row buffers per wave.  Streams of several MB run best
+// as one 1024-thread block per CU (4 waves per SIMD; more resident waves
+// measured slower); small matrices, which finish in a few microseconds, start
+// faster with 256-thread blocks (less activation preparation per block, more
+// blocks).
 #ifndef Q4K_LARGE_BLOCK
 #define Q4K_LARGE_BLOCK 1024
 #endif
 #ifndef Q4K_LARGE_MINW
 #define Q4K_LARGE_MINW 4
+#endif
+#ifndef Q4K_LARGE_NB
+#define Q4K_LARGE_NB 2
 #endif
 #ifndef Q4K_SMALL_BLOCK
 #define Q4K_SMALL_BLOCK 256
@@ -298,17 +405,20 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const float *x, f
 #ifndef Q4K_SMALL_MINW
 #define Q4K_SMALL_MINW 3
 #endif
+#ifndef Q4K_SMALL_NB
+#define Q4K_SMALL_NB 2
+#endif
 #ifndef Q4K_SWIGLU_BLOCK
 #define Q4K_SWIGLU_BLOCK 512
 #endif
 #ifndef Q4K_SWIGLU_MINW
 #define Q4K_SWIGLU_MINW 2
 #endif
-#ifndef Q4K_BIGK_BLOCK
-#define Q4K_BIGK_BLOCK 1024
+#ifndef Q4K_SWIGLU_NB
+#define Q4K_SWIGLU_NB 2
 #endif
-#ifndef Q4K_BIGK_MINW
-#define Q4K_BIGK_MINW 4
+#ifndef Q4K_SPLIT_NB
+#define Q4K_SPLIT_NB 2
 #endif
 // matrices below this many bytes use the small launch shape
 #ifndef Q4K_SMALL_BYTES
@@ -316,16 +426,16 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const float *x, f
 #endif
 
 template <int LPR, bool SWIGLU>
-hipError_t dispatch_regx(const uint8_t *w, const uint8_t *wu, const float *x, float *y, int64_t n, int64_t k,
-                         hipStream_t stream) {
+hipError_t dispatch_lpr(const uint8_t *w, const uint8_t *wu, const float *x, float *y, int64_t n, int64_t k,
+                        hipStream_t stream) {
     if constexpr (SWIGLU) {
-        return launch_fast<LPR, 1, true, true, Q4K_SWIGLU_BLOCK, Q4K_SWIGLU_MINW>(w, wu, x, y, n, k, stream);
+        return launch_fast<LPR, true, Q4K_SWIGLU_NB, Q4K_SWIGLU_BLOCK, Q4K_SWIGLU_MINW>(w, wu, x, y, n, k, stream);
     } else {
         const int64_t bytes = n * (k / kBlockWeights) * kBlockBytes;
         if (bytes < Q4K_SMALL_BYTES) {
-            return launch_fast<LPR, 1, false, true, Q4K_SMALL_BLOCK, Q4K_SMALL_MINW>(w, wu, x, y, n, k, stream);
+            return launch_fast<LPR, false, Q4K_SMALL_NB, Q4K_SMALL_BLOCK, Q4K_SMALL_MINW>(w, wu, x, y, n, k, stream);
         }
-        return launch_fast<LPR, 1, false, true, Q4K_LARGE_BLOCK, Q4K_LARGE_MINW>(w, wu, x, y, n, k, stream);
+        return launch_fast<LPR, false, Q4K_LARGE_NB, Q4K_LARGE_BLOCK, Q4K_LARGE_MINW>(w, wu, x, y, n, k, stream);
     }
 }
 
@@ -333,18 +443,24 @@ template <bool SWIGLU>
 hipError_t dispatch(const uint8_t *w, const uint8_t *wu, const float *x, float *y, int64_t n, int64_t k,
                     hipStream_t stream) {
     const int64_t ngroups = k / 64;
-    if (ngroups <= 4) return dispatch_regx<4, SWIGLU>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 8) return dispatch_regx<8, SWIGLU>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 16) return dispatch_regx<16, SWIGLU>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 32) return dispatch_regx<32, SWIGLU>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 64) return dispatch_regx<64, SWIGLU>(w, wu, x, y, n, k, stream);
-    // two matrices' row buffers need twice the registers
-    constexpr int BB = Q4K_BIGK_BLOCK;
-    constexpr int BMW = SWIGLU ? 2 : Q4K_BIGK_MINW;
-    constexpr int BBS = SWIGLU ? (BB > 512 ? 512 : BB) : BB;
-    if (ngroups <= 128) return launch_fast<64, 2, SWIGLU, false, BBS, BMW>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 192) return launch_fast<64, 3, SWIGLU, false, BBS, BMW>(w, wu, x, y, n, k, stream);
-    // beyond K = 12288 the per-row register buffers no longer fit
+    if (ngroups <= 4) return dispatch_lpr<4, SWIGLU>(w, wu, x, y, n, k, stream);
+    if (ngroups <= 8) return dispatch_lpr<8, SWIGLU>(w, wu, x, y, n, k, stream);
+    if (ngroups <= 16) return dispatch_lpr<16, SWIGLU>(w, wu, x, y, n, k, stream);
+    if (ngroups <= 32) return dispatch_lpr<32, SWIGLU>(w, wu, x, y, n, k, stream);
+    if (ngroups <= 64) return dispatch_lpr<64, SWIGLU>(w, wu, x, y, n, k, stream);
+    // split rows: S waves per row; two matrices' row buffers need more
+    // registers, so the SwiGLU shapes keep fewer rows per workgroup
+    constexpr int NB = Q4K_SPLIT_NB;
+    if constexpr (SWIGLU) {
+        if (ngroups <= 128) return launch_split<2, 4, true, NB, 2>(w, wu, x, y, n, k, stream);
+        if (ngroups <= 192) return launch_split<3, 4, true, NB, 3>(w, wu, x, y, n, k, stream);
+        if (ngroups <= 256) return launch_split<4, 2, true, NB, 2>(w, wu, x, y, n, k, stream);
+    } else {
+        if (ngroups <= 128) return launch_split<2, 8, false, NB, 4>(w, wu, x, y, n, k, stream);
+        if (ngroups <= 192) return launch_split<3, 4, false, NB, 3>(w, wu, x, y, n, k, stream);
+        if (ngroups <= 256) return launch_split<4, 4, false, NB, 4>(w, wu, x, y, n, k, stream);
+    }
+    // beyond K = 16384: the plain kernel
     return launch_generic<SWIGLU>(w, wu, x, y, n, k, stream);
 }
 

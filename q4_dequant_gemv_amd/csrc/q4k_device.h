@@ -183,6 +183,23 @@ __device__ __forceinline__ float lane_group_sum(float v) {
     return v;
 }
 
+// Integer sum over aligned groups of W lanes, W in {4, 8, 16} (inside one
+// 16-lane row, so DPP alone reaches every partner).
+template <int CTRL>
+__device__ __forceinline__ int dpp_add_int(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true) + v;
+}
+
+template <int W>
+__device__ __forceinline__ int lane_group_sum_int(int v) {
+    static_assert(W == 4 || W == 8 || W == 16, "group width");
+    v = dpp_add_int<0xb1>(v);
+    v = dpp_add_int<0x4e>(v);
+    if constexpr (W >= 8) v = dpp_add_int<0x141>(v);
+    if constexpr (W >= 16) v = dpp_add_int<0x140>(v);
+    return v;
+}
+
 // Maximum over aligned groups of W lanes (same lane pairings as lane_group_sum).
 template <int CTRL>
 __device__ __forceinline__ float dpp_max(float v) {

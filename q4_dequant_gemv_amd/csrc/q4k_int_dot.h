@@ -35,9 +35,6 @@ static_assert(sizeof(XGroup) == 208, "XGroup layout");
 // Converts x[0 .. 64*ngroups) into XGroups, 16 threads per group, 4
 // activations per thread.  BLOCK is a multiple of 64, so the 16 threads of a
 // group are 16 aligned lanes of one wave and are either all active or all not.
-// Converts x[0 .. 64*ngroups) into XGroups, 16 threads per group, 4
-// activations per thread.  BLOCK is a multiple of 64, so the 16 threads of a
-// group are 16 aligned lanes of one wave and are either all active or all not.
 // The activations are loaded first (load_x) so that a kernel can issue them
 // ahead of its weight loads: waits are counted in issue order, so waiting for
 // the activations then leaves the weight loads in flight.  NCH covers
@@ -82,7 +79,7 @@ __device__ __forceinline__ void prepare_x(const XLoaded<NCH> &f, int ngroups, XG
             a = (a <= FLT_MAX) ? a : INFINITY;  // NaN counts as non-finite
             amax = fmaxf(amax, a);
         }
-        amax = group_max<16>(amax);
+        amax = lane_group_max<16>(amax);  // DPP inside the 16-lane row: no LDS round trip
         const bool finite = amax <= FLT_MAX;
         const bool zero = amax == 0.0f;
         int sexp = 0;
@@ -108,7 +105,7 @@ __device__ __forceinline__ void prepare_x(const XLoaded<NCH> &f, int ngroups, XG
             l1 |= static_cast<uint32_t>(x1 & 0xff) << (8 * b);
             l2 |= static_cast<uint32_t>(x2 & 0xff) << (8 * b);
         }
-        s = group_sum_int<8>(s);
+        s = lane_group_sum_int<8>(s);
         xg[j].limb[half][0][i] = l0;
         xg[j].limb[half][1][i] = l1;
         xg[j].limb[half][2][i] = l2;

@@ -113,11 +113,66 @@ def test_gemv_0p8b_projections(q4k, name, tid):
 
 @pytest.mark.parametrize("name,cfg,tid", [("lm_head_0p8b", 1, 3), ("lm_head_9b", 3, 0), ("down_9b", 2, 2)])
 def test_gemv_full_size_sampled(q4k, name, cfg, tid):
+    """Whole matrix on the GPU (y pre-filled with NaN, so a row that no wave
+    wrote shows up), sampled rows against the oracle."""
+    import torch
+
     n, k = inputs.SHAPES[name]
     w = inputs.make_q4k(n, k, config_id=cfg, tensor_id=tid)
     x = inputs.make_x(1, k, config_id=cfg, tensor_id=100 + tid)[0]
+    y = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    q4k.gemv(to_dev(w.reshape(-1)), to_dev(x), y=y)
+    got = to_host(y)
+    assert np.isfinite(got).all(), f"{int((~np.isfinite(got)).sum())} rows not written"
     rows = _sample_rows(n, 3000, seed=cfg)
-    _report(name, check_bound(*_gemv_case(q4k, w, x, rows), name))
+    yr, ar = oracle.gemv(w[rows], x, threads=THREADS)
+    _report(name, check_bound(got[rows], yr, ar, name))
+
+
+def test_gemv_work_counter_across_streams(q4k):
+    """Large matrices hand rows out through a per-stream work counter that
+    each launch leaves at zero: repeated launches on one stream, and launches
+    on two streams running at the same time, all write every row with the
+    same bits (each row is still summed by one wave in a fixed order)."""
+    import torch
+
+    n, k = inputs.SHAPES["lm_head_0p8b"]
+    w = to_dev(inputs.make_q4k(n, k, config_id=97, tensor_id=0).reshape(-1))
+    x = to_dev(inputs.make_x(1, k, config_id=97)[0])
+    base = to_host(q4k.gemv(w, x))
+    assert np.isfinite(base).all()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        for s in (s1, s2):
+            y = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                q4k.gemv(w, x, y=y)
+            outs.append(y)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        outs.append(q4k.gemv(w, x))
+    for y in outs:
+        np.testing.assert_array_equal(to_host(y), base)
+    h0 = None
+    for s in (None, s1, s2, s1):
+        h = torch.full((12288,), float("nan"), dtype=torch.float32, device="cuda")
+        wg = to_dev(inputs.make_q4k(12288, 4096, config_id=97, tensor_id=1).reshape(-1)) if h0 is None else wg
+        wu = to_dev(inputs.make_q4k(12288, 4096, config_id=97, tensor_id=2).reshape(-1)) if h0 is None else wu
+        x2 = to_dev(inputs.make_x(1, 4096, config_id=97, tensor_id=3)[0]) if h0 is None else x2
+        if s is None:
+            q4k.fused_swiglu(wg, wu, x2, h=h)
+        else:
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                q4k.fused_swiglu(wg, wu, x2, h=h)
+        torch.cuda.synchronize()
+        got = to_host(h)
+        if h0 is None:
+            assert np.isfinite(got).all()
+            h0 = got
+        np.testing.assert_array_equal(got, h0)
 
 
 @pytest.mark.parametrize("n,k", [(1, 256), (3, 256), (5, 512), (7, 768), (4097, 1024), (33, 2304), (129, 8192),
@@ -126,6 +181,25 @@ def test_gemv_edge_shapes(q4k, n, k):
     w = inputs.make_q4k(n, k, config_id=91, tensor_id=k)
     x = inputs.make_x(1, k, config_id=91, tensor_id=k)[0]
     _report(f"gemv {n}x{k}", check_bound(*_gemv_case(q4k, w, x), f"gemv {n}x{k}"))
+
+
+@pytest.mark.parametrize("n,k", [(20483, 12288), (16389, 8192), (9001, 16384)])
+def test_gemv_split_rows_many_iterations(q4k, n, k):
+    """Rows wider than 4096 are split over several waves whose partial sums
+    meet in LDS; these sizes give every workgroup more block iterations than
+    one exchange holds, and a ragged last iteration.  Two runs agree bitwise
+    (the partials are added in a fixed order)."""
+    import torch
+
+    w = inputs.make_q4k(n, k, config_id=96, tensor_id=k)
+    x = inputs.make_x(1, k, config_id=96, tensor_id=k)[0]
+    wd, xd = to_dev(w.reshape(-1)), to_dev(x)
+    y1 = q4k.gemv(wd, xd)
+    y2 = q4k.gemv(wd, xd)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    y, a = oracle.gemv(w, x, threads=THREADS)
+    _report(f"gemv split {n}x{k}", check_bound(to_host(y1), y, a, f"gemv split {n}x{k}"))
 
 
 def test_gemv_row_subrange_matches_whole(q4k):
@@ -226,7 +300,8 @@ def test_swiglu_ffn_9b(q4k):
     _report("swiglu 9b", check_swiglu_bound(h[rows], ref, "swiglu 9b"))
 
 
-@pytest.mark.parametrize("n,k", [(1, 256), (77, 1024), (300, 2048), (65, 12288), (9, 16384)])
+@pytest.mark.parametrize("n,k", [(1, 256), (77, 1024), (300, 2048), (65, 12288), (9, 16384), (8195, 12288),
+                                 (4103, 8192), (2049, 16384)])
 def test_swiglu_shapes(q4k, n, k):
     wg = inputs.make_q4k(n, k, config_id=95, tensor_id=2 * k)
     wu = inputs.make_q4k(n, k, config_id=95, tensor_id=2 * k + 1)
