@@ -26,10 +26,10 @@
  *    Every call only enqueues work on `stream` (a hipStream_t passed as
  *    void*; NULL means the null stream) and returns; it never synchronises.
  *    Results are ready when the stream is.  Only q4k_gemv_batched with
- *    m >= 16 needs device scratch: it takes it stream-ordered from the
+ *    m >= 2 needs device scratch: it takes it stream-ordered from the
  *    device's default memory pool (hipMallocAsync / hipFreeAsync on
- *    `stream`), (528*m' + 8*ceil4(m')) * k/128 bytes for m' = min(m, 64)
- *    tokens (about 1.1 MB at m = 64, k = 4096).
+ *    `stream`), 536 * ceil(m'/16) * k/8 bytes for m' = min(m, 64) tokens
+ *    (about 1.1 MB at m = 64, k = 4096).
  *  - Arguments are validated on the host before anything is enqueued; on any
  *    error nothing is launched and the status says why.  Launch failures are
  *    reported as Q4K_ERR_LAUNCH.
@@ -87,11 +87,13 @@ Q4K_API q4k_status q4k_gemv(const void *w, const float *x, float *y, int64_t n, 
  * non-M1 variant; "Module qwen3_attention" names a W4A16 batched path).
  *   x : f32 [m, k] row-major (token-major), y : f32 [m, n] row-major:
  *   y[t, r] = sum_c W[r,c] x[t,c].
- * m < 16 runs on the vector ALUs (each weight decoded once, used m times)
- * and is bitwise reproducible.  m >= 16 decodes tiles of weights into f16
- * operands for the matrix cores and adds partial tiles of the K dimension
- * into y with f32 atomics, so its last bits may differ between runs (every
- * run is inside the error bound).  y is overwritten, not accumulated.
+ * m >= 2 runs on the matrix cores (each weight decoded once per 64
+ * tokens).  With n >= 16 * (compute units of the device) every output is
+ * summed by one workgroup in a fixed order and the call is bitwise
+ * reproducible; with fewer rows the K range is split across workgroups whose
+ * partial sums are added into y with f32 atomics, so the last bits may
+ * differ between runs (every run is inside the error bound).  y is
+ * overwritten, not accumulated.
  */
 Q4K_API q4k_status q4k_gemv_batched(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
                             void *stream);

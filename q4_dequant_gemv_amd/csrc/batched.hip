@@ -1,115 +1,72 @@
-// Skinny Q4_K GEMM: y[t, r] = sum_c W[r,c] x[t,c] for m tokens.
+// Skinny Q4_K GEMM: y[t, r] = sum_c W[r,c] x[t,c] for m >= 2 tokens.
 //
 // selectQ4KFusedVariant ("@simulatte/doppler 0.1.7 -> 0.1.8",
 // matmul-selection.js) picks a fused Q4K kernel by whether M == 1; this file
-// is the M > 1 side.  Two kernels:
+// is the M > 1 side ("Module qwen3_attention" names a W4A16 batched path).
 //
-//  * m < 16, vector ALUs.  A workgroup owns 64 rows and walks K in chunks of
-//    1024 activations; per chunk the m activation rows are converted to the
-//    integer limbs of q4k_int_dot.h and staged in LDS, and each 64-weight group
-//    of codes is decoded once and multiplied against all m activation rows
-//    (v_dot4_i32_i8), so a weight byte is read from HBM once per call.
+// Once several tokens share each weight the work is a dense contraction, so
+// it runs on the matrix cores (v_mfma_f32_16x16x32_f16: 16 tokens x 16 rows x
+// 32 weights per instruction; fewer than 16 tokens leave the other rows of the
+// activation operand zero).  Exactness of the operands:
+//   * B (weights) holds 1024 + sc*q in f16: exact, since sc*q <= 945 < 1024,
+//     and built with one packed 16-bit multiply-add per two codes.  Folding
+//     the six-bit scale into the operand lets a whole half super-block (4
+//     sub-blocks, 128 weights) accumulate into one f32 tile.
+//   * A (activations) holds x * 2^-e as f16 hi + lo parts (e per token and
+//     half super-block), so every product is exact and the tile carries about
+//     22 bits of each x.
+// Per half super-block the f32 tile P is finished as
+//     acc += 2^e * (d * (P - 1024 * sum(hi + lo)) - dmin * Q),
+// where Q = sum_s m_s * sum_{x in s}(hi + lo) comes from a second, small MFMA
+// (mins in B, per-sub-block activation sums in A).  A bf16 operand could not
+// hold sc*q exactly (8 significant bits), and a bf16 dequantized weight misses
+// the 2e-4 * sum|w x| bound at K = 4096.
 //
-//  * m >= 16, matrix cores.  Only here is the work a real dense contraction,
-//    so the codes are turned into f16 MFMA operands: the B operand holds
-//    1024 + sc*q (exact in f16 since sc*q <= 945 < 1024, built with one packed
-//    16-bit multiply-add per two codes), which folds each sub-block's six-bit
-//    scale into the operand so that a whole half super-block (4 sub-blocks,
-//    128 weights) accumulates into one f32 tile.  Activations enter as f16
-//    hi + lo parts of x * 2^-e (e per token and half super-block), so the
-//    products are exact and the tile carries f32 accuracy.  Per half super-
-//    block the tile is finished in f32: subtract the 1024 * sum(x) bias, scale
-//    by d and 2^e, subtract dmin * sum_s m_s * sum(x over s).
-//    v_mfma_f32_16x16x32_f16: 16 tokens x 16 rows x 32 weights per step.
-//    (A bf16 operand cannot hold sc*q exactly -- 8 significant bits -- and a
-//    bf16 dequantized weight misses the 2e-4 * sum|w x| bound at K = 4096.)
+// Data flow (gfx950).  A preparation kernel converts x once per call into
+// scratch, already in the lane order of the MFMA operand fragments, so each
+// wave reads its activations with fully coalesced 1 KB loads straight into
+// registers.  A workgroup owns 16*NT rows and a K range; its W waves split the
+// K range between them (no activation byte is read twice inside a workgroup,
+// and the main loop has no barrier).  Each wave streams its weights and
+// activations one step ahead of the matrix cores.  At the end the waves' f32
+// tiles are added in LDS in a fixed order and stored; only when the K range
+// is split across workgroups (large m with few rows) are the partial tiles
+// added into y with f32 atomics.
 #include <float.h>
 #include <math.h>
 
 #include "launch.h"
 #include "q4k_device.h"
-#include "q4k_int_dot.h"
 
 namespace q4k {
 
-// ------------------------------------------------------------ m < 16 (VALU)
-constexpr int kValuChunkGroups = 16;  // 1024 activations per LDS chunk
-constexpr int kValuRowsPerBlock = 64;
-
-template <int M>
-__global__ __launch_bounds__(256) void batched_valu_kernel(const uint8_t *__restrict__ w,
-                                                           const float *__restrict__ x, float *__restrict__ y,
-                                                           int64_t n, int64_t k, int64_t row_bytes) {
-    __shared__ XGroup xg[M][kValuChunkGroups];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int sub = lane & 15;   // group inside the chunk
-    const int slot = lane >> 4;  // row inside a pass of four rows
-    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kValuRowsPerBlock + wave * 16;
-    const int ngroups = static_cast<int>(k / 64);
-
-    float acc[4][M];
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int t = 0; t < M; ++t) acc[p][t] = 0.0f;
-
-    for (int g0 = 0; g0 < ngroups; g0 += kValuChunkGroups) {
-        const int cg = min(kValuChunkGroups, ngroups - g0);
-        __syncthreads();
-        for (int t = 0; t < M; ++t) prepare_x<256>(x + t * k + 64 * g0, cg, &xg[t][0]);
-        __syncthreads();
-        const int j = g0 + sub;
-        const bool gok = sub < cg;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int64_t row = row0 + 4 * p + slot;
-            if (row < n && gok) {
-                const uint8_t *blk = w + row * row_bytes + (j >> 2) * kBlockBytes;
-                const int grp = j & 3;
-                const uint4 hdr = load_stream16(blk);
-                const uint4 qa = load_stream16(blk + 16 + 32 * grp);
-                const uint4 qb = load_stream16(blk + 32 + 32 * grp);
-                GroupCodes c;
-                decode_group(hdr, qa, qb, pair_select(grp), c);
-#pragma unroll
-                for (int t = 0; t < M; ++t) acc[p][t] += xg[t][sub].scale * group_dot(c, xg[t][sub]);
-            }
-        }
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int64_t row = row0 + 4 * p + slot;
-#pragma unroll
-        for (int t = 0; t < M; ++t) {
-            const float v = group_sum<16>(acc[p][t]);
-            if (sub == 0 && row < n) y[t * n + row] = v;
-        }
-    }
-}
-
-// ------------------------------------------------------- m >= 16 (MFMA)
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kMfmaWaves = 8;          // 512 threads per block
-// 16-row weight tiles per wave: two for up to 32 tokens, one above (registers)
-template <int MT>
-constexpr int mfma_tiles_n() { return MT <= 2 ? 2 : 1; }
-template <int MT>
-constexpr int mfma_rows() { return kMfmaWaves * mfma_tiles_n<MT>() * 16; }
-constexpr int kStageK = 128;           // activations per LDS stage: half a super-block
-constexpr int kARowHalves = kStageK + 8;  // staged token row, padded by 16 bytes
+__device__ __forceinline__ uint4 as_uint4(u32x4_t v) { return make_uint4(v.x, v.y, v.z, v.w); }
+__device__ __forceinline__ float4_t as_float4(u32x4_t v) { return __builtin_bit_cast(float4_t, v); }
 
-// Position of in-stage activation kk (0..127) inside a staged token row: the
-// order in which the B operand below consumes the codes.  A lane-quarter kq
-// (lanes 16kq..16kq+15) owns code bytes [16kq, 16kq+16) of the half block's 64
-// code bytes: group 2h + kq/2, bytes 16*(kq%2).. of that group.  Its dword d
-// (bytes 4d..4d+3) splits into the nibble pairs (byte0, byte2) and
-// (byte1, byte3); MFMA step i takes the low (i even) or high (i odd) nibbles
-// of dwords 2*(i/2) and 2*(i/2)+1.
+constexpr int kStageK = 128;  // activations per stage: half a super-block
+
+// Scratch block of one (stage, 16-token tile):
+//   [0, 8192)     A fragments: [MFMA step i][part: hi, lo][lane][8 f16]
+//   [8192, 8448)  per token: f16 hi[4], lo[4] of the four sub-block sums of (hi + lo)
+//   [8448, 8512)  per token: f32 sum over the stage of (hi + lo)
+//   [8512, 8576)  per token: f32 2^e (0: all zero; NaN: a non-finite input)
+constexpr int kSubOff = 8192;
+constexpr int kBiasOff = 8448;
+constexpr int kEscOff = 8512;
+constexpr int kTileStageBytes = 8576;
+
+// Position of in-stage activation kk (0..127) in the operand order: the order
+// in which the B operand below consumes the codes.  A lane-quarter kq (lanes
+// 16kq..16kq+15) owns code bytes [16kq, 16kq+16) of the half block's 64 code
+// bytes: group 2h + kq/2, bytes 16*(kq%2).. of that group.  Its dword d (bytes
+// 4d..4d+3) splits into the nibble pairs (byte0, byte2) and (byte1, byte3);
+// MFMA step i takes the low (i even) or high (i odd) nibbles of dwords
+// 2*(i/2) and 2*(i/2)+1.  Result: kq*32 + i*8 + j, j the slot in the lane's 8.
 __device__ __forceinline__ int stage_pos(int kk) {
     const int gg = kk >> 6;
     const int r = kk & 63;
@@ -134,40 +91,33 @@ __device__ __forceinline__ uint32_t pair_operand(uint32_t pair, uint32_t sc2) {
 }
 
 // ---- activations, converted once per call ----------------------------------
-// For every stage s (activations [128 s, 128 s + 128)) the scratch holds one
-// block of stage_bytes(m) bytes, laid out exactly as the LDS copy consumes it:
-//   hi[m][128]  f16 of x * 2^-e in staged order (stage_pos)
-//   lo[m][128]  f16 of the remainder
-//   sub[m][4]   f32 sums of (hi + lo) over each of the stage's four sub-blocks
-//   bias[m4]    f32 sum of (hi + lo) over the stage           (m4 = m rounded up to 4)
-//   escale[m4]  f32 2^e (0: all zero; NaN: a non-finite input)
-__host__ __device__ constexpr int64_t stage_bytes(int m) {
-    return ((static_cast<int64_t>(m) * 528 + 8 * ((m + 3) / 4 * 4 / 4) * 4 + 15) / 16) * 16;
-}
-
-// One half-wave per (stage, token); each lane converts four activations.  The
-// same kernel zero-fills y, which the matrix-core kernel then accumulates into.
+// One half-wave per (stage, token) of the padded token range 16*mt; each lane
+// converts four activations.  Tokens >= m are written as zeros.  With
+// zero_y the same kernel zero-fills y, which the matrix-core kernel then
+// accumulates into.
 __global__ __launch_bounds__(256) void x_prep_kernel(const float *x, uint8_t *__restrict__ xc, float *__restrict__ y,
-                                                      int m, int64_t k, int64_t ny) {
+                                                      int m, int mt, int64_t k, int64_t ny) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     for (int64_t i = gid; i < ny; i += static_cast<int64_t>(gridDim.x) * 256) y[i] = 0.0f;
 
     const int64_t nst = k / kStageK;
-    const int64_t pairs = nst * m;
+    const int tpad = 16 * mt;
+    const int64_t pairs = nst * tpad;
     const int c = threadIdx.x & 31;
     int64_t pair = gid >> 5;
     const bool live = pair < pairs;
     if (!live) pair = pairs - 1;  // keep the half-wave's shuffles uniform; no writes
-    const int64_t st = pair / m;
-    const int tok = static_cast<int>(pair % m);
-    const float *px = x + static_cast<int64_t>(tok) * k + st * kStageK + 4 * c;
+    const int64_t st = pair / tpad;
+    const int tok = static_cast<int>(pair % tpad);
+    const bool real = tok < m;
+    const float *px = x + static_cast<int64_t>(real ? tok : 0) * k + st * kStageK + 4 * c;
     float v[4];
     float amax = 0.0f;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        v[b] = px[b];
+        v[b] = real ? px[b] : 0.0f;
         float a = fabsf(v[b]);
-        a = (a <= FLT_MAX) ? a : INFINITY;
+        a = (a <= FLT_MAX) ? a : INFINITY;  // NaN counts as non-finite
         amax = fmaxf(amax, a);
     }
     amax = lane_group_max<32>(amax);
@@ -186,308 +136,359 @@ __global__ __launch_bounds__(256) void x_prep_kernel(const float *x, uint8_t *__
     const float sub8 = lane_group_sum<8>(part);
     const float tot = lane_group_sum<32>(part);
     if (!live) return;
-    uint8_t *blk = xc + st * stage_bytes(m);
-    const int m4 = (m + 3) / 4 * 4;
-    const int pos = stage_pos(4 * c);  // activations 4c..4c+3 land at pos + {0, 2, 1, 3}
-    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-    *reinterpret_cast<half4_t *>(blk + (static_cast<int64_t>(tok) * 128 + pos) * 2) = half4_t{hi[0], hi[2], hi[1], hi[3]};
-    *reinterpret_cast<half4_t *>(blk + (static_cast<int64_t>(m + tok) * 128 + pos) * 2) =
+    uint8_t *blk = xc + (st * mt + tok / 16) * kTileStageBytes;
+    const int col = tok & 15;
+    // activations 4c..4c+3 land at positions pos + {0, 2, 1, 3} of one lane
+    const int pos = stage_pos(4 * c);
+    const int kq = pos >> 5;
+    const int i = (pos >> 3) & 3;
+    const int j0 = pos & 7;
+    const int lane_slot = col + 16 * kq;
+    *reinterpret_cast<half4_t *>(blk + ((i * 2 + 0) * 64 + lane_slot) * 16 + j0 * 2) =
+        half4_t{hi[0], hi[2], hi[1], hi[3]};
+    *reinterpret_cast<half4_t *>(blk + ((i * 2 + 1) * 64 + lane_slot) * 16 + j0 * 2) =
         half4_t{lo[0], lo[2], lo[1], lo[3]};
-    float *sub = reinterpret_cast<float *>(blk + static_cast<int64_t>(m) * 512);
-    float *bias = sub + 4 * m;
-    float *esc = bias + m4;
-    if ((c & 7) == 0) sub[4 * tok + (c >> 3)] = sub8;
+    if ((c & 7) == 0) {
+        _Float16 *s = reinterpret_cast<_Float16 *>(blk + kSubOff) + col * 8;
+        const _Float16 sh = static_cast<_Float16>(sub8);
+        s[c >> 3] = sh;
+        s[4 + (c >> 3)] = static_cast<_Float16>(sub8 - static_cast<float>(sh));
+    }
     if (c == 0) {
-        bias[tok] = tot;
-        esc[tok] = finite ? (nz ? ldexpf(1.0f, e) : 0.0f) : NAN;
+        reinterpret_cast<float *>(blk + kBiasOff)[col] = tot;
+        reinterpret_cast<float *>(blk + kEscOff)[col] = finite ? (nz ? ldexpf(1.0f, e) : 0.0f) : NAN;
     }
 }
 
-template <int NT>
-struct StageW {
-    uint4 hdr[NT];
-    uint4 q[NT];
+// ---- the matrix-core kernel ---------------------------------------------------
+// Activations of one (half super-block, token tile) step.
+struct AStep {
+    uint4 f[8];     // fragments: [MFMA step i][hi, lo]
+    uint4 sub;      // the lane's token: f16 hi[4], lo[4] sub-block sums
+    float4_t bias;  // tokens 4kq .. 4kq+3 of the tile
+    float4_t esc;
 };
 
-// Per-block LDS: one stage of activations for 16*MT tokens (rows >= m stay 0).
-template <int MT>
-struct MfmaShared {
-    alignas(16) _Float16 a_hi[16 * MT][kARowHalves];
-    alignas(16) _Float16 a_lo[16 * MT][kARowHalves];
-    alignas(16) float sub[16 * MT][4];
-    alignas(16) float bias[16 * MT];
-    alignas(16) float escale[16 * MT];
+// B operands of one row tile for one half super-block.
+struct BOps {
+    half8_t b[4];
+    half8_t bmin;
+    float d, dmin;
 };
 
-// 16-byte chunks of one stage block: hi rows, lo rows, sub, bias, escale.
-__device__ __forceinline__ int stage_chunks(int m) { return 33 * m + (m + 3) / 4 * 2; }
-
-// y += W x over a stream-K share of the (row block, super-block) units: block
-// b owns units [b U / G, (b+1) U / G) in row-block-major order and adds its
-// partial tiles into y (zero-filled by x_prep_kernel) whenever the row block
-// changes.
+// Workgroup = W = 2S waves, 16*NT rows, a K range [sb0, sb1) of super-blocks
+// (block b: row block b / ksplit, K part b % ksplit).  The range is walked in
+// stages of S super-blocks.  Each stage's weights (16*NT rows x 144*S bytes)
+// are copied into LDS with loads that run along the rows (consecutive lanes,
+// consecutive 16-byte pieces of a row: long runs of each row, as the weights
+// are laid out), P stages ahead of use, into a double-buffered LDS stage;
+// one barrier per stage.  Wave w multiplies half super-block w of the stage
+// for all row and token tiles, with its activations read from scratch into
+// registers one step ahead.  At the end the waves' sums are added in LDS in a
+// fixed order, then stored (ksplit == 1) or added into y with atomics
+// (ksplit > 1, y zeroed first).
+// Stages of weights in flight: fewer with several token tiles, whose
+// operands take the registers.
 template <int MT>
-__global__ __launch_bounds__(512, 2) void batched_mfma_kernel(const uint8_t *__restrict__ w,
-                                                              const uint8_t *__restrict__ xc, float *__restrict__ y,
-                                                              int m, int64_t n, int64_t k, int64_t row_bytes) {
-    constexpr int NT = mfma_tiles_n<MT>();
-    constexpr int kRows = mfma_rows<MT>();
-    constexpr int kCopyPerThread = (33 * 16 * MT + 8 * MT + 511) / 512;
-    __shared__ __align__(16) MfmaShared<MT> sh;
+constexpr int weight_stages_ahead() { return MT == 1 ? 4 : 2; }
+
+template <int NT, int S>
+struct StageGeom {
+    static constexpr int kRows = 16 * NT;
+    static constexpr int kRowLds = 144 * S + 16;  // padded: the 16 rows of a tile hit distinct LDS banks
+    static constexpr int kChunks = kRows * 9 * S;  // 16-byte pieces per stage
+    static constexpr int kBlock = 128 * S;
+    static constexpr int kLoads = (kChunks + kBlock - 1) / kBlock;  // per thread per stage
+    static constexpr int kStageLds = kRows * kRowLds;
+};
+
+template <int NT, int MT, int S>
+__global__ __launch_bounds__(128 * S, 1) void batched_mfma_kernel(const uint8_t *__restrict__ w,
+                                                                  const uint8_t *__restrict__ xc,
+                                                                  float *__restrict__ y, int m, int64_t n,
+                                                                  int64_t k, int64_t row_bytes, int ksplit,
+                                                                  int64_t xc_bytes) {
+    using G = StageGeom<NT, S>;
+    constexpr int W = 2 * S;
+    constexpr int P = weight_stages_ahead<MT>();
+    __shared__ __align__(16) uint8_t stage_lds[2][G::kStageLds];
+    __shared__ __align__(16) float4_t red[W][NT * MT][64];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int col = lane & 15;
     const int kq = lane >> 4;
 
     const int nsb = static_cast<int>(k / kBlockWeights);
-    const int64_t nrb = (n + kRows - 1) / kRows;
-    const int64_t units = nrb * nsb;
-    const int64_t u0 = units * blockIdx.x / gridDim.x;
-    const int64_t u1 = units * (blockIdx.x + 1) / gridDim.x;
+    const int64_t rb = blockIdx.x / ksplit;
+    const int ks = static_cast<int>(blockIdx.x % ksplit);
+    const int sb0 = static_cast<int>(static_cast<int64_t>(nsb) * ks / ksplit);
+    const int sb1 = static_cast<int>(static_cast<int64_t>(nsb) * (ks + 1) / ksplit);
+    const int nstages = (sb1 - sb0 + S - 1) / S;
 
-    // tokens >= m are never copied: clear the whole stage area once
-    for (int i = threadIdx.x; i < static_cast<int>(sizeof(MfmaShared<MT>) / 4); i += 512)
-        reinterpret_cast<float *>(&sh)[i] = 0.0f;
+    const int64_t row0 = rb * G::kRows;
+    const int64_t rows_here = n - row0 < G::kRows ? n - row0 : G::kRows;
+    // rows past n read as zeros; their results are not stored
+    const __amdgpu_buffer_rsrc_t wr = stream_rsrc(w + row0 * row_bytes, static_cast<int>(rows_here * row_bytes));
+    const __amdgpu_buffer_rsrc_t ar = stream_rsrc(xc, static_cast<int>(xc_bytes));
 
-    // ---- stage copy: chunk q of the scratch block -> fixed LDS address
-    const int nchunks = stage_chunks(m);
-    const int m4 = (m + 3) / 4 * 4;
-    uint32_t src_off[kCopyPerThread];
-    uint8_t *dst[kCopyPerThread];
-    bool cp_ok[kCopyPerThread];
+    // ---- this thread's pieces of every stage copy
+    uint32_t g_off[G::kLoads];   // byte offset in the row block, stage base excluded
+    uint32_t l_off[G::kLoads];   // byte offset in the LDS stage
+    int p_sb[G::kLoads];         // super-block of the piece inside the stage (S: padding)
 #pragma unroll
-    for (int j = 0; j < kCopyPerThread; ++j) {
-        const int q = threadIdx.x + 512 * j;
-        cp_ok[j] = q < nchunks;
-        const int qq = cp_ok[j] ? q : 0;
-        src_off[j] = static_cast<uint32_t>(qq) * 16u;
-        uint8_t *d;
-        if (qq < 16 * m) d = reinterpret_cast<uint8_t *>(&sh.a_hi[qq >> 4][8 * (qq & 15)]);
-        else if (qq < 32 * m) d = reinterpret_cast<uint8_t *>(&sh.a_lo[(qq - 16 * m) >> 4][8 * (qq & 15)]);
-        else if (qq < 33 * m) d = reinterpret_cast<uint8_t *>(&sh.sub[qq - 32 * m][0]);
-        else if (qq < 33 * m + m4 / 4) d = reinterpret_cast<uint8_t *>(&sh.bias[4 * (qq - 33 * m)]);
-        else d = reinterpret_cast<uint8_t *>(&sh.escale[4 * (qq - 33 * m - m4 / 4)]);
-        dst[j] = d;
+    for (int j = 0; j < G::kLoads; ++j) {
+        const int c = j * G::kBlock + static_cast<int>(threadIdx.x);
+        const bool ok = c < G::kChunks;
+        const int cc = ok ? c : 0;
+        const int row = cc / (9 * S);
+        const int piece = cc % (9 * S);
+        g_off[j] = static_cast<uint32_t>(row * row_bytes + piece * 16);
+        l_off[j] = static_cast<uint32_t>(row * G::kRowLds + piece * 16);
+        p_sb[j] = ok ? piece / 9 : S;
     }
-    const int64_t sbytes = stage_bytes(m);
-    const int64_t xc_bytes = sbytes * (k / kStageK);
-    struct StageC {
-        uint4 v[kCopyPerThread];
-    };
-    auto load_c = [&](StageC &cs, int64_t st) {
-        const __amdgpu_buffer_rsrc_t r = stream_rsrc(xc + st * sbytes, static_cast<int>(sbytes));
+    typedef uint4 StageRegs[G::kLoads];
+    // loads of stage st (nothing past the range: such pieces point past the
+    // descriptor's end and read zeros without a fetch)
+    auto issue_stage = [&](StageRegs &r, int st) {
+        const int sbs = sb0 + st * S;
+        const int sbn = sb1 - sbs;  // super-blocks left in the range (may be <= 0)
 #pragma unroll
-        for (int j = 0; j < kCopyPerThread; ++j) cs.v[j] = buffer_load16(r, src_off[j]);
+        for (int j = 0; j < G::kLoads; ++j) {
+            const uint32_t off = p_sb[j] < sbn ? g_off[j] : 0x40000000u;
+            r[j] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(wr, static_cast<int>(off), sbs * kBlockBytes, 0));
+        }
     };
-    auto store_c = [&](const StageC &cs) {
+    auto write_stage = [&](const StageRegs &r, int buf) {
 #pragma unroll
-        for (int j = 0; j < kCopyPerThread; ++j)
-            if (cp_ok[j]) *reinterpret_cast<uint4 *>(dst[j]) = cs.v[j];
-    };
-
-    // ---- weights of unit (rb, sb), half h
-    auto load_w = [&](StageW<NT> &ws, int64_t u, int h) {
-        const int64_t rb = u / nsb;
-        const int sb = static_cast<int>(u - rb * nsb);
-        const int64_t row0 = rb * kRows;
-        const int64_t rows_here = min<int64_t>(kRows, n - row0);
-        const __amdgpu_buffer_rsrc_t wr = stream_rsrc(w + row0 * row_bytes, static_cast<int>(rows_here * row_bytes));
-        const int soff = sb * kBlockBytes;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const uint32_t vrow = static_cast<uint32_t>((wave * NT * 16 + t * 16 + col) * row_bytes);
-            const u32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(wr, static_cast<int>(vrow + 16 + 64 * h + 16 * kq),
-                                                                     soff, 0);
-            ws.q[t] = make_uint4(q.x, q.y, q.z, q.w);
-            if (h == 0) {
-                const u32x4_t hd = __builtin_amdgcn_raw_buffer_load_b128(wr, static_cast<int>(vrow), soff, 0);
-                ws.hdr[t] = make_uint4(hd.x, hd.y, hd.z, hd.w);
-            }
+        for (int j = 0; j < G::kLoads; ++j) {
+            if (j * G::kBlock + static_cast<int>(threadIdx.x) < G::kChunks)
+                *reinterpret_cast<uint4 *>(&stage_lds[buf][l_off[j]]) = r[j];
         }
     };
 
-    const PairSelect psel0 = pair_select(kq >> 1);
-    const PairSelect psel1 = pair_select(2 + (kq >> 1));
+    // ---- activations: a lane whose token (per tile) is past m reads nothing
+    uint32_t a_lane[MT];
+#pragma unroll
+    for (int p = 0; p < MT; ++p) a_lane[p] = 16 * p + col < m ? 0u : 0x40000000u;
+    auto load_a = [&](AStep &a, int h, int p) {
+        const int soff = (h * MT + p) * kTileStageBytes;
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+            a.f[f] = as_uint4(
+                __builtin_amdgcn_raw_buffer_load_b128(ar, static_cast<int>(a_lane[p] + f * 1024 + lane * 16), soff, 0));
+        a.sub = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(ar, static_cast<int>(a_lane[p] + kSubOff + col * 16), soff, 0));
+        a.bias = as_float4(__builtin_amdgcn_raw_buffer_load_b128(ar, kBiasOff + kq * 16, soff, 0));
+        a.esc = as_float4(__builtin_amdgcn_raw_buffer_load_b128(ar, kEscOff + kq * 16, soff, 0));
+    };
+    // the wave's half super-block of stage st (past the range: the last stage,
+    // whose results are not used)
+    const int sbl = wave >> 1;   // super-block inside the stage
+    const int hw = wave & 1;     // half of that super-block
+    auto half_of = [&](int st) { return 2 * (sb0 + st * S + sbl) + hw; };
+    auto half_live = [&](int st) { return st < nstages && sb0 + st * S + sbl < sb1; };
+
+    // B operands of row tile t from the LDS stage
+    const PairSelect ps = pair_select(2 * hw + (kq >> 1));
+    auto build_b = [&](BOps &o, int buf, int t) {
+        const uint8_t *rowp = &stage_lds[buf][(16 * t + col) * G::kRowLds + sbl * kBlockBytes];
+        const uint4 hdr = *reinterpret_cast<const uint4 *>(rowp);
+        const uint4 qv = *reinterpret_cast<const uint4 *>(rowp + 16 + 64 * hw + 16 * kq);
+        o.d = half_bits_to_float(hdr.x);
+        o.dmin = half_bits_to_float(hdr.x >> 16);
+        uint32_t scp, mp;
+        scale_min_pair(hdr.y, hdr.z, hdr.w, ps, scp, mp);
+        const uint32_t sc2_lo = (scp & 0xffu) * 0x00010001u;
+        const uint32_t sc2_hi = ((scp >> 8) & 0xffu) * 0x00010001u;
+        const uint32_t u[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t sc2 = (i & 1) ? sc2_hi : sc2_lo;
+            const int shn = (i & 1) ? 4 : 0;
+            uint32_t v4[4];
+#pragma unroll
+            for (int d2 = 0; d2 < 2; ++d2) {
+                const uint32_t word = u[2 * (i >> 1) + d2];
+                v4[2 * d2 + 0] = pair_operand((word >> shn) & 0x000f000fu, sc2);
+                v4[2 * d2 + 1] = pair_operand((word >> (8 + shn)) & 0x000f000fu, sc2);
+            }
+            o.b[i] = __builtin_bit_cast(half8_t, u32x4_t{v4[0], v4[1], v4[2], v4[3]});
+        }
+        // mins of the quarter's two sub-blocks (even quarters only) as exact f16
+        const _Float16 m0 = (kq & 1) ? _Float16(0) : static_cast<_Float16>(static_cast<float>(mp & 0xffu));
+        const _Float16 m1 = (kq & 1) ? _Float16(0) : static_cast<_Float16>(static_cast<float>((mp >> 8) & 0xffu));
+        o.bmin = half8_t{m0, m1, 0, 0, 0, 0, 0, 0};
+    };
 
     float4_t acc[NT][MT];
-    auto zero_acc = [&]() {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int p = 0; p < MT; ++p) acc[t][p] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    };
-    auto flush = [&](int64_t rb) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int64_t row = rb * kRows + wave * NT * 16 + t * 16 + col;
-#pragma unroll
-            for (int p = 0; p < MT; ++p) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tok = 16 * p + 4 * kq + r;
-                    if (row < n && tok < m) unsafeAtomicAdd(&y[static_cast<int64_t>(tok) * n + row], acc[t][p][r]);
-                }
-            }
-        }
-    };
+        for (int p = 0; p < MT; ++p) acc[t][p] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto compute = [&](const StageW<NT> &ws, const uint4 (&hdr)[NT], int h) {
-        const PairSelect &ps = h ? psel1 : psel0;
+    // One (row tile, token tile) product of the step and its epilogue.
+    auto multiply = [&](const BOps &bo, const AStep &a, float4_t &out) {
+        // the lane's token's sums of its quarter's two sub-blocks, hi and lo
         const int gg = kq >> 1;
+        const uint32_t shi = (kq & 1) ? 0u : (gg ? a.sub.y : a.sub.x);
+        const uint32_t slo = (kq & 1) ? 0u : (gg ? a.sub.w : a.sub.z);
+        const half8_t amin_hi = __builtin_bit_cast(half8_t, u32x4_t{shi, 0u, 0u, 0u});
+        const half8_t amin_lo = __builtin_bit_cast(half8_t, u32x4_t{slo, 0u, 0u, 0u});
+        float4_t pacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const float dd = half_bits_to_float(hdr[t].x);
-            const float dm = half_bits_to_float(hdr[t].x >> 16);
-            uint32_t scp, mp;
-            scale_min_pair(hdr[t].y, hdr[t].z, hdr[t].w, ps, scp, mp);
-            const uint32_t sc2_lo = (scp & 0xffu) * 0x00010001u;
-            const uint32_t sc2_hi = ((scp >> 8) & 0xffu) * 0x00010001u;
-            const uint32_t u[4] = {ws.q[t].x, ws.q[t].y, ws.q[t].z, ws.q[t].w};
-            half8_t bop[4];
+        for (int i = 0; i < 4; ++i) {
+            pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a.f[2 * i]), bo.b[i], pacc, 0, 0,
+                                                         0);
+            pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a.f[2 * i + 1]), bo.b[i], pacc, 0,
+                                                         0, 0);
+        }
+        float4_t qacc = {0.0f, 0.0f, 0.0f, 0.0f};
+        qacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(amin_hi, bo.bmin, qacc, 0, 0, 0);
+        qacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(amin_lo, bo.bmin, qacc, 0, 0, 0);
+        // pacc[r] = sum_k A[tok_r, k] * (1024 + sc q)[k, row]; tok_r = 16p + 4kq + r
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t sc2 = (i & 1) ? sc2_hi : sc2_lo;
-                const int shn = (i & 1) ? 4 : 0;
-                uint32_t v4[4];
-#pragma unroll
-                for (int d2 = 0; d2 < 2; ++d2) {
-                    const uint32_t word = u[2 * (i >> 1) + d2];
-                    v4[2 * d2 + 0] = pair_operand((word >> shn) & 0x000f000fu, sc2);
-                    v4[2 * d2 + 1] = pair_operand((word >> (8 + shn)) & 0x000f000fu, sc2);
-                }
-                bop[i] = __builtin_bit_cast(half8_t, u32x4_t{v4[0], v4[1], v4[2], v4[3]});
-            }
-            // mins of the lane's two sub-blocks (even quarters only) as exact f16
-            const _Float16 m0 = (kq & 1) ? _Float16(0) : static_cast<_Float16>(static_cast<float>(mp & 0xffu));
-            const _Float16 m1 = (kq & 1) ? _Float16(0) : static_cast<_Float16>(static_cast<float>((mp >> 8) & 0xffu));
-            const half8_t bmin = {m0, m1, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-            for (int p = 0; p < MT; ++p) {
-                const int tok = 16 * p + col;
-                float4_t pacc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const half8_t ahi = *reinterpret_cast<const half8_t *>(&sh.a_hi[tok][kq * 32 + i * 8]);
-                    const half8_t alo = *reinterpret_cast<const half8_t *>(&sh.a_lo[tok][kq * 32 + i * 8]);
-                    pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bop[i], pacc, 0, 0, 0);
-                    pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bop[i], pacc, 0, 0, 0);
-                }
-                // sub-block sums of this quarter's group as the A operand of the min product
-                const float s0 = sh.sub[tok][2 * gg], s1 = sh.sub[tok][2 * gg + 1];
-                const _Float16 s0h = static_cast<_Float16>(s0), s1h = static_cast<_Float16>(s1);
-                const _Float16 s0l = static_cast<_Float16>(s0 - static_cast<float>(s0h));
-                const _Float16 s1l = static_cast<_Float16>(s1 - static_cast<float>(s1h));
-                const half8_t shi = {s0h, s1h, 0, 0, 0, 0, 0, 0};
-                const half8_t slo = {s0l, s1l, 0, 0, 0, 0, 0, 0};
-                float4_t qacc = {0.0f, 0.0f, 0.0f, 0.0f};
-                qacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(shi, bmin, qacc, 0, 0, 0);
-                qacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(slo, bmin, qacc, 0, 0, 0);
-                // pacc[r] = sum_k A[tok_r, k] * (1024 + sc q)[k, col]; tok_r = 16p + 4kq + r
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tr = 16 * p + 4 * kq + r;
-                    const float code_part = pacc[r] - 1024.0f * sh.bias[tr];
-                    acc[t][p][r] += sh.escale[tr] * (dd * code_part - dm * qacc[r]);
-                }
-                // one token tile's operands live at a time (register budget)
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int r = 0; r < 4; ++r) {
+            const float code_part = pacc[r] - 1024.0f * a.bias[r];
+            out[r] += a.esc[r] * (bo.d * code_part - bo.dmin * qacc[r]);
         }
     };
 
-    zero_acc();
-    if (u0 >= u1) return;
-    // Pipeline: the weights and activations of the next half block are loaded
-    // while the current one is multiplied.  Loads past the last unit re-read
-    // the last unit (unused).
-    StageC ca, cb;
-    StageW<NT> wa, wb;
-    int64_t cur_rb = u0 / nsb;
-    load_c(ca, 2 * (u0 % nsb));
-    load_w(wa, u0, 0);
-    for (int64_t u = u0; u < u1; ++u) {
-        const int64_t rb = u / nsb;
-        const int sb = static_cast<int>(u - rb * nsb);
-        if (rb != cur_rb) {
-            flush(cur_rb);
-            zero_acc();
-            cur_rb = rb;
-        }
-        // half 0
-        load_c(cb, 2 * sb + 1);
-        load_w(wb, u, 1);
-        __syncthreads();
-        store_c(ca);
-        __syncthreads();
-        compute(wa, wa.hdr, 0);
-        // half 1 (headers of this super-block still in wa)
-        uint4 hdr[NT];
+    // ---- pipeline: weights P stages ahead (register ring -> LDS), the wave's
+    // activations one step ahead.  Unrolled by P so every ring slot, LDS
+    // buffer and activation buffer index is a constant.
+    static_assert(P % 2 == 0, "LDS buffer parity must repeat with the ring");
+    StageRegs ring[P];
+    AStep abuf[2];
+    BOps bo[MT == 1 ? 1 : NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) hdr[t] = wa.hdr[t];
-        const int64_t un = u + 1 < u1 ? u + 1 : u;
-        load_c(ca, 2 * (un % nsb));
-        load_w(wa, un, 0);
-        __syncthreads();
-        store_c(cb);
-        __syncthreads();
-        compute(wb, hdr, 1);
+    for (int q = 0; q < P; ++q) issue_stage(ring[q], q);
+    load_a(abuf[0], half_of(0), 0);
+    write_stage(ring[0], 0);
+    issue_stage(ring[0], P);
+    for (int s0 = 0; s0 < nstages; s0 += P) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+            const int st = s0 + u;
+            __syncthreads();  // stage st is in LDS; every wave is done with stage st-1
+            if (st >= nstages) break;
+            const bool live = half_live(st);
+#pragma unroll
+            for (int p = 0; p < MT; ++p) {
+                const int step = u * MT + p;
+                if (p + 1 < MT) load_a(abuf[(step + 1) & 1], half_of(st), p + 1);
+                else load_a(abuf[(step + 1) & 1], half_of(st + 1), 0);
+                if (live) {
+                    if constexpr (MT == 1) {
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) {
+                            build_b(bo[0], u & 1, t);
+                            multiply(bo[0], abuf[step & 1], acc[t][0]);
+                        }
+                    } else {
+                        if (p == 0) {
+#pragma unroll
+                            for (int t = 0; t < NT; ++t) build_b(bo[t], u & 1, t);
+                        }
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) multiply(bo[t], abuf[step & 1], acc[t][p]);
+                    }
+                }
+            }
+            // stage st+1 into the other LDS buffer (its loads were issued P-1
+            // stages ago), then reuse the ring slot for stage st+1+P
+            write_stage(ring[(u + 1) % P], (u + 1) & 1);
+            issue_stage(ring[(u + 1) % P], st + 1 + P);
+        }
     }
-    flush(cur_rb);
-    (void)xc_bytes;
+
+    // add the W waves' tiles in wave order, then store or accumulate
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int p = 0; p < MT; ++p) red[wave][t * MT + p][lane] = acc[t][p];
+    __syncthreads();
+    for (int e = static_cast<int>(threadIdx.x); e < NT * MT * 64; e += G::kBlock) {
+        const int tp = e >> 6;
+        const int ln = e & 63;
+        float4_t sum = red[0][tp][ln];
+#pragma unroll
+        for (int v = 1; v < W; ++v) sum += red[v][tp][ln];
+        const int t = tp / MT;
+        const int p = tp % MT;
+        const int64_t row = row0 + 16 * t + (ln & 15);
+        if (row >= n) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tok = 16 * p + 4 * (ln >> 4) + r;
+            if (tok >= m) continue;
+            float *dst = y + static_cast<int64_t>(tok) * n + row;
+            if (ksplit == 1) *dst = sum[r];
+            else unsafeAtomicAdd(dst, sum[r]);
+        }
+    }
 }
 
 // ------------------------------------------------------------- launchers
 namespace {
 
-template <int M>
-hipError_t launch_valu(const uint8_t *w, const float *x, float *y, int64_t n, int64_t k, hipStream_t stream) {
-    const int64_t grid = (n + kValuRowsPerBlock - 1) / kValuRowsPerBlock;
-    hipLaunchKernelGGL(batched_valu_kernel<M>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, w, x, y, n, k,
-                       (k / kBlockWeights) * kBlockBytes);
-    return hipGetLastError();
-}
+// Super-blocks per stage (the workgroup has 2 waves per super-block).
+#ifndef Q4K_BATCH_STAGE_SB
+#define Q4K_BATCH_STAGE_SB 4
+#endif
 
-hipError_t dispatch_valu(const uint8_t *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
-                         hipStream_t stream) {
-    switch (m) {
-        case 2: return launch_valu<2>(w, x, y, n, k, stream);
-        case 3: return launch_valu<3>(w, x, y, n, k, stream);
-        case 4: return launch_valu<4>(w, x, y, n, k, stream);
-        case 5: return launch_valu<5>(w, x, y, n, k, stream);
-        case 6: return launch_valu<6>(w, x, y, n, k, stream);
-        case 7: return launch_valu<7>(w, x, y, n, k, stream);
-        case 8: return launch_valu<8>(w, x, y, n, k, stream);
-        case 9: return launch_valu<9>(w, x, y, n, k, stream);
-        case 10: return launch_valu<10>(w, x, y, n, k, stream);
-        case 11: return launch_valu<11>(w, x, y, n, k, stream);
-        case 12: return launch_valu<12>(w, x, y, n, k, stream);
-        case 13: return launch_valu<13>(w, x, y, n, k, stream);
-        case 14: return launch_valu<14>(w, x, y, n, k, stream);
-        default: return launch_valu<15>(w, x, y, n, k, stream);
-    }
-}
-
-template <int MT>
-hipError_t launch_mfma(const uint8_t *w, const float *x, float *y, int m, int64_t n, int64_t k,
+template <int NT, int MT>
+hipError_t launch_mfma(const uint8_t *w, const float *x, float *y, int m, int64_t n, int64_t k, int ksplit,
                        hipStream_t stream) {
+    constexpr int S = Q4K_BATCH_STAGE_SB;
     const int64_t nst = k / kStageK;
-    const int64_t bytes = stage_bytes(m) * nst;
+    const int64_t bytes = nst * MT * kTileStageBytes;
     uint8_t *xc = nullptr;
     hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&xc), static_cast<size_t>(bytes), stream);
     if (e != hipSuccess) return e;
-    const int64_t prep_threads = nst * m * 32;
+    const int64_t prep_threads = nst * 16 * MT * 32;
+    const int64_t ny = ksplit > 1 ? static_cast<int64_t>(m) * n : 0;
     const int64_t prep_blocks = (prep_threads + 255) / 256;
-    hipLaunchKernelGGL(x_prep_kernel, dim3(static_cast<unsigned>(prep_blocks)), dim3(256), 0, stream, x, xc, y, m, k,
-                       static_cast<int64_t>(m) * n);
+    hipLaunchKernelGGL(x_prep_kernel, dim3(static_cast<unsigned>(prep_blocks)), dim3(256), 0, stream, x, xc, y, m, MT,
+                       k, ny);
     e = hipGetLastError();
     if (e == hipSuccess) {
-        const int grid = device_cu_count();
-        hipLaunchKernelGGL(batched_mfma_kernel<MT>, dim3(grid), dim3(512), 0, stream, w, xc, y, m, n, k,
-                           (k / kBlockWeights) * kBlockBytes);
+        const int64_t nrb = (n + 16 * NT - 1) / (16 * NT);
+        hipLaunchKernelGGL((batched_mfma_kernel<NT, MT, S>), dim3(static_cast<unsigned>(nrb * ksplit)), dim3(128 * S), 0,
+                           stream, w, xc, y, m, n, k, (k / kBlockWeights) * kBlockBytes, ksplit, bytes);
         e = hipGetLastError();
     }
     const hipError_t f = hipFreeAsync(xc, stream);
     return e != hipSuccess ? e : f;
+}
+
+// Rows per workgroup (16*NT) and the split of K across workgroups.  Each
+// workgroup reads its whole K range of activations (16*MT tokens x 4 bytes
+// per activation) besides its weights (0.5625 bytes per weight), so when
+// there are too few rows for every CU to get several, rows are grouped into
+// larger blocks and K is split across workgroups instead (their partial tiles
+// are then added into y with atomics).  The register budget caps the rows per
+// workgroup at 64 / 32 / 16 for 1 / 2-3 / 4 token tiles.
+#ifndef Q4K_BATCH_NT_CAP
+#define Q4K_BATCH_NT_CAP 4
+#endif
+template <int MT>
+hipError_t dispatch_mt(const uint8_t *w, const float *x, float *y, int m, int64_t n, int64_t k, hipStream_t stream) {
+    constexpr int kNtMax0 = MT == 1 ? 4 : (MT <= 3 ? 2 : 1);
+    constexpr int kNtMax = kNtMax0 < Q4K_BATCH_NT_CAP ? kNtMax0 : Q4K_BATCH_NT_CAP;
+    const int64_t cus = device_cu_count();
+    const int64_t nsb = k / kBlockWeights;
+    const int64_t per = n / (16 * cus);  // row tiles per CU with one row block each
+    if (per >= 1 || nsb < 2) {
+        const int64_t nt = per < 1 ? 1 : (per > kNtMax ? kNtMax : per);
+        if (nt >= 4) return launch_mfma<kNtMax, MT>(w, x, y, m, n, k, 1, stream);
+        if (nt == 3) return launch_mfma<(kNtMax < 3 ? kNtMax : 3), MT>(w, x, y, m, n, k, 1, stream);
+        if (nt == 2) return launch_mfma<(kNtMax < 2 ? kNtMax : 2), MT>(w, x, y, m, n, k, 1, stream);
+        return launch_mfma<1, MT>(w, x, y, m, n, k, 1, stream);
+    }
+    // fewer than 16 rows per CU: the largest row blocks, K split to fill the CUs
+    const int64_t nrb = (n + 16 * kNtMax - 1) / (16 * kNtMax);
+    int64_t ksplit = (cus + nrb - 1) / nrb;
+    if (ksplit > nsb) ksplit = nsb;
+    return launch_mfma<kNtMax, MT>(w, x, y, m, n, k, static_cast<int>(ksplit), stream);
 }
 
 }  // namespace
@@ -497,17 +498,16 @@ hipError_t launch_gemv_batched(const uint8_t *w, const float *x, float *y, int64
     if (m == 0 || n == 0) return hipSuccess;
     if (k == 0) return launch_fill_zero(y, m * n, stream);
     if (m == 1) return launch_gemv(w, nullptr, x, y, n, k, stream);
-    if (m < 16) return dispatch_valu(w, x, y, m, n, k, stream);
     hipError_t e = hipSuccess;
     // up to 64 tokens per launch; the weights are re-read per 64-token slice
     for (int64_t t0 = 0; t0 < m; t0 += 64) {
         const int mt = static_cast<int>(m - t0 < 64 ? m - t0 : 64);
         const float *xs = x + t0 * k;
         float *ys = y + t0 * n;
-        if (mt <= 16) e = launch_mfma<1>(w, xs, ys, mt, n, k, stream);
-        else if (mt <= 32) e = launch_mfma<2>(w, xs, ys, mt, n, k, stream);
-        else if (mt <= 48) e = launch_mfma<3>(w, xs, ys, mt, n, k, stream);
-        else e = launch_mfma<4>(w, xs, ys, mt, n, k, stream);
+        if (mt <= 16) e = dispatch_mt<1>(w, xs, ys, mt, n, k, stream);
+        else if (mt <= 32) e = dispatch_mt<2>(w, xs, ys, mt, n, k, stream);
+        else if (mt <= 48) e = dispatch_mt<3>(w, xs, ys, mt, n, k, stream);
+        else e = dispatch_mt<4>(w, xs, ys, mt, n, k, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
