@@ -62,6 +62,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-batched", action="store_true", help="skip the skinny-GEMM timings")
     ap.add_argument("--sweep", action="store_true",
                     help="also time every kernel at every config shape (table on stderr)")
     ap.add_argument("--case", default=None,
@@ -183,21 +184,35 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(wbytes["lm_head_9b"]),
                 "kernel": "q4k_gemv lm_head 248320x4096", "bytes_per_launch": kernel_bytes["gemv_lm_head"]}
 
-    # Context only: a plain read-only stream (a sum over 1 GiB) on this part.
-    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    big.sum()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for _ in range(20):
-        big.sum()
-    b.record(stream)
-    torch.cuda.synchronize()
-    stream_ceiling = big.numel() * 4 / (a.elapsed_time(b) / 20 * 1e-3) / 1e9
-    del big
+    # The skinny-GEMM workload over the same FFN weights (m tokens): one call
+    # per launch, weights rotated over >= 512 MiB of copies.
+    batched = {}
+    if not args.no_batched:
+        for nm in ("gate_9b", "down_9b"):
+            n_, k_ = shapes[nm]
+            sets_b = rotated([nm])
+            for mtok in (4, 16, 32, 64):
+                xs = torch.from_numpy(inputs.make_x(mtok, k_, config_id=4, tensor_id=100 + mtok)).to(dev)
+                yb = torch.empty((mtok, n_), dtype=torch.float32, device=dev)
+                for i in range(5):
+                    q4k.gemv_batched(sets_b[i % len(sets_b)][0], xs, y=yb, stream=stream)
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                reps = 50
+                torch.cuda.synchronize()
+                a.record(stream)
+                for i in range(reps):
+                    q4k.gemv_batched(sets_b[i % len(sets_b)][0], xs, y=yb, stream=stream)
+                b.record(stream)
+                torch.cuda.synchronize()
+                t = a.elapsed_time(b) / reps * 1e-3
+                batched[f"{nm} m={mtok}"] = {"mean_us": round(t * 1e6, 2),
+                                             "weight_GB/s": round(wbytes[nm] / t / 1e9, 1),
+                                             "TFLOP/s": round(2.0 * mtok * n_ * k_ / t / 1e12, 2)}
+            del sets_b
+
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s; per kernel {kernels}; "
-        f"read-only stream {stream_ceiling:.0f} GB/s; host wall {wall:.3f}s")
+        f"batched {batched}; host wall {wall:.3f}s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -243,7 +258,7 @@ def main():
             "weight_bytes_per_step": step_weight_bytes,
             "frac_hbm_peak_step": round(value / HBM_PEAK_GBS, 4),
             "kernels": kernels,
-            "read_only_stream_GBps": round(stream_ceiling, 1),
+            "batched_9b_ffn": batched,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
