@@ -169,6 +169,21 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const uint8_t *_
     // The loads are never inside a branch: at a control-flow join the wait
     // counters would have to assume the fewest loads in flight and drain the
     // prefetch.  Iterations past the end load nothing (0-byte descriptor).
+    //
+    // Results are not stored row by row: gfx9 counts stores with the loads,
+    // and a store on some paths through the loop but not others makes the
+    // wait counters drain loads still in flight.  Lane k of a row's lane group
+    // keeps the group's k-th result of the current window of LPR rows; the
+    // window is stored in one go when it is full (a wave streaming fewer than
+    // LPR rows per group stores only after the loop).
+    float yv = 0.0f;
+    int64_t yrow = -1;
+    int win = 0;
+    auto flush = [&]() {
+        if (yrow >= 0) y[yrow] = yv;
+        yrow = -1;
+        win = 0;
+    };
     for (int it = it0; it < niters; it += NB * nwaves) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -180,10 +195,15 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const uint8_t *_
             lane_dot(buf[b], g, xr, rok && g.ok, acc);
 #pragma unroll
             for (int mt = 0; mt < NMAT; ++mt) acc[mt] = lane_group_sum<LPR>(acc[mt]);
-            if (sub == 0 && rok) y[row] = SWIGLU ? silu(acc[0]) * acc[1] : acc[0];
+            const float out = SWIGLU ? silu(acc[0]) * acc[1] : acc[0];
+            const bool mine = sub == win;
+            yv = mine ? out : yv;
+            yrow = mine ? (rok ? row : -1) : yrow;
+            if (++win == LPR) flush();
             if (cur + nwaves >= niters) break;
         }
     }
+    flush();
 }
 
 // ------------------------------------------------------ 4096 < K <= 16384
