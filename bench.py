@@ -67,7 +67,8 @@ def parse():
                     help="also time every kernel at every config shape (table on stderr)")
     ap.add_argument("--case", default=None,
                     help="only run one kernel in a loop, for profilers: gemv:NAME, swiglu:NAME, "
-                         "dequant:NAME or batched:M:NAME with NAME a shape of inputs.SHAPES")
+                         "residual:NAME, dequant:NAME or batched:M:NAME with NAME a shape of "
+                         "inputs.SHAPES, or multi:gdn_0p8b")
     return ap.parse_args()
 
 
@@ -211,8 +212,10 @@ def main():
                                              "TFLOP/s": round(2.0 * mtok * n_ * k_ / t / 1e12, 2)}
             del sets_b
 
+    blocks = decode_blocks(q4k, inputs, torch, dev, stream, args.steps, args.warmup)
+
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s; per kernel {kernels}; "
-        f"batched {batched}; host wall {wall:.3f}s")
+        f"batched {batched}; decode blocks {blocks}; host wall {wall:.3f}s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -259,11 +262,80 @@ def main():
             "frac_hbm_peak_step": round(value / HBM_PEAK_GBS, 4),
             "kernels": kernels,
             "batched_9b_ffn": batched,
+            "decode_blocks": blocks,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def _time_launches(fn, torch, stream, steps, warmup):
+    """Mean time of one fn(i) over `steps` back-to-back calls between two
+    events on the launch stream."""
+    for i in range(warmup):
+        fn(i)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(steps):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps * 1e-3
+
+
+def decode_blocks(q4k, inputs, torch, dev, stream, steps, warmup):
+    """The multi-matrix and residual entry points on their decode workloads,
+    each beside the separate calls it replaces; weights rotated over
+    >= 512 MiB of copies:
+      * the four input projections of a 0.8B linear-attention layer (qkv 6144,
+        z 2048, a 16, b 16 rows, K = 1024) against one x: one gemv_multi
+        launch, and four gemv launches;
+      * the 9B down projection (4096 x 12288) with the residual added in its
+        epilogue, and the plain GEMV."""
+    out = {}
+    names = inputs.GDN_PROJECTIONS_0P8B
+    k = inputs.SHAPES[names[0]][1]
+    ns = [inputs.SHAPES[nm][0] for nm in names]
+    mats = [inputs.make_q4k(n, k, config_id=4, tensor_id=i).reshape(-1) for i, n in enumerate(ns)]
+    nbytes = sum(m.nbytes for m in mats)
+    copies = max(1, -(-(512 << 20) // nbytes))
+    sets = [[torch.from_numpy(m).to(dev) for m in mats] for _ in range(copies)]
+    x = torch.from_numpy(inputs.make_x(1, k, config_id=4, tensor_id=100)[0]).to(dev)
+    ys = [torch.empty(n, dtype=torch.float32, device=dev) for n in ns]
+    t_multi = _time_launches(lambda i: q4k.gemv_multi(sets[i % copies], x, ys=ys, ns=ns, stream=stream), torch,
+                             stream, steps, warmup)
+
+    def four(i):
+        for w, y, n in zip(sets[i % copies], ys, ns):
+            q4k.gemv(w, x, y=y, n=n, stream=stream)
+
+    t_four = _time_launches(four, torch, stream, steps, warmup)
+    abytes = nbytes + 4 * k + 4 * sum(ns)
+    out["gdn_in_proj_0p8b"] = {"weight_bytes": nbytes, "multi_us": round(t_multi * 1e6, 3),
+                               "multi_GB/s": round(abytes / t_multi / 1e9, 1),
+                               "four_calls_us": round(t_four * 1e6, 3),
+                               "four_calls_GB/s": round(abytes / t_four / 1e9, 1)}
+    del sets
+    n, k = inputs.SHAPES["down_9b"]
+    w0 = inputs.make_q4k(n, k, config_id=6, tensor_id=1).reshape(-1)
+    copies = max(1, -(-(512 << 20) // w0.nbytes))
+    ws = [torch.from_numpy(w0).to(dev) for _ in range(copies)]
+    h = torch.from_numpy(inputs.make_x(1, k, config_id=6, tensor_id=101)[0]).to(dev)
+    r = torch.from_numpy(inputs.make_x(1, n, config_id=6, tensor_id=102)[0]).to(dev)
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    t_res = _time_launches(lambda i: q4k.gemv_residual(ws[i % copies], h, r, y=y, stream=stream), torch, stream,
+                           steps, warmup)
+    t_plain = _time_launches(lambda i: q4k.gemv(ws[i % copies], h, y=y, stream=stream), torch, stream, steps,
+                             warmup)
+    abytes = w0.nbytes + 4 * k + 8 * n
+    out["down_residual_9b"] = {"weight_bytes": w0.nbytes, "residual_us": round(t_res * 1e6, 3),
+                               "residual_GB/s": round(abytes / t_res / 1e9, 1),
+                               "plain_gemv_us": round(t_plain * 1e6, 3)}
+    del ws
+    return out
 
 
 def time_call(fn, torch, reps=50, warm=5):
@@ -303,6 +375,23 @@ def run_case(case, steps, warmup, q4k, inputs, torch, np, dev):
         return
     parts = case.split(":")
     kind, name = parts[0], parts[-1]
+    if kind == "multi":
+        if name != "gdn_0p8b":
+            raise SystemExit("multi case: only multi:gdn_0p8b")
+        names = inputs.GDN_PROJECTIONS_0P8B
+        k = inputs.SHAPES[names[0]][1]
+        ns = [inputs.SHAPES[nm][0] for nm in names]
+        mats = [inputs.make_q4k(n, k, config_id=7, tensor_id=i).reshape(-1) for i, n in enumerate(ns)]
+        nbytes = sum(m.nbytes for m in mats)
+        copies = max(1, -(-(512 << 20) // nbytes))
+        sets = [[torch.from_numpy(m).to(dev) for m in mats] for _ in range(copies)]
+        x = torch.from_numpy(inputs.make_x(1, k, config_id=7)[0]).to(dev)
+        ys = [torch.empty(n, dtype=torch.float32, device=dev) for n in ns]
+        stream = torch.cuda.current_stream()
+        t = _time_launches(lambda i: q4k.gemv_multi(sets[i % copies], x, ys=ys, ns=ns), torch, stream, steps,
+                           warmup)
+        log(f"[case] {case}: {t * 1e6:.2f} us per call (host-enqueued back to back), {nbytes / t / 1e9:.1f} GB/s")
+        return
     m = int(parts[1]) if kind == "batched" else 1
     n, k = inputs.SHAPES[name]
     w0 = inputs.make_q4k(n, k, config_id=7, tensor_id=1).reshape(-1)
@@ -311,6 +400,7 @@ def run_case(case, steps, warmup, q4k, inputs, torch, np, dev):
     ws = [torch.from_numpy(w0).to(dev) for _ in range(copies * mats)]
     xs = torch.from_numpy(inputs.make_x(m, k, config_id=7)).to(dev)
     out = torch.empty((n, k) if kind == "dequant" else (m, n), dtype=torch.float32, device=dev)
+    res = torch.from_numpy(inputs.make_x(1, n, config_id=7, tensor_id=102)[0]).to(dev)
 
     def call(i):
         c = i % copies
@@ -322,6 +412,8 @@ def run_case(case, steps, warmup, q4k, inputs, torch, np, dev):
             q4k.gemv_batched(ws[c], xs, y=out)
         elif kind == "dequant":
             q4k.dequant(ws[c], k, out=out)
+        elif kind == "residual":
+            q4k.gemv_residual(ws[c], xs[0], res, y=out[0])
         else:
             raise SystemExit(f"unknown case kind {kind}")
 

@@ -83,6 +83,40 @@ typedef enum {
 Q4K_API q4k_status q4k_gemv(const void *w, const float *x, float *y, int64_t n, int64_t k, void *stream);
 
 /*
+ * Batch-1 GEMV with a residual added in the same pass: y = W x + r (the
+ * down projection of a decode step feeding the residual stream;
+ * "qualia_core_db/inference/cuda_lane/mod.rs" re-exports
+ * try_q4k_soa_ffn_block_residual from its gemv module).
+ *   w : Q4_K matrix [n, k];  x : f32 [k];  r : f32 [n]
+ *   y : f32 [n], written: y[i] = sum_c W[i,c] x[c] + r[i].
+ * r may be y itself (an in-place residual add); otherwise r and y must not
+ * overlap.  y must not overlap w or x.
+ */
+Q4K_API q4k_status q4k_gemv_residual(const void *w, const float *x, const float *r, float *y, int64_t n, int64_t k,
+                                     void *stream);
+
+/* One matrix of q4k_gemv_multi. */
+typedef struct {
+    const void *w; /* Q4_K matrix [n, k], 16-byte aligned */
+    float *y;      /* f32 [n] output */
+    int64_t n;     /* rows (0: skipped) */
+} q4k_gemv_item;
+
+/* Largest number of matrices in one q4k_gemv_multi call. */
+#define Q4K_MAX_MULTI 8
+
+/*
+ * Several batch-1 GEMVs with the same k against one x, in one launch where
+ * k <= 4096 (the q, k and v projections of a decode step;
+ * "qualia_core_db/inference/cuda_lane/mod.rs" re-exports try_q4k_soa_qkv
+ * from its gemv module).  For each item: y[i] = sum_c W[i,c] x[c].
+ *   items : host array of `count` items, 0 <= count <= Q4K_MAX_MULTI
+ * No output may overlap another output, any weight matrix, or x.  Each
+ * result equals what q4k_gemv gives for that matrix.
+ */
+Q4K_API q4k_status q4k_gemv_multi(const q4k_gemv_item *items, int count, const float *x, int64_t k, void *stream);
+
+/*
  * Skinny GEMM over the same weights for m tokens (selectQ4KFusedVariant's
  * non-M1 variant; "Module qwen3_attention" names a W4A16 batched path).
  *   x : f32 [m, k] row-major (token-major), y : f32 [m, n] row-major:

@@ -68,6 +68,8 @@ def _load():
         lib.q4k_gemv_batched_oracle_into.restype = None
         lib.q4k_fused_swiglu_oracle_into.argtypes = [p, p, p, i64, i64, i64, p, p, p, p, p]
         lib.q4k_fused_swiglu_oracle_into.restype = None
+        lib.q4k_gemv_residual_oracle_into.argtypes = [p, p, p, i64, i64, i64, p, p]
+        lib.q4k_gemv_residual_oracle_into.restype = None
         _lib = lib
     return _lib
 
@@ -184,3 +186,25 @@ def fused_swiglu(wg: np.ndarray, wu: np.ndarray, x: np.ndarray, threads: int = 1
         _ptr(rg[r0:r1]), _ptr(ru[r0:r1]), _ptr(x), k, 0, r1 - r0,
         *(_ptr(out[nm][r0:r1]) for nm in ("h", "g", "u", "ag", "au"))), n, threads)
     return out
+
+
+def gemv_residual(w: np.ndarray, x: np.ndarray, r: np.ndarray, threads: int = 1):
+    """(y, A): y[n] = sum_k W[n,k] x[k] + r[n] (f64), A[n] = sum_k |W[n,k] x[k]| + |r[n]|."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    r = np.ascontiguousarray(r, dtype=np.float32).reshape(-1)
+    k = x.size
+    rows = _as_rows(w, k)
+    n = rows.shape[0]
+    if r.size != n:
+        raise ValueError(f"residual has {r.size} entries for {n} rows")
+    y = np.empty(n, dtype=np.float64)
+    a = np.empty(n, dtype=np.float64)
+    lib = _load()
+    _run(lambda r0, r1: lib.q4k_gemv_residual_oracle_into(_ptr(rows[r0:r1]), _ptr(x), _ptr(r[r0:r1]), k, 0, r1 - r0,
+                                                          _ptr(y[r0:r1]), _ptr(a[r0:r1])), n, threads)
+    return y, a
+
+
+def gemv_multi(ws, x: np.ndarray, threads: int = 1):
+    """[(y_j, A_j)]: one GEMV per matrix of ``ws``, all against the same x."""
+    return [gemv(w, x, threads=threads) for w in ws]

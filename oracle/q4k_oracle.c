@@ -165,3 +165,19 @@ void q4k_fused_swiglu_oracle_into(const uint8_t *wg, const uint8_t *wu, const fl
         h[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
     }
 }
+
+/* GEMV with a residual added ("qualia_core_db/inference/cuda_lane/mod.rs"
+ * exports try_q4k_soa_ffn_block_residual: the down projection whose result is
+ * added to the residual stream), rows [r0, r1):
+ * y[r-r0] = sum_k W[r,k] x[k] + res[r], the sum in f64 and then the residual
+ * added in f64; a[r-r0] = sum_k |W[r,k] x[k]| + |res[r]|. */
+void q4k_gemv_residual_oracle_into(const uint8_t *w, const float *x, const float *res, int64_t k, int64_t r0,
+                                   int64_t r1, double *y, double *a) {
+    const int64_t row_bytes = (k / Q4K_BLOCK_WEIGHTS) * Q4K_BLOCK_BYTES;
+    for (int64_t r = r0; r < r1; ++r) {
+        double dot, mag;
+        q4k_oracle_row_dot(w + r * row_bytes, k, x, &dot, &mag);
+        y[r - r0] = dot + (double)res[r];
+        a[r - r0] = mag + fabs((double)res[r]);
+    }
+}

@@ -21,6 +21,11 @@ __global__ void fill_zero_kernel(float *__restrict__ y, int64_t count) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride) y[i] = 0.0f;
 }
 
+__global__ void copy_kernel(float *y, const float *src, int64_t count) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride) y[i] = src[i];
+}
+
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // [a, a+na) and [b, b+nb) overlap (byte ranges, both non-empty).
@@ -68,6 +73,14 @@ hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream) {
     return hipGetLastError();
 }
 
+hipError_t launch_copy(float *y, const float *src, int64_t count, hipStream_t stream) {
+    if (count == 0 || y == src) return hipSuccess;
+    const int64_t need = (count + 255) / 256;
+    const int grid = static_cast<int>(need < 4096 ? need : 4096);
+    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, stream, y, src, count);
+    return hipGetLastError();
+}
+
 }  // namespace q4k
 
 using q4k::aligned;
@@ -86,8 +99,59 @@ q4k_status q4k_gemv(const void *w, const float *x, float *y, int64_t n, int64_t 
     if (!aligned(w, 16) || !aligned(x, 4) || !aligned(y, 4)) return Q4K_ERR_MISALIGNED;
     const uint64_t yb = static_cast<uint64_t>(n) * 4, xb = static_cast<uint64_t>(k) * 4;
     if (overlap(y, yb, w, wb) || overlap(y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
-    return from_hip(q4k::launch_gemv(static_cast<const uint8_t *>(w), nullptr, x, y, n, k,
+    return from_hip(q4k::launch_gemv(static_cast<const uint8_t *>(w), nullptr, x, nullptr, y, n, k,
                                      static_cast<hipStream_t>(stream)));
+}
+
+q4k_status q4k_gemv_residual(const void *w, const float *x, const float *r, float *y, int64_t n, int64_t k,
+                             void *stream) {
+    uint64_t wb = 0;
+    const q4k_status s = check_shape(n, k, &wb);
+    if (s != Q4K_OK) return s;
+    if (n == 0) return Q4K_OK;
+    if (y == nullptr || r == nullptr || (k > 0 && (w == nullptr || x == nullptr))) return Q4K_ERR_INVALID_ARG;
+    if (!aligned(w, 16) || !aligned(x, 4) || !aligned(y, 4) || !aligned(r, 4)) return Q4K_ERR_MISALIGNED;
+    const uint64_t yb = static_cast<uint64_t>(n) * 4, xb = static_cast<uint64_t>(k) * 4;
+    if (overlap(y, yb, w, wb) || overlap(y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
+    if (r != y && overlap(y, yb, r, yb)) return Q4K_ERR_INVALID_ARG;  // in place, or apart
+    return from_hip(q4k::launch_gemv(static_cast<const uint8_t *>(w), nullptr, x, r, y, n, k,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+q4k_status q4k_gemv_multi(const q4k_gemv_item *items, int count, const float *x, int64_t k, void *stream) {
+    if (count < 0 || count > Q4K_MAX_MULTI) return Q4K_ERR_INVALID_ARG;
+    if (count == 0) return Q4K_OK;
+    if (items == nullptr) return Q4K_ERR_INVALID_ARG;
+    uint64_t wbytes[Q4K_MAX_MULTI];
+    int64_t rows = 0;
+    for (int i = 0; i < count; ++i) {
+        const q4k_status s = check_shape(items[i].n, k, &wbytes[i]);
+        if (s != Q4K_OK) return s;
+        rows += items[i].n;
+    }
+    if (rows == 0) return Q4K_OK;
+    if (k > 0 && x == nullptr) return Q4K_ERR_INVALID_ARG;
+    if (!aligned(x, 4)) return Q4K_ERR_MISALIGNED;
+    const uint64_t xb = static_cast<uint64_t>(k) * 4;
+    q4k::GemvJob jobs[Q4K_MAX_MULTI];
+    for (int i = 0; i < count; ++i) {
+        const q4k_gemv_item &it = items[i];
+        if (it.n == 0) {
+            jobs[i] = q4k::GemvJob{nullptr, nullptr, nullptr, 0};
+            continue;
+        }
+        if (it.y == nullptr || (k > 0 && it.w == nullptr)) return Q4K_ERR_INVALID_ARG;
+        if (!aligned(it.w, 16) || !aligned(it.y, 4)) return Q4K_ERR_MISALIGNED;
+        const uint64_t yb = static_cast<uint64_t>(it.n) * 4;
+        if (overlap(it.y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
+        for (int j = 0; j < count; ++j) {
+            if (items[j].n == 0) continue;
+            if (overlap(it.y, yb, items[j].w, wbytes[j])) return Q4K_ERR_INVALID_ARG;
+            if (j != i && overlap(it.y, yb, items[j].y, static_cast<uint64_t>(items[j].n) * 4)) return Q4K_ERR_INVALID_ARG;
+        }
+        jobs[i] = q4k::GemvJob{static_cast<const uint8_t *>(it.w), it.y, nullptr, it.n};
+    }
+    return from_hip(q4k::launch_gemv_multi(jobs, count, nullptr, x, k, static_cast<hipStream_t>(stream)));
 }
 
 q4k_status q4k_gemv_batched(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
@@ -117,7 +181,7 @@ q4k_status q4k_fused_swiglu(const void *w_gate, const void *w_up, const float *x
     const uint64_t hb = static_cast<uint64_t>(n) * 4, xb = static_cast<uint64_t>(k) * 4;
     if (overlap(h, hb, w_gate, wb) || overlap(h, hb, w_up, wb) || overlap(h, hb, x, xb)) return Q4K_ERR_INVALID_ARG;
     return from_hip(q4k::launch_gemv(static_cast<const uint8_t *>(w_gate), static_cast<const uint8_t *>(w_up), x,
-                                     h, n, k, static_cast<hipStream_t>(stream)));
+                                     nullptr, h, n, k, static_cast<hipStream_t>(stream)));
 }
 
 q4k_status q4k_dequant(const void *w, float *out, int64_t n, int64_t k, void *stream) {
@@ -143,6 +207,6 @@ const char *q4k_status_string(q4k_status s) {
     return "unknown status";
 }
 
-int q4k_abi_version(void) { return 100; }
+int q4k_abi_version(void) { return 101; }
 
 }  // extern "C"

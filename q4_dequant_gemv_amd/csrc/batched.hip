@@ -497,7 +497,7 @@ hipError_t launch_gemv_batched(const uint8_t *w, const float *x, float *y, int64
                                hipStream_t stream) {
     if (m == 0 || n == 0) return hipSuccess;
     if (k == 0) return launch_fill_zero(y, m * n, stream);
-    if (m == 1) return launch_gemv(w, nullptr, x, y, n, k, stream);
+    if (m == 1) return launch_gemv(w, nullptr, x, nullptr, y, n, k, stream);
     hipError_t e = hipSuccess;
     // up to 64 tokens per launch; the weights are re-read per 64-token slice
     for (int64_t t0 = 0; t0 < m; t0 += 64) {

@@ -112,11 +112,24 @@ __device__ __forceinline__ void lane_dot(const RowLoads<NMAT> &b, const LaneGrou
 // decoded, multiplied and reduced, the next NB-1 rows' loads are in flight;
 // the first rows are issued before the activations are prepared.  Wave
 // iterations are dealt round-robin over the persistent grid.
+// Up to kMaxMats matrices of the same k against one x in a single launch (the
+// q, k and v projections of a decode step, say).  Matrix i owns the wave
+// iterations [it_begin[i], it_begin[i+1]); its last iteration covers
+// tail_bytes of weights.  r[i], if set, is added to each output (a residual).
+constexpr int kMaxMats = 8;
+struct MatTable {
+    const uint8_t *w[kMaxMats];
+    float *y[kMaxMats];
+    const float *r[kMaxMats];
+    int64_t n[kMaxMats];
+    int it_begin[kMaxMats + 1];
+    int tail_bytes[kMaxMats];
+    int count;
+};
+
 template <int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES>
-__global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const uint8_t *__restrict__ w,
-                                                                const uint8_t *__restrict__ wu, const float *x,
-                                                                float *__restrict__ y, int64_t n, int ngroups,
-                                                                int64_t row_bytes) {
+__global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable mt, const uint8_t *__restrict__ wu,
+                                                                const float *x, int ngroups, int64_t row_bytes) {
     static_assert(NB >= 2, "at least one row in flight");
     constexpr int NMAT = SWIGLU ? 2 : 1;
     constexpr int kRowsPerWave = kWave / LPR;
@@ -136,13 +149,56 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const uint8_t *_
     // below 2^31): gfx9 has no 64-bit scalar compare, and a vector compare in
     // the loop would borrow registers that earlier memory operations still own.
     const int iter_bytes = kRowsPerWave * static_cast<int>(row_bytes);
-    const int niters = static_cast<int>((n + kRowsPerWave - 1) / kRowsPerWave);
-    const int tail_bytes = static_cast<int>(n - static_cast<int64_t>(niters - 1) * kRowsPerWave) *
-                           static_cast<int>(row_bytes);
+    const int count = mt.count;
+    const int niters = mt.it_begin[count];
+    // A wave's iterations only move forward, so each side (the loads issued
+    // ahead, the rows being finished) follows its own cursor over the
+    // matrices and reads a table entry only when it crosses into the next
+    // matrix (a scalar load from the argument segment).  Past the end a cursor
+    // stays on the last matrix, with nothing left to load.
+    struct LoadCursor {
+        int mi, begin, end, tail;
+        const uint8_t *w;
+    };
+    struct RowCursor {
+        int mi, begin, end;
+        int64_t n;
+        float *y;
+        const float *r;
+    };
+    LoadCursor lc{0, 0, mt.it_begin[1], mt.tail_bytes[0], mt.w[0]};
+    RowCursor rc{0, 0, mt.it_begin[1], mt.n[0], mt.y[0], mt.r[0]};
     auto issue = [&](RowLoads<NMAT> &b, int it) {
-        const int left = niters - it;
-        issue_row(b, w, wu, static_cast<int64_t>(it) * iter_bytes,
-                  left > 1 ? iter_bytes : (left == 1 ? tail_bytes : 0), g);
+        while (it >= lc.end && lc.mi + 1 < count) {
+            ++lc.mi;
+            lc.begin = lc.end;
+            lc.end = mt.it_begin[lc.mi + 1];
+            lc.tail = mt.tail_bytes[lc.mi];
+            lc.w = mt.w[lc.mi];
+        }
+        const int left = lc.end - it;
+        const int64_t off = static_cast<int64_t>(it - lc.begin) * iter_bytes;
+        const int nrec = __builtin_amdgcn_readfirstlane(left > 1 ? iter_bytes : (left == 1 ? lc.tail : 0));
+        // uniform by construction; said again so that the descriptor is built
+        // in scalar registers whatever the compiler concluded across the joins
+        const uint8_t *wbase = reinterpret_cast<const uint8_t *>(wave_uniform(reinterpret_cast<int64_t>(lc.w)));
+#pragma unroll
+        for (int m2 = 0; m2 < NMAT; ++m2) {
+            const __amdgpu_buffer_rsrc_t r = stream_rsrc((m2 == 0 ? wbase : wu) + off, nrec);
+            b.hdr[m2] = buffer_load16(r, g.off_hdr);
+            b.qa[m2] = buffer_load16(r, g.off_qa);
+            b.qb[m2] = buffer_load16(r, g.off_qa + 16u);
+        }
+    };
+    auto row_cursor = [&](int it) {
+        while (it >= rc.end && rc.mi + 1 < count) {
+            ++rc.mi;
+            rc.begin = rc.end;
+            rc.end = mt.it_begin[rc.mi + 1];
+            rc.n = mt.n[rc.mi];
+            rc.y = mt.y[rc.mi];
+            rc.r = mt.r[rc.mi];
+        }
     };
 
     const int nwaves = static_cast<int>(gridDim.x) * kWavesPerBlock;
@@ -173,36 +229,46 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const uint8_t *_
     // Results are not stored row by row: gfx9 counts stores with the loads,
     // and a store on some paths through the loop but not others makes the
     // wait counters drain loads still in flight.  Lane k of a row's lane group
-    // keeps the group's k-th result of the current window of LPR rows; the
-    // window is stored in one go when it is full (a wave streaming fewer than
-    // LPR rows per group stores only after the loop).
+    // keeps the group's k-th result of the current window of LPR rows (and
+    // where it goes); the window is stored in one go when it is full (a wave
+    // streaming fewer than LPR rows per group stores only after the loop).
     float yv = 0.0f;
-    int64_t yrow = -1;
+    float *yp = nullptr;
+    const float *rp = nullptr;
     int win = 0;
     auto flush = [&]() {
-        if (yrow >= 0) y[yrow] = yv;
-        yrow = -1;
+        if (yp != nullptr) *yp = rp != nullptr ? yv + *rp : yv;
+        yp = nullptr;
         win = 0;
     };
-    for (int it = it0; it < niters; it += NB * nwaves) {
+    // The last iteration leaves both loops at once (goto): a break that fell
+    // back to the outer loop's test would join the loop head with loads of
+    // the unfinished unrolled pass still in flight, and the wait counters
+    // would have to drain them there.
+    if (it0 < niters) {
+        for (int it = it0;; it += NB * nwaves) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const int cur = it + b * nwaves;
-            issue(buf[(b + NB - 1) % NB], cur + (NB - 1) * nwaves);
-            const int64_t row = static_cast<int64_t>(cur) * kRowsPerWave + slot;
-            const bool rok = row < n;
-            float acc[NMAT];
-            lane_dot(buf[b], g, xr, rok && g.ok, acc);
+            for (int b = 0; b < NB; ++b) {
+                const int cur = it + b * nwaves;
+                issue(buf[(b + NB - 1) % NB], cur + (NB - 1) * nwaves);
+                row_cursor(cur);
+                const int64_t row = static_cast<int64_t>(cur - rc.begin) * kRowsPerWave + slot;
+                const bool rok = row < rc.n;
+                float acc[NMAT];
+                lane_dot(buf[b], g, xr, rok && g.ok, acc);
 #pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt) acc[mt] = lane_group_sum<LPR>(acc[mt]);
-            const float out = SWIGLU ? silu(acc[0]) * acc[1] : acc[0];
-            const bool mine = sub == win;
-            yv = mine ? out : yv;
-            yrow = mine ? (rok ? row : -1) : yrow;
-            if (++win == LPR) flush();
-            if (cur + nwaves >= niters) break;
+                for (int m2 = 0; m2 < NMAT; ++m2) acc[m2] = lane_group_sum<LPR>(acc[m2]);
+                const float out = SWIGLU ? silu(acc[0]) * acc[1] : acc[0];
+                const bool mine = sub == win;
+                yv = mine ? out : yv;
+                yp = mine ? (rok ? rc.y + row : nullptr) : yp;
+                rp = mine ? (rc.r != nullptr ? rc.r + row : nullptr) : rp;
+                if (++win == LPR) flush();
+                if (cur + nwaves >= niters) goto done;
+            }
         }
     }
+done:
     flush();
 }
 
@@ -214,14 +280,16 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const uint8_t *_
 // LDS; every kFlush iterations (and at the end) a barrier, then one thread per
 // row adds the S partials in slice order and stores the result, so the result
 // does not depend on timing.  The partial buffer has two halves, so the next
-// stretch of iterations writes while the last one is read.
+// stretch of iterations writes while the last one is read.  res, if set, is
+// added to each result (it may be y itself: each thread reads a row's
+// residual before it writes that row).
 constexpr int kFlush = 8;
 
 template <int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
 __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const uint8_t *__restrict__ w,
                                                                            const uint8_t *__restrict__ wu,
-                                                                           const float *x, float *__restrict__ y,
-                                                                           int64_t n, int ngroups,
+                                                                           const float *x, float *y,
+                                                                           const float *res, int64_t n, int ngroups,
                                                                            int64_t row_bytes) {
     constexpr int BLOCK = 64 * S * R;
     constexpr int NMAT = SWIGLU ? 2 : 1;
@@ -291,7 +359,8 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
 #pragma unroll
                             for (int mt = 0; mt < NMAT; ++mt) sum[mt] += q[s * NMAT + mt];
                         }
-                        y[row] = SWIGLU ? silu(sum[0]) * sum[1] : sum[0];
+                        const float v = SWIGLU ? silu(sum[0]) * sum[1] : sum[0];
+                        y[row] = res != nullptr ? v + res[row] : v;
                     }
                 }
             }
@@ -305,8 +374,8 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
 template <bool SWIGLU>
 __global__ __launch_bounds__(256) void gemv_generic_kernel(const uint8_t *__restrict__ w,
                                                            const uint8_t *__restrict__ wu,
-                                                           const float *__restrict__ x, float *__restrict__ y,
-                                                           int64_t n, int64_t k, int64_t row_bytes) {
+                                                           const float *__restrict__ x, float *y,
+                                                           const float *res, int64_t n, int64_t k, int64_t row_bytes) {
     const int lane = threadIdx.x & 63;
     const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
     const int64_t quads = k / 4;
@@ -337,7 +406,10 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(const uint8_t *__rest
             }
             acc[mat] = group_sum<64>(acc[mat]);
         }
-        if (lane == 0) y[row] = SWIGLU ? silu(acc[0]) * acc[1] : acc[0];
+        if (lane == 0) {
+            const float v = SWIGLU ? silu(acc[0]) * acc[1] : acc[0];
+            y[row] = res != nullptr ? v + res[row] : v;
+        }
     }
 }
 
@@ -357,27 +429,44 @@ int resident_blocks_per_cu(Kernel kern, int block, size_t lds, std::atomic<int> 
     return nb;
 }
 
+// One launch of the batch-1 kernel over `count` matrices (all with k columns).
 template <int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES>
-hipError_t launch_fast(const uint8_t *w, const uint8_t *wu, const float *x, float *y, int64_t n, int64_t k,
+hipError_t launch_fast(const GemvJob *jobs, int count, const uint8_t *wu, const float *x, int64_t k,
                        hipStream_t stream) {
     auto kern = gemv_kernel<LPR, SWIGLU, NB, BLOCK, MIN_WAVES>;
     const int ngroups = static_cast<int>(k / 64);
+    const int64_t row_bytes = (k / kBlockWeights) * kBlockBytes;
     const size_t lds = static_cast<size_t>(ngroups) * sizeof(XGroup);
     static std::atomic<int> cache[kMaxDevices];
     const int per_cu = resident_blocks_per_cu(kern, BLOCK, lds, cache);
     constexpr int kRowsPerWave = kWave / LPR;
-    const int64_t niters = (n + kRowsPerWave - 1) / kRowsPerWave;
-    const int64_t need = (niters + BLOCK / kWave - 1) / (BLOCK / kWave);
+    MatTable mt{};
+    mt.count = count;
+    int64_t total = 0;
+    for (int i = 0; i < count; ++i) {
+        const int64_t iters = (jobs[i].n + kRowsPerWave - 1) / kRowsPerWave;
+        mt.w[i] = jobs[i].w;
+        mt.y[i] = jobs[i].y;
+        mt.r[i] = jobs[i].r;
+        mt.n[i] = jobs[i].n;
+        mt.it_begin[i] = static_cast<int>(total);
+        mt.tail_bytes[i] = static_cast<int>((jobs[i].n - (iters - 1) * kRowsPerWave) * row_bytes);
+        total += iters;
+    }
+    // 32-bit loop control in the kernel (unreachable: 2^30 iterations are
+    // terabytes of weights)
+    if (total >= (int64_t{1} << 30)) return hipErrorInvalidValue;
+    for (int i = count; i <= kMaxMats; ++i) mt.it_begin[i] = static_cast<int>(total);
+    const int64_t need = (total + BLOCK / kWave - 1) / (BLOCK / kWave);
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
     const int grid = static_cast<int>(need < cap ? need : cap);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, w, wu, x, y, n, ngroups,
-                       (k / kBlockWeights) * kBlockBytes);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, mt, wu, x, ngroups, row_bytes);
     return hipGetLastError();
 }
 
 template <int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
-hipError_t launch_split(const uint8_t *w, const uint8_t *wu, const float *x, float *y, int64_t n, int64_t k,
-                        hipStream_t stream) {
+hipError_t launch_split(const uint8_t *w, const uint8_t *wu, const float *x, const float *r, float *y, int64_t n,
+                        int64_t k, hipStream_t stream) {
     auto kern = gemv_split_kernel<S, R, SWIGLU, NB, MIN_WAVES>;
     constexpr int BLOCK = 64 * S * R;
     const int ngroups = static_cast<int>(k / 64);
@@ -388,18 +477,18 @@ hipError_t launch_split(const uint8_t *w, const uint8_t *wu, const float *x, flo
     const int64_t need = (n + R - 1) / R;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
     const int grid = static_cast<int>(need < cap ? need : cap);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, w, wu, x, y, n, ngroups,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, w, wu, x, y, r, n, ngroups,
                        (k / kBlockWeights) * kBlockBytes);
     return hipGetLastError();
 }
 
 template <bool SWIGLU>
-hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const float *x, float *y, int64_t n, int64_t k,
-                          hipStream_t stream) {
+hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const float *x, const float *r, float *y, int64_t n,
+                          int64_t k, hipStream_t stream) {
     const int64_t need = (n + 3) / 4;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
     const int grid = static_cast<int>(need < cap ? need : cap);
-    hipLaunchKernelGGL(gemv_generic_kernel<SWIGLU>, dim3(grid), dim3(256), 0, stream, w, wu, x, y, n, k,
+    hipLaunchKernelGGL(gemv_generic_kernel<SWIGLU>, dim3(grid), dim3(256), 0, stream, w, wu, x, y, r, n, k,
                        (k / kBlockWeights) * kBlockBytes);
     return hipGetLastError();
 }
@@ -446,52 +535,85 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const float *x, f
 #endif
 
 template <int LPR, bool SWIGLU>
-hipError_t dispatch_lpr(const uint8_t *w, const uint8_t *wu, const float *x, float *y, int64_t n, int64_t k,
+hipError_t dispatch_lpr(const GemvJob *jobs, int count, const uint8_t *wu, const float *x, int64_t k,
                         hipStream_t stream) {
     if constexpr (SWIGLU) {
-        return launch_fast<LPR, true, Q4K_SWIGLU_NB, Q4K_SWIGLU_BLOCK, Q4K_SWIGLU_MINW>(w, wu, x, y, n, k, stream);
+        return launch_fast<LPR, true, Q4K_SWIGLU_NB, Q4K_SWIGLU_BLOCK, Q4K_SWIGLU_MINW>(jobs, count, wu, x, k, stream);
     } else {
-        const int64_t bytes = n * (k / kBlockWeights) * kBlockBytes;
+        int64_t bytes = 0;
+        for (int i = 0; i < count; ++i) bytes += jobs[i].n * (k / kBlockWeights) * kBlockBytes;
         if (bytes < Q4K_SMALL_BYTES) {
-            return launch_fast<LPR, false, Q4K_SMALL_NB, Q4K_SMALL_BLOCK, Q4K_SMALL_MINW>(w, wu, x, y, n, k, stream);
+            return launch_fast<LPR, false, Q4K_SMALL_NB, Q4K_SMALL_BLOCK, Q4K_SMALL_MINW>(jobs, count, wu, x, k,
+                                                                                          stream);
         }
-        return launch_fast<LPR, false, Q4K_LARGE_NB, Q4K_LARGE_BLOCK, Q4K_LARGE_MINW>(w, wu, x, y, n, k, stream);
+        return launch_fast<LPR, false, Q4K_LARGE_NB, Q4K_LARGE_BLOCK, Q4K_LARGE_MINW>(jobs, count, wu, x, k, stream);
     }
 }
 
+// Rows wider than 4096 weights: one launch per matrix.
 template <bool SWIGLU>
-hipError_t dispatch(const uint8_t *w, const uint8_t *wu, const float *x, float *y, int64_t n, int64_t k,
-                    hipStream_t stream) {
+hipError_t dispatch_wide(const GemvJob &j, const uint8_t *wu, const float *x, int64_t k, hipStream_t stream) {
     const int64_t ngroups = k / 64;
-    if (ngroups <= 4) return dispatch_lpr<4, SWIGLU>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 8) return dispatch_lpr<8, SWIGLU>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 16) return dispatch_lpr<16, SWIGLU>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 32) return dispatch_lpr<32, SWIGLU>(w, wu, x, y, n, k, stream);
-    if (ngroups <= 64) return dispatch_lpr<64, SWIGLU>(w, wu, x, y, n, k, stream);
     // split rows: S waves per row; two matrices' row buffers need more
     // registers, so the SwiGLU shapes keep fewer rows per workgroup
     constexpr int NB = Q4K_SPLIT_NB;
     if constexpr (SWIGLU) {
-        if (ngroups <= 128) return launch_split<2, 4, true, NB, 2>(w, wu, x, y, n, k, stream);
-        if (ngroups <= 192) return launch_split<3, 4, true, NB, 3>(w, wu, x, y, n, k, stream);
-        if (ngroups <= 256) return launch_split<4, 2, true, NB, 2>(w, wu, x, y, n, k, stream);
+        if (ngroups <= 128) return launch_split<2, 4, true, NB, 2>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 192) return launch_split<3, 4, true, NB, 3>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 256) return launch_split<4, 2, true, NB, 2>(j.w, wu, x, j.r, j.y, j.n, k, stream);
     } else {
-        if (ngroups <= 128) return launch_split<2, 8, false, NB, 4>(w, wu, x, y, n, k, stream);
-        if (ngroups <= 192) return launch_split<3, 4, false, NB, 3>(w, wu, x, y, n, k, stream);
-        if (ngroups <= 256) return launch_split<4, 4, false, NB, 4>(w, wu, x, y, n, k, stream);
+        if (ngroups <= 128) return launch_split<2, 8, false, NB, 4>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 192) return launch_split<3, 4, false, NB, 3>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 256) return launch_split<4, 4, false, NB, 4>(j.w, wu, x, j.r, j.y, j.n, k, stream);
     }
     // beyond K = 16384: the plain kernel
-    return launch_generic<SWIGLU>(w, wu, x, y, n, k, stream);
+    return launch_generic<SWIGLU>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+}
+
+template <bool SWIGLU>
+hipError_t dispatch(const GemvJob *jobs, int count, const uint8_t *wu, const float *x, int64_t k,
+                    hipStream_t stream) {
+    const int64_t ngroups = k / 64;
+    if (ngroups <= 4) return dispatch_lpr<4, SWIGLU>(jobs, count, wu, x, k, stream);
+    if (ngroups <= 8) return dispatch_lpr<8, SWIGLU>(jobs, count, wu, x, k, stream);
+    if (ngroups <= 16) return dispatch_lpr<16, SWIGLU>(jobs, count, wu, x, k, stream);
+    if (ngroups <= 32) return dispatch_lpr<32, SWIGLU>(jobs, count, wu, x, k, stream);
+    if (ngroups <= 64) return dispatch_lpr<64, SWIGLU>(jobs, count, wu, x, k, stream);
+    for (int i = 0; i < count; ++i) {
+        const hipError_t e = dispatch_wide<SWIGLU>(jobs[i], wu, x, k, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_gemv(const uint8_t *w, const uint8_t *w_up, const float *x, float *y, int64_t n, int64_t k,
-                       hipStream_t stream) {
+hipError_t launch_gemv(const uint8_t *w, const uint8_t *w_up, const float *x, const float *r, float *y, int64_t n,
+                       int64_t k, hipStream_t stream) {
     if (n == 0) return hipSuccess;
-    if (k == 0) return launch_fill_zero(y, n, stream);
-    if (w_up != nullptr) return dispatch<true>(w, w_up, x, y, n, k, stream);
-    return dispatch<false>(w, nullptr, x, y, n, k, stream);
+    const GemvJob job{w, y, r, n};
+    return launch_gemv_multi(&job, 1, w_up, x, k, stream);
+}
+
+hipError_t launch_gemv_multi(const GemvJob *jobs, int count, const uint8_t *w_up, const float *x, int64_t k,
+                             hipStream_t stream) {
+    if (count < 0 || count > kMaxMats) return hipErrorInvalidValue;
+    // empty matrices launch nothing; k == 0 is an empty sum (plus any residual)
+    GemvJob live[kMaxMats];
+    int nlive = 0;
+    for (int i = 0; i < count; ++i) {
+        if (jobs[i].n == 0) continue;
+        if (k == 0) {
+            const hipError_t e = jobs[i].r != nullptr ? launch_copy(jobs[i].y, jobs[i].r, jobs[i].n, stream)
+                                                      : launch_fill_zero(jobs[i].y, jobs[i].n, stream);
+            if (e != hipSuccess) return e;
+            continue;
+        }
+        live[nlive++] = jobs[i];
+    }
+    if (nlive == 0) return hipSuccess;
+    if (w_up != nullptr) return dispatch<true>(live, nlive, w_up, x, k, stream);
+    return dispatch<false>(live, nlive, nullptr, x, k, stream);
 }
 
 }  // namespace q4k

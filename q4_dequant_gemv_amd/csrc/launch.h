@@ -13,10 +13,24 @@ int device_cu_count();
 
 hipError_t launch_dequant(const uint8_t *w, float *out, int64_t n, int64_t k, hipStream_t stream);
 
-// y[r] = sum_c W[r,c] x[c]; with w_up != nullptr computes
-// h[r] = silu((W x)[r]) * (W_up x)[r] instead.
-hipError_t launch_gemv(const uint8_t *w, const uint8_t *w_up, const float *x, float *y, int64_t n, int64_t k,
-                       hipStream_t stream);
+// One matrix of a batch-1 GEMV launch: y[i] = sum_c W[i,c] x[c] (+ r[i] if
+// r != nullptr; r may equal y).
+struct GemvJob {
+    const uint8_t *w;
+    float *y;
+    const float *r;
+    int64_t n;
+};
+
+// y[i] = sum_c W[i,c] x[c] (+ r[i]); with w_up != nullptr computes
+// h[i] = silu((W x)[i]) * (W_up x)[i] instead (r must be null then).
+hipError_t launch_gemv(const uint8_t *w, const uint8_t *w_up, const float *x, const float *r, float *y, int64_t n,
+                       int64_t k, hipStream_t stream);
+
+// Up to 8 matrices with the same k against one x; those with k/64 <= 64
+// groups share one launch.
+hipError_t launch_gemv_multi(const GemvJob *jobs, int count, const uint8_t *w_up, const float *x, int64_t k,
+                             hipStream_t stream);
 
 // y[t, r] = sum_c W[r,c] x[t,c] for t < m.
 hipError_t launch_gemv_batched(const uint8_t *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
@@ -24,5 +38,8 @@ hipError_t launch_gemv_batched(const uint8_t *w, const float *x, float *y, int64
 
 // Writes zeros to y[0..count) (the k == 0 empty sum).
 hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream);
+
+// y[0..count) = src[0..count) (the k == 0 sum plus a residual; src may equal y).
+hipError_t launch_copy(float *y, const float *src, int64_t count, hipStream_t stream);
 
 }  // namespace q4k

@@ -36,7 +36,16 @@ SHAPES = {
     "up_9b": (12288, 4096),
     "down_9b": (4096, 12288),
     "lm_head_9b": (248320, 4096),
+    # input projections of a Qwen3.5-0.8B linear-attention (GatedDeltaNet)
+    # layer, all read against the same normed hidden state (the
+    # hf_qwen35_linear_attn_debug.py trace: qkv is 6144 wide, 16 heads of 128;
+    # z has one value per v channel, a and b one per v head)
+    "gdn_qkv_0p8b": (6144, 1024),
+    "gdn_z_0p8b": (2048, 1024),
+    "gdn_a_0p8b": (16, 1024),
+    "gdn_b_0p8b": (16, 1024),
 }
+GDN_PROJECTIONS_0P8B = ("gdn_qkv_0p8b", "gdn_z_0p8b", "gdn_a_0p8b", "gdn_b_0p8b")
 
 
 def rng(config_id: int, tensor_id: int, seed: int = 0) -> np.random.Generator:

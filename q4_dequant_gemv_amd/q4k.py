@@ -23,8 +23,17 @@ STATUS = {0: "Q4K_OK", 1: "Q4K_ERR_INVALID_ARG", 2: "Q4K_ERR_UNSUPPORTED_SHAPE",
           4: "Q4K_ERR_LAUNCH"}
 
 # exported symbols, in the order include/q4k.h declares them
-EXPORTS = ("q4k_gemv", "q4k_gemv_batched", "q4k_fused_swiglu", "q4k_dequant", "q4k_status_string",
-           "q4k_abi_version")
+EXPORTS = ("q4k_gemv", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_gemv_batched", "q4k_fused_swiglu",
+           "q4k_dequant", "q4k_status_string", "q4k_abi_version")
+
+# largest number of matrices in one gemv_multi call (Q4K_MAX_MULTI)
+MAX_MULTI = 8
+
+
+class GemvItem(ctypes.Structure):
+    """q4k_gemv_item: one matrix of a gemv_multi call."""
+
+    _fields_ = [("w", ctypes.c_void_p), ("y", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
 class Q4KError(RuntimeError):
@@ -45,10 +54,13 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         p, i64, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.q4k_gemv.argtypes = [p, p, p, i64, i64, p]
+        L.q4k_gemv_residual.argtypes = [p, p, p, p, i64, i64, p]
+        L.q4k_gemv_multi.argtypes = [ctypes.POINTER(GemvItem), ctypes.c_int, p, i64, p]
         L.q4k_gemv_batched.argtypes = [p, p, p, i64, i64, i64, p]
         L.q4k_fused_swiglu.argtypes = [p, p, p, p, i64, i64, p]
         L.q4k_dequant.argtypes = [p, p, i64, i64, p]
-        for f in (L.q4k_gemv, L.q4k_gemv_batched, L.q4k_fused_swiglu, L.q4k_dequant):
+        for f in (L.q4k_gemv, L.q4k_gemv_residual, L.q4k_gemv_multi, L.q4k_gemv_batched, L.q4k_fused_swiglu,
+                  L.q4k_dequant):
             f.restype = st
         L.q4k_status_string.argtypes = [st]
         L.q4k_status_string.restype = ctypes.c_char_p
@@ -111,6 +123,41 @@ def gemv(w, x, y=None, n: int | None = None, stream=None):
     _check(lib().q4k_gemv(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float32), _dev(y, "y", torch.float32),
                           n, k, _stream(stream)), "q4k_gemv")
     return y
+
+
+def gemv_residual(w, x, r, y=None, n: int | None = None, stream=None):
+    """y[i] = sum_c W[i,c] x[c] + r[i]; ``y`` may be ``r`` itself (in-place residual add)."""
+    import torch
+
+    k = x.numel()
+    n = rows_of(w, k) if n is None else n
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=x.device)
+    _check(lib().q4k_gemv_residual(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float32),
+                                   _dev(r, "r", torch.float32), _dev(y, "y", torch.float32), n, k, _stream(stream)),
+           "q4k_gemv_residual")
+    return y
+
+
+def gemv_multi(ws, x, ys=None, ns=None, stream=None):
+    """ys[j][i] = sum_c W_j[i,c] x[c] for up to MAX_MULTI matrices sharing ``x``, in one launch."""
+    import torch
+
+    k = x.numel()
+    ws = list(ws)
+    ns = [rows_of(w, k) for w in ws] if ns is None else list(ns)
+    if ys is None:
+        ys = [torch.empty(n, dtype=torch.float32, device=x.device) for n in ns]
+    ys = list(ys)
+    if not (len(ws) == len(ys) == len(ns)):
+        raise ValueError("ws, ys and ns must have the same length")
+    items = (GemvItem * max(len(ws), 1))()
+    for i, (w, y, n) in enumerate(zip(ws, ys, ns)):
+        items[i].w = _dev(w, f"ws[{i}]", torch.uint8).value
+        items[i].y = _dev(y, f"ys[{i}]", torch.float32).value
+        items[i].n = n
+    _check(lib().q4k_gemv_multi(items, len(ws), _dev(x, "x", torch.float32), k, _stream(stream)), "q4k_gemv_multi")
+    return ys
 
 
 def gemv_batched(w, x, y=None, n: int | None = None, stream=None):

@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
-        ["q4k_gemv", "q4k_gemv_batched", "q4k_fused_swiglu", "q4k_dequant", "q4k_status_string", "q4k_abi_version"])
+        ["q4k_gemv", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_gemv_batched", "q4k_fused_swiglu", "q4k_dequant",
+         "q4k_status_string", "q4k_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -54,7 +55,7 @@ def test_only_the_abi_is_exported():
 
 
 def test_status_strings(L):
-    assert L.q4k_abi_version() == 100
+    assert L.q4k_abi_version() == 101
     for s in range(5):
         assert len(L.q4k_status_string(s)) > 0
     assert L.q4k_status_string(99) == b"unknown status"
@@ -85,6 +86,59 @@ OK, INVALID, SHAPE, MISALIGNED = 0, 1, 2, 3
 def test_gemv_validation(L, args, status):
     w, x, y, n, k = args
     assert L.q4k_gemv(ctypes.c_void_p(w), ctypes.c_void_p(x), ctypes.c_void_p(y), n, k, None) == status
+
+
+R = A + 0x40000000
+
+
+@pytest.mark.parametrize("args,status", [
+    ((W, X, R, Y, 16, 300), SHAPE),
+    ((W, X, 0, Y, 16, 256), INVALID),             # null residual
+    ((W, X, R + 2, Y, 16, 256), MISALIGNED),
+    ((W, X, Y + 4, Y, 16, 256), INVALID),         # r overlaps y without being y
+    ((W, X, R, X + 4, 16, 256), INVALID),         # y overlaps x
+    ((W, X, R, W, 16, 256), INVALID),             # y overlaps w
+    ((W, X, R, Y, 0, 256), OK),
+    ((0, 0, 0, 0, 0, 0), OK),
+])
+def test_residual_validation(L, args, status):
+    w, x, r, y, n, k = args
+    assert L.q4k_gemv_residual(ctypes.c_void_p(w), ctypes.c_void_p(x), ctypes.c_void_p(r), ctypes.c_void_p(y), n, k,
+                               None) == status
+
+
+def _items(*triples):
+    from q4_dequant_gemv_amd import q4k
+
+    items = (q4k.GemvItem * max(len(triples), 1))()
+    for i, (w, y, n) in enumerate(triples):
+        items[i].w, items[i].y, items[i].n = w, y, n
+    return items
+
+
+@pytest.mark.parametrize("triples,count,x,k,status", [
+    ([(W, Y, 16)], 1, X, 300, SHAPE),
+    ([(W, Y, 16)] * 9, 9, X, 256, INVALID),                      # more than Q4K_MAX_MULTI
+    ([(W, Y, 16)], -1, X, 256, INVALID),
+    ([(W, Y, 16), (Y2, Y, 16)], 2, X, 256, INVALID),             # two outputs alias
+    ([(W, Y, 16), (Y2, Y + 60, 16)], 2, X, 256, INVALID),        # outputs overlap
+    ([(W, Y, 16), (Y2, Y2 + 64, 16)], 2, X, 256, INVALID),       # an output overlaps another matrix
+    ([(W, X, 16)], 1, X, 256, INVALID),                          # output aliases x
+    ([(W, Y, 16), (0, Y2, 16)], 2, X, 256, INVALID),             # null matrix
+    ([(W, Y, 16), (Y2, 0, 16)], 2, X, 256, INVALID),             # null output
+    ([(W, Y, 16), (Y2 + 8, R, 16)], 2, X, 256, MISALIGNED),
+    ([(W, Y, 16)], 1, 0, 256, INVALID),                          # null x
+    ([(W, Y, -16)], 1, X, 256, INVALID),
+    ([(W, Y, 0), (0, 0, 0)], 2, X, 256, OK),                     # no rows: nothing launched
+    ([], 0, 0, 256, OK),
+])
+def test_multi_validation(L, triples, count, x, k, status):
+    assert L.q4k_gemv_multi(_items(*triples), count, ctypes.c_void_p(x), k, None) == status
+
+
+def test_multi_null_items(L):
+    assert L.q4k_gemv_multi(None, 1, ctypes.c_void_p(X), 256, None) == INVALID
+    assert L.q4k_gemv_multi(None, 0, ctypes.c_void_p(X), 256, None) == OK
 
 
 @pytest.mark.parametrize("args,status", [

@@ -6,8 +6,9 @@ The oracle is checked against things other than itself:
   * IEEE binary16 decoding by numpy for all 65,536 patterns,
   * the inverse of the six-bit scale packing, exhaustively,
   * closed forms and invariants: zero codes give -dmin*m, linearity in x,
-    integer matrices against an int64 numpy matmul, exactness of the f32
-    dequant at the configs' value ranges, silu against scipy's expit.
+    integer matrices against an int64 numpy matmul (also with a residual
+    added), exactness of the f32 dequant at the configs' value ranges, silu
+    against scipy's expit.
 ``test_pins_catch_planted_mistakes`` plants plausible bugs in a copy of the
 oracle source and checks that these pins reject every one.
 """
@@ -180,8 +181,32 @@ def check_one_hot(orc):
     np.testing.assert_array_equal(w.astype(np.float64), want)
 
 
+def check_residual(orc):
+    # integer weights and activations with a residual of halves: every sum is
+    # exact in f64, so y must equal the int64 product plus r exactly
+    n, k = 40, 512
+    blocks = _integer_blocks(n * k // 256, 16)
+    q = ind_codes(blocks).reshape(n, k)
+    g = np.random.default_rng(17)
+    x = g.integers(-20, 21, k)
+    r = (g.integers(-4000, 4001, n) / 2.0).astype(np.float32)
+    y, a = orc.gemv_residual(blocks.reshape(-1), x.astype(np.float32), r)
+    np.testing.assert_array_equal(y, (q @ x).astype(np.float64) + r.astype(np.float64))
+    np.testing.assert_array_equal(a, (np.abs(q * x[None, :])).sum(axis=1).astype(np.float64)
+                                  + np.abs(r.astype(np.float64)))
+    # x = 0: the product vanishes and the residual passes through unchanged
+    y0, _ = orc.gemv_residual(blocks.reshape(-1), np.zeros(k, np.float32), r)
+    np.testing.assert_array_equal(y0, r.astype(np.float64))
+    # the several-matrix form is one plain GEMV per matrix
+    b2 = _integer_blocks(7 * k // 256, 18)
+    q2 = ind_codes(b2).reshape(7, k)
+    outs = orc.gemv_multi([blocks.reshape(-1), b2.reshape(-1)], x.astype(np.float32))
+    np.testing.assert_array_equal(outs[0][0], (q @ x).astype(np.float64))
+    np.testing.assert_array_equal(outs[1][0], (q2 @ x).astype(np.float64))
+
+
 ALL_PINS = [check_golden_block, check_independent_decoder, check_zero_codes, check_linearity,
-            check_integer_matrix, check_closed_form, check_one_hot]
+            check_integer_matrix, check_closed_form, check_one_hot, check_residual]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -268,6 +293,9 @@ MUTATIONS = {
     "min_uses_scale": ("const float ml = dmin * (float)m;", "const float ml = dmin * (float)sc;"),
     "subblock_of_weight_wrong": ("const int j = e / 32; /* sub-block */", "const int j = (e % 128) / 16; /* sub-block */"),
     "silu_sign": ("exp(-g[i])", "exp(g[i])"),
+    "residual_dropped": ("y[r - r0] = dot + (double)res[r];", "y[r - r0] = dot;"),
+    "residual_subtracted": ("y[r - r0] = dot + (double)res[r];", "y[r - r0] = dot - (double)res[r];"),
+    "residual_row_shifted": ("y[r - r0] = dot + (double)res[r];", "y[r - r0] = dot + (double)res[r1 - 1 - r];"),
 }
 
 
@@ -301,7 +329,7 @@ def test_pins_catch_planted_mistakes(oracle_mod, name, tmp_path):
     real = oracle_mod._load()
     for fn in ("q4k_oracle_f16_to_f32", "q4k_oracle_scale_min", "q4k_oracle_dequant_block",
                "q4k_oracle_dequant_rows", "q4k_gemv_oracle_into", "q4k_gemv_batched_oracle_into",
-               "q4k_fused_swiglu_oracle_into"):
+               "q4k_fused_swiglu_oracle_into", "q4k_gemv_residual_oracle_into"):
         getattr(lib, fn).argtypes = getattr(real, fn).argtypes
         getattr(lib, fn).restype = getattr(real, fn).restype
     assert _run_pins_with(lib) > 0, f"no pin caught the planted mistake {name}"
