@@ -67,8 +67,8 @@ def parse():
                     help="also time every kernel at every config shape (table on stderr)")
     ap.add_argument("--case", default=None,
                     help="only run one kernel in a loop, for profilers: gemv:NAME, swiglu:NAME, "
-                         "residual:NAME, dequant:NAME or batched:M:NAME with NAME a shape of "
-                         "inputs.SHAPES, or multi:gdn_0p8b")
+                         "residual:NAME, q8_0:NAME, dequant:NAME or batched:M:NAME with NAME a shape "
+                         "of inputs.SHAPES, or multi:gdn_0p8b")
     return ap.parse_args()
 
 
@@ -213,9 +213,10 @@ def main():
             del sets_b
 
     blocks = decode_blocks(q4k, inputs, torch, dev, stream, args.steps, args.warmup)
+    q8 = q8_0_kernels(q4k, inputs, torch, dev, stream, args.steps, args.warmup)
 
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s; per kernel {kernels}; "
-        f"batched {batched}; decode blocks {blocks}; host wall {wall:.3f}s")
+        f"batched {batched}; decode blocks {blocks}; q8_0 {q8}; host wall {wall:.3f}s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -263,6 +264,7 @@ def main():
             "kernels": kernels,
             "batched_9b_ffn": batched,
             "decode_blocks": blocks,
+            "q8_0_9b": q8,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -338,6 +340,26 @@ def decode_blocks(q4k, inputs, torch, dev, stream, steps, warmup):
     return out
 
 
+def q8_0_kernels(q4k, inputs, torch, dev, stream, steps, warmup):
+    """The Q8_0 GEMV on the 9B shapes (34-byte blocks of 32 weights, 1.0625
+    bytes per weight), weights rotated over >= 512 MiB of copies."""
+    out = {}
+    for nm, tid in (("lm_head_9b", 0), ("gate_9b", 1), ("down_9b", 2)):
+        n, k = inputs.SHAPES[nm]
+        w0 = inputs.make_q8_0(n, k, config_id=52, tensor_id=tid).reshape(-1)
+        copies = max(1, -(-(512 << 20) // w0.nbytes))
+        ws = [torch.from_numpy(w0).to(dev) for _ in range(copies)]
+        x = torch.from_numpy(inputs.make_x(1, k, config_id=52, tensor_id=100 + tid)[0]).to(dev)
+        y = torch.empty(n, dtype=torch.float32, device=dev)
+        t = _time_launches(lambda i: q4k.q8_0_gemv(ws[i % copies], x, y=y, stream=stream), torch, stream, steps,
+                           warmup)
+        abytes = w0.nbytes + 4 * k + 4 * n
+        out[nm] = {"weight_bytes": w0.nbytes, "mean_us": round(t * 1e6, 3), "GB/s": round(abytes / t / 1e9, 1),
+                   "frac_hbm_peak": round(abytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del ws
+    return out
+
+
 def time_call(fn, torch, reps=50, warm=5):
     for _ in range(warm):
         fn()
@@ -394,7 +416,10 @@ def run_case(case, steps, warmup, q4k, inputs, torch, np, dev):
         return
     m = int(parts[1]) if kind == "batched" else 1
     n, k = inputs.SHAPES[name]
-    w0 = inputs.make_q4k(n, k, config_id=7, tensor_id=1).reshape(-1)
+    if kind == "q8_0":
+        w0 = inputs.make_q8_0(n, k, config_id=7, tensor_id=1).reshape(-1)
+    else:
+        w0 = inputs.make_q4k(n, k, config_id=7, tensor_id=1).reshape(-1)
     mats = 2 if kind == "swiglu" else 1
     copies = max(1, -(-(512 << 20) // (mats * w0.nbytes)))
     ws = [torch.from_numpy(w0).to(dev) for _ in range(copies * mats)]
@@ -414,6 +439,8 @@ def run_case(case, steps, warmup, q4k, inputs, torch, np, dev):
             q4k.dequant(ws[c], k, out=out)
         elif kind == "residual":
             q4k.gemv_residual(ws[c], xs[0], res, y=out[0])
+        elif kind == "q8_0":
+            q4k.q8_0_gemv(ws[c], xs[0], y=out[0])
         else:
             raise SystemExit(f"unknown case kind {kind}")
 

@@ -72,6 +72,11 @@ typedef enum {
 #define Q4K_BLOCK_BYTES 144
 #define Q4K_BLOCK_WEIGHTS 256
 
+/* Bytes of one Q8_0 block and weights per block (an f16 scale, then 32
+ * signed bytes). */
+#define Q4K_Q8_0_BLOCK_BYTES 34
+#define Q4K_Q8_0_BLOCK_WEIGHTS 32
+
 /*
  * Batch-1 GEMV (the decode case: "@simulatte/doppler 0.1.7 -> 0.1.8",
  * matmul-selection.js, resolveMatmulPhase treats M == 1 as decode and
@@ -115,6 +120,21 @@ typedef struct {
  * result equals what q4k_gemv gives for that matrix.
  */
 Q4K_API q4k_status q4k_gemv_multi(const q4k_gemv_item *items, int count, const float *x, int64_t k, void *stream);
+
+/*
+ * Batch-1 GEMV over Q8_0 weights, the second block format of the decode path
+ * ("qualia_core_db/inference/cuda_lane/mod.rs" re-exports try_q8_0_cuda_gemv,
+ * q8_0_gemv_oracle_into, Q8_0_BLOCK_BYTES and Q8_0_BLOCK_ELEMS from its q8
+ * module).  Each row of k weights is k/32 blocks of 34 bytes: d (IEEE
+ * binary16, little-endian), then 32 signed bytes q; weight e of a block is
+ * f32(d) * q[e] (the GGUF Q8_0 block).
+ *   w : Q8_0 matrix [n, k] (n*(k/32)*34 bytes), 2-byte aligned
+ *   x : f32 [k];  y : f32 [n], written: y[i] = sum_c W[i,c] x[c].
+ * k % 32 != 0 -> Q4K_ERR_UNSUPPORTED_SHAPE.  Rows with an even number of
+ * blocks in a 4-byte aligned matrix take the streaming kernels; any other
+ * layout a slower one-wave-per-row kernel.  Accuracy as q4k_gemv.
+ */
+Q4K_API q4k_status q4k_q8_0_gemv(const void *w, const float *x, float *y, int64_t n, int64_t k, void *stream);
 
 /*
  * Skinny GEMM over the same weights for m tokens (selectQ4KFusedVariant's

@@ -29,6 +29,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 BLOCK_BYTES = 144
 BLOCK_WEIGHTS = 256
+Q8_0_BLOCK_BYTES = 34
+Q8_0_BLOCK_WEIGHTS = 32
 
 
 def build(force: bool = True) -> str:
@@ -70,6 +72,12 @@ def _load():
         lib.q4k_fused_swiglu_oracle_into.restype = None
         lib.q4k_gemv_residual_oracle_into.argtypes = [p, p, p, i64, i64, i64, p, p]
         lib.q4k_gemv_residual_oracle_into.restype = None
+        lib.q8_0_oracle_dequant_block.argtypes = [p, p]
+        lib.q8_0_oracle_dequant_block.restype = None
+        lib.q8_0_oracle_dequant_rows.argtypes = [p, i64, i64, i64, p]
+        lib.q8_0_oracle_dequant_rows.restype = None
+        lib.q8_0_gemv_oracle_into.argtypes = [p, p, i64, i64, i64, p, p]
+        lib.q8_0_gemv_oracle_into.restype = None
         _lib = lib
     return _lib
 
@@ -208,3 +216,48 @@ def gemv_residual(w: np.ndarray, x: np.ndarray, r: np.ndarray, threads: int = 1)
 def gemv_multi(ws, x: np.ndarray, threads: int = 1):
     """[(y_j, A_j)]: one GEMV per matrix of ``ws``, all against the same x."""
     return [gemv(w, x, threads=threads) for w in ws]
+
+
+# ------------------------------------------------------------------- Q8_0
+def _q8_rows(w: np.ndarray, k: int) -> np.ndarray:
+    if k % Q8_0_BLOCK_WEIGHTS != 0:
+        raise ValueError(f"k={k} is not a multiple of {Q8_0_BLOCK_WEIGHTS}")
+    rb = (k // Q8_0_BLOCK_WEIGHTS) * Q8_0_BLOCK_BYTES
+    w = np.ascontiguousarray(w, dtype=np.uint8).reshape(-1)
+    if rb == 0 or w.size % rb != 0:
+        raise ValueError(f"{w.size} bytes is not a whole number of {rb}-byte rows")
+    return w.reshape(-1, rb)
+
+
+def q8_0_dequant_block(block34: bytes) -> np.ndarray:
+    """The 32 f32 weights of one Q8_0 block."""
+    buf = np.frombuffer(bytes(block34), dtype=np.uint8).copy()
+    if buf.size != Q8_0_BLOCK_BYTES:
+        raise ValueError("a Q8_0 block is 34 bytes")
+    out = np.empty(Q8_0_BLOCK_WEIGHTS, dtype=np.float32)
+    _load().q8_0_oracle_dequant_block(_ptr(buf), _ptr(out))
+    return out
+
+
+def q8_0_dequant(w: np.ndarray, k: int, threads: int = 1) -> np.ndarray:
+    """A Q8_0 matrix as f32 [n, k]."""
+    rows = _q8_rows(w, k)
+    n = rows.shape[0]
+    out = np.empty((n, k), dtype=np.float32)
+    lib = _load()
+    _run(lambda a, b: lib.q8_0_oracle_dequant_rows(_ptr(rows), k, a, b, _ptr(out[a:b])), n, threads)
+    return out
+
+
+def q8_0_gemv(w: np.ndarray, x: np.ndarray, threads: int = 1):
+    """(y, A): y[n] = sum_k W[n,k] x[k] (f64) for a Q8_0 matrix, A[n] = sum_k |W[n,k] x[k]|."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    k = x.size
+    rows = _q8_rows(w, k)
+    n = rows.shape[0]
+    y = np.empty(n, dtype=np.float64)
+    a = np.empty(n, dtype=np.float64)
+    lib = _load()
+    _run(lambda r0, r1: lib.q8_0_gemv_oracle_into(_ptr(rows[r0:r1]), _ptr(x), k, 0, r1 - r0,
+                                                  _ptr(y[r0:r1]), _ptr(a[r0:r1])), n, threads)
+    return y, a

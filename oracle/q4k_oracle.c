@@ -181,3 +181,58 @@ void q4k_gemv_residual_oracle_into(const uint8_t *w, const float *x, const float
         a[r - r0] = mag + fabs((double)res[r]);
     }
 }
+
+/* ------------------------------------------------------------------ Q8_0
+ * The second block format of the decode path ("qualia_core_db/inference/
+ * cuda_lane/mod.rs" re-exports q8_0_gemv_oracle_into, try_q8_0_cuda_gemv,
+ * Q8_0_BLOCK_BYTES and Q8_0_BLOCK_ELEMS from its q8 module).  The block layout
+ * is not printed on the pages; as for Q4_K the public GGUF block is used:
+ *     bytes 0-1    d   IEEE binary16, little-endian
+ *     bytes 2-33   q   32 signed bytes (two's complement)
+ * and weight e of the block is f32(d) * q[e] (exact in f32: 11 x 8 bits).
+ * A row of k weights (k % 32 == 0) is k/32 consecutive blocks. */
+#define Q8_0_BLOCK_BYTES 34
+#define Q8_0_BLOCK_WEIGHTS 32
+
+/* Dequantize one 34-byte block into 32 f32 weights. */
+void q8_0_oracle_dequant_block(const uint8_t *blk, float *out) {
+    const float d = q4k_oracle_f16_to_f32((uint16_t)((blk[1] << 8) | blk[0]));
+    for (int e = 0; e < Q8_0_BLOCK_WEIGHTS; ++e) {
+        const int q = (int)(int8_t)blk[2 + e];
+        out[e] = d * (float)q;
+    }
+}
+
+/* W[r, :] as f32 for rows [r0, r1); out is [(r1-r0), k] row-major. */
+void q8_0_oracle_dequant_rows(const uint8_t *w, int64_t k, int64_t r0, int64_t r1, float *out) {
+    const int64_t nb = k / Q8_0_BLOCK_WEIGHTS;
+    const int64_t row_bytes = nb * Q8_0_BLOCK_BYTES;
+    for (int64_t r = r0; r < r1; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            q8_0_oracle_dequant_block(w + r * row_bytes + b * Q8_0_BLOCK_BYTES,
+                                      out + (r - r0) * k + b * Q8_0_BLOCK_WEIGHTS);
+        }
+    }
+}
+
+/* GEMV, rows [r0, r1): y[r-r0] = sum_k W[r,k] x[k] in f64, k order;
+ * a[r-r0] = sum_k |W[r,k] x[k]|. */
+void q8_0_gemv_oracle_into(const uint8_t *w, const float *x, int64_t k, int64_t r0, int64_t r1, double *y,
+                           double *a) {
+    const int64_t nb = k / Q8_0_BLOCK_WEIGHTS;
+    const int64_t row_bytes = nb * Q8_0_BLOCK_BYTES;
+    float wblk[Q8_0_BLOCK_WEIGHTS];
+    for (int64_t r = r0; r < r1; ++r) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            q8_0_oracle_dequant_block(w + r * row_bytes + b * Q8_0_BLOCK_BYTES, wblk);
+            for (int e = 0; e < Q8_0_BLOCK_WEIGHTS; ++e) {
+                const double p = (double)wblk[e] * (double)x[b * Q8_0_BLOCK_WEIGHTS + e];
+                acc += p;
+                mag += p < 0.0 ? -p : p;
+            }
+        }
+        y[r - r0] = acc;
+        a[r - r0] = mag;
+    }
+}

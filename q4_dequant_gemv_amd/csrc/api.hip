@@ -154,6 +154,21 @@ q4k_status q4k_gemv_multi(const q4k_gemv_item *items, int count, const float *x,
     return from_hip(q4k::launch_gemv_multi(jobs, count, nullptr, x, k, static_cast<hipStream_t>(stream)));
 }
 
+q4k_status q4k_q8_0_gemv(const void *w, const float *x, float *y, int64_t n, int64_t k, void *stream) {
+    if (n < 0 || k < 0) return Q4K_ERR_INVALID_ARG;
+    if (k % Q4K_Q8_0_BLOCK_WEIGHTS != 0) return Q4K_ERR_UNSUPPORTED_SHAPE;
+    if (k > 0 && n > q4k::kMaxElems / k) return Q4K_ERR_INVALID_ARG;
+    if (n == 0) return Q4K_OK;
+    const uint64_t wb = static_cast<uint64_t>(n) * static_cast<uint64_t>(k / Q4K_Q8_0_BLOCK_WEIGHTS) *
+                        Q4K_Q8_0_BLOCK_BYTES;
+    if (y == nullptr || (k > 0 && (w == nullptr || x == nullptr))) return Q4K_ERR_INVALID_ARG;
+    if (!aligned(w, 2) || !aligned(x, 4) || !aligned(y, 4)) return Q4K_ERR_MISALIGNED;
+    const uint64_t yb = static_cast<uint64_t>(n) * 4, xb = static_cast<uint64_t>(k) * 4;
+    if (overlap(y, yb, w, wb) || overlap(y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
+    return from_hip(q4k::launch_q8_0_gemv(static_cast<const uint8_t *>(w), x, nullptr, y, n, k,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 q4k_status q4k_gemv_batched(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
                             void *stream) {
     uint64_t wb = 0;
@@ -207,6 +222,6 @@ const char *q4k_status_string(q4k_status s) {
     return "unknown status";
 }
 
-int q4k_abi_version(void) { return 101; }
+int q4k_abi_version(void) { return 102; }
 
 }  // extern "C"

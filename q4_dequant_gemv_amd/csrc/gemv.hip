@@ -38,6 +38,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "launch.h"
 #include "q4k_device.h"
@@ -45,63 +46,135 @@
 
 namespace q4k {
 
-// One row's weight bytes for one lane (its 64-weight group), per matrix: the
-// super-block header and the group's 32 code bytes.
-template <int NMAT>
+// A weight format of the streaming kernels: what one lane loads for its
+// 64-weight group of a row, where those bytes sit, and their dot product with
+// the group's activations.  Lanes past the row's last group (K/64 not a power
+// of two) read group 0 again and drop it.
+//
+// Q4_K: the group is sub-block pair (2g, 2g+1) of a 144-byte super-block; the
+// lane loads the super-block's 16-byte header and the group's 32 code bytes.
+struct Q4KFormat {
+    struct Lane {
+        uint32_t off_hdr;  // byte offset of the super-block header
+        uint32_t off_qa;   // byte offset of the group's first 16 code bytes
+        PairSelect ps;
+        int j;             // group index (clamped)
+        bool ok;           // the group exists
+    };
+    struct Loads {
+        uint4 hdr, qa, qb;
+    };
+    static int64_t row_bytes(int64_t k) { return (k / kBlockWeights) * kBlockBytes; }
+    static __device__ __forceinline__ Lane lane(int j, int ngroups, uint32_t row_off) {
+        Lane g;
+        g.ok = j < ngroups;
+        g.j = g.ok ? j : 0;
+        g.ps = pair_select(g.j & 3);
+        g.off_hdr = row_off + static_cast<uint32_t>(g.j >> 2) * kBlockBytes;
+        g.off_qa = g.off_hdr + 16u + 32u * static_cast<uint32_t>(g.j & 3);
+        return g;
+    }
+    static __device__ __forceinline__ void issue(Loads &l, __amdgpu_buffer_rsrc_t r, const Lane &g) {
+        l.hdr = buffer_load16(r, g.off_hdr);
+        l.qa = buffer_load16(r, g.off_qa);
+        l.qb = buffer_load16(r, g.off_qa + 16u);
+    }
+    // sum over the group of w * x in units of the group's activation scale
+    static __device__ __forceinline__ float dot(const Loads &l, const Lane &g, const XRegs &xr) {
+        GroupCodes c;
+        decode_group(l.hdr, l.qa, l.qb, g.ps, c);
+        return group_dot(c, xr);
+    }
+};
+
+// Q8_0: 34-byte blocks of 32 weights, an f16 scale d then 32 signed bytes q,
+// w = d * q.  The lane's 64-weight group is two blocks, 68 bytes starting at
+// 68*j, dword-aligned whenever the row is (K % 64 == 0 and a 4-byte aligned
+// matrix): 17 dwords, loaded as four 16-byte loads and one 4-byte load.  The
+// second block's codes are dword-aligned; the first block's start two bytes
+// into a dword and are realigned with v_alignbyte.  The codes are signed
+// bytes, so v_dot4_i32_i8 multiplies them with the activation limbs directly.
+// A limb sum stays within 32 * 128 * 128 = 2^19, but the recombined sum of a
+// block reaches 2^34, beyond int32: the three limb sums are converted to f32
+// (exactly) and combined with two FMAs, one rounding each (a relative 2^-24
+// of the block's sum).
+struct Q8_0Format {
+    static constexpr int kBlockWeights = 32;
+    static constexpr int kBlockBytes = 34;
+    struct Lane {
+        uint32_t off;  // byte offset of the group's first block
+        int j;
+        bool ok;
+    };
+    struct Loads {
+        uint4 a, b, c, d;
+        uint32_t e;
+    };
+    static int64_t row_bytes(int64_t k) { return (k / kBlockWeights) * kBlockBytes; }
+    static __device__ __forceinline__ Lane lane(int j, int ngroups, uint32_t row_off) {
+        Lane g;
+        g.ok = j < ngroups;
+        g.j = g.ok ? j : 0;
+        g.off = row_off + 68u * static_cast<uint32_t>(g.j);
+        return g;
+    }
+    static __device__ __forceinline__ void issue(Loads &l, __amdgpu_buffer_rsrc_t r, const Lane &g) {
+        l.a = buffer_load16(r, g.off);
+        l.b = buffer_load16(r, g.off + 16u);
+        l.c = buffer_load16(r, g.off + 32u);
+        l.d = buffer_load16(r, g.off + 48u);
+        l.e = buffer_load4(r, g.off + 64u);
+    }
+    static __device__ __forceinline__ float dot(const Loads &l, const Lane &, const XRegs &xr) {
+        const uint32_t dw[17] = {l.a.x, l.a.y, l.a.z, l.a.w, l.b.x, l.b.y, l.b.z, l.b.w, l.c.x,
+                                 l.c.y, l.c.z, l.c.w, l.d.x, l.d.y, l.d.z, l.d.w, l.e};
+        const float d0 = half_bits_to_float(dw[0]);
+        const float d1 = half_bits_to_float(dw[8] >> 16);
+        int a00 = 0, a01 = 0, a02 = 0, a10 = 0, a11 = 0, a12 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            // bytes 2+4i .. 5+4i of the group: codes 4i .. 4i+3 of the first block
+            const int q0 = static_cast<int>(__builtin_amdgcn_alignbyte(dw[i + 1], dw[i], 2));
+            const int q1 = static_cast<int>(dw[9 + i]);
+            a00 = __builtin_amdgcn_sdot4(q0, static_cast<int>(xr.limb[0][0][i]), a00, false);
+            a01 = __builtin_amdgcn_sdot4(q0, static_cast<int>(xr.limb[0][1][i]), a01, false);
+            a02 = __builtin_amdgcn_sdot4(q0, static_cast<int>(xr.limb[0][2][i]), a02, false);
+            a10 = __builtin_amdgcn_sdot4(q1, static_cast<int>(xr.limb[1][0][i]), a10, false);
+            a11 = __builtin_amdgcn_sdot4(q1, static_cast<int>(xr.limb[1][1][i]), a11, false);
+            a12 = __builtin_amdgcn_sdot4(q1, static_cast<int>(xr.limb[1][2][i]), a12, false);
+        }
+        const float s0 = fmaf(static_cast<float>(a02), 65536.0f, fmaf(static_cast<float>(a01), 256.0f,
+                                                                        static_cast<float>(a00)));
+        const float s1 = fmaf(static_cast<float>(a12), 65536.0f, fmaf(static_cast<float>(a11), 256.0f,
+                                                                        static_cast<float>(a10)));
+        return d0 * s0 + d1 * s1;
+    }
+};
+
+// One row's weight bytes for one lane, per matrix.
+template <class F, int NMAT>
 struct RowLoads {
-    uint4 hdr[NMAT];
-    uint4 qa[NMAT];
-    uint4 qb[NMAT];
+    typename F::Loads m[NMAT];
 };
-
-// Where a lane's group sits inside a row (fixed for the whole kernel).  Lanes
-// past the row's last group (K/64 not a power of two) read group 0 again and
-// drop it.
-struct LaneGroup {
-    uint32_t off_hdr;  // byte offset of the super-block header
-    uint32_t off_qa;   // byte offset of the group's first 16 code bytes
-    PairSelect ps;
-    int j;             // group index (clamped)
-    bool ok;           // the group exists
-};
-
-__device__ __forceinline__ LaneGroup lane_group(int j, int ngroups, uint32_t row_off) {
-    LaneGroup g;
-    g.ok = j < ngroups;
-    g.j = g.ok ? j : 0;
-    g.ps = pair_select(g.j & 3);
-    g.off_hdr = row_off + static_cast<uint32_t>(g.j >> 2) * kBlockBytes;
-    g.off_qa = g.off_hdr + 16u + 32u * static_cast<uint32_t>(g.j & 3);
-    return g;
-}
 
 // Issues one row's loads from descriptors based at `base` (wave-uniform) that
 // cover `nrec` bytes: loads at or past nrec return zeros, so a row past the
 // end costs no memory traffic and needs no branch.
-template <int NMAT>
-__device__ __forceinline__ void issue_row(RowLoads<NMAT> &b, const uint8_t *w, const uint8_t *wu, int64_t base,
-                                          int nrec, const LaneGroup &g) {
+template <class F, int NMAT>
+__device__ __forceinline__ void issue_row(RowLoads<F, NMAT> &b, const uint8_t *w, const uint8_t *wu, int64_t base,
+                                          int nrec, const typename F::Lane &g) {
 #pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt) {
-        const __amdgpu_buffer_rsrc_t r = stream_rsrc((mt == 0 ? w : wu) + base, nrec);
-        b.hdr[mt] = buffer_load16(r, g.off_hdr);
-        b.qa[mt] = buffer_load16(r, g.off_qa);
-        b.qb[mt] = buffer_load16(r, g.off_qa + 16u);
-    }
+    for (int mt = 0; mt < NMAT; ++mt) F::issue(b.m[mt], stream_rsrc((mt == 0 ? w : wu) + base, nrec), g);
 }
 
 // The lane's share of the row, per matrix: sum over its group of w * x.
-template <int NMAT>
-__device__ __forceinline__ void lane_dot(const RowLoads<NMAT> &b, const LaneGroup &g, const XRegs &xr, bool active,
-                                         float (&acc)[NMAT]) {
+template <class F, int NMAT>
+__device__ __forceinline__ void lane_dot(const RowLoads<F, NMAT> &b, const typename F::Lane &g, const XRegs &xr,
+                                         bool active, float (&acc)[NMAT]) {
 #pragma unroll
     for (int mt = 0; mt < NMAT; ++mt) {
         acc[mt] = 0.0f;
-        if (active) {
-            GroupCodes c;
-            decode_group(b.hdr[mt], b.qa[mt], b.qb[mt], g.ps, c);
-            acc[mt] = xr.scale * group_dot(c, xr);
-        }
+        if (active) acc[mt] = xr.scale * F::dot(b.m[mt], g, xr);
     }
 }
 
@@ -127,7 +200,7 @@ struct MatTable {
     int count;
 };
 
-template <int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES>
+template <class F, int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES>
 __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable mt, const uint8_t *__restrict__ wu,
                                                                 const float *x, int ngroups, int64_t row_bytes) {
     static_assert(NB >= 2, "at least one row in flight");
@@ -144,7 +217,7 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     // +kRowsPerWave-1): the iteration's base address is wave-uniform (scalar
     // registers), so the loop rewrites no per-lane address registers while
     // earlier loads are in flight
-    const LaneGroup g = lane_group(sub, ngroups, static_cast<uint32_t>(slot * row_bytes));
+    const typename F::Lane g = F::lane(sub, ngroups, static_cast<uint32_t>(slot * row_bytes));
     // Loop control is 32-bit and scalar (the host keeps the iteration count
     // below 2^31): gfx9 has no 64-bit scalar compare, and a vector compare in
     // the loop would borrow registers that earlier memory operations still own.
@@ -168,7 +241,7 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     };
     LoadCursor lc{0, 0, mt.it_begin[1], mt.tail_bytes[0], mt.w[0]};
     RowCursor rc{0, 0, mt.it_begin[1], mt.n[0], mt.y[0], mt.r[0]};
-    auto issue = [&](RowLoads<NMAT> &b, int it) {
+    auto issue = [&](RowLoads<F, NMAT> &b, int it) {
         while (it >= lc.end && lc.mi + 1 < count) {
             ++lc.mi;
             lc.begin = lc.end;
@@ -183,12 +256,7 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
         // in scalar registers whatever the compiler concluded across the joins
         const uint8_t *wbase = reinterpret_cast<const uint8_t *>(wave_uniform(reinterpret_cast<int64_t>(lc.w)));
 #pragma unroll
-        for (int m2 = 0; m2 < NMAT; ++m2) {
-            const __amdgpu_buffer_rsrc_t r = stream_rsrc((m2 == 0 ? wbase : wu) + off, nrec);
-            b.hdr[m2] = buffer_load16(r, g.off_hdr);
-            b.qa[m2] = buffer_load16(r, g.off_qa);
-            b.qb[m2] = buffer_load16(r, g.off_qa + 16u);
-        }
+        for (int m2 = 0; m2 < NMAT; ++m2) F::issue(b.m[m2], stream_rsrc((m2 == 0 ? wbase : wu) + off, nrec), g);
     };
     auto row_cursor = [&](int it) {
         while (it >= rc.end && rc.mi + 1 < count) {
@@ -213,7 +281,7 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     // memory clobber: no instruction, only an ordering point for the compiler;
     // x is deliberately not __restrict__ so its loads cannot move across it)
     asm volatile("" ::: "memory");
-    RowLoads<NMAT> buf[NB];
+    RowLoads<F, NMAT> buf[NB];
 #pragma unroll
     for (int b = 0; b + 1 < NB; ++b) issue(buf[b], it0 + b * nwaves);
 
@@ -285,7 +353,7 @@ done:
 // residual before it writes that row).
 constexpr int kFlush = 8;
 
-template <int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
+template <class F, int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
 __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const uint8_t *__restrict__ w,
                                                                            const uint8_t *__restrict__ wu,
                                                                            const float *x, float *y,
@@ -301,7 +369,7 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int slice = wave % S;
     const int rslot = wave / S;
-    const LaneGroup g = lane_group(slice * kWave + lane, ngroups, 0u);
+    const typename F::Lane g = F::lane(slice * kWave + lane, ngroups, 0u);
     // block iterations b = blockIdx.x + c * gridDim.x cover rows b*R .. b*R+R-1;
     // the host keeps gridDim.x <= the number of block iterations
     const int64_t nbi = (n + R - 1) / R;
@@ -309,7 +377,7 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
     auto row_of = [&](int c, int r) -> int64_t {
         return (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(c) * gridDim.x) * R + r;
     };
-    auto issue = [&](RowLoads<NMAT> &b, int c) {
+    auto issue = [&](RowLoads<F, NMAT> &b, int c) {
         const int64_t row = row_of(c, rslot);
         const bool live = c < my_iters && row < n;
         issue_row(b, w, wu, live ? row * row_bytes : 0, live ? static_cast<int>(row_bytes) : 0, g);
@@ -318,7 +386,7 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
     constexpr int kXChunks = (S * kWave * 16 + BLOCK - 1) / BLOCK;
     const XLoaded<kXChunks> xl = load_x<BLOCK, kXChunks>(x, ngroups);
     asm volatile("" ::: "memory");
-    RowLoads<NMAT> buf[NB];
+    RowLoads<F, NMAT> buf[NB];
 #pragma unroll
     for (int b = 0; b + 1 < NB; ++b) issue(buf[b], b);
 
@@ -413,6 +481,34 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(const uint8_t *__rest
     }
 }
 
+// Q8_0, any K % 32 == 0 and any 2-byte aligned matrix: one wave per row, each
+// lane takes whole blocks (16-bit loads) and accumulates d*q*x with FMA.
+__global__ __launch_bounds__(256) void q8_0_generic_kernel(const uint8_t *__restrict__ w,
+                                                           const float *__restrict__ x, float *y, const float *res,
+                                                           int64_t n, int64_t k, int64_t row_bytes) {
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
+    const int64_t nblocks = k / Q8_0Format::kBlockWeights;
+    for (int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6); row < n; row += nwaves) {
+        float acc = 0.0f;
+        for (int64_t b = lane; b < nblocks; b += 64) {
+            const uint16_t *blk = reinterpret_cast<const uint16_t *>(w + row * row_bytes + b * Q8_0Format::kBlockBytes);
+            const float d = half_bits_to_float(blk[0]);
+            const float *xp = x + b * Q8_0Format::kBlockWeights;
+#pragma unroll
+            for (int h = 0; h < 16; ++h) {
+                const uint32_t pair = blk[1 + h];
+                const float w0 = d * static_cast<float>(static_cast<int8_t>(pair & 0xffu));
+                const float w1 = d * static_cast<float>(static_cast<int8_t>(pair >> 8));
+                acc = fmaf(w0, xp[2 * h], acc);
+                acc = fmaf(w1, xp[2 * h + 1], acc);
+            }
+        }
+        acc = group_sum<64>(acc);
+        if (lane == 0) y[row] = res != nullptr ? acc + res[row] : acc;
+    }
+}
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -430,12 +526,12 @@ int resident_blocks_per_cu(Kernel kern, int block, size_t lds, std::atomic<int> 
 }
 
 // One launch of the batch-1 kernel over `count` matrices (all with k columns).
-template <int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES>
+template <class F, int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES>
 hipError_t launch_fast(const GemvJob *jobs, int count, const uint8_t *wu, const float *x, int64_t k,
                        hipStream_t stream) {
-    auto kern = gemv_kernel<LPR, SWIGLU, NB, BLOCK, MIN_WAVES>;
+    auto kern = gemv_kernel<F, LPR, SWIGLU, NB, BLOCK, MIN_WAVES>;
     const int ngroups = static_cast<int>(k / 64);
-    const int64_t row_bytes = (k / kBlockWeights) * kBlockBytes;
+    const int64_t row_bytes = F::row_bytes(k);
     const size_t lds = static_cast<size_t>(ngroups) * sizeof(XGroup);
     static std::atomic<int> cache[kMaxDevices];
     const int per_cu = resident_blocks_per_cu(kern, BLOCK, lds, cache);
@@ -464,10 +560,10 @@ hipError_t launch_fast(const GemvJob *jobs, int count, const uint8_t *wu, const 
     return hipGetLastError();
 }
 
-template <int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
+template <class F, int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
 hipError_t launch_split(const uint8_t *w, const uint8_t *wu, const float *x, const float *r, float *y, int64_t n,
                         int64_t k, hipStream_t stream) {
-    auto kern = gemv_split_kernel<S, R, SWIGLU, NB, MIN_WAVES>;
+    auto kern = gemv_split_kernel<F, S, R, SWIGLU, NB, MIN_WAVES>;
     constexpr int BLOCK = 64 * S * R;
     const int ngroups = static_cast<int>(k / 64);
     const size_t lds = static_cast<size_t>(ngroups) * sizeof(XGroup) +
@@ -477,19 +573,23 @@ hipError_t launch_split(const uint8_t *w, const uint8_t *wu, const float *x, con
     const int64_t need = (n + R - 1) / R;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
     const int grid = static_cast<int>(need < cap ? need : cap);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, w, wu, x, y, r, n, ngroups,
-                       (k / kBlockWeights) * kBlockBytes);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, w, wu, x, y, r, n, ngroups, F::row_bytes(k));
     return hipGetLastError();
 }
 
-template <bool SWIGLU>
+template <class F, bool SWIGLU>
 hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const float *x, const float *r, float *y, int64_t n,
                           int64_t k, hipStream_t stream) {
     const int64_t need = (n + 3) / 4;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
     const int grid = static_cast<int>(need < cap ? need : cap);
-    hipLaunchKernelGGL(gemv_generic_kernel<SWIGLU>, dim3(grid), dim3(256), 0, stream, w, wu, x, y, r, n, k,
-                       (k / kBlockWeights) * kBlockBytes);
+    if constexpr (std::is_same_v<F, Q8_0Format>) {
+        static_assert(!SWIGLU, "Q8_0 has no SwiGLU form");
+        hipLaunchKernelGGL(q8_0_generic_kernel, dim3(grid), dim3(256), 0, stream, w, x, y, r, n, k, F::row_bytes(k));
+    } else {
+        hipLaunchKernelGGL(gemv_generic_kernel<SWIGLU>, dim3(grid), dim3(256), 0, stream, w, wu, x, y, r, n, k,
+                           F::row_bytes(k));
+    }
     return hipGetLastError();
 }
 
@@ -534,53 +634,55 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const float *x, c
 #define Q4K_SMALL_BYTES (8 << 20)
 #endif
 
-template <int LPR, bool SWIGLU>
+template <class F, int LPR, bool SWIGLU>
 hipError_t dispatch_lpr(const GemvJob *jobs, int count, const uint8_t *wu, const float *x, int64_t k,
                         hipStream_t stream) {
     if constexpr (SWIGLU) {
-        return launch_fast<LPR, true, Q4K_SWIGLU_NB, Q4K_SWIGLU_BLOCK, Q4K_SWIGLU_MINW>(jobs, count, wu, x, k, stream);
+        return launch_fast<F, LPR, true, Q4K_SWIGLU_NB, Q4K_SWIGLU_BLOCK, Q4K_SWIGLU_MINW>(jobs, count, wu, x, k,
+                                                                                          stream);
     } else {
         int64_t bytes = 0;
-        for (int i = 0; i < count; ++i) bytes += jobs[i].n * (k / kBlockWeights) * kBlockBytes;
+        for (int i = 0; i < count; ++i) bytes += jobs[i].n * F::row_bytes(k);
         if (bytes < Q4K_SMALL_BYTES) {
-            return launch_fast<LPR, false, Q4K_SMALL_NB, Q4K_SMALL_BLOCK, Q4K_SMALL_MINW>(jobs, count, wu, x, k,
-                                                                                          stream);
+            return launch_fast<F, LPR, false, Q4K_SMALL_NB, Q4K_SMALL_BLOCK, Q4K_SMALL_MINW>(jobs, count, wu, x, k,
+                                                                                             stream);
         }
-        return launch_fast<LPR, false, Q4K_LARGE_NB, Q4K_LARGE_BLOCK, Q4K_LARGE_MINW>(jobs, count, wu, x, k, stream);
+        return launch_fast<F, LPR, false, Q4K_LARGE_NB, Q4K_LARGE_BLOCK, Q4K_LARGE_MINW>(jobs, count, wu, x, k,
+                                                                                          stream);
     }
 }
 
 // Rows wider than 4096 weights: one launch per matrix.
-template <bool SWIGLU>
+template <class F, bool SWIGLU>
 hipError_t dispatch_wide(const GemvJob &j, const uint8_t *wu, const float *x, int64_t k, hipStream_t stream) {
     const int64_t ngroups = k / 64;
     // split rows: S waves per row; two matrices' row buffers need more
     // registers, so the SwiGLU shapes keep fewer rows per workgroup
     constexpr int NB = Q4K_SPLIT_NB;
     if constexpr (SWIGLU) {
-        if (ngroups <= 128) return launch_split<2, 4, true, NB, 2>(j.w, wu, x, j.r, j.y, j.n, k, stream);
-        if (ngroups <= 192) return launch_split<3, 4, true, NB, 3>(j.w, wu, x, j.r, j.y, j.n, k, stream);
-        if (ngroups <= 256) return launch_split<4, 2, true, NB, 2>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 128) return launch_split<F, 2, 4, true, NB, 2>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 192) return launch_split<F, 3, 4, true, NB, 3>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 256) return launch_split<F, 4, 2, true, NB, 2>(j.w, wu, x, j.r, j.y, j.n, k, stream);
     } else {
-        if (ngroups <= 128) return launch_split<2, 8, false, NB, 4>(j.w, wu, x, j.r, j.y, j.n, k, stream);
-        if (ngroups <= 192) return launch_split<3, 4, false, NB, 3>(j.w, wu, x, j.r, j.y, j.n, k, stream);
-        if (ngroups <= 256) return launch_split<4, 4, false, NB, 4>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 128) return launch_split<F, 2, 8, false, NB, 4>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 192) return launch_split<F, 3, 4, false, NB, 3>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 256) return launch_split<F, 4, 4, false, NB, 4>(j.w, wu, x, j.r, j.y, j.n, k, stream);
     }
     // beyond K = 16384: the plain kernel
-    return launch_generic<SWIGLU>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+    return launch_generic<F, SWIGLU>(j.w, wu, x, j.r, j.y, j.n, k, stream);
 }
 
-template <bool SWIGLU>
+template <class F, bool SWIGLU>
 hipError_t dispatch(const GemvJob *jobs, int count, const uint8_t *wu, const float *x, int64_t k,
                     hipStream_t stream) {
     const int64_t ngroups = k / 64;
-    if (ngroups <= 4) return dispatch_lpr<4, SWIGLU>(jobs, count, wu, x, k, stream);
-    if (ngroups <= 8) return dispatch_lpr<8, SWIGLU>(jobs, count, wu, x, k, stream);
-    if (ngroups <= 16) return dispatch_lpr<16, SWIGLU>(jobs, count, wu, x, k, stream);
-    if (ngroups <= 32) return dispatch_lpr<32, SWIGLU>(jobs, count, wu, x, k, stream);
-    if (ngroups <= 64) return dispatch_lpr<64, SWIGLU>(jobs, count, wu, x, k, stream);
+    if (ngroups <= 4) return dispatch_lpr<F, 4, SWIGLU>(jobs, count, wu, x, k, stream);
+    if (ngroups <= 8) return dispatch_lpr<F, 8, SWIGLU>(jobs, count, wu, x, k, stream);
+    if (ngroups <= 16) return dispatch_lpr<F, 16, SWIGLU>(jobs, count, wu, x, k, stream);
+    if (ngroups <= 32) return dispatch_lpr<F, 32, SWIGLU>(jobs, count, wu, x, k, stream);
+    if (ngroups <= 64) return dispatch_lpr<F, 64, SWIGLU>(jobs, count, wu, x, k, stream);
     for (int i = 0; i < count; ++i) {
-        const hipError_t e = dispatch_wide<SWIGLU>(jobs[i], wu, x, k, stream);
+        const hipError_t e = dispatch_wide<F, SWIGLU>(jobs[i], wu, x, k, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -612,8 +714,21 @@ hipError_t launch_gemv_multi(const GemvJob *jobs, int count, const uint8_t *w_up
         live[nlive++] = jobs[i];
     }
     if (nlive == 0) return hipSuccess;
-    if (w_up != nullptr) return dispatch<true>(live, nlive, w_up, x, k, stream);
-    return dispatch<false>(live, nlive, nullptr, x, k, stream);
+    if (w_up != nullptr) return dispatch<Q4KFormat, true>(live, nlive, w_up, x, k, stream);
+    return dispatch<Q4KFormat, false>(live, nlive, nullptr, x, k, stream);
+}
+
+hipError_t launch_q8_0_gemv(const uint8_t *w, const float *x, const float *r, float *y, int64_t n, int64_t k,
+                            hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    if (k == 0) return r != nullptr ? launch_copy(y, r, n, stream) : launch_fill_zero(y, n, stream);
+    const GemvJob job{w, y, r, n};
+    // the streaming kernels need dword-aligned groups: an even number of
+    // blocks per row and a 4-byte aligned matrix
+    if (k % 64 != 0 || (reinterpret_cast<uintptr_t>(w) & 3) != 0) {
+        return launch_generic<Q8_0Format, false>(w, nullptr, x, r, y, n, k, stream);
+    }
+    return dispatch<Q8_0Format, false>(&job, 1, nullptr, x, k, stream);
 }
 
 }  // namespace q4k

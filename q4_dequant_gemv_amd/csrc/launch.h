@@ -32,6 +32,10 @@ hipError_t launch_gemv(const uint8_t *w, const uint8_t *w_up, const float *x, co
 hipError_t launch_gemv_multi(const GemvJob *jobs, int count, const uint8_t *w_up, const float *x, int64_t k,
                              hipStream_t stream);
 
+// Q8_0 weights (34-byte blocks of 32): y[i] = sum_c W[i,c] x[c] (+ r[i]).
+hipError_t launch_q8_0_gemv(const uint8_t *w, const float *x, const float *r, float *y, int64_t n, int64_t k,
+                            hipStream_t stream);
+
 // y[t, r] = sum_c W[r,c] x[t,c] for t < m.
 hipError_t launch_gemv_batched(const uint8_t *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
                                hipStream_t stream);

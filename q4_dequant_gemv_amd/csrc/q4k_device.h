@@ -44,6 +44,10 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, Q4K_WEIGHT_CPOL);
+}
+
 // A value the caller knows is equal in every lane, moved to scalar registers.
 __device__ __forceinline__ int64_t wave_uniform(int64_t v) {
     const uint64_t u = static_cast<uint64_t>(v);

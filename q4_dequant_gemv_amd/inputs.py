@@ -86,6 +86,38 @@ def make_q4k(n: int, k: int, config_id: int = 0, tensor_id: int = 0, seed: int =
     return assemble_blocks(qs, scales, d, dmin).reshape(n, rb)
 
 
+Q8_0_BLOCK_BYTES = 34
+Q8_0_BLOCK_WEIGHTS = 32
+
+
+def q8_0_row_bytes(k: int) -> int:
+    if k % Q8_0_BLOCK_WEIGHTS != 0:
+        raise ValueError(f"k={k} is not a multiple of {Q8_0_BLOCK_WEIGHTS}")
+    return (k // Q8_0_BLOCK_WEIGHTS) * Q8_0_BLOCK_BYTES
+
+
+def assemble_q8_0(q: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Lay fields out as 34-byte Q8_0 blocks: d (f16) | q[32] (int8).  Returns [nb, 34] u8."""
+    nb = q.shape[0]
+    out = np.empty((nb, Q8_0_BLOCK_BYTES), dtype=np.uint8)
+    out[:, 0:2] = np.ascontiguousarray(d, dtype="<f2").view(np.uint8).reshape(nb, 2)
+    out[:, 2:] = np.ascontiguousarray(q, dtype=np.int8).view(np.uint8)
+    return out
+
+
+def make_q8_0(n: int, k: int, config_id: int = 0, tensor_id: int = 0, seed: int = 0,
+              d_range=(1e-4, 1e-3)) -> np.ndarray:
+    """A random Q8_0 matrix of n rows by k columns as u8 [n, (k/32)*34]: codes
+    uniform in [-127, 127] (a symmetric quantizer's range), d uniform in
+    d_range rounded to f16.  Draw order: codes, then d."""
+    rb = q8_0_row_bytes(k)
+    nb = n * (k // Q8_0_BLOCK_WEIGHTS)
+    g = rng(config_id, tensor_id, seed)
+    q = g.integers(-127, 128, size=(nb, Q8_0_BLOCK_WEIGHTS), dtype=np.int8)
+    d = g.uniform(d_range[0], d_range[1], size=nb).astype(np.float16)
+    return assemble_q8_0(q, d).reshape(n, rb)
+
+
 def make_x(m: int, k: int, config_id: int = 0, tensor_id: int = 100, seed: int = 0) -> np.ndarray:
     """Activations f32 [m, k], standard normal."""
     g = rng(config_id, tensor_id, seed)

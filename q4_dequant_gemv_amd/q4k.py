@@ -23,8 +23,11 @@ STATUS = {0: "Q4K_OK", 1: "Q4K_ERR_INVALID_ARG", 2: "Q4K_ERR_UNSUPPORTED_SHAPE",
           4: "Q4K_ERR_LAUNCH"}
 
 # exported symbols, in the order include/q4k.h declares them
-EXPORTS = ("q4k_gemv", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_gemv_batched", "q4k_fused_swiglu",
-           "q4k_dequant", "q4k_status_string", "q4k_abi_version")
+EXPORTS = ("q4k_gemv", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_q8_0_gemv", "q4k_gemv_batched",
+           "q4k_fused_swiglu", "q4k_dequant", "q4k_status_string", "q4k_abi_version")
+
+Q8_0_BLOCK_BYTES = 34
+Q8_0_BLOCK_WEIGHTS = 32
 
 # largest number of matrices in one gemv_multi call (Q4K_MAX_MULTI)
 MAX_MULTI = 8
@@ -56,11 +59,12 @@ def lib() -> ctypes.CDLL:
         L.q4k_gemv.argtypes = [p, p, p, i64, i64, p]
         L.q4k_gemv_residual.argtypes = [p, p, p, p, i64, i64, p]
         L.q4k_gemv_multi.argtypes = [ctypes.POINTER(GemvItem), ctypes.c_int, p, i64, p]
+        L.q4k_q8_0_gemv.argtypes = [p, p, p, i64, i64, p]
         L.q4k_gemv_batched.argtypes = [p, p, p, i64, i64, i64, p]
         L.q4k_fused_swiglu.argtypes = [p, p, p, p, i64, i64, p]
         L.q4k_dequant.argtypes = [p, p, i64, i64, p]
-        for f in (L.q4k_gemv, L.q4k_gemv_residual, L.q4k_gemv_multi, L.q4k_gemv_batched, L.q4k_fused_swiglu,
-                  L.q4k_dequant):
+        for f in (L.q4k_gemv, L.q4k_gemv_residual, L.q4k_gemv_multi, L.q4k_q8_0_gemv, L.q4k_gemv_batched,
+                  L.q4k_fused_swiglu, L.q4k_dequant):
             f.restype = st
         L.q4k_status_string.argtypes = [st]
         L.q4k_status_string.restype = ctypes.c_char_p
@@ -158,6 +162,30 @@ def gemv_multi(ws, x, ys=None, ns=None, stream=None):
         items[i].n = n
     _check(lib().q4k_gemv_multi(items, len(ws), _dev(x, "x", torch.float32), k, _stream(stream)), "q4k_gemv_multi")
     return ys
+
+
+def q8_0_rows_of(w, k: int) -> int:
+    if k % Q8_0_BLOCK_WEIGHTS != 0:
+        raise ValueError(f"k={k} is not a multiple of {Q8_0_BLOCK_WEIGHTS}")
+    rb = (k // Q8_0_BLOCK_WEIGHTS) * Q8_0_BLOCK_BYTES
+    if rb == 0:
+        raise ValueError("k must be positive to infer the row count; pass n")
+    if w.numel() % rb != 0:
+        raise ValueError(f"weight tensor of {w.numel()} bytes is not a whole number of {rb}-byte rows")
+    return w.numel() // rb
+
+
+def q8_0_gemv(w, x, y=None, n: int | None = None, stream=None):
+    """y[r] = sum_c W[r,c] x[c] for a Q8_0 matrix ``w`` (uint8) and f32 ``x`` [k]."""
+    import torch
+
+    k = x.numel()
+    n = q8_0_rows_of(w, k) if n is None else n
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=x.device)
+    _check(lib().q4k_q8_0_gemv(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float32), _dev(y, "y", torch.float32),
+                               n, k, _stream(stream)), "q4k_q8_0_gemv")
+    return y
 
 
 def gemv_batched(w, x, y=None, n: int | None = None, stream=None):

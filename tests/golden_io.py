@@ -40,3 +40,22 @@ def single_block() -> dict:
         "y_alternating": float(kv["y_alternating"]),
         "y_index": float(kv["y_index"]),
     }
+
+
+def q8_0_two_blocks() -> dict:
+    kv = read_kv("q8_0_two_blocks.txt")
+    d0 = int(kv["d0_bits"], 16)
+    d1 = int(kv["d1_bits"], 16)
+    q0 = [-128] + [e - 16 for e in range(1, 31)] + [127]
+    q1 = [(e % 4) - 1 for e in range(32)]
+    row = (bytes([d0 & 0xFF, d0 >> 8]) + bytes(v & 0xFF for v in q0)
+           + bytes([d1 & 0xFF, d1 >> 8]) + bytes(v & 0xFF for v in q1))
+    assert len(row) == 68
+    return {
+        "row": row,
+        "weights": {int(a): float(b) for a, b in (p.split(":") for p in kv["weights"].split())},
+        "y_ones": float(kv["y_ones"]),
+        "a_ones": float(kv["a_ones"]),
+        "y_alternating": float(kv["y_alternating"]),
+        "y_index": float(kv["y_index"]),
+    }

@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
-        ["q4k_gemv", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_gemv_batched", "q4k_fused_swiglu", "q4k_dequant",
-         "q4k_status_string", "q4k_abi_version"])
+        ["q4k_gemv", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_q8_0_gemv", "q4k_gemv_batched", "q4k_fused_swiglu",
+         "q4k_dequant", "q4k_status_string", "q4k_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -55,7 +55,7 @@ def test_only_the_abi_is_exported():
 
 
 def test_status_strings(L):
-    assert L.q4k_abi_version() == 101
+    assert L.q4k_abi_version() == 102
     for s in range(5):
         assert len(L.q4k_status_string(s)) > 0
     assert L.q4k_status_string(99) == b"unknown status"
@@ -105,6 +105,27 @@ def test_residual_validation(L, args, status):
     w, x, r, y, n, k = args
     assert L.q4k_gemv_residual(ctypes.c_void_p(w), ctypes.c_void_p(x), ctypes.c_void_p(r), ctypes.c_void_p(y), n, k,
                                None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((W, X, Y, 16, 48), SHAPE),                   # k % 32 != 0
+    ((W, X, Y, -1, 64), INVALID),
+    ((W, X, Y, 16, -64), INVALID),
+    ((0, X, Y, 16, 64), INVALID),
+    ((W, 0, Y, 16, 64), INVALID),
+    ((W, X, 0, 16, 64), INVALID),
+    ((W + 1, X, Y, 16, 64), MISALIGNED),          # w must be 2-B aligned
+    ((W, X + 2, Y, 16, 64), MISALIGNED),
+    ((W, X, Y + 2, 16, 64), MISALIGNED),
+    ((W, X, W + 16 * 68 - 4, 16, 64), INVALID),   # y overlaps the last bytes of w
+    ((W, X, X + 252, 16, 64), INVALID),           # y overlaps x
+    ((W, X, Y, 1 << 50, 1 << 20), INVALID),
+    ((W, X, Y, 0, 64), OK),
+    ((0, 0, 0, 0, 32), OK),
+])
+def test_q8_0_validation(L, args, status):
+    w, x, y, n, k = args
+    assert L.q4k_q8_0_gemv(ctypes.c_void_p(w), ctypes.c_void_p(x), ctypes.c_void_p(y), n, k, None) == status
 
 
 def _items(*triples):

@@ -1,8 +1,10 @@
 """Pins for the CPU oracle (runs without a GPU).
 
 The oracle is checked against things other than itself:
-  * a super-block worked by hand (tests/golden/q4k_single_block.txt),
-  * an independent bit-position decoder (tests/independent_decoder.py),
+  * a super-block worked by hand (tests/golden/q4k_single_block.txt) and two
+    Q8_0 blocks worked by hand (tests/golden/q8_0_two_blocks.txt),
+  * an independent bit-position decoder (tests/independent_decoder.py), and
+    numpy's binary16 / int8 views for Q8_0,
   * IEEE binary16 decoding by numpy for all 65,536 patterns,
   * the inverse of the six-bit scale packing, exhaustively,
   * closed forms and invariants: zero codes give -dmin*m, linearity in x,
@@ -24,7 +26,7 @@ import pytest
 import scipy.special
 
 import oracle as oracle_pkg
-from golden_io import single_block
+from golden_io import q8_0_two_blocks, single_block
 from independent_decoder import codes as ind_codes
 from independent_decoder import dequant as ind_dequant
 from independent_decoder import pack_scales
@@ -205,8 +207,60 @@ def check_residual(orc):
     np.testing.assert_array_equal(outs[1][0], (q2 @ x).astype(np.float64))
 
 
+# ------------------------------------------------------------------- Q8_0
+def _q8_numpy_dequant(blocks):
+    # independent of the oracle: numpy's binary16 and int8 views of the bytes
+    d = blocks[:, 0:2].copy().view("<f2").astype(np.float32)
+    q = blocks[:, 2:].copy().view(np.int8).astype(np.float32)
+    return d * q
+
+
+def check_q8_golden(orc):
+    gb = q8_0_two_blocks()
+    row = np.frombuffer(gb["row"], np.uint8)
+    w = orc.q8_0_dequant(row, 64)[0]
+    for k, v in gb["weights"].items():
+        assert w[k] == np.float32(v), f"q8 w[{k}] = {w[k]}, hand value {v}"
+    y, a = orc.q8_0_gemv(row, np.ones(64, np.float32))
+    assert y[0] == gb["y_ones"] and a[0] == gb["a_ones"]
+    alt = np.where(np.arange(64) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    assert orc.q8_0_gemv(row, alt)[0][0] == gb["y_alternating"]
+    assert orc.q8_0_gemv(row, np.arange(64, dtype=np.float32))[0][0] == gb["y_index"]
+
+
+def check_q8_independent_decoder(orc):
+    g = np.random.default_rng(31)
+    nb = 20000
+    q = g.integers(-128, 128, size=(nb, 32), dtype=np.int8)  # -128 included
+    bits = g.integers(0, 0x7C00, size=nb, dtype=np.uint16) | (g.integers(0, 2, size=nb, dtype=np.uint16) << 15)
+    blocks = inputs.assemble_q8_0(q, bits.view(np.float16))
+    got = orc.q8_0_dequant(blocks.reshape(-1), 32)
+    np.testing.assert_array_equal(got.view(np.uint32), _q8_numpy_dequant(blocks).view(np.uint32))
+    # dense f64 matvec over rows of 32 blocks (K = 1024)
+    w = inputs.make_q8_0(48, 1024, config_id=0, tensor_id=32)
+    x = g.standard_normal(1024).astype(np.float32)
+    wd = _q8_numpy_dequant(w.reshape(-1, 34)).reshape(48, 1024).astype(np.float64)
+    y, a = orc.q8_0_gemv(w, x)
+    np.testing.assert_allclose(y, wd @ x.astype(np.float64), rtol=0, atol=1e-12 * np.abs(wd * x).sum(axis=1).max())
+    np.testing.assert_allclose(a, np.abs(wd * x.astype(np.float64)).sum(axis=1), rtol=1e-13)
+
+
+def check_q8_integer_matrix(orc):
+    # d = 1: the weights are the codes; y equals an int64 matmul exactly
+    n, k = 40, 1024
+    g = np.random.default_rng(33)
+    q = g.integers(-128, 128, size=(n * k // 32, 32), dtype=np.int8)
+    w = inputs.assemble_q8_0(q, np.ones(n * k // 32, np.float16)).reshape(n, -1)
+    x = g.integers(-60, 61, k)
+    y, a = orc.q8_0_gemv(w, x.astype(np.float32))
+    qi = q.astype(np.int64).reshape(n, k)
+    np.testing.assert_array_equal(y, (qi @ x).astype(np.float64))
+    np.testing.assert_array_equal(a, np.abs(qi * x[None, :]).sum(axis=1).astype(np.float64))
+
+
 ALL_PINS = [check_golden_block, check_independent_decoder, check_zero_codes, check_linearity,
-            check_integer_matrix, check_closed_form, check_one_hot, check_residual]
+            check_integer_matrix, check_closed_form, check_one_hot, check_residual,
+            check_q8_golden, check_q8_independent_decoder, check_q8_integer_matrix]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -296,6 +350,13 @@ MUTATIONS = {
     "residual_dropped": ("y[r - r0] = dot + (double)res[r];", "y[r - r0] = dot;"),
     "residual_subtracted": ("y[r - r0] = dot + (double)res[r];", "y[r - r0] = dot - (double)res[r];"),
     "residual_row_shifted": ("y[r - r0] = dot + (double)res[r];", "y[r - r0] = dot + (double)res[r1 - 1 - r];"),
+    "q8_codes_unsigned": ("const int q = (int)(int8_t)blk[2 + e];", "const int q = (int)blk[2 + e];"),
+    "q8_scale_bytes_swapped": ("(uint16_t)((blk[1] << 8) | blk[0])", "(uint16_t)((blk[0] << 8) | blk[1])"),
+    "q8_codes_off_by_one": ("(int8_t)blk[2 + e]", "(int8_t)blk[1 + e]"),
+    "q8_block_stride": ("q8_0_oracle_dequant_block(w + r * row_bytes + b * Q8_0_BLOCK_BYTES, wblk);",
+                        "q8_0_oracle_dequant_block(w + r * row_bytes + b * Q8_0_BLOCK_WEIGHTS, wblk);"),
+    "q8_x_index": ("x[b * Q8_0_BLOCK_WEIGHTS + e]", "x[e * nb + b]"),
+    "q8_abs_signed": ("mag += p < 0.0 ? -p : p;", "mag += p;"),
 }
 
 
@@ -329,7 +390,8 @@ def test_pins_catch_planted_mistakes(oracle_mod, name, tmp_path):
     real = oracle_mod._load()
     for fn in ("q4k_oracle_f16_to_f32", "q4k_oracle_scale_min", "q4k_oracle_dequant_block",
                "q4k_oracle_dequant_rows", "q4k_gemv_oracle_into", "q4k_gemv_batched_oracle_into",
-               "q4k_fused_swiglu_oracle_into", "q4k_gemv_residual_oracle_into"):
+               "q4k_fused_swiglu_oracle_into", "q4k_gemv_residual_oracle_into", "q8_0_oracle_dequant_block",
+               "q8_0_oracle_dequant_rows", "q8_0_gemv_oracle_into"):
         getattr(lib, fn).argtypes = getattr(real, fn).argtypes
         getattr(lib, fn).restype = getattr(real, fn).restype
     assert _run_pins_with(lib) > 0, f"no pin caught the planted mistake {name}"
