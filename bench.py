@@ -214,9 +214,10 @@ def main():
 
     blocks = decode_blocks(q4k, inputs, torch, dev, stream, args.steps, args.warmup)
     q8 = q8_0_kernels(q4k, inputs, torch, dev, stream, args.steps, args.warmup)
+    f16io = f16_variants(q4k, inputs, torch, dev, stream, args.steps, args.warmup, not args.no_batched)
 
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s; per kernel {kernels}; "
-        f"batched {batched}; decode blocks {blocks}; q8_0 {q8}; host wall {wall:.3f}s")
+        f"batched {batched}; decode blocks {blocks}; q8_0 {q8}; f16 i/o {f16io}; host wall {wall:.3f}s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -265,6 +266,7 @@ def main():
             "batched_9b_ffn": batched,
             "decode_blocks": blocks,
             "q8_0_9b": q8,
+            "f16_io_9b": f16io,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -356,6 +358,36 @@ def q8_0_kernels(q4k, inputs, torch, dev, stream, steps, warmup):
         abytes = w0.nbytes + 4 * k + 4 * n
         out[nm] = {"weight_bytes": w0.nbytes, "mean_us": round(t * 1e6, 3), "GB/s": round(abytes / t / 1e9, 1),
                    "frac_hbm_peak": round(abytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del ws
+    return out
+
+
+def f16_variants(q4k, inputs, torch, dev, stream, steps, warmup, batched):
+    """f16 activations and outputs (q4k_gemv_dt, q4k_gemv_batched_dt) on the
+    9B lm_head and gate, beside the f32 calls; weights rotated over >= 512 MiB."""
+    out = {}
+    n, k = inputs.SHAPES["lm_head_9b"]
+    w = torch.from_numpy(inputs.make_q4k(n, k, config_id=61, tensor_id=0).reshape(-1)).to(dev)
+    x = torch.from_numpy(inputs.make_x(1, k, config_id=61)[0]).to(dev)
+    xh = x.half()
+    y = torch.empty(n, dtype=torch.float16, device=dev)
+    t = _time_launches(lambda i: q4k.gemv_dt(w, xh, y=y, stream=stream), torch, stream, steps, warmup)
+    out["lm_head_9b f16->f16"] = {"mean_us": round(t * 1e6, 3),
+                                  "GB/s": round((w.numel() + 2 * k + 2 * n) / t / 1e9, 1)}
+    del w
+    if batched:
+        n, k = inputs.SHAPES["gate_9b"]
+        w0 = torch.from_numpy(inputs.make_q4k(n, k, config_id=61, tensor_id=1).reshape(-1)).to(dev)
+        copies = max(1, -(-(512 << 20) // w0.numel()))
+        ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+        for m in (16, 64):
+            xs = torch.from_numpy(inputs.make_x(m, k, config_id=61, tensor_id=m)).to(dev)
+            for label, xin, yd in (("f32->f32", xs, torch.float32), ("f16->f16", xs.half(), torch.float16)):
+                yb = torch.empty((m, n), dtype=yd, device=dev)
+                t = _time_launches(lambda i: q4k.gemv_batched_dt(ws[i % copies], xin, y=yb, stream=stream), torch,
+                                   stream, min(steps, 50), min(warmup, 5))
+                out[f"gate_9b m={m} {label}"] = {"mean_us": round(t * 1e6, 2),
+                                                 "TFLOP/s": round(2.0 * m * n * k / t / 1e12, 2)}
         del ws
     return out
 

@@ -68,6 +68,12 @@ typedef enum {
     Q4K_ERR_LAUNCH = 4             /* the HIP runtime refused a launch */
 } q4k_status;
 
+/* Element type of activations and outputs in the *_dt calls. */
+typedef enum {
+    Q4K_F32 = 0, /* IEEE binary32 */
+    Q4K_F16 = 1  /* IEEE binary16: inputs widened exactly, outputs rounded to nearest even */
+} q4k_dtype;
+
 /* Bytes of one Q4_K super-block and weights per super-block. */
 #define Q4K_BLOCK_BYTES 144
 #define Q4K_BLOCK_WEIGHTS 256
@@ -86,6 +92,21 @@ typedef enum {
  *   y : f32 [n], written: y[r] = sum_c W[r,c] x[c]
  */
 Q4K_API q4k_status q4k_gemv(const void *w, const float *x, float *y, int64_t n, int64_t k, void *stream);
+
+/*
+ * Batch-1 GEMV with f16 or f32 activations and outputs ("@simulatte/doppler
+ * 0.1.7 -> 0.1.8", matmul-selection.js: selectQ4KFusedVariant chooses the
+ * fused Q4K kernel by aDtype and wantF16Output, and an f16 activation may
+ * still produce an f32 output).  Computes what q4k_gemv computes on the
+ * activations widened to f32; an f16 output is that f32 result rounded to
+ * nearest even (beyond the f16 range: +-inf).
+ *   x : [k] of x_dtype, aligned to its element size
+ *   y : [n] of y_dtype, aligned to its element size
+ * Other arguments, errors and aliasing rules as q4k_gemv; an unknown dtype is
+ * Q4K_ERR_INVALID_ARG.
+ */
+Q4K_API q4k_status q4k_gemv_dt(const void *w, const void *x, q4k_dtype x_dtype, void *y, q4k_dtype y_dtype,
+                               int64_t n, int64_t k, void *stream);
 
 /*
  * Batch-1 GEMV with a residual added in the same pass: y = W x + r (the
@@ -151,6 +172,20 @@ Q4K_API q4k_status q4k_q8_0_gemv(const void *w, const float *x, float *y, int64_
  */
 Q4K_API q4k_status q4k_gemv_batched(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
                             void *stream);
+
+/*
+ * q4k_gemv_batched with f16 or f32 activations and outputs (x [m, k] of
+ * x_dtype, y [m, n] of y_dtype, each aligned to its element size): the
+ * skinny-GEMM side of selectQ4KFusedVariant's aDtype / wantF16Output choice
+ * ("@simulatte/doppler 0.1.7 -> 0.1.8", matmul-selection.js).  Computes what
+ * q4k_gemv_batched computes on the activations widened to f32; f16 outputs
+ * are rounded to nearest even.  The scratch is that of q4k_gemv_batched,
+ * plus 4*m*n bytes for an f16 output when K is split across workgroups (the
+ * partial sums are added in f32 first).  Errors and aliasing as
+ * q4k_gemv_batched; an unknown dtype is Q4K_ERR_INVALID_ARG.
+ */
+Q4K_API q4k_status q4k_gemv_batched_dt(const void *w, const void *x, q4k_dtype x_dtype, void *y, q4k_dtype y_dtype,
+                                       int64_t m, int64_t n, int64_t k, void *stream);
 
 /*
  * Fused gate/up GEMV with SwiGLU ("qualia_core_db/inference/cuda_lane/mod.rs",

@@ -26,6 +26,13 @@ __global__ void copy_kernel(float *y, const float *src, int64_t count) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride) y[i] = src[i];
 }
 
+__global__ void fill_zero_f16_kernel(_Float16 *y, int64_t count) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride) {
+        y[i] = static_cast<_Float16>(0.0f);
+    }
+}
+
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // [a, a+na) and [b, b+nb) overlap (byte ranges, both non-empty).
@@ -73,6 +80,14 @@ hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream) {
     return hipGetLastError();
 }
 
+hipError_t launch_fill_zero_f16(_Float16 *y, int64_t count, hipStream_t stream) {
+    if (count == 0) return hipSuccess;
+    const int64_t need = (count + 255) / 256;
+    const int grid = static_cast<int>(need < 4096 ? need : 4096);
+    hipLaunchKernelGGL(fill_zero_f16_kernel, dim3(grid), dim3(256), 0, stream, y, count);
+    return hipGetLastError();
+}
+
 hipError_t launch_copy(float *y, const float *src, int64_t count, hipStream_t stream) {
     if (count == 0 || y == src) return hipSuccess;
     const int64_t need = (count + 255) / 256;
@@ -101,6 +116,24 @@ q4k_status q4k_gemv(const void *w, const float *x, float *y, int64_t n, int64_t 
     if (overlap(y, yb, w, wb) || overlap(y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
     return from_hip(q4k::launch_gemv(static_cast<const uint8_t *>(w), nullptr, x, nullptr, y, n, k,
                                      static_cast<hipStream_t>(stream)));
+}
+
+q4k_status q4k_gemv_dt(const void *w, const void *x, q4k_dtype x_dtype, void *y, q4k_dtype y_dtype, int64_t n,
+                       int64_t k, void *stream) {
+    if ((x_dtype != Q4K_F32 && x_dtype != Q4K_F16) || (y_dtype != Q4K_F32 && y_dtype != Q4K_F16)) {
+        return Q4K_ERR_INVALID_ARG;
+    }
+    uint64_t wb = 0;
+    const q4k_status s = check_shape(n, k, &wb);
+    if (s != Q4K_OK) return s;
+    if (n == 0) return Q4K_OK;
+    if (y == nullptr || (k > 0 && (w == nullptr || x == nullptr))) return Q4K_ERR_INVALID_ARG;
+    const uint64_t xe = x_dtype == Q4K_F16 ? 2 : 4, ye = y_dtype == Q4K_F16 ? 2 : 4;
+    if (!aligned(w, 16) || !aligned(x, xe) || !aligned(y, ye)) return Q4K_ERR_MISALIGNED;
+    const uint64_t yb = static_cast<uint64_t>(n) * ye, xb = static_cast<uint64_t>(k) * xe;
+    if (overlap(y, yb, w, wb) || overlap(y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
+    return from_hip(q4k::launch_gemv_dt(static_cast<const uint8_t *>(w), x, x_dtype == Q4K_F16, y,
+                                        y_dtype == Q4K_F16, n, k, static_cast<hipStream_t>(stream)));
 }
 
 q4k_status q4k_gemv_residual(const void *w, const float *x, const float *r, float *y, int64_t n, int64_t k,
@@ -185,6 +218,26 @@ q4k_status q4k_gemv_batched(const void *w, const float *x, float *y, int64_t m, 
                                              static_cast<hipStream_t>(stream)));
 }
 
+q4k_status q4k_gemv_batched_dt(const void *w, const void *x, q4k_dtype x_dtype, void *y, q4k_dtype y_dtype,
+                               int64_t m, int64_t n, int64_t k, void *stream) {
+    if ((x_dtype != Q4K_F32 && x_dtype != Q4K_F16) || (y_dtype != Q4K_F32 && y_dtype != Q4K_F16)) {
+        return Q4K_ERR_INVALID_ARG;
+    }
+    uint64_t wb = 0;
+    const q4k_status s = check_shape(n, k, &wb);
+    if (s != Q4K_OK) return s;
+    if (m < 0) return Q4K_ERR_INVALID_ARG;
+    if (m > 0 && (n > q4k::kMaxElems / m || (k > 0 && m > q4k::kMaxElems / k))) return Q4K_ERR_INVALID_ARG;
+    if (n == 0 || m == 0) return Q4K_OK;
+    if (y == nullptr || (k > 0 && (w == nullptr || x == nullptr))) return Q4K_ERR_INVALID_ARG;
+    const uint64_t xe = x_dtype == Q4K_F16 ? 2 : 4, ye = y_dtype == Q4K_F16 ? 2 : 4;
+    if (!aligned(w, 16) || !aligned(x, xe) || !aligned(y, ye)) return Q4K_ERR_MISALIGNED;
+    const uint64_t yb = static_cast<uint64_t>(m) * n * ye, xb = static_cast<uint64_t>(m) * k * xe;
+    if (overlap(y, yb, w, wb) || overlap(y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
+    return from_hip(q4k::launch_gemv_batched_dt(static_cast<const uint8_t *>(w), x, x_dtype == Q4K_F16, y,
+                                                y_dtype == Q4K_F16, m, n, k, static_cast<hipStream_t>(stream)));
+}
+
 q4k_status q4k_fused_swiglu(const void *w_gate, const void *w_up, const float *x, float *h, int64_t n, int64_t k,
                             void *stream) {
     uint64_t wb = 0;
@@ -222,6 +275,6 @@ const char *q4k_status_string(q4k_status s) {
     return "unknown status";
 }
 
-int q4k_abi_version(void) { return 102; }
+int q4k_abi_version(void) { return 104; }
 
 }  // extern "C"

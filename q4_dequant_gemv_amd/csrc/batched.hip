@@ -35,6 +35,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "launch.h"
 #include "q4k_device.h"
 
@@ -94,8 +96,9 @@ __device__ __forceinline__ uint32_t pair_operand(uint32_t pair, uint32_t sc2) {
 // One half-wave per (stage, token) of the padded token range 16*mt; each lane
 // converts four activations.  Tokens >= m are written as zeros.  With
 // zero_y the same kernel zero-fills y, which the matrix-core kernel then
-// accumulates into.
-__global__ __launch_bounds__(256) void x_prep_kernel(const float *x, uint8_t *__restrict__ xc, float *__restrict__ y,
+// accumulates into.  XT: float or _Float16 activations (widened exactly).
+template <typename XT>
+__global__ __launch_bounds__(256) void x_prep_kernel(const XT *x, uint8_t *__restrict__ xc, float *__restrict__ y,
                                                       int m, int mt, int64_t k, int64_t ny) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     for (int64_t i = gid; i < ny; i += static_cast<int64_t>(gridDim.x) * 256) y[i] = 0.0f;
@@ -110,12 +113,12 @@ __global__ __launch_bounds__(256) void x_prep_kernel(const float *x, uint8_t *__
     const int64_t st = pair / tpad;
     const int tok = static_cast<int>(pair % tpad);
     const bool real = tok < m;
-    const float *px = x + static_cast<int64_t>(real ? tok : 0) * k + st * kStageK + 4 * c;
+    const XT *px = x + static_cast<int64_t>(real ? tok : 0) * k + st * kStageK + 4 * c;
     float v[4];
     float amax = 0.0f;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        v[b] = real ? px[b] : 0.0f;
+        v[b] = real ? static_cast<float>(px[b]) : 0.0f;
         float a = fabsf(v[b]);
         a = (a <= FLT_MAX) ? a : INFINITY;  // NaN counts as non-finite
         amax = fmaxf(amax, a);
@@ -202,10 +205,11 @@ struct StageGeom {
     static constexpr int kStageLds = kRows * kRowLds;
 };
 
-template <int NT, int MT, int S>
+// YT: float or _Float16 output (f16 only with ksplit == 1: the atomics add f32).
+template <int NT, int MT, int S, typename YT>
 __global__ __launch_bounds__(128 * S, 1) void batched_mfma_kernel(const uint8_t *__restrict__ w,
                                                                   const uint8_t *__restrict__ xc,
-                                                                  float *__restrict__ y, int m, int64_t n,
+                                                                  YT *__restrict__ y, int m, int64_t n,
                                                                   int64_t k, int64_t row_bytes, int ksplit,
                                                                   int64_t xc_bytes) {
     using G = StageGeom<NT, S>;
@@ -420,10 +424,22 @@ __global__ __launch_bounds__(128 * S, 1) void batched_mfma_kernel(const uint8_t 
         for (int r = 0; r < 4; ++r) {
             const int tok = 16 * p + 4 * (ln >> 4) + r;
             if (tok >= m) continue;
-            float *dst = y + static_cast<int64_t>(tok) * n + row;
-            if (ksplit == 1) *dst = sum[r];
-            else unsafeAtomicAdd(dst, sum[r]);
+            YT *dst = y + static_cast<int64_t>(tok) * n + row;
+            if constexpr (std::is_same_v<YT, float>) {
+                if (ksplit == 1) *dst = sum[r];
+                else unsafeAtomicAdd(dst, sum[r]);
+            } else {
+                *dst = static_cast<YT>(sum[r]);
+            }
         }
+    }
+}
+
+__global__ __launch_bounds__(256) void f32_to_f16_kernel(const float *__restrict__ src, _Float16 *__restrict__ dst,
+                                                          int64_t count) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < count; i += stride) {
+        dst[i] = static_cast<_Float16>(src[i]);
     }
 }
 
@@ -435,26 +451,48 @@ namespace {
 #define Q4K_BATCH_STAGE_SB 4
 #endif
 
-template <int NT, int MT>
-hipError_t launch_mfma(const uint8_t *w, const float *x, float *y, int m, int64_t n, int64_t k, int ksplit,
+// x: [m, k] of XT; y: [m, n] of YT.  An f16 output with K split across
+// workgroups is accumulated in f32 in the call's scratch, then converted.
+template <int NT, int MT, typename XT, typename YT>
+hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, int ksplit,
                        hipStream_t stream) {
     constexpr int S = Q4K_BATCH_STAGE_SB;
     const int64_t nst = k / kStageK;
     const int64_t bytes = nst * MT * kTileStageBytes;
-    uint8_t *xc = nullptr;
-    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&xc), static_cast<size_t>(bytes), stream);
-    if (e != hipSuccess) return e;
-    const int64_t prep_threads = nst * 16 * MT * 32;
+    constexpr bool kF32Out = std::is_same_v<YT, float>;
+    const bool staged = !kF32Out && ksplit > 1;
     const int64_t ny = ksplit > 1 ? static_cast<int64_t>(m) * n : 0;
+    uint8_t *xc = nullptr;
+    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&xc),
+                                  static_cast<size_t>(bytes + (staged ? ny * 4 : 0)), stream);
+    if (e != hipSuccess) return e;
+    float *acc_y = nullptr;  // where the matrix-core kernel accumulates with atomics
+    if constexpr (kF32Out) acc_y = y;
+    if (staged) acc_y = reinterpret_cast<float *>(xc + bytes);
+    const int64_t prep_threads = nst * 16 * MT * 32;
     const int64_t prep_blocks = (prep_threads + 255) / 256;
-    hipLaunchKernelGGL(x_prep_kernel, dim3(static_cast<unsigned>(prep_blocks)), dim3(256), 0, stream, x, xc, y, m, MT,
-                       k, ny);
+    hipLaunchKernelGGL(x_prep_kernel<XT>, dim3(static_cast<unsigned>(prep_blocks)), dim3(256), 0, stream, x, xc,
+                       acc_y, m, MT, k, ny);
     e = hipGetLastError();
     if (e == hipSuccess) {
         const int64_t nrb = (n + 16 * NT - 1) / (16 * NT);
-        hipLaunchKernelGGL((batched_mfma_kernel<NT, MT, S>), dim3(static_cast<unsigned>(nrb * ksplit)), dim3(128 * S), 0,
-                           stream, w, xc, y, m, n, k, (k / kBlockWeights) * kBlockBytes, ksplit, bytes);
-        e = hipGetLastError();
+        const dim3 grid(static_cast<unsigned>(nrb * ksplit));
+        const int64_t rb = (k / kBlockWeights) * kBlockBytes;
+        if (staged) {
+            hipLaunchKernelGGL((batched_mfma_kernel<NT, MT, S, float>), grid, dim3(128 * S), 0, stream, w, xc, acc_y,
+                               m, n, k, rb, ksplit, bytes);
+            e = hipGetLastError();
+            if (e == hipSuccess) {
+                const int64_t need = (ny + 255) / 256;
+                hipLaunchKernelGGL(f32_to_f16_kernel, dim3(static_cast<unsigned>(need < 4096 ? need : 4096)),
+                                   dim3(256), 0, stream, acc_y, reinterpret_cast<_Float16 *>(y), ny);
+                e = hipGetLastError();
+            }
+        } else {
+            hipLaunchKernelGGL((batched_mfma_kernel<NT, MT, S, YT>), grid, dim3(128 * S), 0, stream, w, xc, y, m, n, k,
+                               rb, ksplit, bytes);
+            e = hipGetLastError();
+        }
     }
     const hipError_t f = hipFreeAsync(xc, stream);
     return e != hipSuccess ? e : f;
@@ -470,8 +508,8 @@ hipError_t launch_mfma(const uint8_t *w, const float *x, float *y, int m, int64_
 #ifndef Q4K_BATCH_NT_CAP
 #define Q4K_BATCH_NT_CAP 4
 #endif
-template <int MT>
-hipError_t dispatch_mt(const uint8_t *w, const float *x, float *y, int m, int64_t n, int64_t k, hipStream_t stream) {
+template <int MT, typename XT, typename YT>
+hipError_t dispatch_mt(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, hipStream_t stream) {
     constexpr int kNtMax0 = MT == 1 ? 4 : (MT <= 3 ? 2 : 1);
     constexpr int kNtMax = kNtMax0 < Q4K_BATCH_NT_CAP ? kNtMax0 : Q4K_BATCH_NT_CAP;
     const int64_t cus = device_cu_count();
@@ -479,31 +517,28 @@ hipError_t dispatch_mt(const uint8_t *w, const float *x, float *y, int m, int64_
     const int64_t per = n / (16 * cus);  // row tiles per CU with one row block each
     if (per >= 1 || nsb < 2) {
         const int64_t nt = per < 1 ? 1 : (per > kNtMax ? kNtMax : per);
-        if (nt >= 4) return launch_mfma<kNtMax, MT>(w, x, y, m, n, k, 1, stream);
-        if (nt == 3) return launch_mfma<(kNtMax < 3 ? kNtMax : 3), MT>(w, x, y, m, n, k, 1, stream);
-        if (nt == 2) return launch_mfma<(kNtMax < 2 ? kNtMax : 2), MT>(w, x, y, m, n, k, 1, stream);
-        return launch_mfma<1, MT>(w, x, y, m, n, k, 1, stream);
+        if (nt >= 4) return launch_mfma<kNtMax, MT, XT, YT>(w, x, y, m, n, k, 1, stream);
+        if (nt == 3) return launch_mfma<(kNtMax < 3 ? kNtMax : 3), MT, XT, YT>(w, x, y, m, n, k, 1, stream);
+        if (nt == 2) return launch_mfma<(kNtMax < 2 ? kNtMax : 2), MT, XT, YT>(w, x, y, m, n, k, 1, stream);
+        return launch_mfma<1, MT, XT, YT>(w, x, y, m, n, k, 1, stream);
     }
     // fewer than 16 rows per CU: the largest row blocks, K split to fill the CUs
     const int64_t nrb = (n + 16 * kNtMax - 1) / (16 * kNtMax);
     int64_t ksplit = (cus + nrb - 1) / nrb;
     if (ksplit > nsb) ksplit = nsb;
-    return launch_mfma<kNtMax, MT>(w, x, y, m, n, k, static_cast<int>(ksplit), stream);
+    return launch_mfma<kNtMax, MT, XT, YT>(w, x, y, m, n, k, static_cast<int>(ksplit), stream);
 }
 
 }  // namespace
 
-hipError_t launch_gemv_batched(const uint8_t *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
-                               hipStream_t stream) {
-    if (m == 0 || n == 0) return hipSuccess;
-    if (k == 0) return launch_fill_zero(y, m * n, stream);
-    if (m == 1) return launch_gemv(w, nullptr, x, nullptr, y, n, k, stream);
+template <typename XT, typename YT>
+hipError_t batched_slices(const uint8_t *w, const XT *x, YT *y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
     hipError_t e = hipSuccess;
     // up to 64 tokens per launch; the weights are re-read per 64-token slice
     for (int64_t t0 = 0; t0 < m; t0 += 64) {
         const int mt = static_cast<int>(m - t0 < 64 ? m - t0 : 64);
-        const float *xs = x + t0 * k;
-        float *ys = y + t0 * n;
+        const XT *xs = x + t0 * k;
+        YT *ys = y + t0 * n;
         if (mt <= 16) e = dispatch_mt<1>(w, xs, ys, mt, n, k, stream);
         else if (mt <= 32) e = dispatch_mt<2>(w, xs, ys, mt, n, k, stream);
         else if (mt <= 48) e = dispatch_mt<3>(w, xs, ys, mt, n, k, stream);
@@ -511,6 +546,26 @@ hipError_t launch_gemv_batched(const uint8_t *w, const float *x, float *y, int64
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_gemv_batched_dt(const uint8_t *w, const void *x, bool x_f16, void *y, bool y_f16, int64_t m,
+                                  int64_t n, int64_t k, hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    if (k == 0) {
+        return y_f16 ? launch_fill_zero_f16(static_cast<_Float16 *>(y), m * n, stream)
+                     : launch_fill_zero(static_cast<float *>(y), m * n, stream);
+    }
+    if (m == 1) return launch_gemv_dt(w, x, x_f16, y, y_f16, n, k, stream);
+    using H = _Float16;
+    if (x_f16 && y_f16) return batched_slices(w, static_cast<const H *>(x), static_cast<H *>(y), m, n, k, stream);
+    if (x_f16) return batched_slices(w, static_cast<const H *>(x), static_cast<float *>(y), m, n, k, stream);
+    if (y_f16) return batched_slices(w, static_cast<const float *>(x), static_cast<H *>(y), m, n, k, stream);
+    return batched_slices(w, static_cast<const float *>(x), static_cast<float *>(y), m, n, k, stream);
+}
+
+hipError_t launch_gemv_batched(const uint8_t *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
+                               hipStream_t stream) {
+    return launch_gemv_batched_dt(w, x, false, y, false, m, n, k, stream);
 }
 
 }  // namespace q4k

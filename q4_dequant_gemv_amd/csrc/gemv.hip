@@ -192,7 +192,7 @@ __device__ __forceinline__ void lane_dot(const RowLoads<F, NMAT> &b, const typen
 constexpr int kMaxMats = 8;
 struct MatTable {
     const uint8_t *w[kMaxMats];
-    float *y[kMaxMats];
+    void *y[kMaxMats];  // YT [n] each
     const float *r[kMaxMats];
     int64_t n[kMaxMats];
     int it_begin[kMaxMats + 1];
@@ -200,9 +200,10 @@ struct MatTable {
     int count;
 };
 
-template <class F, int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES>
+// XT, YT: activation and output element types (float or _Float16).
+template <class F, typename XT, typename YT, int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES>
 __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable mt, const uint8_t *__restrict__ wu,
-                                                                const float *x, int ngroups, int64_t row_bytes) {
+                                                                const XT *x, int ngroups, int64_t row_bytes) {
     static_assert(NB >= 2, "at least one row in flight");
     constexpr int NMAT = SWIGLU ? 2 : 1;
     constexpr int kRowsPerWave = kWave / LPR;
@@ -236,11 +237,11 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     struct RowCursor {
         int mi, begin, end;
         int64_t n;
-        float *y;
+        YT *y;
         const float *r;
     };
     LoadCursor lc{0, 0, mt.it_begin[1], mt.tail_bytes[0], mt.w[0]};
-    RowCursor rc{0, 0, mt.it_begin[1], mt.n[0], mt.y[0], mt.r[0]};
+    RowCursor rc{0, 0, mt.it_begin[1], mt.n[0], static_cast<YT *>(mt.y[0]), mt.r[0]};
     auto issue = [&](RowLoads<F, NMAT> &b, int it) {
         while (it >= lc.end && lc.mi + 1 < count) {
             ++lc.mi;
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
             rc.begin = rc.end;
             rc.end = mt.it_begin[rc.mi + 1];
             rc.n = mt.n[rc.mi];
-            rc.y = mt.y[rc.mi];
+            rc.y = static_cast<YT *>(mt.y[rc.mi]);
             rc.r = mt.r[rc.mi];
         }
     };
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     // activations first, then the first rows' weights: waiting for the
     // activations (in issue order) then leaves the weight loads in flight
     constexpr int kXChunks = (LPR * 16 + BLOCK - 1) / BLOCK;
-    const XLoaded<kXChunks> xl = load_x<BLOCK, kXChunks>(x, ngroups);
+    const XLoaded<kXChunks> xl = load_x<BLOCK, kXChunks, XT>(x, ngroups);
     // keep the activation loads ahead of the weight loads (an empty asm with a
     // memory clobber: no instruction, only an ordering point for the compiler;
     // x is deliberately not __restrict__ so its loads cannot move across it)
@@ -301,11 +302,11 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     // where it goes); the window is stored in one go when it is full (a wave
     // streaming fewer than LPR rows per group stores only after the loop).
     float yv = 0.0f;
-    float *yp = nullptr;
+    YT *yp = nullptr;
     const float *rp = nullptr;
     int win = 0;
     auto flush = [&]() {
-        if (yp != nullptr) *yp = rp != nullptr ? yv + *rp : yv;
+        if (yp != nullptr) *yp = static_cast<YT>(rp != nullptr ? yv + *rp : yv);
         yp = nullptr;
         win = 0;
     };
@@ -353,10 +354,10 @@ done:
 // residual before it writes that row).
 constexpr int kFlush = 8;
 
-template <class F, int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
+template <class F, typename XT, typename YT, int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
 __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const uint8_t *__restrict__ w,
                                                                            const uint8_t *__restrict__ wu,
-                                                                           const float *x, float *y,
+                                                                           const XT *x, YT *y,
                                                                            const float *res, int64_t n, int ngroups,
                                                                            int64_t row_bytes) {
     constexpr int BLOCK = 64 * S * R;
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
     };
 
     constexpr int kXChunks = (S * kWave * 16 + BLOCK - 1) / BLOCK;
-    const XLoaded<kXChunks> xl = load_x<BLOCK, kXChunks>(x, ngroups);
+    const XLoaded<kXChunks> xl = load_x<BLOCK, kXChunks, XT>(x, ngroups);
     asm volatile("" ::: "memory");
     RowLoads<F, NMAT> buf[NB];
 #pragma unroll
@@ -428,7 +429,7 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
                             for (int mt = 0; mt < NMAT; ++mt) sum[mt] += q[s * NMAT + mt];
                         }
                         const float v = SWIGLU ? silu(sum[0]) * sum[1] : sum[0];
-                        y[row] = res != nullptr ? v + res[row] : v;
+                        y[row] = static_cast<YT>(res != nullptr ? v + res[row] : v);
                     }
                 }
             }
@@ -439,10 +440,10 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
 
 // Any K: one wave per row, each lane dequantizes four weights at a time in f32
 // and accumulates x * w with FMA; activations read straight from memory.
-template <bool SWIGLU>
+template <typename XT, typename YT, bool SWIGLU>
 __global__ __launch_bounds__(256) void gemv_generic_kernel(const uint8_t *__restrict__ w,
                                                            const uint8_t *__restrict__ wu,
-                                                           const float *__restrict__ x, float *y,
+                                                           const XT *__restrict__ x, YT *y,
                                                            const float *res, int64_t n, int64_t k, int64_t row_bytes) {
     const int lane = threadIdx.x & 63;
     const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
@@ -465,18 +466,18 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(const uint8_t *__rest
                 scale_min(hdr.y, hdr.z, hdr.w, 2 * g + (rr >> 5), sc, m);
                 const float dl = half_bits_to_float(hdr.x) * static_cast<float>(sc);
                 const float ml = half_bits_to_float(hdr.x >> 16) * static_cast<float>(m);
-                const float *xp = x + 4 * t;
+                const XT *xp = x + 4 * t;
 #pragma unroll
                 for (int b4 = 0; b4 < 4; ++b4) {
                     const float wv = dl * static_cast<float>((nib >> (8 * b4)) & 0xffu) - ml;
-                    acc[mat] = fmaf(wv, xp[b4], acc[mat]);
+                    acc[mat] = fmaf(wv, static_cast<float>(xp[b4]), acc[mat]);
                 }
             }
             acc[mat] = group_sum<64>(acc[mat]);
         }
         if (lane == 0) {
             const float v = SWIGLU ? silu(acc[0]) * acc[1] : acc[0];
-            y[row] = res != nullptr ? v + res[row] : v;
+            y[row] = static_cast<YT>(res != nullptr ? v + res[row] : v);
         }
     }
 }
@@ -526,10 +527,10 @@ int resident_blocks_per_cu(Kernel kern, int block, size_t lds, std::atomic<int> 
 }
 
 // One launch of the batch-1 kernel over `count` matrices (all with k columns).
-template <class F, int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES>
-hipError_t launch_fast(const GemvJob *jobs, int count, const uint8_t *wu, const float *x, int64_t k,
+template <class F, typename XT, typename YT, int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES>
+hipError_t launch_fast(const GemvJob *jobs, int count, const uint8_t *wu, const void *x, int64_t k,
                        hipStream_t stream) {
-    auto kern = gemv_kernel<F, LPR, SWIGLU, NB, BLOCK, MIN_WAVES>;
+    auto kern = gemv_kernel<F, XT, YT, LPR, SWIGLU, NB, BLOCK, MIN_WAVES>;
     const int ngroups = static_cast<int>(k / 64);
     const int64_t row_bytes = F::row_bytes(k);
     const size_t lds = static_cast<size_t>(ngroups) * sizeof(XGroup);
@@ -556,14 +557,15 @@ hipError_t launch_fast(const GemvJob *jobs, int count, const uint8_t *wu, const 
     const int64_t need = (total + BLOCK / kWave - 1) / (BLOCK / kWave);
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
     const int grid = static_cast<int>(need < cap ? need : cap);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, mt, wu, x, ngroups, row_bytes);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, mt, wu, static_cast<const XT *>(x), ngroups,
+                       row_bytes);
     return hipGetLastError();
 }
 
-template <class F, int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
-hipError_t launch_split(const uint8_t *w, const uint8_t *wu, const float *x, const float *r, float *y, int64_t n,
+template <class F, typename XT, typename YT, int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
+hipError_t launch_split(const uint8_t *w, const uint8_t *wu, const void *x, const float *r, void *y, int64_t n,
                         int64_t k, hipStream_t stream) {
-    auto kern = gemv_split_kernel<F, S, R, SWIGLU, NB, MIN_WAVES>;
+    auto kern = gemv_split_kernel<F, XT, YT, S, R, SWIGLU, NB, MIN_WAVES>;
     constexpr int BLOCK = 64 * S * R;
     const int ngroups = static_cast<int>(k / 64);
     const size_t lds = static_cast<size_t>(ngroups) * sizeof(XGroup) +
@@ -573,22 +575,24 @@ hipError_t launch_split(const uint8_t *w, const uint8_t *wu, const float *x, con
     const int64_t need = (n + R - 1) / R;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
     const int grid = static_cast<int>(need < cap ? need : cap);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, w, wu, x, y, r, n, ngroups, F::row_bytes(k));
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, w, wu, static_cast<const XT *>(x),
+                       static_cast<YT *>(y), r, n, ngroups, F::row_bytes(k));
     return hipGetLastError();
 }
 
-template <class F, bool SWIGLU>
-hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const float *x, const float *r, float *y, int64_t n,
+template <class F, typename XT, typename YT, bool SWIGLU>
+hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const void *x, const float *r, void *y, int64_t n,
                           int64_t k, hipStream_t stream) {
     const int64_t need = (n + 3) / 4;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
     const int grid = static_cast<int>(need < cap ? need : cap);
     if constexpr (std::is_same_v<F, Q8_0Format>) {
-        static_assert(!SWIGLU, "Q8_0 has no SwiGLU form");
-        hipLaunchKernelGGL(q8_0_generic_kernel, dim3(grid), dim3(256), 0, stream, w, x, y, r, n, k, F::row_bytes(k));
+        static_assert(!SWIGLU && std::is_same_v<XT, float> && std::is_same_v<YT, float>, "Q8_0: f32 GEMV only");
+        hipLaunchKernelGGL(q8_0_generic_kernel, dim3(grid), dim3(256), 0, stream, w, static_cast<const float *>(x),
+                           static_cast<float *>(y), r, n, k, F::row_bytes(k));
     } else {
-        hipLaunchKernelGGL(gemv_generic_kernel<SWIGLU>, dim3(grid), dim3(256), 0, stream, w, wu, x, y, r, n, k,
-                           F::row_bytes(k));
+        hipLaunchKernelGGL((gemv_generic_kernel<XT, YT, SWIGLU>), dim3(grid), dim3(256), 0, stream, w, wu,
+                           static_cast<const XT *>(x), static_cast<YT *>(y), r, n, k, F::row_bytes(k));
     }
     return hipGetLastError();
 }
@@ -634,55 +638,55 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const float *x, c
 #define Q4K_SMALL_BYTES (8 << 20)
 #endif
 
-template <class F, int LPR, bool SWIGLU>
-hipError_t dispatch_lpr(const GemvJob *jobs, int count, const uint8_t *wu, const float *x, int64_t k,
+template <class F, typename XT, typename YT, int LPR, bool SWIGLU>
+hipError_t dispatch_lpr(const GemvJob *jobs, int count, const uint8_t *wu, const void *x, int64_t k,
                         hipStream_t stream) {
     if constexpr (SWIGLU) {
-        return launch_fast<F, LPR, true, Q4K_SWIGLU_NB, Q4K_SWIGLU_BLOCK, Q4K_SWIGLU_MINW>(jobs, count, wu, x, k,
+        return launch_fast<F, XT, YT, LPR, true, Q4K_SWIGLU_NB, Q4K_SWIGLU_BLOCK, Q4K_SWIGLU_MINW>(jobs, count, wu, x, k,
                                                                                           stream);
     } else {
         int64_t bytes = 0;
         for (int i = 0; i < count; ++i) bytes += jobs[i].n * F::row_bytes(k);
         if (bytes < Q4K_SMALL_BYTES) {
-            return launch_fast<F, LPR, false, Q4K_SMALL_NB, Q4K_SMALL_BLOCK, Q4K_SMALL_MINW>(jobs, count, wu, x, k,
+            return launch_fast<F, XT, YT, LPR, false, Q4K_SMALL_NB, Q4K_SMALL_BLOCK, Q4K_SMALL_MINW>(jobs, count, wu, x, k,
                                                                                              stream);
         }
-        return launch_fast<F, LPR, false, Q4K_LARGE_NB, Q4K_LARGE_BLOCK, Q4K_LARGE_MINW>(jobs, count, wu, x, k,
+        return launch_fast<F, XT, YT, LPR, false, Q4K_LARGE_NB, Q4K_LARGE_BLOCK, Q4K_LARGE_MINW>(jobs, count, wu, x, k,
                                                                                           stream);
     }
 }
 
 // Rows wider than 4096 weights: one launch per matrix.
-template <class F, bool SWIGLU>
-hipError_t dispatch_wide(const GemvJob &j, const uint8_t *wu, const float *x, int64_t k, hipStream_t stream) {
+template <class F, typename XT, typename YT, bool SWIGLU>
+hipError_t dispatch_wide(const GemvJob &j, const uint8_t *wu, const void *x, int64_t k, hipStream_t stream) {
     const int64_t ngroups = k / 64;
     // split rows: S waves per row; two matrices' row buffers need more
     // registers, so the SwiGLU shapes keep fewer rows per workgroup
     constexpr int NB = Q4K_SPLIT_NB;
     if constexpr (SWIGLU) {
-        if (ngroups <= 128) return launch_split<F, 2, 4, true, NB, 2>(j.w, wu, x, j.r, j.y, j.n, k, stream);
-        if (ngroups <= 192) return launch_split<F, 3, 4, true, NB, 3>(j.w, wu, x, j.r, j.y, j.n, k, stream);
-        if (ngroups <= 256) return launch_split<F, 4, 2, true, NB, 2>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 128) return launch_split<F, XT, YT, 2, 4, true, NB, 2>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 192) return launch_split<F, XT, YT, 3, 4, true, NB, 3>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 256) return launch_split<F, XT, YT, 4, 2, true, NB, 2>(j.w, wu, x, j.r, j.y, j.n, k, stream);
     } else {
-        if (ngroups <= 128) return launch_split<F, 2, 8, false, NB, 4>(j.w, wu, x, j.r, j.y, j.n, k, stream);
-        if (ngroups <= 192) return launch_split<F, 3, 4, false, NB, 3>(j.w, wu, x, j.r, j.y, j.n, k, stream);
-        if (ngroups <= 256) return launch_split<F, 4, 4, false, NB, 4>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 128) return launch_split<F, XT, YT, 2, 8, false, NB, 4>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 192) return launch_split<F, XT, YT, 3, 4, false, NB, 3>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 256) return launch_split<F, XT, YT, 4, 4, false, NB, 4>(j.w, wu, x, j.r, j.y, j.n, k, stream);
     }
     // beyond K = 16384: the plain kernel
-    return launch_generic<F, SWIGLU>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+    return launch_generic<F, XT, YT, SWIGLU>(j.w, wu, x, j.r, j.y, j.n, k, stream);
 }
 
-template <class F, bool SWIGLU>
-hipError_t dispatch(const GemvJob *jobs, int count, const uint8_t *wu, const float *x, int64_t k,
+template <class F, typename XT, typename YT, bool SWIGLU>
+hipError_t dispatch(const GemvJob *jobs, int count, const uint8_t *wu, const void *x, int64_t k,
                     hipStream_t stream) {
     const int64_t ngroups = k / 64;
-    if (ngroups <= 4) return dispatch_lpr<F, 4, SWIGLU>(jobs, count, wu, x, k, stream);
-    if (ngroups <= 8) return dispatch_lpr<F, 8, SWIGLU>(jobs, count, wu, x, k, stream);
-    if (ngroups <= 16) return dispatch_lpr<F, 16, SWIGLU>(jobs, count, wu, x, k, stream);
-    if (ngroups <= 32) return dispatch_lpr<F, 32, SWIGLU>(jobs, count, wu, x, k, stream);
-    if (ngroups <= 64) return dispatch_lpr<F, 64, SWIGLU>(jobs, count, wu, x, k, stream);
+    if (ngroups <= 4) return dispatch_lpr<F, XT, YT, 4, SWIGLU>(jobs, count, wu, x, k, stream);
+    if (ngroups <= 8) return dispatch_lpr<F, XT, YT, 8, SWIGLU>(jobs, count, wu, x, k, stream);
+    if (ngroups <= 16) return dispatch_lpr<F, XT, YT, 16, SWIGLU>(jobs, count, wu, x, k, stream);
+    if (ngroups <= 32) return dispatch_lpr<F, XT, YT, 32, SWIGLU>(jobs, count, wu, x, k, stream);
+    if (ngroups <= 64) return dispatch_lpr<F, XT, YT, 64, SWIGLU>(jobs, count, wu, x, k, stream);
     for (int i = 0; i < count; ++i) {
-        const hipError_t e = dispatch_wide<F, SWIGLU>(jobs[i], wu, x, k, stream);
+        const hipError_t e = dispatch_wide<F, XT, YT, SWIGLU>(jobs[i], wu, x, k, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -706,16 +710,31 @@ hipError_t launch_gemv_multi(const GemvJob *jobs, int count, const uint8_t *w_up
     for (int i = 0; i < count; ++i) {
         if (jobs[i].n == 0) continue;
         if (k == 0) {
-            const hipError_t e = jobs[i].r != nullptr ? launch_copy(jobs[i].y, jobs[i].r, jobs[i].n, stream)
-                                                      : launch_fill_zero(jobs[i].y, jobs[i].n, stream);
+            float *y = static_cast<float *>(jobs[i].y);
+            const hipError_t e = jobs[i].r != nullptr ? launch_copy(y, jobs[i].r, jobs[i].n, stream)
+                                                      : launch_fill_zero(y, jobs[i].n, stream);
             if (e != hipSuccess) return e;
             continue;
         }
         live[nlive++] = jobs[i];
     }
     if (nlive == 0) return hipSuccess;
-    if (w_up != nullptr) return dispatch<Q4KFormat, true>(live, nlive, w_up, x, k, stream);
-    return dispatch<Q4KFormat, false>(live, nlive, nullptr, x, k, stream);
+    if (w_up != nullptr) return dispatch<Q4KFormat, float, float, true>(live, nlive, w_up, x, k, stream);
+    return dispatch<Q4KFormat, float, float, false>(live, nlive, nullptr, x, k, stream);
+}
+
+hipError_t launch_gemv_dt(const uint8_t *w, const void *x, bool x_f16, void *y, bool y_f16, int64_t n, int64_t k,
+                          hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    if (k == 0) {
+        return y_f16 ? launch_fill_zero_f16(static_cast<_Float16 *>(y), n, stream)
+                     : launch_fill_zero(static_cast<float *>(y), n, stream);
+    }
+    const GemvJob job{w, y, nullptr, n};
+    if (x_f16 && y_f16) return dispatch<Q4KFormat, _Float16, _Float16, false>(&job, 1, nullptr, x, k, stream);
+    if (x_f16) return dispatch<Q4KFormat, _Float16, float, false>(&job, 1, nullptr, x, k, stream);
+    if (y_f16) return dispatch<Q4KFormat, float, _Float16, false>(&job, 1, nullptr, x, k, stream);
+    return dispatch<Q4KFormat, float, float, false>(&job, 1, nullptr, x, k, stream);
 }
 
 hipError_t launch_q8_0_gemv(const uint8_t *w, const float *x, const float *r, float *y, int64_t n, int64_t k,
@@ -726,9 +745,9 @@ hipError_t launch_q8_0_gemv(const uint8_t *w, const float *x, const float *r, fl
     // the streaming kernels need dword-aligned groups: an even number of
     // blocks per row and a 4-byte aligned matrix
     if (k % 64 != 0 || (reinterpret_cast<uintptr_t>(w) & 3) != 0) {
-        return launch_generic<Q8_0Format, false>(w, nullptr, x, r, y, n, k, stream);
+        return launch_generic<Q8_0Format, float, float, false>(w, nullptr, x, r, y, n, k, stream);
     }
-    return dispatch<Q8_0Format, false>(&job, 1, nullptr, x, k, stream);
+    return dispatch<Q8_0Format, float, float, false>(&job, 1, nullptr, x, k, stream);
 }
 
 }  // namespace q4k

@@ -17,7 +17,7 @@ hipError_t launch_dequant(const uint8_t *w, float *out, int64_t n, int64_t k, hi
 // r != nullptr; r may equal y).
 struct GemvJob {
     const uint8_t *w;
-    float *y;
+    void *y;  // f32 [n] (f16 for launch_gemv_dt with y_f16)
     const float *r;
     int64_t n;
 };
@@ -32,6 +32,11 @@ hipError_t launch_gemv(const uint8_t *w, const uint8_t *w_up, const float *x, co
 hipError_t launch_gemv_multi(const GemvJob *jobs, int count, const uint8_t *w_up, const float *x, int64_t k,
                              hipStream_t stream);
 
+// Batch-1 GEMV with f16 or f32 activations (x_f16) and outputs (y_f16); f16
+// activations are widened exactly, outputs rounded to nearest even.
+hipError_t launch_gemv_dt(const uint8_t *w, const void *x, bool x_f16, void *y, bool y_f16, int64_t n, int64_t k,
+                          hipStream_t stream);
+
 // Q8_0 weights (34-byte blocks of 32): y[i] = sum_c W[i,c] x[c] (+ r[i]).
 hipError_t launch_q8_0_gemv(const uint8_t *w, const float *x, const float *r, float *y, int64_t n, int64_t k,
                             hipStream_t stream);
@@ -40,8 +45,13 @@ hipError_t launch_q8_0_gemv(const uint8_t *w, const float *x, const float *r, fl
 hipError_t launch_gemv_batched(const uint8_t *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
                                hipStream_t stream);
 
+// The same with f16 or f32 activations and outputs.
+hipError_t launch_gemv_batched_dt(const uint8_t *w, const void *x, bool x_f16, void *y, bool y_f16, int64_t m,
+                                  int64_t n, int64_t k, hipStream_t stream);
+
 // Writes zeros to y[0..count) (the k == 0 empty sum).
 hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream);
+hipError_t launch_fill_zero_f16(_Float16 *y, int64_t count, hipStream_t stream);
 
 // y[0..count) = src[0..count) (the k == 0 sum plus a residual; src may equal y).
 hipError_t launch_copy(float *y, const float *src, int64_t count, hipStream_t stream);

@@ -44,8 +44,9 @@ struct XLoaded {
     float v[NCH][4];
 };
 
-template <int BLOCK, int NCH>
-__device__ __forceinline__ XLoaded<NCH> load_x(const float *x, int ngroups) {
+// T is float or _Float16 (f16 activations are widened exactly).
+template <int BLOCK, int NCH, typename T>
+__device__ __forceinline__ XLoaded<NCH> load_x(const T *x, int ngroups) {
     XLoaded<NCH> f;
     const int total = ngroups * 16;
     // every load is issued (items past the end re-read item 0) so that no
@@ -53,9 +54,9 @@ __device__ __forceinline__ XLoaded<NCH> load_x(const float *x, int ngroups) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int it = static_cast<int>(threadIdx.x) + c * BLOCK;
-        const float *p = x + 4 * (it < total ? it : 0);
+        const T *p = x + 4 * (it < total ? it : 0);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) f.v[c][b] = p[b];
+        for (int b = 0; b < 4; ++b) f.v[c][b] = static_cast<float>(p[b]);
     }
     return f;
 }
@@ -119,7 +120,7 @@ template <int BLOCK>
 __device__ __forceinline__ void prepare_x(const float *__restrict__ x, int ngroups, XGroup *__restrict__ xg) {
     const int total = ngroups * 16;
     for (int base = 0; base < total; base += BLOCK) {
-        const XLoaded<1> f = load_x<BLOCK, 1>(x + 4 * base, (total - base + 15) / 16);
+        const XLoaded<1> f = load_x<BLOCK, 1, float>(x + 4 * base, (total - base + 15) / 16);
         prepare_x<BLOCK, 1>(f, (total - base + 15) / 16, xg + base / 16);
     }
 }

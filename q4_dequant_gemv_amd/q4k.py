@@ -23,8 +23,11 @@ STATUS = {0: "Q4K_OK", 1: "Q4K_ERR_INVALID_ARG", 2: "Q4K_ERR_UNSUPPORTED_SHAPE",
           4: "Q4K_ERR_LAUNCH"}
 
 # exported symbols, in the order include/q4k.h declares them
-EXPORTS = ("q4k_gemv", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_q8_0_gemv", "q4k_gemv_batched",
-           "q4k_fused_swiglu", "q4k_dequant", "q4k_status_string", "q4k_abi_version")
+EXPORTS = ("q4k_gemv", "q4k_gemv_dt", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_q8_0_gemv", "q4k_gemv_batched",
+           "q4k_gemv_batched_dt", "q4k_fused_swiglu", "q4k_dequant", "q4k_status_string", "q4k_abi_version")
+
+# q4k_dtype
+F32, F16 = 0, 1
 
 Q8_0_BLOCK_BYTES = 34
 Q8_0_BLOCK_WEIGHTS = 32
@@ -60,11 +63,13 @@ def lib() -> ctypes.CDLL:
         L.q4k_gemv_residual.argtypes = [p, p, p, p, i64, i64, p]
         L.q4k_gemv_multi.argtypes = [ctypes.POINTER(GemvItem), ctypes.c_int, p, i64, p]
         L.q4k_q8_0_gemv.argtypes = [p, p, p, i64, i64, p]
+        L.q4k_gemv_dt.argtypes = [p, p, ctypes.c_int, p, ctypes.c_int, i64, i64, p]
+        L.q4k_gemv_batched_dt.argtypes = [p, p, ctypes.c_int, p, ctypes.c_int, i64, i64, i64, p]
         L.q4k_gemv_batched.argtypes = [p, p, p, i64, i64, i64, p]
         L.q4k_fused_swiglu.argtypes = [p, p, p, p, i64, i64, p]
         L.q4k_dequant.argtypes = [p, p, i64, i64, p]
-        for f in (L.q4k_gemv, L.q4k_gemv_residual, L.q4k_gemv_multi, L.q4k_q8_0_gemv, L.q4k_gemv_batched,
-                  L.q4k_fused_swiglu, L.q4k_dequant):
+        for f in (L.q4k_gemv, L.q4k_gemv_dt, L.q4k_gemv_residual, L.q4k_gemv_multi, L.q4k_q8_0_gemv,
+                  L.q4k_gemv_batched, L.q4k_gemv_batched_dt, L.q4k_fused_swiglu, L.q4k_dequant):
             f.restype = st
         L.q4k_status_string.argtypes = [st]
         L.q4k_status_string.restype = ctypes.c_char_p
@@ -126,6 +131,57 @@ def gemv(w, x, y=None, n: int | None = None, stream=None):
         y = torch.empty(n, dtype=torch.float32, device=x.device)
     _check(lib().q4k_gemv(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float32), _dev(y, "y", torch.float32),
                           n, k, _stream(stream)), "q4k_gemv")
+    return y
+
+
+def _dtype_code(t, name):
+    import torch
+
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.float16:
+        return F16
+    raise TypeError(f"{name} must be float32 or float16 (got {t.dtype})")
+
+
+def _dev_any(t, name):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def gemv_dt(w, x, y=None, n: int | None = None, out_dtype=None, stream=None):
+    """``gemv`` with f16 or f32 ``x`` and ``y`` (the tensors' dtypes say which)."""
+    import torch
+
+    k = x.numel()
+    n = rows_of(w, k) if n is None else n
+    if y is None:
+        y = torch.empty(n, dtype=out_dtype or x.dtype, device=x.device)
+    _check(lib().q4k_gemv_dt(_dev(w, "w", torch.uint8), _dev_any(x, "x"), _dtype_code(x, "x"), _dev_any(y, "y"),
+                             _dtype_code(y, "y"), n, k, _stream(stream)), "q4k_gemv_dt")
+    return y
+
+
+def gemv_batched_dt(w, x, y=None, n: int | None = None, out_dtype=None, stream=None):
+    """``gemv_batched`` with f16 or f32 ``x`` [m, k] and ``y`` [m, n]."""
+    import torch
+
+    if x.dim() != 2:
+        raise ValueError("x must be [m, k]")
+    m, k = x.shape
+    n = rows_of(w, k) if n is None else n
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype or x.dtype, device=x.device)
+    _check(lib().q4k_gemv_batched_dt(_dev(w, "w", torch.uint8), _dev_any(x, "x"), _dtype_code(x, "x"),
+                                     _dev_any(y, "y"), _dtype_code(y, "y"), m, n, k, _stream(stream)),
+           "q4k_gemv_batched_dt")
     return y
 
 

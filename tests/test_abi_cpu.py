@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
-        ["q4k_gemv", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_q8_0_gemv", "q4k_gemv_batched", "q4k_fused_swiglu",
-         "q4k_dequant", "q4k_status_string", "q4k_abi_version"])
+        ["q4k_gemv", "q4k_gemv_dt", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_q8_0_gemv", "q4k_gemv_batched",
+         "q4k_gemv_batched_dt", "q4k_fused_swiglu", "q4k_dequant", "q4k_status_string", "q4k_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -55,7 +55,7 @@ def test_only_the_abi_is_exported():
 
 
 def test_status_strings(L):
-    assert L.q4k_abi_version() == 102
+    assert L.q4k_abi_version() == 104
     for s in range(5):
         assert len(L.q4k_status_string(s)) > 0
     assert L.q4k_status_string(99) == b"unknown status"
@@ -126,6 +126,37 @@ def test_residual_validation(L, args, status):
 def test_q8_0_validation(L, args, status):
     w, x, y, n, k = args
     assert L.q4k_q8_0_gemv(ctypes.c_void_p(w), ctypes.c_void_p(x), ctypes.c_void_p(y), n, k, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((W, X, 1, Y, 1, 16, 300), SHAPE),
+    ((W, X, 2, Y, 0, 16, 256), INVALID),          # unknown dtype
+    ((W, X, 0, Y, -1, 16, 256), INVALID),
+    ((W, X + 2, 0, Y, 0, 16, 256), MISALIGNED),   # f32 x at 2-B
+    ((W, X + 1, 1, Y, 1, 16, 256), MISALIGNED),   # f16 x at 1-B
+    ((W, X, 1, Y + 1, 1, 16, 256), MISALIGNED),
+    ((W, X, 1, Y + 2, 0, 16, 256), MISALIGNED),   # f32 y at 2-B
+    ((W, X, 1, X + 510, 1, 16, 256), INVALID),    # f16 y overlaps the last f16 of x
+    ((W, X, 0, Y, 1, 0, 256), OK),
+])
+def test_gemv_dt_validation(L, args, status):
+    w, x, xd, y, yd, n, k = args
+    assert L.q4k_gemv_dt(ctypes.c_void_p(w), ctypes.c_void_p(x), xd, ctypes.c_void_p(y), yd, n, k, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((W, X, 1, Y, 1, 4, 16, 300), SHAPE),
+    ((W, X, 3, Y, 1, 4, 16, 256), INVALID),
+    ((W, X + 2, 0, Y, 1, 4, 16, 256), MISALIGNED),
+    ((W, X, 1, Y + 2, 0, 4, 16, 256), MISALIGNED),
+    ((W, X, 1, X + 4 * 256 * 2 - 2, 1, 4, 16, 256), INVALID),  # y starts inside f16 x[4, 256]
+    ((W, X, 1, Y, 1, 0, 16, 256), OK),
+    ((W, X, 1, Y, 1, -1, 16, 256), INVALID),
+])
+def test_batched_dt_validation(L, args, status):
+    w, x, xd, y, yd, m, n, k = args
+    assert L.q4k_gemv_batched_dt(ctypes.c_void_p(w), ctypes.c_void_p(x), xd, ctypes.c_void_p(y), yd, m, n, k,
+                                 None) == status
 
 
 def _items(*triples):
