@@ -67,8 +67,8 @@ def parse():
                     help="also time every kernel at every config shape (table on stderr)")
     ap.add_argument("--case", default=None,
                     help="only run one kernel in a loop, for profilers: gemv:NAME, swiglu:NAME, "
-                         "residual:NAME, q8_0:NAME, dequant:NAME or batched:M:NAME with NAME a shape "
-                         "of inputs.SHAPES, or multi:gdn_0p8b")
+                         "residual:NAME, q8_0:NAME, dequant:NAME, batched:M:NAME or prefill:M:NAME "
+                         "with NAME a shape of inputs.SHAPES, or multi:gdn_0p8b")
     return ap.parse_args()
 
 
@@ -215,9 +215,11 @@ def main():
     blocks = decode_blocks(q4k, inputs, torch, dev, stream, args.steps, args.warmup)
     q8 = q8_0_kernels(q4k, inputs, torch, dev, stream, args.steps, args.warmup)
     f16io = f16_variants(q4k, inputs, torch, dev, stream, args.steps, args.warmup, not args.no_batched)
+    prefill = prefill_kernels(q4k, inputs, torch, dev, stream) if not args.no_batched else {}
 
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s; per kernel {kernels}; "
-        f"batched {batched}; decode blocks {blocks}; q8_0 {q8}; f16 i/o {f16io}; host wall {wall:.3f}s")
+        f"batched {batched}; decode blocks {blocks}; q8_0 {q8}; f16 i/o {f16io}; prefill {prefill}; "
+        f"host wall {wall:.3f}s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -267,6 +269,7 @@ def main():
             "decode_blocks": blocks,
             "q8_0_9b": q8,
             "f16_io_9b": f16io,
+            "prefill_9b_ffn": prefill,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -392,6 +395,32 @@ def f16_variants(q4k, inputs, torch, dev, stream, steps, warmup, batched):
     return out
 
 
+F16_DENSE_PEAK_TFLOPS = 2500.0
+
+
+def prefill_kernels(q4k, inputs, torch, dev, stream):
+    """The prefill GEMM (q4k_prefill_gemm, f16 activations, f32 outputs) on
+    the 9B gate and down projections at m = 128 .. 2048 tokens, and the
+    batched call on the same f16 activations for comparison."""
+    out = {}
+    for nm in ("gate_9b", "down_9b"):
+        n, k = inputs.SHAPES[nm]
+        w = torch.from_numpy(inputs.make_q4k(n, k, config_id=73, tensor_id=0).reshape(-1)).to(dev)
+        for m in (128, 256, 512, 1024, 2048):
+            xh = torch.from_numpy(inputs.make_x(m, k, config_id=73, tensor_id=m)).to(dev).half()
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            t = _time_launches(lambda i: q4k.prefill_gemm(w, xh, y=y, stream=stream), torch, stream, 20, 3)
+            tf = 2.0 * m * n * k / t / 1e12
+            rec = {"mean_us": round(t * 1e6, 2), "TFLOP/s": round(tf, 1),
+                   "frac_f16_peak": round(tf / F16_DENSE_PEAK_TFLOPS, 4)}
+            if m <= 512:
+                tb = _time_launches(lambda i: q4k.gemv_batched_dt(w, xh, y=y, stream=stream), torch, stream, 10, 2)
+                rec["batched_call_us"] = round(tb * 1e6, 2)
+            out[f"{nm} m={m}"] = rec
+        del w
+    return out
+
+
 def time_call(fn, torch, reps=50, warm=5):
     for _ in range(warm):
         fn()
@@ -429,6 +458,16 @@ def run_case(case, steps, warmup, q4k, inputs, torch, np, dev):
         return
     parts = case.split(":")
     kind, name = parts[0], parts[-1]
+    if kind == "prefill":
+        m = int(parts[1])
+        n, k = inputs.SHAPES[name]
+        w = torch.from_numpy(inputs.make_q4k(n, k, config_id=7, tensor_id=1).reshape(-1)).to(dev)
+        xh = torch.from_numpy(inputs.make_x(m, k, config_id=7)).to(dev).half()
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream()
+        t = _time_launches(lambda i: q4k.prefill_gemm(w, xh, y=y), torch, stream, steps, warmup)
+        log(f"[case] {case}: {t * 1e6:.2f} us per call, {2.0 * m * n * k / t / 1e12:.1f} TFLOP/s")
+        return
     if kind == "multi":
         if name != "gdn_0p8b":
             raise SystemExit("multi case: only multi:gdn_0p8b")

@@ -188,6 +188,27 @@ Q4K_API q4k_status q4k_gemv_batched_dt(const void *w, const void *x, q4k_dtype x
                                        int64_t m, int64_t n, int64_t k, void *stream);
 
 /*
+ * Prefill-size GEMM with f16 activations (W4A16): the prefill side of
+ * resolveMatmulPhase / selectQ4KFusedVariant ("@simulatte/doppler 0.1.7 ->
+ * 0.1.8", matmul-selection.js), for hundreds of tokens at once.
+ *   w : Q4_K matrix [n, k], 16-byte aligned
+ *   x : f16 [m, k] token-major, 16-byte aligned
+ *   y : [m, n] of y_dtype (f32 or f16), aligned to its element size:
+ *       y[t, r] = sum_c W[r,c] x[t,c], computed from exact f16 operands on the
+ *       matrix cores with f32 accumulation (the same bound as q4k_gemv);
+ *       bitwise reproducible; an f16 y is the f32 result rounded to nearest
+ *       even.
+ * Any m >= 1 is accepted; the kernel works in 128-token tiles, so it is
+ * meant for m >= 128 (q4k_gemv_batched_dt covers fewer tokens).  Takes
+ * stream-ordered scratch (hipMallocAsync / hipFreeAsync) of
+ * 2*m'*k + 32*(m'/128)*(k/256)*128 bytes, m' = m rounded up to 128.
+ * k > 2^24 -> Q4K_ERR_UNSUPPORTED_SHAPE.  Other errors and aliasing as
+ * q4k_gemv_batched.
+ */
+Q4K_API q4k_status q4k_prefill_gemm(const void *w, const void *x, void *y, q4k_dtype y_dtype, int64_t m, int64_t n,
+                                    int64_t k, void *stream);
+
+/*
  * Fused gate/up GEMV with SwiGLU ("qualia_core_db/inference/cuda_lane/mod.rs",
  * try_q4k_soa_fused_swiglu; "Struct WgslForwardPass", silu_mul_shader):
  *   w_gate, w_up : two separate Q4_K matrices [n, k]

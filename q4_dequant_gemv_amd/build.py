@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libq4k.so")
-SOURCES = ["api.hip", "dequant.hip", "gemv.hip", "batched.hip"]
+SOURCES = ["api.hip", "dequant.hip", "gemv.hip", "batched.hip", "prefill.hip"]
 ARCH = os.environ.get("Q4K_OFFLOAD_ARCH", "gfx950")
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 are generated anywhere.

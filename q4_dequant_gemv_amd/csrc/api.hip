@@ -238,6 +238,26 @@ q4k_status q4k_gemv_batched_dt(const void *w, const void *x, q4k_dtype x_dtype, 
                                                 y_dtype == Q4K_F16, m, n, k, static_cast<hipStream_t>(stream)));
 }
 
+q4k_status q4k_prefill_gemm(const void *w, const void *x, void *y, q4k_dtype y_dtype, int64_t m, int64_t n,
+                            int64_t k, void *stream) {
+    if (y_dtype != Q4K_F32 && y_dtype != Q4K_F16) return Q4K_ERR_INVALID_ARG;
+    uint64_t wb = 0;
+    const q4k_status s = check_shape(n, k, &wb);
+    if (s != Q4K_OK) return s;
+    // the kernel addresses one 128-row block of weights with 32-bit offsets
+    if (k > (int64_t{1} << 24)) return Q4K_ERR_UNSUPPORTED_SHAPE;
+    if (m < 0) return Q4K_ERR_INVALID_ARG;
+    if (m > 0 && (n > q4k::kMaxElems / m || (k > 0 && m > q4k::kMaxElems / k))) return Q4K_ERR_INVALID_ARG;
+    if (n == 0 || m == 0) return Q4K_OK;
+    if (y == nullptr || (k > 0 && (w == nullptr || x == nullptr))) return Q4K_ERR_INVALID_ARG;
+    const uint64_t ye = y_dtype == Q4K_F16 ? 2 : 4;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, ye)) return Q4K_ERR_MISALIGNED;
+    const uint64_t yb = static_cast<uint64_t>(m) * n * ye, xb = static_cast<uint64_t>(m) * k * 2;
+    if (overlap(y, yb, w, wb) || overlap(y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
+    return from_hip(q4k::launch_prefill(static_cast<const uint8_t *>(w), static_cast<const _Float16 *>(x), y,
+                                        y_dtype == Q4K_F16, m, n, k, static_cast<hipStream_t>(stream)));
+}
+
 q4k_status q4k_fused_swiglu(const void *w_gate, const void *w_up, const float *x, float *h, int64_t n, int64_t k,
                             void *stream) {
     uint64_t wb = 0;
@@ -275,6 +295,6 @@ const char *q4k_status_string(q4k_status s) {
     return "unknown status";
 }
 
-int q4k_abi_version(void) { return 104; }
+int q4k_abi_version(void) { return 105; }
 
 }  // extern "C"

@@ -45,7 +45,6 @@ namespace q4k {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 as_uint4(u32x4_t v) { return make_uint4(v.x, v.y, v.z, v.w); }
 __device__ __forceinline__ float4_t as_float4(u32x4_t v) { return __builtin_bit_cast(float4_t, v); }
@@ -81,15 +80,6 @@ __device__ __forceinline__ int stage_pos(int kk) {
     const int i = 2 * (dd >> 1) + sd;
     const int tb = (b == 1) ? 2 : (b == 2) ? 1 : b;
     return kq * 32 + i * 8 + 4 * (dd & 1) + tb;
-}
-
-// f16 bit patterns of 1024 + sc*q for the two codes of a nibble pair (one
-// packed 16-bit multiply-add: sc*q <= 945 fits the 10-bit fraction of 1024).
-__device__ __forceinline__ uint32_t pair_operand(uint32_t pair, uint32_t sc2) {
-    const u16x2_t p = __builtin_bit_cast(u16x2_t, pair);
-    const u16x2_t s = __builtin_bit_cast(u16x2_t, sc2);
-    const u16x2_t magic = {0x6400, 0x6400};
-    return __builtin_bit_cast(uint32_t, static_cast<u16x2_t>(p * s + magic));
 }
 
 // ---- activations, converted once per call ----------------------------------

@@ -49,6 +49,11 @@ hipError_t launch_gemv_batched(const uint8_t *w, const float *x, float *y, int64
 hipError_t launch_gemv_batched_dt(const uint8_t *w, const void *x, bool x_f16, void *y, bool y_f16, int64_t m,
                                   int64_t n, int64_t k, hipStream_t stream);
 
+// Prefill-size GEMM with f16 activations: y[t, r] = sum_c W[r,c] x[t,c],
+// x f16 [m, k] (16-byte aligned), y f32 or f16 [m, n].
+hipError_t launch_prefill(const uint8_t *w, const _Float16 *x, void *y, bool y_f16, int64_t m, int64_t n, int64_t k,
+                          hipStream_t stream);
+
 // Writes zeros to y[0..count) (the k == 0 empty sum).
 hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream);
 hipError_t launch_fill_zero_f16(_Float16 *y, int64_t count, hipStream_t stream);

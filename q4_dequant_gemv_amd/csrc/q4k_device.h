@@ -48,6 +48,19 @@ __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint3
     return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, Q4K_WEIGHT_CPOL);
 }
 
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// f16 bit patterns of 1024 + sc*q for the two codes of a nibble pair (the
+// codes in the low and high 16 bits of `pair`, the scale in both halves of
+// `sc2`): one packed 16-bit multiply-add, since sc*q <= 945 fits the 10-bit
+// fraction of 1024.
+__device__ __forceinline__ uint32_t pair_operand(uint32_t pair, uint32_t sc2) {
+    const u16x2_t p = __builtin_bit_cast(u16x2_t, pair);
+    const u16x2_t s = __builtin_bit_cast(u16x2_t, sc2);
+    const u16x2_t magic = {0x6400, 0x6400};
+    return __builtin_bit_cast(uint32_t, static_cast<u16x2_t>(p * s + magic));
+}
+
 // A value the caller knows is equal in every lane, moved to scalar registers.
 __device__ __forceinline__ int64_t wave_uniform(int64_t v) {
     const uint64_t u = static_cast<uint64_t>(v);

@@ -24,7 +24,8 @@ STATUS = {0: "Q4K_OK", 1: "Q4K_ERR_INVALID_ARG", 2: "Q4K_ERR_UNSUPPORTED_SHAPE",
 
 # exported symbols, in the order include/q4k.h declares them
 EXPORTS = ("q4k_gemv", "q4k_gemv_dt", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_q8_0_gemv", "q4k_gemv_batched",
-           "q4k_gemv_batched_dt", "q4k_fused_swiglu", "q4k_dequant", "q4k_status_string", "q4k_abi_version")
+           "q4k_gemv_batched_dt", "q4k_prefill_gemm", "q4k_fused_swiglu", "q4k_dequant", "q4k_status_string",
+           "q4k_abi_version")
 
 # q4k_dtype
 F32, F16 = 0, 1
@@ -65,11 +66,13 @@ def lib() -> ctypes.CDLL:
         L.q4k_q8_0_gemv.argtypes = [p, p, p, i64, i64, p]
         L.q4k_gemv_dt.argtypes = [p, p, ctypes.c_int, p, ctypes.c_int, i64, i64, p]
         L.q4k_gemv_batched_dt.argtypes = [p, p, ctypes.c_int, p, ctypes.c_int, i64, i64, i64, p]
+        L.q4k_prefill_gemm.argtypes = [p, p, p, ctypes.c_int, i64, i64, i64, p]
         L.q4k_gemv_batched.argtypes = [p, p, p, i64, i64, i64, p]
         L.q4k_fused_swiglu.argtypes = [p, p, p, p, i64, i64, p]
         L.q4k_dequant.argtypes = [p, p, i64, i64, p]
         for f in (L.q4k_gemv, L.q4k_gemv_dt, L.q4k_gemv_residual, L.q4k_gemv_multi, L.q4k_q8_0_gemv,
-                  L.q4k_gemv_batched, L.q4k_gemv_batched_dt, L.q4k_fused_swiglu, L.q4k_dequant):
+                  L.q4k_gemv_batched, L.q4k_gemv_batched_dt, L.q4k_prefill_gemm, L.q4k_fused_swiglu,
+                  L.q4k_dequant):
             f.restype = st
         L.q4k_status_string.argtypes = [st]
         L.q4k_status_string.restype = ctypes.c_char_p
@@ -182,6 +185,21 @@ def gemv_batched_dt(w, x, y=None, n: int | None = None, out_dtype=None, stream=N
     _check(lib().q4k_gemv_batched_dt(_dev(w, "w", torch.uint8), _dev_any(x, "x"), _dtype_code(x, "x"),
                                      _dev_any(y, "y"), _dtype_code(y, "y"), m, n, k, _stream(stream)),
            "q4k_gemv_batched_dt")
+    return y
+
+
+def prefill_gemm(w, x, y=None, n: int | None = None, out_dtype=None, stream=None):
+    """y[t, r] = sum_c W[r,c] x[t,c] for f16 ``x`` [m, k] (prefill sizes); ``y`` f32 or f16 [m, n]."""
+    import torch
+
+    if x.dim() != 2:
+        raise ValueError("x must be [m, k]")
+    m, k = x.shape
+    n = rows_of(w, k) if n is None else n
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype or torch.float32, device=x.device)
+    _check(lib().q4k_prefill_gemm(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float16), _dev_any(y, "y"),
+                                  _dtype_code(y, "y"), m, n, k, _stream(stream)), "q4k_prefill_gemm")
     return y
 
 

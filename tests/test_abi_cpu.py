@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
         ["q4k_gemv", "q4k_gemv_dt", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_q8_0_gemv", "q4k_gemv_batched",
-         "q4k_gemv_batched_dt", "q4k_fused_swiglu", "q4k_dequant", "q4k_status_string", "q4k_abi_version"])
+         "q4k_gemv_batched_dt", "q4k_prefill_gemm", "q4k_fused_swiglu", "q4k_dequant", "q4k_status_string",
+         "q4k_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -55,7 +56,7 @@ def test_only_the_abi_is_exported():
 
 
 def test_status_strings(L):
-    assert L.q4k_abi_version() == 104
+    assert L.q4k_abi_version() == 105
     for s in range(5):
         assert len(L.q4k_status_string(s)) > 0
     assert L.q4k_status_string(99) == b"unknown status"
@@ -157,6 +158,25 @@ def test_batched_dt_validation(L, args, status):
     w, x, xd, y, yd, m, n, k = args
     assert L.q4k_gemv_batched_dt(ctypes.c_void_p(w), ctypes.c_void_p(x), xd, ctypes.c_void_p(y), yd, m, n, k,
                                  None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((W, X, Y, 0, 128, 16, 300), SHAPE),
+    ((W, X, Y, 0, 128, 16, (1 << 24) + 256), SHAPE),  # beyond the kernel's 32-bit row-block offsets
+    ((W, X, Y, 2, 128, 16, 256), INVALID),           # unknown output dtype
+    ((W, X, Y, 0, -1, 16, 256), INVALID),
+    ((W, X + 8, Y, 0, 128, 16, 256), MISALIGNED),    # x must be 16-B aligned
+    ((W + 8, X, Y, 0, 128, 16, 256), MISALIGNED),
+    ((W, X, Y + 2, 0, 128, 16, 256), MISALIGNED),    # f32 y at 2-B
+    ((W, X, Y + 1, 1, 128, 16, 256), MISALIGNED),
+    ((W, X, X + 128 * 512 - 2, 1, 128, 16, 256), INVALID),  # f16 y starts inside x [128, 256] f16
+    ((W, 0, Y, 0, 128, 16, 256), INVALID),
+    ((W, X, Y, 0, 0, 16, 256), OK),
+    ((W, X, Y, 1, 128, 0, 256), OK),
+])
+def test_prefill_validation(L, args, status):
+    w, x, y, yd, m, n, k = args
+    assert L.q4k_prefill_gemm(ctypes.c_void_p(w), ctypes.c_void_p(x), ctypes.c_void_p(y), yd, m, n, k, None) == status
 
 
 def _items(*triples):
