@@ -314,11 +314,24 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     // back to the outer loop's test would join the loop head with loads of
     // the unfinished unrolled pass still in flight, and the wait counters
     // would have to drain them there.
+    // The sequencer issues from the oldest wave first, so with equal shares
+    // the younger waves of a CU fall behind and finish alone, long after the
+    // others.  Each wave therefore lowers its own priority as the share of its
+    // iterations still to do drops (1/2, 1/4, 1/8): a wave that is behind
+    // outranks the ones ahead of it, and the finish times close up.
+    const int mine = (niters - it0 + nwaves - 1) / nwaves;
     if (it0 < niters) {
         for (int it = it0;; it += NB * nwaves) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const int cur = it + b * nwaves;
+                {
+                    const int left = (niters - cur + nwaves - 1) / nwaves;
+                    if (2 * left > mine) __builtin_amdgcn_s_setprio(3);
+                    else if (4 * left > mine) __builtin_amdgcn_s_setprio(2);
+                    else if (8 * left > mine) __builtin_amdgcn_s_setprio(1);
+                    else __builtin_amdgcn_s_setprio(0);
+                }
                 issue(buf[(b + NB - 1) % NB], cur + (NB - 1) * nwaves);
                 row_cursor(cur);
                 const int64_t row = static_cast<int64_t>(cur - rc.begin) * kRowsPerWave + slot;
@@ -397,6 +410,14 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
     load_xregs(xg[g.j], xr);
 
     for (int c = 0; c < my_iters; c += NB) {
+        {
+            // priority falls with the share of iterations left, as in gemv_kernel
+            const int left = my_iters - c;
+            if (4 * left > 3 * my_iters) __builtin_amdgcn_s_setprio(3);
+            else if (4 * left > 2 * my_iters) __builtin_amdgcn_s_setprio(2);
+            else if (4 * left > my_iters) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const int cur = c + b;

@@ -50,6 +50,20 @@ constexpr int kAStage = 8 * 4 * 64 * 16;      // [token tile][MFMA step][lane][8
 constexpr int kWStage = kPfTile * kBlockBytes;  // one super-block of 128 rows = 18 KB
 constexpr int kMinBlock = 8 * 64 * 8;         // [token tile][lane][4 f16] = 4 KB per super-block
 constexpr int kWPieces = kWStage / 16;        // 1152 16-byte pieces = 18 wave-wide copies
+#ifndef Q4K_PREFILL_RT
+#define Q4K_PREFILL_RT 2
+#endif
+#ifndef Q4K_PREFILL_TT
+#define Q4K_PREFILL_TT 8
+#endif
+constexpr int kPfRT = Q4K_PREFILL_RT;  // row tiles per wave
+constexpr int kPfTT = Q4K_PREFILL_TT;  // token tiles per wave
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8): wait for vector memory down to N in flight, nothing else
+constexpr int wait_vm(int nvm) { return (nvm & 15) | ((nvm >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitVm0 = wait_vm(0);
+constexpr int kWaitVm8 = wait_vm(8);
+constexpr int kWStagePad = 20 * 1024;  // 18 KB of weights + the two padding copies
 
 __device__ __forceinline__ half8_t as_half8(u32x4_t v) { return __builtin_bit_cast(half8_t, v); }
 
@@ -101,170 +115,254 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(const _Float16 *__res
 }
 
 // ---- the matrix-core kernel ---------------------------------------------------
-template <typename YT>
+// Each wave owns RT row tiles x TT token tiles of 16 x 16; (128/16/RT) x
+// (128/16/TT) = 4 waves cover the 128 x 128 tile.  Building a B operand costs
+// about 20 vector instructions per 8 weights and each is used TT times; each
+// A operand is read from LDS by every wave with those tokens.  RT = 2, TT = 8
+// builds every B operand once per workgroup and keeps the vector units under
+// the matrix cores' time.  With ksplit > 1 the workgroup covers super-blocks
+// [ks*nsb/ksplit, (ks+1)*nsb/ksplit) and writes its f32 partial tile to
+// part[ks] instead of y (added up in a fixed order by prefill_reduce_kernel).
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+template <typename YT, int RT, int TT>
 __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(const uint8_t *__restrict__ w,
                                                               const uint8_t *__restrict__ xa,
                                                               const uint8_t *__restrict__ xs, YT *__restrict__ y,
-                                                              int64_t m, int64_t n, int64_t k, int64_t row_bytes,
-                                                              int nblocks, int nrb) {
-    __shared__ __align__(16) uint8_t a_lds[2][kAStage];
-    __shared__ __align__(16) uint8_t w_lds[2][kWStage];
+                                                              float *__restrict__ part, int64_t m, int64_t n,
+                                                              int64_t k, int64_t row_bytes, int nblocks, int nrb,
+                                                              int ksplit) {
+    constexpr int WR = kPfTile / (16 * RT);  // waves along the rows
+    static_assert(WR * (kPfTile / (16 * TT)) == 4, "four waves cover the tile");
+    // Three buffers each for the activations (one per step, copied two steps
+    // ahead) and the weights (one per super-block, copied one super-block
+    // ahead).  Every buffer is its own array and every access names it at
+    // compile time (the super-block loop is unrolled by three), so the
+    // compiler can tell a copy in flight into one buffer from reads of
+    // another and adds no waits of its own.
+    __shared__ __align__(16) uint8_t a0[kAStage], a1[kAStage], a2[kAStage];
+    __shared__ __align__(16) uint8_t w0[kWStagePad], w1[kWStagePad], w2[kWStagePad];
+    uint8_t *const abuf[3] = {a0, a1, a2};
+    uint8_t *const wbuf[3] = {w0, w1, w2};
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    const int wr = wave & 1;   // the wave's 64 rows of the tile
-    const int wt = wave >> 1;  // the wave's 64 tokens of the tile
+    const int wr = wave % WR;  // the wave's rows of the tile: 16*RT from 16*RT*wr
+    const int wt = wave / WR;  // the wave's tokens: 16*TT from 16*TT*wt
     const int col = lane & 15;
     const int kb = lane >> 4;
 
     const int rbk = static_cast<int>(blockIdx.x % nrb);
-    const int tbk = static_cast<int>(blockIdx.x / nrb);
+    const int tbk = static_cast<int>((blockIdx.x / nrb) % nblocks);
+    const int ks = static_cast<int>(blockIdx.x / (static_cast<int64_t>(nrb) * nblocks));
     const int64_t row0 = static_cast<int64_t>(rbk) * kPfTile;
     const int64_t tok0 = static_cast<int64_t>(tbk) * kPfTile;
-    const int nsb = static_cast<int>(k / kBlockWeights);
+    const int nsb_all = static_cast<int>(k / kBlockWeights);
+    const int sb_begin = static_cast<int>(static_cast<int64_t>(nsb_all) * ks / ksplit);
+    const int nsb = static_cast<int>(static_cast<int64_t>(nsb_all) * (ks + 1) / ksplit) - sb_begin;
     const int64_t rows_here = n - row0 < kPfTile ? n - row0 : kPfTile;
     // rows past n read as zeros; their results are not stored
     const __amdgpu_buffer_rsrc_t wrs = stream_rsrc(w + row0 * row_bytes, static_cast<int>(rows_here * row_bytes));
 
-    // direct-to-LDS copies: each instruction moves 64 x 16 bytes to LDS
-    // base + 16 * lane
-    auto dma_a = [&](int h, int buf) {
-        const __amdgpu_buffer_rsrc_t ar =
-            stream_rsrc(xa + (static_cast<int64_t>(h) * nblocks + tbk) * kAStage, kAStage);
+    // Direct-to-LDS copies: each instruction moves 64 x 16 bytes to LDS base
+    // + 16 * lane.  h, s count steps and super-blocks from sb_begin.
+    // Copies past the end of the range go through a 0-byte descriptor (or
+    // read rows of the next range): they fill buffers nobody reads, and every
+    // step issues the same number of copies, so every wait is a constant.
+    auto dma_a = [&](int h, uint8_t *dst) {
+        const __amdgpu_buffer_rsrc_t ar = stream_rsrc(
+            xa + (static_cast<int64_t>(2 * sb_begin + h) * nblocks + tbk) * kAStage, h < 2 * nsb ? kAStage : 0);
+        lds_u8 *base = (lds_u8 *)dst;  // generic -> LDS address space
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int c = wave * 8 + i;
-            lds_u8 *dst = (lds_u8 *)(&a_lds[buf][0]) + c * 1024;  // generic -> LDS address space
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, reinterpret_cast<lds_void *>(dst), 16, c * 1024 + lane * 16,
-                                                     0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, reinterpret_cast<lds_void *>(base + c * 1024), 16,
+                                                     c * 1024 + lane * 16, 0, 0, 0);
         }
     };
-    auto dma_w = [&](int s, int buf) {
+    auto dma_w = [&](int s, uint8_t *dst) {
+        lds_u8 *base = (lds_u8 *)dst;
+        // 18 copies of 64 x 16 bytes per super-block, 5 per wave: the last two
+        // read past the descriptor (zeros) into the padding
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
-            const int ii = wave + 4 * i;  // 18 copies over 4 waves
-            if (ii < kWPieces / 64) {
-                const int p = ii * 64 + lane;
-                const int row = p / 9;
-                const int pc = p % 9;
-                const uint32_t off = static_cast<uint32_t>(row * row_bytes) + static_cast<uint32_t>(s) * kBlockBytes +
-                                     static_cast<uint32_t>(pc * 16);
-                lds_u8 *dst = (lds_u8 *)(&w_lds[buf][0]) + ii * 1024;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, reinterpret_cast<lds_void *>(dst), 16, off, 0, 0, 0);
-            }
+            const int ii = wave + 4 * i;
+            const int p = ii * 64 + lane;
+            const int row = p / 9;
+            const int pc = p % 9;
+            const uint32_t off = ii < kWPieces / 64 && s < nsb
+                                     ? static_cast<uint32_t>(row * row_bytes) +
+                                           static_cast<uint32_t>(sb_begin + s) * kBlockBytes +
+                                           static_cast<uint32_t>(pc * 16)
+                                     : 0x80000000u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, reinterpret_cast<lds_void *>(base + ii * 1024), 16, off, 0,
+                                                     0, 0);
         }
     };
+    // a barrier without a memory fence: the waits before it are explicit
+    auto barrier = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
 
-    float4_t acc[4][4];
+    float4_t acc[RT][TT];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) acc[rt][tt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
     const half8_t k1024 = {1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024};
 
-    dma_a(0, 0);
-    dma_w(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int s = 0; s < nsb; ++s) {
-        const uint8_t *wl = w_lds[s & 1];
-        // headers of the wave's rows: d, dmin, and the mins as the B operand
-        // of the min-term product (k-group kb: sub-blocks 4*(kb&1) .. +3)
-        uint4 hdr[4];
-        float dd[4], dm[4];
-        half4_t qb[4];
+    // One super-block; S3 = s % 3 names the buffers: weights wbuf[S3],
+    // activations of its two steps abuf[(2 S3) % 3] and abuf[(2 S3 + 1) % 3].
+    // Each step ends by issuing the copies for later steps (after all of its
+    // own LDS reads): the activations two steps ahead, and after the second
+    // step the weights two super-blocks ahead.
+    auto super_block = [&](auto S3c, int s) {
+        constexpr int S3 = decltype(S3c)::value;
+        const uint8_t *wl = wbuf[S3];
+        // the wave's tokens' sub-block sums (A of the min-term product),
+        // issued before this super-block's copies so that the waits below
+        // cover them
+        half4_t qa[TT];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            hdr[rt] = *reinterpret_cast<const uint4 *>(wl + (wr * 64 + rt * 16 + col) * kBlockBytes);
-            dd[rt] = half_bits_to_float(hdr[rt].x);
-            dm[rt] = 32.0f * half_bits_to_float(hdr[rt].x >> 16);  // the sums are stored / 32
+        for (int tt = 0; tt < TT; ++tt) {
+            qa[tt] = *reinterpret_cast<const half4_t *>(
+                xs + (static_cast<int64_t>(sb_begin + s) * nblocks + tbk) * kMinBlock + ((wt * TT + tt) * 64 + lane) * 8);
+        }
+        // headers of the wave's rows: d, dmin, the eight scales (as packed
+        // 16-bit pairs) and the mins as the B operand of the min-term product
+        // (k-group kb: sub-blocks 4*(kb&1) .. +3)
+        float dd[RT], dm[RT];
+        uint32_t sc2[RT][8];
+        half4_t qb[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const uint4 hdr = *reinterpret_cast<const uint4 *>(wl + (wr * 16 * RT + rt * 16 + col) * kBlockBytes);
+            dd[rt] = half_bits_to_float(hdr.x);
+            dm[rt] = 32.0f * half_bits_to_float(hdr.x >> 16);  // the sums are stored / 32
             half4_t mv;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 8; ++q) {
                 int sc, mm;
-                scale_min(hdr[rt].y, hdr[rt].z, hdr[rt].w, 4 * (kb & 1) + q, sc, mm);
-                mv[q] = static_cast<_Float16>(static_cast<float>(mm));
+                scale_min(hdr.y, hdr.z, hdr.w, q, sc, mm);
+                sc2[rt][q] = static_cast<uint32_t>(sc) * 0x00010001u;
+                const _Float16 mh = static_cast<_Float16>(static_cast<float>(mm));
+                if (q < 4) mv[q] = mh;
+                else mv[q - 4] = (kb & 1) ? mh : mv[q - 4];
             }
             qb[rt] = mv;
         }
-        // the wave's tokens' sub-block sums (A of the min-term product)
-        half4_t qa[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            qa[tt] = *reinterpret_cast<const half4_t *>(
-                xs + (static_cast<int64_t>(s) * nblocks + tbk) * kMinBlock + ((wt * 4 + tt) * 64 + lane) * 8);
-        }
 
-        float4_t P[4][4];
+        float4_t P[RT][TT];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
+            constexpr int kCur[2] = {(2 * S3) % 3, (2 * S3 + 1) % 3};
+            constexpr int kAhead[2] = {(2 * S3 + 2) % 3, (2 * S3 + 3) % 3};
             const int h = 2 * s + half;
-            if (h + 1 < 2 * nsb) {
-                dma_a(h + 1, (h + 1) & 1);
-                if (half == 1) dma_w(s + 1, (s + 1) & 1);
-            }
-            const uint8_t *al = a_lds[half];
-            uint2 codes[4];
+            const uint8_t *al = abuf[kCur[half]];
+            uint2 codes[RT];
 #pragma unroll
             for (int sp = 0; sp < 4; ++sp) {
                 const int j = 4 * half + sp;  // sub-block of the super-block
-                half8_t a[4];
+                half8_t a[TT];
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
-                    a[tt] = *reinterpret_cast<const half8_t *>(al + (((wt * 4 + tt) * 4 + sp) * 64 + lane) * 16);
+                for (int tt = 0; tt < TT; ++tt)
+                    a[tt] = *reinterpret_cast<const half8_t *>(al + (((wt * TT + tt) * 4 + sp) * 64 + lane) * 16);
                 if ((sp & 1) == 0) {
                     // 8 code bytes of group j/2 for this lane's k-group
 #pragma unroll
-                    for (int rt = 0; rt < 4; ++rt)
-                        codes[rt] = *reinterpret_cast<const uint2 *>(wl + (wr * 64 + rt * 16 + col) * kBlockBytes + 16 +
-                                                                     32 * (j >> 1) + 8 * kb);
+                    for (int rt = 0; rt < RT; ++rt)
+                        codes[rt] = *reinterpret_cast<const uint2 *>(wl + (wr * 16 * RT + rt * 16 + col) * kBlockBytes +
+                                                                     16 + 32 * (j >> 1) + 8 * kb);
                 }
                 const int shn = (sp & 1) ? 4 : 0;
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    int sc, mm;
-                    scale_min(hdr[rt].y, hdr[rt].z, hdr[rt].w, j, sc, mm);
-                    const uint32_t sc2 = static_cast<uint32_t>(sc) * 0x00010001u;
-                    const uint32_t v0 = pair_operand((codes[rt].x >> shn) & 0x000f000fu, sc2);
-                    const uint32_t v1 = pair_operand((codes[rt].x >> (8 + shn)) & 0x000f000fu, sc2);
-                    const uint32_t v2 = pair_operand((codes[rt].y >> shn) & 0x000f000fu, sc2);
-                    const uint32_t v3 = pair_operand((codes[rt].y >> (8 + shn)) & 0x000f000fu, sc2);
+                for (int rt = 0; rt < RT; ++rt) {
+                    const uint32_t v0 = pair_operand((codes[rt].x >> shn) & 0x000f000fu, sc2[rt][j]);
+                    const uint32_t v1 = pair_operand((codes[rt].x >> (8 + shn)) & 0x000f000fu, sc2[rt][j]);
+                    const uint32_t v2 = pair_operand((codes[rt].y >> shn) & 0x000f000fu, sc2[rt][j]);
+                    const uint32_t v3 = pair_operand((codes[rt].y >> (8 + shn)) & 0x000f000fu, sc2[rt][j]);
                     const half8_t b = as_half8(u32x4_t{v0, v1, v2, v3}) - k1024;  // sc*q, exact
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt)
+                    for (int tt = 0; tt < TT; ++tt)
                         P[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tt], b, j == 0 ? zero : P[rt][tt], 0, 0, 0);
                 }
             }
-            // the next step's copies have landed; every wave is done with this step's buffers
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+            dma_a(h + 2, abuf[kAhead[half]]);
+            if (half == 1) dma_w(s + 2, wbuf[(S3 + 2) % 3]);
+            // Copies land in issue order.  At the end of the first step the
+            // next step's activations (issued at the end of the previous step)
+            // must have landed; after them came this super-block's min-term
+            // loads (TT) and the activations two steps ahead (8).  At the end
+            // of the second step the activations of the next step (issued at
+            // the end of the first) must have landed, and with them the
+            // min-term loads and the next super-block's weights (issued a
+            // super-block ago); after them only this step's copies (8 + 5).
+            if (half == 0) {
+                __builtin_amdgcn_s_waitcnt(wait_vm(TT + 8));
+            } else {
+                __builtin_amdgcn_s_waitcnt(wait_vm(8 + 5));
+                // finish super-block s: acc += d * P - dmin * Q
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt) {
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) {
+                        const float4_t q = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[tt], qb[rt], zero, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[rt][tt][r] += dd[rt] * P[rt][tt][r] - dm[rt] * q[r];
+                    }
+                }
+            }
+            barrier();
         }
-        // finish super-block s: acc += d * P - dmin * Q
+    };
+
+    dma_w(0, w0);
+    dma_w(1, w1);
+    dma_a(0, a0);
+    dma_a(1, a1);
+    // step 0's activations and super-block 0's weights have landed (step 1's
+    // activations may still fly: 8 copies)
+    __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    barrier();
+    for (int s = 0; s < nsb; s += 3) {
+        super_block(ic<0>{}, s);
+        if (s + 1 < nsb) super_block(ic<1>{}, s + 1);
+        if (s + 2 < nsb) super_block(ic<2>{}, s + 2);
+    }
+    // no copy may still be writing LDS when the workgroup ends
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+    // lane: row col of each row tile, tokens 4*kb .. 4*kb+3 of each token tile
+    float *pk = part + static_cast<int64_t>(ks) * m * n;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
+        const int64_t row = row0 + wr * 16 * RT + rt * 16 + col;
+        if (row >= n) continue;
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const float4_t q = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[tt], qb[rt], zero, 0, 0, 0);
+        for (int tt = 0; tt < TT; ++tt) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[rt][tt][r] += dd[rt] * P[rt][tt][r] - dm[rt] * q[r];
+            for (int r = 0; r < 4; ++r) {
+                const int64_t tok = tok0 + wt * 16 * TT + tt * 16 + kb * 4 + r;
+                if (tok >= m) continue;
+                if (ksplit == 1) y[tok * n + row] = static_cast<YT>(acc[rt][tt][r]);
+                else pk[tok * n + row] = acc[rt][tt][r];
             }
         }
     }
+}
 
-    // lane: row col of each row tile, tokens 4*kb .. 4*kb+3 of each token tile
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const int64_t row = row0 + wr * 64 + rt * 16 + col;
-        if (row >= n) continue;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t tok = tok0 + wt * 64 + tt * 16 + kb * 4 + r;
-                if (tok < m) y[tok * n + row] = static_cast<YT>(acc[rt][tt][r]);
-            }
-        }
+// y = the K parts added in order (part[0] + part[1] + ...), rounded once to YT.
+template <typename YT>
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *__restrict__ part, YT *__restrict__ y,
+                                                             int64_t count, int ksplit) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < count; i += stride) {
+        float v = part[i];
+        for (int s = 1; s < ksplit; ++s) v += part[static_cast<int64_t>(s) * count + i];
+        y[i] = static_cast<YT>(v);
     }
 }
 
@@ -281,28 +379,49 @@ hipError_t launch_prefill(const uint8_t *w, const _Float16 *x, void *y, bool y_f
     const int64_t nsb = k / kBlockWeights;
     const int64_t xa_bytes = mpad * k * 2;
     const int64_t xs_bytes = nsb * nblocks * kMinBlock;
+    // Too few tiles to fill the CUs: split K across workgroups (each keeps
+    // at least 4 super-blocks), partial tiles added by a second kernel.
+    const int64_t tiles = nrb * nblocks;
+    const int64_t want = (2 * static_cast<int64_t>(device_cu_count()) + tiles - 1) / tiles;
+    int64_t ksplit = want < nsb / 4 ? want : nsb / 4;
+    if (ksplit < 1) ksplit = 1;
+    const int64_t part_bytes = ksplit > 1 ? ksplit * m * n * 4 : 0;
     uint8_t *scratch = nullptr;
-    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&scratch), static_cast<size_t>(xa_bytes + xs_bytes),
-                                  stream);
+    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&scratch),
+                                  static_cast<size_t>(xa_bytes + xs_bytes + part_bytes), stream);
     if (e != hipSuccess) return e;
     uint8_t *xa = scratch;
     uint8_t *xs = scratch + xa_bytes;
+    float *part = reinterpret_cast<float *>(scratch + xa_bytes + xs_bytes);
     const int64_t prep_threads = mpad * (k / 8);
     hipLaunchKernelGGL(prefill_prep_kernel, dim3(static_cast<unsigned>((prep_threads + 255) / 256)), dim3(256), 0,
                        stream, x, xa, xs, m, mpad, k);
     e = hipGetLastError();
     if (e == hipSuccess) {
-        const dim3 grid(static_cast<unsigned>(nrb * nblocks));
+        const dim3 grid(static_cast<unsigned>(tiles * ksplit));
         const int64_t rb = (k / kBlockWeights) * kBlockBytes;
+        const int nb = static_cast<int>(nblocks), nr = static_cast<int>(nrb), ksp = static_cast<int>(ksplit);
         if (y_f16) {
-            hipLaunchKernelGGL(prefill_mfma_kernel<_Float16>, grid, dim3(256), 0, stream, w, xa, xs,
-                               static_cast<_Float16 *>(y), m, n, k, rb, static_cast<int>(nblocks),
-                               static_cast<int>(nrb));
+            hipLaunchKernelGGL((prefill_mfma_kernel<_Float16, kPfRT, kPfTT>), grid, dim3(256), 0, stream, w, xa, xs,
+                               static_cast<_Float16 *>(y), part, m, n, k, rb, nb, nr, ksp);
         } else {
-            hipLaunchKernelGGL(prefill_mfma_kernel<float>, grid, dim3(256), 0, stream, w, xa, xs,
-                               static_cast<float *>(y), m, n, k, rb, static_cast<int>(nblocks), static_cast<int>(nrb));
+            hipLaunchKernelGGL((prefill_mfma_kernel<float, kPfRT, kPfTT>), grid, dim3(256), 0, stream, w, xa, xs,
+                               static_cast<float *>(y), part, m, n, k, rb, nb, nr, ksp);
         }
         e = hipGetLastError();
+        if (e == hipSuccess && ksplit > 1) {
+            const int64_t count = m * n;
+            const int64_t need = (count + 255) / 256;
+            const dim3 rg(static_cast<unsigned>(need < 8192 ? need : 8192));
+            if (y_f16) {
+                hipLaunchKernelGGL(prefill_reduce_kernel<_Float16>, rg, dim3(256), 0, stream, part,
+                                   static_cast<_Float16 *>(y), count, ksp);
+            } else {
+                hipLaunchKernelGGL(prefill_reduce_kernel<float>, rg, dim3(256), 0, stream, part,
+                                   static_cast<float *>(y), count, ksp);
+            }
+            e = hipGetLastError();
+        }
     }
     const hipError_t f = hipFreeAsync(scratch, stream);
     return e != hipSuccess ? e : f;
