@@ -11,7 +11,9 @@ every step streams its weights from HBM).  Inputs are seeded synthetic data of
 the pages' value distributions (q4_dequant_gemv_amd/inputs.py).
 
 Prints ONE JSON line.  `value` is step weight bytes / mean step time over K
-steps bracketed by HIP events on the launch stream.  `roofline` covers the
+steps bracketed by HIP events on the launch stream; by default the K steps
+are captured once into a HIP graph and the timed region is one replay of it
+(`--eager` times plain launches; both rates are in the line).  `roofline` covers the
 dominant kernel (the lm_head GEMV): algorithmic bytes per launch / mean launch
 time over K back-to-back launches, again between events on the launch stream.  `traffic` comes from the
 committed rocprofv3 counter summary (profiles/traffic_lm_head_9b.json) when it
@@ -63,6 +65,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-batched", action="store_true", help="skip the skinny-GEMM timings")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the steps as eager launches instead of one captured HIP graph")
     ap.add_argument("--sweep", action="store_true",
                     help="also time every kernel at every config shape (table on stderr)")
     ap.add_argument("--case", default=None,
@@ -114,30 +118,54 @@ def main():
     step_weight_bytes = sum(wbytes.values())
     stream = torch.cuda.current_stream()
 
-    def step():
-        q4k.fused_swiglu(W["gate_9b"], W["up_9b"], x, h=h, stream=stream)
-        q4k.gemv(W["down_9b"], h, y=y, stream=stream)
-        q4k.gemv(W["lm_head_9b"], y, y=logits, stream=stream)
+    def step(s=stream):
+        q4k.fused_swiglu(W["gate_9b"], W["up_9b"], x, h=h, stream=s)
+        q4k.gemv(W["down_9b"], h, y=y, stream=s)
+        q4k.gemv(W["lm_head_9b"], y, y=logits, stream=s)
 
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # Timed region 1: K whole steps, bracketed by two events on the launch
-    # stream (no events between the kernels: each one costs microseconds).
+    def time_eager():
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            step()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps
+
+    # Timed region 1: K whole steps between two events on the launch stream
+    # (no events between the kernels).  By default the K steps are captured
+    # once into a HIP graph (the way a decode loop is deployed) and the timed
+    # region is one replay of it; the eager rate is reported beside it.
     log(f"[bench] timing {args.steps} steps")
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    eager_ms = time_eager()
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
+    if args.eager:
+        ms_per_step = eager_ms
+        launch = "eager launches"
+    else:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                step(None)  # the capture stream
+        graph.replay()  # warm replay
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = start.elapsed_time(end) / args.steps
+        launch = f"one HIP graph of {args.steps} steps, replayed once"
+        del graph
     wall = time.perf_counter() - t0
-    ms_per_step = start.elapsed_time(end) / args.steps
     value = step_weight_bytes / (ms_per_step * 1e-3) / 1e9
 
     # Timed region 2, per kernel: K launches of that kernel alone, back to
@@ -263,6 +291,8 @@ def main():
             "workload": "qwen3.5-9b-shaped decode FFN + lm_head at batch 1: fused gate+up SwiGLU "
                         "(2 x 12288x4096), down (4096x12288), untied lm_head (248320x4096), Q4_K weights, f32 activations",
             "weight_bytes_per_step": step_weight_bytes,
+            "launch": launch,
+            "eager_ms_per_step": round(eager_ms, 5),
             "frac_hbm_peak_step": round(value / HBM_PEAK_GBS, 4),
             "kernels": kernels,
             "batched_9b_ffn": batched,

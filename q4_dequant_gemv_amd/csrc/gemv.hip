@@ -200,13 +200,21 @@ struct MatTable {
     int count;
 };
 
-// XT, YT: activation and output element types (float or _Float16).
-template <class F, typename XT, typename YT, int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES>
+// XT, YT: activation and output element types (float or _Float16).  RES:
+// some matrix of the table has a residual.  Only then does the store path
+// load it: a load there, though rarely executed, makes the compiler's wait
+// counts in the streaming loop more conservative.  RPG: rows per lane group
+// and iteration (the lane takes its group of RPG rows, 64/LPR rows apart),
+// which puts RPG rows per buffer in flight with the same activation
+// registers.
+template <class F, typename XT, typename YT, int LPR, bool SWIGLU, bool RES, int NB, int BLOCK, int MIN_WAVES,
+          int RPG>
 __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable mt, const uint8_t *__restrict__ wu,
                                                                 const XT *x, int ngroups, int64_t row_bytes) {
     static_assert(NB >= 2, "at least one row in flight");
     constexpr int NMAT = SWIGLU ? 2 : 1;
-    constexpr int kRowsPerWave = kWave / LPR;
+    constexpr int kRowsPerGroup = kWave / LPR;  // rows per wave and row slot q
+    constexpr int kRowsPerWave = RPG * kRowsPerGroup;
     constexpr int kWavesPerBlock = BLOCK / kWave;
     extern __shared__ __align__(16) unsigned char smem[];
     XGroup *xg = reinterpret_cast<XGroup *>(smem);
@@ -242,7 +250,7 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     };
     LoadCursor lc{0, 0, mt.it_begin[1], mt.tail_bytes[0], mt.w[0]};
     RowCursor rc{0, 0, mt.it_begin[1], mt.n[0], static_cast<YT *>(mt.y[0]), mt.r[0]};
-    auto issue = [&](RowLoads<F, NMAT> &b, int it) {
+    auto issue = [&](RowLoads<F, NMAT> (&b)[RPG], int it) {
         while (it >= lc.end && lc.mi + 1 < count) {
             ++lc.mi;
             lc.begin = lc.end;
@@ -257,7 +265,13 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
         // in scalar registers whatever the compiler concluded across the joins
         const uint8_t *wbase = reinterpret_cast<const uint8_t *>(wave_uniform(reinterpret_cast<int64_t>(lc.w)));
 #pragma unroll
-        for (int m2 = 0; m2 < NMAT; ++m2) F::issue(b.m[m2], stream_rsrc((m2 == 0 ? wbase : wu) + off, nrec), g);
+        for (int q = 0; q < RPG; ++q) {
+            const int sh = q * kRowsPerGroup * static_cast<int>(row_bytes);
+            const int nq = nrec > sh ? nrec - sh : 0;
+#pragma unroll
+            for (int m2 = 0; m2 < NMAT; ++m2)
+                F::issue(b[q].m[m2], stream_rsrc((m2 == 0 ? wbase : wu) + off + sh, nq), g);
+        }
     };
     auto row_cursor = [&](int it) {
         while (it >= rc.end && rc.mi + 1 < count) {
@@ -282,7 +296,7 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     // memory clobber: no instruction, only an ordering point for the compiler;
     // x is deliberately not __restrict__ so its loads cannot move across it)
     asm volatile("" ::: "memory");
-    RowLoads<F, NMAT> buf[NB];
+    RowLoads<F, NMAT> buf[NB][RPG];
 #pragma unroll
     for (int b = 0; b + 1 < NB; ++b) issue(buf[b], it0 + b * nwaves);
 
@@ -306,7 +320,10 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     const float *rp = nullptr;
     int win = 0;
     auto flush = [&]() {
-        if (yp != nullptr) *yp = static_cast<YT>(rp != nullptr ? yv + *rp : yv);
+        if (yp != nullptr) {
+            if constexpr (RES) *yp = static_cast<YT>(rp != nullptr ? yv + *rp : yv);
+            else *yp = static_cast<YT>(yv);
+        }
         yp = nullptr;
         win = 0;
     };
@@ -319,7 +336,7 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     // others.  Each wave therefore lowers its own priority as the share of its
     // iterations still to do drops (1/2, 1/4, 1/8): a wave that is behind
     // outranks the ones ahead of it, and the finish times close up.
-    const int mine = (niters - it0 + nwaves - 1) / nwaves;
+    const int my_iters = (niters - it0 + nwaves - 1) / nwaves;
     if (it0 < niters) {
         for (int it = it0;; it += NB * nwaves) {
 #pragma unroll
@@ -327,25 +344,29 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
                 const int cur = it + b * nwaves;
                 {
                     const int left = (niters - cur + nwaves - 1) / nwaves;
-                    if (2 * left > mine) __builtin_amdgcn_s_setprio(3);
-                    else if (4 * left > mine) __builtin_amdgcn_s_setprio(2);
-                    else if (8 * left > mine) __builtin_amdgcn_s_setprio(1);
+                    if (2 * left > my_iters) __builtin_amdgcn_s_setprio(3);
+                    else if (4 * left > my_iters) __builtin_amdgcn_s_setprio(2);
+                    else if (8 * left > my_iters) __builtin_amdgcn_s_setprio(1);
                     else __builtin_amdgcn_s_setprio(0);
                 }
                 issue(buf[(b + NB - 1) % NB], cur + (NB - 1) * nwaves);
                 row_cursor(cur);
-                const int64_t row = static_cast<int64_t>(cur - rc.begin) * kRowsPerWave + slot;
-                const bool rok = row < rc.n;
-                float acc[NMAT];
-                lane_dot(buf[b], g, xr, rok && g.ok, acc);
 #pragma unroll
-                for (int m2 = 0; m2 < NMAT; ++m2) acc[m2] = lane_group_sum<LPR>(acc[m2]);
-                const float out = SWIGLU ? silu(acc[0]) * acc[1] : acc[0];
-                const bool mine = sub == win;
-                yv = mine ? out : yv;
-                yp = mine ? (rok ? rc.y + row : nullptr) : yp;
-                rp = mine ? (rc.r != nullptr ? rc.r + row : nullptr) : rp;
-                if (++win == LPR) flush();
+                for (int q = 0; q < RPG; ++q) {
+                    const int64_t row =
+                        static_cast<int64_t>(cur - rc.begin) * kRowsPerWave + q * kRowsPerGroup + slot;
+                    const bool rok = row < rc.n;
+                    float acc[NMAT];
+                    lane_dot(buf[b][q], g, xr, rok && g.ok, acc);
+#pragma unroll
+                    for (int m2 = 0; m2 < NMAT; ++m2) acc[m2] = lane_group_sum<LPR>(acc[m2]);
+                    const float out = SWIGLU ? silu(acc[0]) * acc[1] : acc[0];
+                    const bool mine = sub == win;
+                    yv = mine ? out : yv;
+                    yp = mine ? (rok ? rc.y + row : nullptr) : yp;
+                    if constexpr (RES) rp = mine ? (rc.r != nullptr ? rc.r + row : nullptr) : rp;
+                    if (++win == LPR) flush();
+                }
                 if (cur + nwaves >= niters) goto done;
             }
         }
@@ -548,16 +569,17 @@ int resident_blocks_per_cu(Kernel kern, int block, size_t lds, std::atomic<int> 
 }
 
 // One launch of the batch-1 kernel over `count` matrices (all with k columns).
-template <class F, typename XT, typename YT, int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES>
-hipError_t launch_fast(const GemvJob *jobs, int count, const uint8_t *wu, const void *x, int64_t k,
-                       hipStream_t stream) {
-    auto kern = gemv_kernel<F, XT, YT, LPR, SWIGLU, NB, BLOCK, MIN_WAVES>;
+template <class F, typename XT, typename YT, int LPR, bool SWIGLU, bool RES, int NB, int BLOCK, int MIN_WAVES,
+          int RPG>
+hipError_t launch_fast_kernel(const GemvJob *jobs, int count, const uint8_t *wu, const void *x, int64_t k,
+                              hipStream_t stream) {
+    auto kern = gemv_kernel<F, XT, YT, LPR, SWIGLU, RES, NB, BLOCK, MIN_WAVES, RPG>;
     const int ngroups = static_cast<int>(k / 64);
     const int64_t row_bytes = F::row_bytes(k);
     const size_t lds = static_cast<size_t>(ngroups) * sizeof(XGroup);
     static std::atomic<int> cache[kMaxDevices];
     const int per_cu = resident_blocks_per_cu(kern, BLOCK, lds, cache);
-    constexpr int kRowsPerWave = kWave / LPR;
+    constexpr int kRowsPerWave = RPG * (kWave / LPR);
     MatTable mt{};
     mt.count = count;
     int64_t total = 0;
@@ -581,6 +603,20 @@ hipError_t launch_fast(const GemvJob *jobs, int count, const uint8_t *wu, const 
     hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, mt, wu, static_cast<const XT *>(x), ngroups,
                        row_bytes);
     return hipGetLastError();
+}
+
+template <class F, typename XT, typename YT, int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES, int RPG = 1>
+hipError_t launch_fast(const GemvJob *jobs, int count, const uint8_t *wu, const void *x, int64_t k,
+                       hipStream_t stream) {
+    bool res = false;
+    for (int i = 0; i < count; ++i) res = res || jobs[i].r != nullptr;
+    if constexpr (std::is_same_v<XT, float> && std::is_same_v<YT, float> && !SWIGLU) {
+        if (res) {
+            return launch_fast_kernel<F, XT, YT, LPR, SWIGLU, true, NB, BLOCK, MIN_WAVES, RPG>(jobs, count, wu, x, k,
+                                                                                              stream);
+        }
+    }
+    return launch_fast_kernel<F, XT, YT, LPR, SWIGLU, false, NB, BLOCK, MIN_WAVES, RPG>(jobs, count, wu, x, k, stream);
 }
 
 template <class F, typename XT, typename YT, int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
@@ -633,6 +669,9 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const void *x, co
 #ifndef Q4K_LARGE_NB
 #define Q4K_LARGE_NB 2
 #endif
+#ifndef Q4K_LARGE_RPG
+#define Q4K_LARGE_RPG 1
+#endif
 #ifndef Q4K_SMALL_BLOCK
 #define Q4K_SMALL_BLOCK 256
 #endif
@@ -672,8 +711,8 @@ hipError_t dispatch_lpr(const GemvJob *jobs, int count, const uint8_t *wu, const
             return launch_fast<F, XT, YT, LPR, false, Q4K_SMALL_NB, Q4K_SMALL_BLOCK, Q4K_SMALL_MINW>(jobs, count, wu, x, k,
                                                                                              stream);
         }
-        return launch_fast<F, XT, YT, LPR, false, Q4K_LARGE_NB, Q4K_LARGE_BLOCK, Q4K_LARGE_MINW>(jobs, count, wu, x, k,
-                                                                                          stream);
+        return launch_fast<F, XT, YT, LPR, false, Q4K_LARGE_NB, Q4K_LARGE_BLOCK, Q4K_LARGE_MINW, Q4K_LARGE_RPG>(
+            jobs, count, wu, x, k, stream);
     }
 }
 

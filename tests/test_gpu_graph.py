@@ -1,0 +1,68 @@
+"""HIP graph capture of the decode calls: a graph holding a fused SwiGLU, a
+K-split GEMV with a residual, a multi-matrix GEMV, a batch-1 GEMV and a Q8_0
+GEMV, replayed several times with the program's own eager work and
+synchronizations between replays; every replay must equal the eager results
+bit for bit (no call on this path records a memset or allocates)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from gpu_helpers import to_dev
+from q4_dequant_gemv_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_step_graph_replays_equal_eager():
+    import torch
+
+    from q4_dequant_gemv_amd import q4k
+
+    torch.cuda.init()
+    k, nff, nv = 2048, 6144, 5000
+    wg = to_dev(inputs.make_q4k(nff, k, config_id=80, tensor_id=0).reshape(-1))
+    wu = to_dev(inputs.make_q4k(nff, k, config_id=80, tensor_id=1).reshape(-1))
+    wd = to_dev(inputs.make_q4k(k, nff, config_id=80, tensor_id=2).reshape(-1))
+    wq = [to_dev(inputs.make_q4k(n, k, config_id=80, tensor_id=3 + i).reshape(-1)) for i, n in enumerate((512, 64, 3))]
+    wl = to_dev(inputs.make_q4k(nv, k, config_id=80, tensor_id=6).reshape(-1))
+    w8 = to_dev(inputs.make_q8_0(777, k, config_id=80, tensor_id=7).reshape(-1))
+    x = to_dev(inputs.make_x(1, k, config_id=80)[0])
+    r = to_dev(inputs.make_x(1, k, config_id=80, tensor_id=101)[0])
+    h = torch.empty(nff, device="cuda")
+    y = torch.empty(k, device="cuda")
+    qs = [torch.empty(n, device="cuda") for n in (512, 64, 3)]
+    lg = torch.empty(nv, device="cuda")
+    y8 = torch.empty(777, device="cuda")
+
+    def step():
+        q4k.fused_swiglu(wg, wu, x, h=h)
+        q4k.gemv_residual(wd, h, r, y=y)
+        q4k.gemv_multi(wq, y, ys=qs, ns=[512, 64, 3])
+        q4k.gemv(wl, y, y=lg)
+        q4k.q8_0_gemv(w8, y, y=y8)
+
+    outs = (h, y, *qs, lg, y8)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on a side stream before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (t, e) in enumerate(zip(outs, ref)):
+            assert torch.equal(t, e), f"replay {rep}: output {i} differs from the eager run"
+        step()  # the program's own eager work between replays
+        torch.cuda.synchronize()
+        assert np.isfinite(lg.cpu().numpy()).all()
