@@ -25,11 +25,12 @@
  *  - All pointers except `stream` are DEVICE pointers owned by the caller.
  *    Every call only enqueues work on `stream` (a hipStream_t passed as
  *    void*; NULL means the null stream) and returns; it never synchronises.
- *    Results are ready when the stream is.  Only q4k_gemv_batched with
- *    m >= 2 needs device scratch: it takes it stream-ordered from the
- *    device's default memory pool (hipMallocAsync / hipFreeAsync on
- *    `stream`), 536 * ceil(m'/16) * k/8 bytes for m' = min(m, 64) tokens
- *    (about 1.1 MB at m = 64, k = 4096).
+ *    Results are ready when the stream is.  Only the batched calls with
+ *    m >= 2 and the prefill GEMM need device scratch: they take it
+ *    stream-ordered from the device's default memory pool (hipMallocAsync /
+ *    hipFreeAsync on `stream`), 536 * ceil(m'/16) * k/8 bytes for the batched
+ *    call with m' = min(m, 64) tokens (about 1.1 MB at m = 64, k = 4096), or,
+ *    through their *_ws forms, from a workspace the caller passes in.
  *  - Arguments are validated on the host before anything is enqueued; on any
  *    error nothing is launched and the status says why.  Launch failures are
  *    reported as Q4K_ERR_LAUNCH.
@@ -207,6 +208,37 @@ Q4K_API q4k_status q4k_gemv_batched_dt(const void *w, const void *x, q4k_dtype x
  */
 Q4K_API q4k_status q4k_prefill_gemm(const void *w, const void *x, void *y, q4k_dtype y_dtype, int64_t m, int64_t n,
                                     int64_t k, void *stream);
+
+/*
+ * Caller-provided scratch for the two calls above that need any, so that the
+ * library allocates nothing (a caller that keeps its own pool, or records the
+ * calls into a HIP graph without allocation nodes).
+ *
+ * q4k_gemv_batched_workspace_size / q4k_prefill_workspace_size write to
+ * *bytes the scratch that q4k_gemv_batched_dt / q4k_prefill_gemm need for
+ * these dtypes and sizes on the CURRENT device (the split of K follows the
+ * device's compute-unit count); 0 where none is needed (m <= 1, k == 0, an
+ * empty call).  Same shape checks and status codes as the calls themselves;
+ * bytes == NULL is Q4K_ERR_INVALID_ARG.  Nothing is enqueued.
+ *
+ * q4k_gemv_batched_ws / q4k_prefill_gemm_ws compute exactly what
+ * q4k_gemv_batched_dt / q4k_prefill_gemm compute (the same kernels, the same
+ * order of sums) with `workspace`, a device buffer of workspace_bytes owned by
+ * the caller, in place of the stream-ordered allocation.  The workspace must
+ * be 256-byte aligned, hold at least the queried size (else
+ * Q4K_ERR_INVALID_ARG; it may be NULL when that size is 0) and overlap none of
+ * w, x, y (Q4K_ERR_INVALID_ARG).  Its contents are garbage before and after
+ * the call; the call uses it until the stream reaches the end of the call's
+ * work, so calls in flight at the same time need separate workspaces.
+ */
+Q4K_API q4k_status q4k_gemv_batched_workspace_size(q4k_dtype x_dtype, q4k_dtype y_dtype, int64_t m, int64_t n,
+                                                   int64_t k, int64_t *bytes);
+Q4K_API q4k_status q4k_gemv_batched_ws(const void *w, const void *x, q4k_dtype x_dtype, void *y, q4k_dtype y_dtype,
+                                       int64_t m, int64_t n, int64_t k, void *workspace, int64_t workspace_bytes,
+                                       void *stream);
+Q4K_API q4k_status q4k_prefill_workspace_size(q4k_dtype y_dtype, int64_t m, int64_t n, int64_t k, int64_t *bytes);
+Q4K_API q4k_status q4k_prefill_gemm_ws(const void *w, const void *x, void *y, q4k_dtype y_dtype, int64_t m, int64_t n,
+                                       int64_t k, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * Fused gate/up GEMV with SwiGLU ("qualia_core_db/inference/cuda_lane/mod.rs",

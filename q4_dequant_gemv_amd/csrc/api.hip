@@ -88,6 +88,23 @@ hipError_t launch_fill_zero_f16(_Float16 *y, int64_t count, hipStream_t stream) 
     return hipGetLastError();
 }
 
+hipError_t ws_acquire(Workspace &ws, int64_t total, hipStream_t stream, uint8_t **out, bool *owned) {
+    *owned = false;
+    *out = nullptr;
+    if (ws.ptr != nullptr) {
+        if (total > ws.bytes) return hipErrorInvalidValue;
+        *out = ws.ptr;
+        return hipSuccess;
+    }
+    const hipError_t e = hipMallocAsync(reinterpret_cast<void **>(out), static_cast<size_t>(total), stream);
+    *owned = e == hipSuccess;
+    return e;
+}
+
+hipError_t ws_release(uint8_t *p, bool owned, hipStream_t stream) {
+    return owned ? hipFreeAsync(p, stream) : hipSuccess;
+}
+
 hipError_t launch_copy(float *y, const float *src, int64_t count, hipStream_t stream) {
     if (count == 0 || y == src) return hipSuccess;
     const int64_t need = (count + 255) / 256;
@@ -218,13 +235,17 @@ q4k_status q4k_gemv_batched(const void *w, const float *x, float *y, int64_t m, 
                                              static_cast<hipStream_t>(stream)));
 }
 
-q4k_status q4k_gemv_batched_dt(const void *w, const void *x, q4k_dtype x_dtype, void *y, q4k_dtype y_dtype,
-                               int64_t m, int64_t n, int64_t k, void *stream) {
+namespace {
+
+// Checks of q4k_gemv_batched_dt and its workspace form; on Q4K_OK with *run
+// set the call has work to launch.
+q4k_status check_batched(const void *w, const void *x, q4k_dtype x_dtype, const void *y, q4k_dtype y_dtype,
+                         int64_t m, int64_t n, int64_t k, bool *run, uint64_t *w_bytes) {
+    *run = false;
     if ((x_dtype != Q4K_F32 && x_dtype != Q4K_F16) || (y_dtype != Q4K_F32 && y_dtype != Q4K_F16)) {
         return Q4K_ERR_INVALID_ARG;
     }
-    uint64_t wb = 0;
-    const q4k_status s = check_shape(n, k, &wb);
+    const q4k_status s = check_shape(n, k, w_bytes);
     if (s != Q4K_OK) return s;
     if (m < 0) return Q4K_ERR_INVALID_ARG;
     if (m > 0 && (n > q4k::kMaxElems / m || (k > 0 && m > q4k::kMaxElems / k))) return Q4K_ERR_INVALID_ARG;
@@ -233,16 +254,17 @@ q4k_status q4k_gemv_batched_dt(const void *w, const void *x, q4k_dtype x_dtype, 
     const uint64_t xe = x_dtype == Q4K_F16 ? 2 : 4, ye = y_dtype == Q4K_F16 ? 2 : 4;
     if (!aligned(w, 16) || !aligned(x, xe) || !aligned(y, ye)) return Q4K_ERR_MISALIGNED;
     const uint64_t yb = static_cast<uint64_t>(m) * n * ye, xb = static_cast<uint64_t>(m) * k * xe;
-    if (overlap(y, yb, w, wb) || overlap(y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
-    return from_hip(q4k::launch_gemv_batched_dt(static_cast<const uint8_t *>(w), x, x_dtype == Q4K_F16, y,
-                                                y_dtype == Q4K_F16, m, n, k, static_cast<hipStream_t>(stream)));
+    if (overlap(y, yb, w, *w_bytes) || overlap(y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
+    *run = true;
+    return Q4K_OK;
 }
 
-q4k_status q4k_prefill_gemm(const void *w, const void *x, void *y, q4k_dtype y_dtype, int64_t m, int64_t n,
-                            int64_t k, void *stream) {
+// Checks of q4k_prefill_gemm and its workspace form.
+q4k_status check_prefill(const void *w, const void *x, const void *y, q4k_dtype y_dtype, int64_t m, int64_t n,
+                         int64_t k, bool *run, uint64_t *w_bytes) {
+    *run = false;
     if (y_dtype != Q4K_F32 && y_dtype != Q4K_F16) return Q4K_ERR_INVALID_ARG;
-    uint64_t wb = 0;
-    const q4k_status s = check_shape(n, k, &wb);
+    const q4k_status s = check_shape(n, k, w_bytes);
     if (s != Q4K_OK) return s;
     // the kernel addresses one 128-row block of weights with 32-bit offsets
     if (k > (int64_t{1} << 24)) return Q4K_ERR_UNSUPPORTED_SHAPE;
@@ -253,9 +275,133 @@ q4k_status q4k_prefill_gemm(const void *w, const void *x, void *y, q4k_dtype y_d
     const uint64_t ye = y_dtype == Q4K_F16 ? 2 : 4;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, ye)) return Q4K_ERR_MISALIGNED;
     const uint64_t yb = static_cast<uint64_t>(m) * n * ye, xb = static_cast<uint64_t>(m) * k * 2;
-    if (overlap(y, yb, w, wb) || overlap(y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
+    if (overlap(y, yb, w, *w_bytes) || overlap(y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
+    *run = true;
+    return Q4K_OK;
+}
+
+// A caller's workspace, before its size is known: a non-negative size and,
+// when given, 256-byte alignment.
+q4k_status check_workspace_arg(const void *ws, int64_t ws_bytes) {
+    if (ws_bytes < 0) return Q4K_ERR_INVALID_ARG;
+    if (ws != nullptr && !aligned(ws, 256)) return Q4K_ERR_MISALIGNED;
+    return Q4K_OK;
+}
+
+// ... and once the call's need is known: large enough, apart from w, x, y.
+q4k_status check_workspace(const void *ws, int64_t ws_bytes, int64_t need, const void *w, uint64_t wb,
+                           const void *x, uint64_t xb, const void *y, uint64_t yb) {
+    if (need == 0) return Q4K_OK;
+    if (ws == nullptr || ws_bytes < need) return Q4K_ERR_INVALID_ARG;
+    const uint64_t b = static_cast<uint64_t>(need);
+    if (overlap(ws, b, w, wb) || overlap(ws, b, x, xb) || overlap(ws, b, y, yb)) return Q4K_ERR_INVALID_ARG;
+    return Q4K_OK;
+}
+
+}  // namespace
+
+q4k_status q4k_gemv_batched_dt(const void *w, const void *x, q4k_dtype x_dtype, void *y, q4k_dtype y_dtype,
+                               int64_t m, int64_t n, int64_t k, void *stream) {
+    bool run = false;
+    uint64_t wb = 0;
+    const q4k_status s = check_batched(w, x, x_dtype, y, y_dtype, m, n, k, &run, &wb);
+    if (s != Q4K_OK || !run) return s;
+    q4k::Workspace ws;
+    return from_hip(q4k::launch_gemv_batched_dt(static_cast<const uint8_t *>(w), x, x_dtype == Q4K_F16, y,
+                                                y_dtype == Q4K_F16, m, n, k, ws, static_cast<hipStream_t>(stream)));
+}
+
+q4k_status q4k_gemv_batched_workspace_size(q4k_dtype x_dtype, q4k_dtype y_dtype, int64_t m, int64_t n, int64_t k,
+                                           int64_t *bytes) {
+    if (bytes == nullptr) return Q4K_ERR_INVALID_ARG;
+    *bytes = 0;
+    if ((x_dtype != Q4K_F32 && x_dtype != Q4K_F16) || (y_dtype != Q4K_F32 && y_dtype != Q4K_F16)) {
+        return Q4K_ERR_INVALID_ARG;
+    }
+    uint64_t wb = 0;
+    const q4k_status s = check_shape(n, k, &wb);
+    if (s != Q4K_OK) return s;
+    if (m < 0) return Q4K_ERR_INVALID_ARG;
+    if (m > 0 && (n > q4k::kMaxElems / m || (k > 0 && m > q4k::kMaxElems / k))) return Q4K_ERR_INVALID_ARG;
+    q4k::Workspace ws;
+    ws.query = true;
+    const hipError_t e = q4k::launch_gemv_batched_dt(nullptr, nullptr, x_dtype == Q4K_F16, nullptr,
+                                                     y_dtype == Q4K_F16, m, n, k, ws, nullptr);
+    if (e != hipSuccess) return Q4K_ERR_LAUNCH;
+    *bytes = ws.need;
+    return Q4K_OK;
+}
+
+q4k_status q4k_gemv_batched_ws(const void *w, const void *x, q4k_dtype x_dtype, void *y, q4k_dtype y_dtype,
+                               int64_t m, int64_t n, int64_t k, void *workspace, int64_t workspace_bytes,
+                               void *stream) {
+    bool run = false;
+    uint64_t wb = 0;
+    q4k_status s = check_batched(w, x, x_dtype, y, y_dtype, m, n, k, &run, &wb);
+    if (s == Q4K_OK) s = check_workspace_arg(workspace, workspace_bytes);
+    if (s != Q4K_OK || !run) return s;
+    int64_t need = 0;
+    s = q4k_gemv_batched_workspace_size(x_dtype, y_dtype, m, n, k, &need);
+    if (s != Q4K_OK) return s;
+    const uint64_t xe = x_dtype == Q4K_F16 ? 2 : 4, ye = y_dtype == Q4K_F16 ? 2 : 4;
+    s = check_workspace(workspace, workspace_bytes, need, w, wb, x, static_cast<uint64_t>(m) * k * xe, y,
+                        static_cast<uint64_t>(m) * n * ye);
+    if (s != Q4K_OK) return s;
+    q4k::Workspace ws;
+    ws.ptr = static_cast<uint8_t *>(workspace);
+    ws.bytes = workspace_bytes;
+    return from_hip(q4k::launch_gemv_batched_dt(static_cast<const uint8_t *>(w), x, x_dtype == Q4K_F16, y,
+                                                y_dtype == Q4K_F16, m, n, k, ws, static_cast<hipStream_t>(stream)));
+}
+
+q4k_status q4k_prefill_gemm(const void *w, const void *x, void *y, q4k_dtype y_dtype, int64_t m, int64_t n,
+                            int64_t k, void *stream) {
+    bool run = false;
+    uint64_t wb = 0;
+    const q4k_status s = check_prefill(w, x, y, y_dtype, m, n, k, &run, &wb);
+    if (s != Q4K_OK || !run) return s;
+    q4k::Workspace ws;
     return from_hip(q4k::launch_prefill(static_cast<const uint8_t *>(w), static_cast<const _Float16 *>(x), y,
-                                        y_dtype == Q4K_F16, m, n, k, static_cast<hipStream_t>(stream)));
+                                        y_dtype == Q4K_F16, m, n, k, ws, static_cast<hipStream_t>(stream)));
+}
+
+q4k_status q4k_prefill_workspace_size(q4k_dtype y_dtype, int64_t m, int64_t n, int64_t k, int64_t *bytes) {
+    if (bytes == nullptr) return Q4K_ERR_INVALID_ARG;
+    *bytes = 0;
+    if (y_dtype != Q4K_F32 && y_dtype != Q4K_F16) return Q4K_ERR_INVALID_ARG;
+    uint64_t wb = 0;
+    const q4k_status s = check_shape(n, k, &wb);
+    if (s != Q4K_OK) return s;
+    if (k > (int64_t{1} << 24)) return Q4K_ERR_UNSUPPORTED_SHAPE;
+    if (m < 0) return Q4K_ERR_INVALID_ARG;
+    if (m > 0 && (n > q4k::kMaxElems / m || (k > 0 && m > q4k::kMaxElems / k))) return Q4K_ERR_INVALID_ARG;
+    q4k::Workspace ws;
+    ws.query = true;
+    const hipError_t e = q4k::launch_prefill(nullptr, nullptr, nullptr, y_dtype == Q4K_F16, m, n, k, ws, nullptr);
+    if (e != hipSuccess) return Q4K_ERR_LAUNCH;
+    *bytes = ws.need;
+    return Q4K_OK;
+}
+
+q4k_status q4k_prefill_gemm_ws(const void *w, const void *x, void *y, q4k_dtype y_dtype, int64_t m, int64_t n,
+                               int64_t k, void *workspace, int64_t workspace_bytes, void *stream) {
+    bool run = false;
+    uint64_t wb = 0;
+    q4k_status s = check_prefill(w, x, y, y_dtype, m, n, k, &run, &wb);
+    if (s == Q4K_OK) s = check_workspace_arg(workspace, workspace_bytes);
+    if (s != Q4K_OK || !run) return s;
+    int64_t need = 0;
+    s = q4k_prefill_workspace_size(y_dtype, m, n, k, &need);
+    if (s != Q4K_OK) return s;
+    const uint64_t ye = y_dtype == Q4K_F16 ? 2 : 4;
+    s = check_workspace(workspace, workspace_bytes, need, w, wb, x, static_cast<uint64_t>(m) * k * 2, y,
+                        static_cast<uint64_t>(m) * n * ye);
+    if (s != Q4K_OK) return s;
+    q4k::Workspace ws;
+    ws.ptr = static_cast<uint8_t *>(workspace);
+    ws.bytes = workspace_bytes;
+    return from_hip(q4k::launch_prefill(static_cast<const uint8_t *>(w), static_cast<const _Float16 *>(x), y,
+                                        y_dtype == Q4K_F16, m, n, k, ws, static_cast<hipStream_t>(stream)));
 }
 
 q4k_status q4k_fused_swiglu(const void *w_gate, const void *w_up, const float *x, float *h, int64_t n, int64_t k,
@@ -295,6 +441,6 @@ const char *q4k_status_string(q4k_status s) {
     return "unknown status";
 }
 
-int q4k_abi_version(void) { return 105; }
+int q4k_abi_version(void) { return 106; }
 
 }  // extern "C"

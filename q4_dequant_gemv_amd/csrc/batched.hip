@@ -444,7 +444,7 @@ namespace {
 // x: [m, k] of XT; y: [m, n] of YT.  An f16 output with K split across
 // workgroups is accumulated in f32 in the call's scratch, then converted.
 template <int NT, int MT, typename XT, typename YT>
-hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, int ksplit,
+hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, int ksplit, Workspace &ws,
                        hipStream_t stream) {
     constexpr int S = Q4K_BATCH_STAGE_SB;
     const int64_t nst = k / kStageK;
@@ -452,9 +452,14 @@ hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, i
     constexpr bool kF32Out = std::is_same_v<YT, float>;
     const bool staged = !kF32Out && ksplit > 1;
     const int64_t ny = ksplit > 1 ? static_cast<int64_t>(m) * n : 0;
+    const int64_t total = bytes + (staged ? ny * 4 : 0);
+    if (ws.query) {
+        if (total > ws.need) ws.need = total;
+        return hipSuccess;
+    }
     uint8_t *xc = nullptr;
-    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&xc),
-                                  static_cast<size_t>(bytes + (staged ? ny * 4 : 0)), stream);
+    bool owned = false;
+    hipError_t e = ws_acquire(ws, total, stream, &xc, &owned);
     if (e != hipSuccess) return e;
     float *acc_y = nullptr;  // where the matrix-core kernel accumulates with atomics
     if constexpr (kF32Out) acc_y = y;
@@ -484,7 +489,7 @@ hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, i
             e = hipGetLastError();
         }
     }
-    const hipError_t f = hipFreeAsync(xc, stream);
+    const hipError_t f = ws_release(xc, owned, stream);
     return e != hipSuccess ? e : f;
 }
 
@@ -499,7 +504,8 @@ hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, i
 #define Q4K_BATCH_NT_CAP 4
 #endif
 template <int MT, typename XT, typename YT>
-hipError_t dispatch_mt(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, hipStream_t stream) {
+hipError_t dispatch_mt(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, Workspace &ws,
+                       hipStream_t stream) {
     constexpr int kNtMax0 = MT == 1 ? 4 : (MT <= 3 ? 2 : 1);
     constexpr int kNtMax = kNtMax0 < Q4K_BATCH_NT_CAP ? kNtMax0 : Q4K_BATCH_NT_CAP;
     const int64_t cus = device_cu_count();
@@ -507,55 +513,58 @@ hipError_t dispatch_mt(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, i
     const int64_t per = n / (16 * cus);  // row tiles per CU with one row block each
     if (per >= 1 || nsb < 2) {
         const int64_t nt = per < 1 ? 1 : (per > kNtMax ? kNtMax : per);
-        if (nt >= 4) return launch_mfma<kNtMax, MT, XT, YT>(w, x, y, m, n, k, 1, stream);
-        if (nt == 3) return launch_mfma<(kNtMax < 3 ? kNtMax : 3), MT, XT, YT>(w, x, y, m, n, k, 1, stream);
-        if (nt == 2) return launch_mfma<(kNtMax < 2 ? kNtMax : 2), MT, XT, YT>(w, x, y, m, n, k, 1, stream);
-        return launch_mfma<1, MT, XT, YT>(w, x, y, m, n, k, 1, stream);
+        if (nt >= 4) return launch_mfma<kNtMax, MT, XT, YT>(w, x, y, m, n, k, 1, ws, stream);
+        if (nt == 3) return launch_mfma<(kNtMax < 3 ? kNtMax : 3), MT, XT, YT>(w, x, y, m, n, k, 1, ws, stream);
+        if (nt == 2) return launch_mfma<(kNtMax < 2 ? kNtMax : 2), MT, XT, YT>(w, x, y, m, n, k, 1, ws, stream);
+        return launch_mfma<1, MT, XT, YT>(w, x, y, m, n, k, 1, ws, stream);
     }
     // fewer than 16 rows per CU: the largest row blocks, K split to fill the CUs
     const int64_t nrb = (n + 16 * kNtMax - 1) / (16 * kNtMax);
     int64_t ksplit = (cus + nrb - 1) / nrb;
     if (ksplit > nsb) ksplit = nsb;
-    return launch_mfma<kNtMax, MT, XT, YT>(w, x, y, m, n, k, static_cast<int>(ksplit), stream);
+    return launch_mfma<kNtMax, MT, XT, YT>(w, x, y, m, n, k, static_cast<int>(ksplit), ws, stream);
 }
 
 }  // namespace
 
 template <typename XT, typename YT>
-hipError_t batched_slices(const uint8_t *w, const XT *x, YT *y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+hipError_t batched_slices(const uint8_t *w, const XT *x, YT *y, int64_t m, int64_t n, int64_t k, Workspace &ws,
+                          hipStream_t stream) {
     hipError_t e = hipSuccess;
     // up to 64 tokens per launch; the weights are re-read per 64-token slice
     for (int64_t t0 = 0; t0 < m; t0 += 64) {
         const int mt = static_cast<int>(m - t0 < 64 ? m - t0 : 64);
         const XT *xs = x + t0 * k;
         YT *ys = y + t0 * n;
-        if (mt <= 16) e = dispatch_mt<1>(w, xs, ys, mt, n, k, stream);
-        else if (mt <= 32) e = dispatch_mt<2>(w, xs, ys, mt, n, k, stream);
-        else if (mt <= 48) e = dispatch_mt<3>(w, xs, ys, mt, n, k, stream);
-        else e = dispatch_mt<4>(w, xs, ys, mt, n, k, stream);
+        if (mt <= 16) e = dispatch_mt<1>(w, xs, ys, mt, n, k, ws, stream);
+        else if (mt <= 32) e = dispatch_mt<2>(w, xs, ys, mt, n, k, ws, stream);
+        else if (mt <= 48) e = dispatch_mt<3>(w, xs, ys, mt, n, k, ws, stream);
+        else e = dispatch_mt<4>(w, xs, ys, mt, n, k, ws, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
 hipError_t launch_gemv_batched_dt(const uint8_t *w, const void *x, bool x_f16, void *y, bool y_f16, int64_t m,
-                                  int64_t n, int64_t k, hipStream_t stream) {
+                                  int64_t n, int64_t k, Workspace &ws, hipStream_t stream) {
     if (m == 0 || n == 0) return hipSuccess;
+    if (ws.query && (k == 0 || m == 1)) return hipSuccess;  // no scratch on these paths
     if (k == 0) {
         return y_f16 ? launch_fill_zero_f16(static_cast<_Float16 *>(y), m * n, stream)
                      : launch_fill_zero(static_cast<float *>(y), m * n, stream);
     }
     if (m == 1) return launch_gemv_dt(w, x, x_f16, y, y_f16, n, k, stream);
     using H = _Float16;
-    if (x_f16 && y_f16) return batched_slices(w, static_cast<const H *>(x), static_cast<H *>(y), m, n, k, stream);
-    if (x_f16) return batched_slices(w, static_cast<const H *>(x), static_cast<float *>(y), m, n, k, stream);
-    if (y_f16) return batched_slices(w, static_cast<const float *>(x), static_cast<H *>(y), m, n, k, stream);
-    return batched_slices(w, static_cast<const float *>(x), static_cast<float *>(y), m, n, k, stream);
+    if (x_f16 && y_f16) return batched_slices(w, static_cast<const H *>(x), static_cast<H *>(y), m, n, k, ws, stream);
+    if (x_f16) return batched_slices(w, static_cast<const H *>(x), static_cast<float *>(y), m, n, k, ws, stream);
+    if (y_f16) return batched_slices(w, static_cast<const float *>(x), static_cast<H *>(y), m, n, k, ws, stream);
+    return batched_slices(w, static_cast<const float *>(x), static_cast<float *>(y), m, n, k, ws, stream);
 }
 
 hipError_t launch_gemv_batched(const uint8_t *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
                                hipStream_t stream) {
-    return launch_gemv_batched_dt(w, x, false, y, false, m, n, k, stream);
+    Workspace ws;
+    return launch_gemv_batched_dt(w, x, false, y, false, m, n, k, ws, stream);
 }
 
 }  // namespace q4k

@@ -13,6 +13,23 @@ int device_cu_count();
 
 hipError_t launch_dequant(const uint8_t *w, float *out, int64_t n, int64_t k, hipStream_t stream);
 
+// Device scratch of one call.  ptr != nullptr: the caller's buffer of `bytes`
+// (hipErrorInvalidValue if the call needs more); ptr == nullptr: taken
+// stream-ordered for the call (hipMallocAsync / hipFreeAsync).  query: nothing
+// is launched and `need` receives the largest block the call would use (the
+// launches of one call run in order on one stream, so they share it).
+struct Workspace {
+    uint8_t *ptr = nullptr;
+    int64_t bytes = 0;
+    bool query = false;
+    int64_t need = 0;
+};
+
+// Takes `total` bytes of ws for a launch sequence (not in query mode): *out,
+// and *owned if they were allocated here (give them back with ws_release).
+hipError_t ws_acquire(Workspace &ws, int64_t total, hipStream_t stream, uint8_t **out, bool *owned);
+hipError_t ws_release(uint8_t *p, bool owned, hipStream_t stream);
+
 // One matrix of a batch-1 GEMV launch: y[i] = sum_c W[i,c] x[c] (+ r[i] if
 // r != nullptr; r may equal y).
 struct GemvJob {
@@ -47,12 +64,12 @@ hipError_t launch_gemv_batched(const uint8_t *w, const float *x, float *y, int64
 
 // The same with f16 or f32 activations and outputs.
 hipError_t launch_gemv_batched_dt(const uint8_t *w, const void *x, bool x_f16, void *y, bool y_f16, int64_t m,
-                                  int64_t n, int64_t k, hipStream_t stream);
+                                  int64_t n, int64_t k, Workspace &ws, hipStream_t stream);
 
 // Prefill-size GEMM with f16 activations: y[t, r] = sum_c W[r,c] x[t,c],
 // x f16 [m, k] (16-byte aligned), y f32 or f16 [m, n].
 hipError_t launch_prefill(const uint8_t *w, const _Float16 *x, void *y, bool y_f16, int64_t m, int64_t n, int64_t k,
-                          hipStream_t stream);
+                          Workspace &ws, hipStream_t stream);
 
 // Writes zeros to y[0..count) (the k == 0 empty sum).
 hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream);

@@ -367,8 +367,9 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *__rest
 }
 
 hipError_t launch_prefill(const uint8_t *w, const _Float16 *x, void *y, bool y_f16, int64_t m, int64_t n, int64_t k,
-                          hipStream_t stream) {
+                          Workspace &ws, hipStream_t stream) {
     if (m == 0 || n == 0) return hipSuccess;
+    if (ws.query && k == 0) return hipSuccess;
     if (k == 0) {
         return y_f16 ? launch_fill_zero_f16(static_cast<_Float16 *>(y), m * n, stream)
                      : launch_fill_zero(static_cast<float *>(y), m * n, stream);
@@ -386,9 +387,14 @@ hipError_t launch_prefill(const uint8_t *w, const _Float16 *x, void *y, bool y_f
     int64_t ksplit = want < nsb / 4 ? want : nsb / 4;
     if (ksplit < 1) ksplit = 1;
     const int64_t part_bytes = ksplit > 1 ? ksplit * m * n * 4 : 0;
+    const int64_t total = xa_bytes + xs_bytes + part_bytes;
+    if (ws.query) {
+        if (total > ws.need) ws.need = total;
+        return hipSuccess;
+    }
     uint8_t *scratch = nullptr;
-    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&scratch),
-                                  static_cast<size_t>(xa_bytes + xs_bytes + part_bytes), stream);
+    bool owned = false;
+    hipError_t e = ws_acquire(ws, total, stream, &scratch, &owned);
     if (e != hipSuccess) return e;
     uint8_t *xa = scratch;
     uint8_t *xs = scratch + xa_bytes;
@@ -423,7 +429,7 @@ hipError_t launch_prefill(const uint8_t *w, const _Float16 *x, void *y, bool y_f
             e = hipGetLastError();
         }
     }
-    const hipError_t f = hipFreeAsync(scratch, stream);
+    const hipError_t f = ws_release(scratch, owned, stream);
     return e != hipSuccess ? e : f;
 }
 

@@ -24,8 +24,12 @@ STATUS = {0: "Q4K_OK", 1: "Q4K_ERR_INVALID_ARG", 2: "Q4K_ERR_UNSUPPORTED_SHAPE",
 
 # exported symbols, in the order include/q4k.h declares them
 EXPORTS = ("q4k_gemv", "q4k_gemv_dt", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_q8_0_gemv", "q4k_gemv_batched",
-           "q4k_gemv_batched_dt", "q4k_prefill_gemm", "q4k_fused_swiglu", "q4k_dequant", "q4k_status_string",
-           "q4k_abi_version")
+           "q4k_gemv_batched_dt", "q4k_prefill_gemm", "q4k_gemv_batched_workspace_size", "q4k_gemv_batched_ws",
+           "q4k_prefill_workspace_size", "q4k_prefill_gemm_ws", "q4k_fused_swiglu", "q4k_dequant",
+           "q4k_status_string", "q4k_abi_version")
+
+# alignment a workspace passed to the *_ws calls must have
+WORKSPACE_ALIGN = 256
 
 # q4k_dtype
 F32, F16 = 0, 1
@@ -68,6 +72,11 @@ def lib() -> ctypes.CDLL:
         L.q4k_gemv_batched_dt.argtypes = [p, p, ctypes.c_int, p, ctypes.c_int, i64, i64, i64, p]
         L.q4k_prefill_gemm.argtypes = [p, p, p, ctypes.c_int, i64, i64, i64, p]
         L.q4k_gemv_batched.argtypes = [p, p, p, i64, i64, i64, p]
+        pi64 = ctypes.POINTER(i64)
+        L.q4k_gemv_batched_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, pi64]
+        L.q4k_gemv_batched_ws.argtypes = [p, p, ctypes.c_int, p, ctypes.c_int, i64, i64, i64, p, i64, p]
+        L.q4k_prefill_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, pi64]
+        L.q4k_prefill_gemm_ws.argtypes = [p, p, p, ctypes.c_int, i64, i64, i64, p, i64, p]
         L.q4k_fused_swiglu.argtypes = [p, p, p, p, i64, i64, p]
         L.q4k_dequant.argtypes = [p, p, i64, i64, p]
         for f in (L.q4k_gemv, L.q4k_gemv_dt, L.q4k_gemv_residual, L.q4k_gemv_multi, L.q4k_q8_0_gemv,
@@ -200,6 +209,79 @@ def prefill_gemm(w, x, y=None, n: int | None = None, out_dtype=None, stream=None
         y = torch.empty((m, n), dtype=out_dtype or torch.float32, device=x.device)
     _check(lib().q4k_prefill_gemm(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float16), _dev_any(y, "y"),
                                   _dtype_code(y, "y"), m, n, k, _stream(stream)), "q4k_prefill_gemm")
+    return y
+
+
+def _code_of(dtype, name):
+    import torch
+
+    if dtype == torch.float32:
+        return F32
+    if dtype == torch.float16:
+        return F16
+    raise TypeError(f"{name} must be float32 or float16 (got {dtype})")
+
+
+def gemv_batched_workspace_size(m: int, n: int, k: int, x_dtype=None, out_dtype=None) -> int:
+    """Bytes of workspace ``gemv_batched_ws`` needs on the current device (0: none)."""
+    import torch
+
+    out = ctypes.c_int64(-1)
+    _check(lib().q4k_gemv_batched_workspace_size(_code_of(x_dtype or torch.float32, "x_dtype"),
+                                                 _code_of(out_dtype or torch.float32, "out_dtype"), m, n, k,
+                                                 ctypes.byref(out)), "q4k_gemv_batched_workspace_size")
+    return out.value
+
+
+def prefill_workspace_size(m: int, n: int, k: int, out_dtype=None) -> int:
+    """Bytes of workspace ``prefill_gemm_ws`` needs on the current device (0: none)."""
+    import torch
+
+    out = ctypes.c_int64(-1)
+    _check(lib().q4k_prefill_workspace_size(_code_of(out_dtype or torch.float32, "out_dtype"), m, n, k,
+                                            ctypes.byref(out)), "q4k_prefill_workspace_size")
+    return out.value
+
+
+def _workspace(t):
+    """(pointer, bytes) of a uint8 device workspace tensor, or (NULL, 0)."""
+    import torch
+
+    if t is None:
+        return ctypes.c_void_p(0), 0
+    return _dev(t, "workspace", torch.uint8), t.numel()
+
+
+def gemv_batched_ws(w, x, workspace, y=None, n: int | None = None, out_dtype=None, stream=None):
+    """``gemv_batched_dt`` with scratch taken from ``workspace`` (uint8, 256-byte aligned)."""
+    import torch
+
+    if x.dim() != 2:
+        raise ValueError("x must be [m, k]")
+    m, k = x.shape
+    n = rows_of(w, k) if n is None else n
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype or x.dtype, device=x.device)
+    wp, wb = _workspace(workspace)
+    _check(lib().q4k_gemv_batched_ws(_dev(w, "w", torch.uint8), _dev_any(x, "x"), _dtype_code(x, "x"),
+                                     _dev_any(y, "y"), _dtype_code(y, "y"), m, n, k, wp, wb, _stream(stream)),
+           "q4k_gemv_batched_ws")
+    return y
+
+
+def prefill_gemm_ws(w, x, workspace, y=None, n: int | None = None, out_dtype=None, stream=None):
+    """``prefill_gemm`` with scratch taken from ``workspace`` (uint8, 256-byte aligned)."""
+    import torch
+
+    if x.dim() != 2:
+        raise ValueError("x must be [m, k]")
+    m, k = x.shape
+    n = rows_of(w, k) if n is None else n
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype or torch.float32, device=x.device)
+    wp, wb = _workspace(workspace)
+    _check(lib().q4k_prefill_gemm_ws(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float16), _dev_any(y, "y"),
+                                     _dtype_code(y, "y"), m, n, k, wp, wb, _stream(stream)), "q4k_prefill_gemm_ws")
     return y
 
 

@@ -66,3 +66,24 @@ def check_swiglu_bound(h_gpu, ref: dict, what: str) -> float:
                              f"row {i}: gpu {h[i]!r} oracle {ref['h'][i]!r} bound {bound[i]!r}")
     with np.errstate(divide="ignore", invalid="ignore"):
         return float(np.nanmax(np.where(bound > 0, err / bound, 0.0)))
+
+
+def check_bound_f16(y16, y_ref, a_ref, what):
+    """f16 output: the f32 bound widened by the output rounding.  An f32 result
+    of magnitude >= 65520 rounds to +-inf: where the bound puts it surely
+    there the output must be inf of the oracle's sign, where it may be on
+    either side, inf of that sign is accepted too."""
+    y = np.asarray(y16, dtype=np.float64)
+    bound = REL * a_ref + 2.0 ** -11 * (np.abs(y_ref) + REL * a_ref) + 2.0 ** -25
+    with np.errstate(invalid="ignore"):
+        err = np.abs(y - y_ref)
+    signed_inf = np.isinf(y) & (np.sign(y) == np.sign(y_ref))
+    must_overflow = np.abs(y_ref) - REL * a_ref >= 65520.0
+    may_overflow = np.abs(y_ref) + REL * a_ref >= 65520.0
+    ok = np.where(must_overflow, signed_inf, (err <= bound) | (may_overflow & signed_inf))
+    err = np.where(np.isinf(y), 0.0, err)
+    if not ok.all():
+        i = np.argwhere(~ok)[0]
+        raise AssertionError(f"{what}: {int((~ok).sum())} of {y.size} f16 outputs outside the bound; first at "
+                             f"{i.tolist()}: gpu {y[tuple(i)]!r} oracle {y_ref[tuple(i)]!r} bound {bound[tuple(i)]!r}")
+    return float(np.max(err / bound)) if err.size else 0.0

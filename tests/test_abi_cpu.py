@@ -30,8 +30,9 @@ def declared_functions():
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
         ["q4k_gemv", "q4k_gemv_dt", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_q8_0_gemv", "q4k_gemv_batched",
-         "q4k_gemv_batched_dt", "q4k_prefill_gemm", "q4k_fused_swiglu", "q4k_dequant", "q4k_status_string",
-         "q4k_abi_version"])
+         "q4k_gemv_batched_dt", "q4k_prefill_gemm", "q4k_gemv_batched_workspace_size", "q4k_gemv_batched_ws",
+         "q4k_prefill_workspace_size", "q4k_prefill_gemm_ws", "q4k_fused_swiglu", "q4k_dequant",
+         "q4k_status_string", "q4k_abi_version"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -56,7 +57,7 @@ def test_only_the_abi_is_exported():
 
 
 def test_status_strings(L):
-    assert L.q4k_abi_version() == 105
+    assert L.q4k_abi_version() == 106
     for s in range(5):
         assert len(L.q4k_status_string(s)) > 0
     assert L.q4k_status_string(99) == b"unknown status"
@@ -177,6 +178,64 @@ def test_batched_dt_validation(L, args, status):
 def test_prefill_validation(L, args, status):
     w, x, y, yd, m, n, k = args
     assert L.q4k_prefill_gemm(ctypes.c_void_p(w), ctypes.c_void_p(x), ctypes.c_void_p(y), yd, m, n, k, None) == status
+
+
+WS = A + 0x40000000  # a 256-byte aligned stand-in workspace address
+
+
+@pytest.mark.parametrize("args,status", [
+    ((W, X, 1, Y, 1, 4, 16, 300, WS, 1 << 20), SHAPE),
+    ((W, X, 3, Y, 1, 4, 16, 256, WS, 1 << 20), INVALID),
+    ((W, X + 2, 0, Y, 1, 4, 16, 256, WS, 1 << 20), MISALIGNED),
+    ((W, X, 1, X + 4 * 256 * 2 - 2, 1, 4, 16, 256, WS, 1 << 20), INVALID),
+    ((W, X, 1, Y, 1, 4, 16, 256, WS, -1), INVALID),        # negative workspace size
+    ((W, X, 1, Y, 1, 4, 16, 256, WS + 128, 1 << 20), MISALIGNED),  # workspace not 256-B aligned
+    ((W, X, 1, Y, 1, 0, 16, 256, WS, -1), INVALID),        # checked even for an empty call
+    ((W, X, 1, Y, 1, 0, 16, 256, 0, 0), OK),
+    ((W, X, 1, Y, 1, 4, 0, 256, 0, 0), OK),
+])
+def test_batched_ws_validation(L, args, status):
+    w, x, xd, y, yd, m, n, k, ws, wsb = args
+    assert L.q4k_gemv_batched_ws(ctypes.c_void_p(w), ctypes.c_void_p(x), xd, ctypes.c_void_p(y), yd, m, n, k,
+                                 ctypes.c_void_p(ws), wsb, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((W, X, Y, 0, 128, 16, 300, WS, 1 << 20), SHAPE),
+    ((W, X, Y, 0, 128, 16, (1 << 24) + 256, WS, 1 << 20), SHAPE),
+    ((W, X + 8, Y, 0, 128, 16, 256, WS, 1 << 20), MISALIGNED),
+    ((W, X, Y, 2, 128, 16, 256, WS, 1 << 20), INVALID),
+    ((W, X, Y, 0, 128, 16, 256, WS, -5), INVALID),
+    ((W, X, Y, 0, 128, 16, 256, WS + 16, 1 << 20), MISALIGNED),
+    ((W, X, Y, 0, 0, 16, 256, 0, 0), OK),
+])
+def test_prefill_ws_validation(L, args, status):
+    w, x, y, yd, m, n, k, ws, wsb = args
+    assert L.q4k_prefill_gemm_ws(ctypes.c_void_p(w), ctypes.c_void_p(x), ctypes.c_void_p(y), yd, m, n, k,
+                                 ctypes.c_void_p(ws), wsb, None) == status
+
+
+def test_workspace_size_queries(L):
+    out = ctypes.c_int64(-1)
+    # sizes that need no device: empty calls, one token, k == 0
+    for m, n, k in ((0, 16, 256), (4, 0, 256), (1, 4096, 4096), (8, 16, 0)):
+        for xd in (0, 1):
+            for yd in (0, 1):
+                out.value = -1
+                assert L.q4k_gemv_batched_workspace_size(xd, yd, m, n, k, ctypes.byref(out)) == OK
+                assert out.value == 0
+    for m, n, k in ((0, 16, 256), (128, 0, 256), (128, 16, 0)):
+        out.value = -1
+        assert L.q4k_prefill_workspace_size(1, m, n, k, ctypes.byref(out)) == OK
+        assert out.value == 0
+    assert L.q4k_gemv_batched_workspace_size(0, 0, 4, 16, 256, None) == INVALID
+    assert L.q4k_gemv_batched_workspace_size(2, 0, 4, 16, 256, ctypes.byref(out)) == INVALID
+    assert L.q4k_gemv_batched_workspace_size(0, 0, 4, 16, 300, ctypes.byref(out)) == SHAPE
+    assert L.q4k_gemv_batched_workspace_size(0, 0, -1, 16, 256, ctypes.byref(out)) == INVALID
+    assert L.q4k_prefill_workspace_size(0, 128, 16, 256, None) == INVALID
+    assert L.q4k_prefill_workspace_size(3, 128, 16, 256, ctypes.byref(out)) == INVALID
+    assert L.q4k_prefill_workspace_size(0, 128, 16, (1 << 24) + 256, ctypes.byref(out)) == SHAPE
+    assert L.q4k_prefill_workspace_size(0, -2, 16, 256, ctypes.byref(out)) == INVALID
 
 
 def _items(*triples):
