@@ -84,14 +84,16 @@ __device__ __forceinline__ int stage_pos(int kk) {
 
 // ---- activations, converted once per call ----------------------------------
 // One half-wave per (stage, token) of the padded token range 16*mt; each lane
-// converts four activations.  Tokens >= m are written as zeros.  With
-// zero_y the same kernel zero-fills y, which the matrix-core kernel then
-// accumulates into.  XT: float or _Float16 activations (widened exactly).
+// converts four activations.  Tokens >= m are written as zeros.  The same
+// kernel zero-fills nzero words at `zero` (an f32 output that the matrix-core
+// kernel then accumulates into, or its counters).  XT: float or _Float16
+// activations (widened exactly).
 template <typename XT>
-__global__ __launch_bounds__(256) void x_prep_kernel(const XT *x, uint8_t *__restrict__ xc, float *__restrict__ y,
-                                                      int m, int mt, int64_t k, int64_t ny) {
+__global__ __launch_bounds__(256) void x_prep_kernel(const XT *x, uint8_t *__restrict__ xc,
+                                                      uint32_t *__restrict__ zero, int m, int mt, int64_t k,
+                                                      int64_t nzero) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    for (int64_t i = gid; i < ny; i += static_cast<int64_t>(gridDim.x) * 256) y[i] = 0.0f;
+    for (int64_t i = gid; i < nzero; i += static_cast<int64_t>(gridDim.x) * 256) zero[i] = 0u;
 
     const int64_t nst = k / kStageK;
     const int tpad = 16 * mt;
@@ -169,6 +171,64 @@ struct BOps {
     float d, dmin;
 };
 
+// B operands of half hw of a super-block for the lane's row (col) and
+// k-quarter kq, from the super-block's 16-byte header and the quarter's 16
+// code bytes; ps = pair_select(2 * hw + kq / 2).
+__device__ __forceinline__ void build_b_ops(BOps &o, uint4 hdr, uint4 qv, const PairSelect &ps, int kq) {
+    o.d = half_bits_to_float(hdr.x);
+    o.dmin = half_bits_to_float(hdr.x >> 16);
+    uint32_t scp, mp;
+    scale_min_pair(hdr.y, hdr.z, hdr.w, ps, scp, mp);
+    const uint32_t sc2_lo = (scp & 0xffu) * 0x00010001u;
+    const uint32_t sc2_hi = ((scp >> 8) & 0xffu) * 0x00010001u;
+    const uint32_t u[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t sc2 = (i & 1) ? sc2_hi : sc2_lo;
+        const int shn = (i & 1) ? 4 : 0;
+        uint32_t v4[4];
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) {
+            const uint32_t word = u[2 * (i >> 1) + d2];
+            v4[2 * d2 + 0] = pair_operand((word >> shn) & 0x000f000fu, sc2);
+            v4[2 * d2 + 1] = pair_operand((word >> (8 + shn)) & 0x000f000fu, sc2);
+        }
+        o.b[i] = __builtin_bit_cast(half8_t, u32x4_t{v4[0], v4[1], v4[2], v4[3]});
+    }
+    // mins of the quarter's two sub-blocks (even quarters only) as exact f16
+    const _Float16 m0 = (kq & 1) ? _Float16(0) : static_cast<_Float16>(static_cast<float>(mp & 0xffu));
+    const _Float16 m1 = (kq & 1) ? _Float16(0) : static_cast<_Float16>(static_cast<float>((mp >> 8) & 0xffu));
+    o.bmin = half8_t{m0, m1, 0, 0, 0, 0, 0, 0};
+}
+
+// One (row tile, token tile) product of a half super-block and its epilogue:
+// out[r] += 2^e * (d * (P - 1024 * sum(hi + lo)) - dmin * Q) for the lane's
+// tokens 4*kq + r.
+__device__ __forceinline__ void mfma_half(const BOps &bo, const AStep &a, float4_t &out, int kq) {
+    // the lane's token's sums of its quarter's two sub-blocks, hi and lo
+    const int gg = kq >> 1;
+    const uint32_t shi = (kq & 1) ? 0u : (gg ? a.sub.y : a.sub.x);
+    const uint32_t slo = (kq & 1) ? 0u : (gg ? a.sub.w : a.sub.z);
+    const half8_t amin_hi = __builtin_bit_cast(half8_t, u32x4_t{shi, 0u, 0u, 0u});
+    const half8_t amin_lo = __builtin_bit_cast(half8_t, u32x4_t{slo, 0u, 0u, 0u});
+    float4_t pacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a.f[2 * i]), bo.b[i], pacc, 0, 0, 0);
+        pacc =
+            __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a.f[2 * i + 1]), bo.b[i], pacc, 0, 0, 0);
+    }
+    float4_t qacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    qacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(amin_hi, bo.bmin, qacc, 0, 0, 0);
+    qacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(amin_lo, bo.bmin, qacc, 0, 0, 0);
+    // pacc[r] = sum_k A[tok_r, k] * (1024 + sc q)[k, row]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float code_part = pacc[r] - 1024.0f * a.bias[r];
+        out[r] += a.esc[r] * (bo.d * code_part - bo.dmin * qacc[r]);
+    }
+}
+
 // Workgroup = W = 2S waves, 16*NT rows, a K range [sb0, sb1) of super-blocks
 // (block b: row block b / ksplit, K part b % ksplit).  The range is walked in
 // stages of S super-blocks.  Each stage's weights (16*NT rows x 144*S bytes)
@@ -180,10 +240,11 @@ struct BOps {
 // registers one step ahead.  At the end the waves' sums are added in LDS in a
 // fixed order, then stored (ksplit == 1) or added into y with atomics
 // (ksplit > 1, y zeroed first).
-// Stages of weights in flight: fewer with several token tiles, whose
-// operands take the registers.
+// Stages of weights in flight.  Two: more only deepens the burst of loads
+// every workgroup issues at the start (the first stage then lands later) and
+// takes registers from the operands.
 template <int MT>
-constexpr int weight_stages_ahead() { return MT == 1 ? 4 : 2; }
+constexpr int weight_stages_ahead() { return 2; }
 
 template <int NT, int S>
 struct StageGeom {
@@ -264,8 +325,12 @@ __global__ __launch_bounds__(128 * S, 1) void batched_mfma_kernel(const uint8_t 
     uint32_t a_lane[MT];
 #pragma unroll
     for (int p = 0; p < MT; ++p) a_lane[p] = 16 * p + col < m ? 0u : 0x40000000u;
+    const int last_half = static_cast<int>(k / kStageK) - 1;
     auto load_a = [&](AStep &a, int h, int p) {
-        const int soff = (h * MT + p) * kTileStageBytes;
+        // past the K range (a prefetch whose results are not used): the last
+        // stage, so that every read stays inside the scratch
+        const int hc = h < last_half ? h : last_half;
+        const int soff = (hc * MT + p) * kTileStageBytes;
 #pragma unroll
         for (int f = 0; f < 8; ++f)
             a.f[f] = as_uint4(
@@ -287,30 +352,7 @@ __global__ __launch_bounds__(128 * S, 1) void batched_mfma_kernel(const uint8_t 
         const uint8_t *rowp = &stage_lds[buf][(16 * t + col) * G::kRowLds + sbl * kBlockBytes];
         const uint4 hdr = *reinterpret_cast<const uint4 *>(rowp);
         const uint4 qv = *reinterpret_cast<const uint4 *>(rowp + 16 + 64 * hw + 16 * kq);
-        o.d = half_bits_to_float(hdr.x);
-        o.dmin = half_bits_to_float(hdr.x >> 16);
-        uint32_t scp, mp;
-        scale_min_pair(hdr.y, hdr.z, hdr.w, ps, scp, mp);
-        const uint32_t sc2_lo = (scp & 0xffu) * 0x00010001u;
-        const uint32_t sc2_hi = ((scp >> 8) & 0xffu) * 0x00010001u;
-        const uint32_t u[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t sc2 = (i & 1) ? sc2_hi : sc2_lo;
-            const int shn = (i & 1) ? 4 : 0;
-            uint32_t v4[4];
-#pragma unroll
-            for (int d2 = 0; d2 < 2; ++d2) {
-                const uint32_t word = u[2 * (i >> 1) + d2];
-                v4[2 * d2 + 0] = pair_operand((word >> shn) & 0x000f000fu, sc2);
-                v4[2 * d2 + 1] = pair_operand((word >> (8 + shn)) & 0x000f000fu, sc2);
-            }
-            o.b[i] = __builtin_bit_cast(half8_t, u32x4_t{v4[0], v4[1], v4[2], v4[3]});
-        }
-        // mins of the quarter's two sub-blocks (even quarters only) as exact f16
-        const _Float16 m0 = (kq & 1) ? _Float16(0) : static_cast<_Float16>(static_cast<float>(mp & 0xffu));
-        const _Float16 m1 = (kq & 1) ? _Float16(0) : static_cast<_Float16>(static_cast<float>((mp >> 8) & 0xffu));
-        o.bmin = half8_t{m0, m1, 0, 0, 0, 0, 0, 0};
+        build_b_ops(o, hdr, qv, ps, kq);
     };
 
     float4_t acc[NT][MT];
@@ -319,32 +361,7 @@ __global__ __launch_bounds__(128 * S, 1) void batched_mfma_kernel(const uint8_t 
 #pragma unroll
         for (int p = 0; p < MT; ++p) acc[t][p] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // One (row tile, token tile) product of the step and its epilogue.
-    auto multiply = [&](const BOps &bo, const AStep &a, float4_t &out) {
-        // the lane's token's sums of its quarter's two sub-blocks, hi and lo
-        const int gg = kq >> 1;
-        const uint32_t shi = (kq & 1) ? 0u : (gg ? a.sub.y : a.sub.x);
-        const uint32_t slo = (kq & 1) ? 0u : (gg ? a.sub.w : a.sub.z);
-        const half8_t amin_hi = __builtin_bit_cast(half8_t, u32x4_t{shi, 0u, 0u, 0u});
-        const half8_t amin_lo = __builtin_bit_cast(half8_t, u32x4_t{slo, 0u, 0u, 0u});
-        float4_t pacc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a.f[2 * i]), bo.b[i], pacc, 0, 0,
-                                                         0);
-            pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a.f[2 * i + 1]), bo.b[i], pacc, 0,
-                                                         0, 0);
-        }
-        float4_t qacc = {0.0f, 0.0f, 0.0f, 0.0f};
-        qacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(amin_hi, bo.bmin, qacc, 0, 0, 0);
-        qacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(amin_lo, bo.bmin, qacc, 0, 0, 0);
-        // pacc[r] = sum_k A[tok_r, k] * (1024 + sc q)[k, row]; tok_r = 16p + 4kq + r
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float code_part = pacc[r] - 1024.0f * a.bias[r];
-            out[r] += a.esc[r] * (bo.d * code_part - bo.dmin * qacc[r]);
-        }
-    };
+    auto multiply = [&](const BOps &bo, const AStep &a, float4_t &out) { mfma_half(bo, a, out, kq); };
 
     // ---- pipeline: weights P stages ahead (register ring -> LDS), the wave's
     // activations one step ahead.  Unrolled by P so every ring slot, LDS
@@ -467,7 +484,7 @@ hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, i
     const int64_t prep_threads = nst * 16 * MT * 32;
     const int64_t prep_blocks = (prep_threads + 255) / 256;
     hipLaunchKernelGGL(x_prep_kernel<XT>, dim3(static_cast<unsigned>(prep_blocks)), dim3(256), 0, stream, x, xc,
-                       acc_y, m, MT, k, ny);
+                       reinterpret_cast<uint32_t *>(acc_y), m, MT, k, ny);
     e = hipGetLastError();
     if (e == hipSuccess) {
         const int64_t nrb = (n + 16 * NT - 1) / (16 * NT);
