@@ -223,27 +223,26 @@ def main():
             for mtok in (4, 16, 32, 64):
                 xs = torch.from_numpy(inputs.make_x(mtok, k_, config_id=4, tensor_id=100 + mtok)).to(dev)
                 yb = torch.empty((mtok, n_), dtype=torch.float32, device=dev)
-                for i in range(5):
-                    q4k.gemv_batched(sets_b[i % len(sets_b)][0], xs, y=yb, stream=stream)
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                reps = 50
-                torch.cuda.synchronize()
-                a.record(stream)
-                for i in range(reps):
-                    q4k.gemv_batched(sets_b[i % len(sets_b)][0], xs, y=yb, stream=stream)
-                b.record(stream)
-                torch.cuda.synchronize()
-                t = a.elapsed_time(b) / reps * 1e-3
+                t = _time_launches(lambda i: q4k.gemv_batched(sets_b[i % len(sets_b)][0], xs, y=yb, stream=stream),
+                                   torch, stream, 50, 20)
+                # the same work with the caller's workspace: no allocation per call
+                ws = torch.empty(max(1, q4k.gemv_batched_workspace_size(mtok, n_, k_)), dtype=torch.uint8,
+                                 device=dev)
+                t_ws = _time_launches(
+                    lambda i: q4k.gemv_batched_ws(sets_b[i % len(sets_b)][0], xs, ws, y=yb, stream=stream), torch,
+                    stream, 50, 20)
                 batched[f"{nm} m={mtok}"] = {"mean_us": round(t * 1e6, 2),
                                              "weight_GB/s": round(wbytes[nm] / t / 1e9, 1),
-                                             "TFLOP/s": round(2.0 * mtok * n_ * k_ / t / 1e12, 2)}
+                                             "TFLOP/s": round(2.0 * mtok * n_ * k_ / t / 1e12, 2),
+                                             "workspace_call_us": round(t_ws * 1e6, 2)}
+                del ws
             del sets_b
 
     blocks = decode_blocks(q4k, inputs, torch, dev, stream, args.steps, args.warmup)
     q8 = q8_0_kernels(q4k, inputs, torch, dev, stream, args.steps, args.warmup)
     f16io = f16_variants(q4k, inputs, torch, dev, stream, args.steps, args.warmup, not args.no_batched)
     prefill = prefill_kernels(q4k, inputs, torch, dev, stream) if not args.no_batched else {}
+    ceiling = stream_read_ceiling(torch, dev, stream, kernels["gemv_lm_head"]["GB/s"])
 
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s; per kernel {kernels}; "
         f"batched {batched}; decode blocks {blocks}; q8_0 {q8}; f16 i/o {f16io}; prefill {prefill}; "
@@ -300,11 +299,52 @@ def main():
             "q8_0_9b": q8,
             "f16_io_9b": f16io,
             "prefill_9b_ffn": prefill,
+            "stream_read_1GiB": ceiling,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def stream_read_ceiling(torch, dev, stream, lm_head_gbs):
+    """The device's achievable HBM read rate, for context: the read-only
+    streaming kernel (libq4k_stream.so) over 1 GiB, the best of a few grid
+    sizes and load depths.  None if that library is not built."""
+    import ctypes
+
+    from q4_dequant_gemv_amd import build as hip_build
+
+    if not os.path.exists(hip_build.STREAM_LIB):
+        log("[bench] libq4k_stream.so not built: no streaming ceiling")
+        return None
+    lib = ctypes.CDLL(hip_build.STREAM_LIB)
+    lib.q4k_stream_read.restype = ctypes.c_int
+    lib.q4k_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
+    nbytes = 1 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(7)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    grids = [cus * g for g in (2, 4, 8, 16)]
+    out = torch.empty(max(grids) * 256, dtype=torch.int32, device=dev)
+    s = ctypes.c_void_p(stream.cuda_stream)
+    best = None
+    for grid in grids:
+        for unroll in (4, 8):
+            def call(i):
+                rc = lib.q4k_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
+                                         grid, unroll, s)
+                if rc != 0:
+                    raise RuntimeError(f"q4k_stream_read: hip error {rc}")
+
+            t = _time_launches(call, torch, stream, 20, 3)
+            gbs = nbytes / t / 1e9
+            if best is None or gbs > best["GB/s"]:
+                best = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "grid": grid,
+                        "loads_in_flight_per_thread": unroll}
+    best["lm_head_gemv_frac_of_it"] = round(lm_head_gbs / best["GB/s"], 4)
+    del buf, out
+    return best
 
 
 def _time_launches(fn, torch, stream, steps, warmup):

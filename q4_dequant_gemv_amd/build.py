@@ -57,5 +57,27 @@ def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
     return out
 
 
+STREAM_SRC = os.path.join(CSRC, "stream_read.hip")
+STREAM_LIB = os.path.join(HERE, "libq4k_stream.so")
+
+
+def build_stream_probe(verbose: bool = False, out: str = STREAM_LIB) -> str:
+    """The read-only streaming kernel the benchmark reports as the device's
+    achievable read rate (a library of its own, outside the q4k ABI)."""
+    tmp = out + ".tmp"
+    cmd = ["hipcc", *FLAGS, "-shared", STREAM_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    lines = [ln for ln in r.stdout.decode(errors="replace").splitlines() if "packed-fp32-ops" not in ln]
+    if lines:
+        print("[stream_read.hip]\n" + "\n".join(lines), file=sys.stderr)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for stream_read.hip")
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_stream_probe(verbose=True))

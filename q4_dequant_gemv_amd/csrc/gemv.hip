@@ -691,7 +691,7 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const void *x, co
 #define Q4K_SWIGLU_NB 2
 #endif
 #ifndef Q4K_SPLIT_NB
-#define Q4K_SPLIT_NB 2
+#define Q4K_SPLIT_NB 3
 #endif
 // matrices below this many bytes use the small launch shape
 #ifndef Q4K_SMALL_BYTES

@@ -333,3 +333,24 @@ def test_product_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "liboracle" not in text and "q4k_oracle" not in text, f
+
+
+def test_stream_read_probe_library():
+    """The benchmark's read-only streaming kernel lives in a library of its
+    own: it exports exactly its one C function and rejects bad arguments on
+    the host (no device call is made for these)."""
+    import subprocess
+
+    from q4_dequant_gemv_amd import build as hip_build
+
+    out = subprocess.run(["nm", "-D", "--defined-only", hip_build.STREAM_LIB], capture_output=True, text=True,
+                         check=True)
+    names = {ln.split()[-1] for ln in out.stdout.splitlines() if ln.strip()}
+    assert {n for n in names if not n.startswith(("__hip_cuid", "_Z"))} == {"q4k_stream_read"}
+    L = ctypes.CDLL(hip_build.STREAM_LIB)
+    L.q4k_stream_read.restype = ctypes.c_int
+    L.q4k_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
+    for args in ((0, 1024, Y, 8, 4), (X, 1000, Y, 8, 4), (X, 1 << 31, Y, 8, 4), (X, 1024, 0, 8, 4),
+                 (X, 1024, Y, 0, 4), (X, 1024, Y, 8, 5), (X, -16, Y, 8, 8)):
+        assert L.q4k_stream_read(*args, None) != 0, args
