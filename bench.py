@@ -206,7 +206,8 @@ def main():
         mean_s = a.elapsed_time(b) / args.steps * 1e-3
         gbs = kernel_bytes[nm] / mean_s / 1e9
         kernels[nm] = {"mean_us": round(mean_s * 1e6, 3), "GB/s": round(gbs, 1),
-                       "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "calls_per_s": round(1.0 / mean_s, 1)}
+                       "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "calls_per_s": round(1.0 / mean_s, 1),
+                       "per_launch_us": _per_launch(fn, torch, stream, 100)}
     del sets_sw, sets_dn
     achieved = kernels["gemv_lm_head"]["GB/s"]
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -269,6 +270,14 @@ def main():
                "kind": "oracle",
                "sample": f"{reps} full steps (gate+up SwiGLU, down, lm_head: all rows, 657 MB of Q4_K each), "
                          f"{cpu_s:.1f} s on {threads} host threads"}
+        # the same oracle on one thread (one full step)
+        t1 = time.perf_counter()
+        ref_h = oracle.fused_swiglu(host["gate_9b"], host["up_9b"], x_host, threads=1)["h"]
+        ref_y = oracle.gemv(host["down_9b"], ref_h.astype(np.float32), threads=1)[0]
+        oracle.gemv(host["lm_head_9b"], ref_y.astype(np.float32), threads=1)
+        one_s = time.perf_counter() - t1
+        cpu["single_thread"] = {"value": round(step_weight_bytes / one_s / 1e9, 3), "unit": "GB/s",
+                                "sample": f"1 full step, {one_s:.1f} s on 1 host thread"}
 
     if args.sweep:
         sweep(q4k, inputs, torch, np, dev)
@@ -345,6 +354,23 @@ def stream_read_ceiling(torch, dev, stream, lm_head_gbs):
     best["lm_head_gemv_frac_of_it"] = round(lm_head_gbs / best["GB/s"], 4)
     del buf, out
     return best
+
+
+def _per_launch(fn, torch, stream, reps):
+    """p10 / median / p90 of single launches, each between its own pair of
+    events on the launch stream (the events add a little to short kernels)."""
+    import numpy as np
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        fn(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = np.sort(np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]))
+    return {"p10": round(float(np.percentile(t, 10)), 3), "median": round(float(np.median(t)), 3),
+            "p90": round(float(np.percentile(t, 90)), 3), "n": reps}
 
 
 def _time_launches(fn, torch, stream, steps, warmup):
