@@ -244,6 +244,7 @@ def main():
     f16io = f16_variants(q4k, inputs, torch, dev, stream, args.steps, args.warmup, not args.no_batched)
     prefill = prefill_kernels(q4k, inputs, torch, dev, stream) if not args.no_batched else {}
     ceiling = stream_read_ceiling(torch, dev, stream, kernels["gemv_lm_head"]["GB/s"])
+    small = small_configs(q4k, inputs, torch, dev, stream)
 
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s; per kernel {kernels}; "
         f"batched {batched}; decode blocks {blocks}; q8_0 {q8}; f16 i/o {f16io}; prefill {prefill}; "
@@ -309,11 +310,65 @@ def main():
             "f16_io_9b": f16io,
             "prefill_9b_ffn": prefill,
             "stream_read_1GiB": ceiling,
+            "configs_0_1": small,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def small_configs(q4k, inputs, torch, dev, stream):
+    """The GEMV and dequant calls at the small config shapes (the 1024 x 1024
+    square; the 0.8B q-proj, out-proj and lm_head), weights rotated over
+    >= 512 MiB of copies: the launches captured in a HIP graph (the rate a
+    decode loop sees; eager Python calls of these sizes are bound by the host),
+    the same launches eager back to back, and single-launch percentiles."""
+    out = {}
+    for kind, name in (("gemv", "square_1k"), ("dequant", "square_1k"), ("gemv", "q_proj_0p8b"),
+                       ("gemv", "out_proj_0p8b"), ("gemv", "lm_head_0p8b")):
+        n, k = inputs.SHAPES[name]
+        w0 = torch.from_numpy(inputs.make_q4k(n, k, config_id=7, tensor_id=1).reshape(-1)).to(dev)
+        copies = max(1, -(-(512 << 20) // w0.numel()))
+        ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+        x = torch.from_numpy(inputs.make_x(1, k, config_id=7)[0]).to(dev)
+        if kind == "gemv":
+            y = torch.empty(n, dtype=torch.float32, device=dev)
+
+            def fn(i, s=stream):
+                q4k.gemv(ws[i % copies], x, y=y, stream=s)
+
+            nbytes = w0.numel() + 4 * (n + k)
+        else:
+            y = torch.empty((n, k), dtype=torch.float32, device=dev)
+
+            def fn(i, s=stream):
+                q4k.dequant(ws[i % copies], k, out=y, stream=s)
+
+            nbytes = w0.numel() + 4 * n * k
+        # enough launches to touch every copy: >= 512 MiB, beyond the Infinity Cache
+        nl = max(200, copies)
+        t = _time_launches(fn, torch, stream, nl, 20)
+        # the same launches captured into a HIP graph, timed over one replay
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(nl):
+                fn(i, None)  # the capture stream
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        tg = a.elapsed_time(b) / nl * 1e-3
+        del graph
+        out[f"{kind} {name}"] = {"shape": f"{n}x{k}", "bytes": nbytes, "graph_us": round(tg * 1e6, 3),
+                                 "graph_GB/s": round(nbytes / tg / 1e9, 1),
+                                 "frac_hbm_peak": round(nbytes / tg / HBM_PEAK_GBS / 1e9, 4),
+                                 "eager_us": round(t * 1e6, 3), "per_launch_us": _per_launch(fn, torch, stream, 100)}
+        del ws, y
+    return out
 
 
 def stream_read_ceiling(torch, dev, stream, lm_head_gbs):
