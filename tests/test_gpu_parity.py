@@ -85,6 +85,35 @@ def test_dequant_row_chunks_of_lm_head_0p8b(q4k):
         np.testing.assert_array_equal(to_host(out).view(np.uint32), want.view(np.uint32))
 
 
+@pytest.mark.parametrize("name,tid", [("gate_9b", 0), ("down_9b", 2)])
+def test_dequant_9b_ffn_whole(q4k, name, tid):
+    """The 9B FFN matrices (28.3 MB of Q4_K, 201 MB of f32) whole, bit for bit."""
+    import torch
+
+    n, k = inputs.SHAPES[name]
+    w = inputs.make_q4k(n, k, config_id=2, tensor_id=tid)
+    out = torch.empty((n, k), dtype=torch.float32, device="cuda")
+    q4k.dequant(to_dev(w.reshape(-1)), k, out=out)
+    want = oracle.dequant(w, k, threads=THREADS)
+    np.testing.assert_array_equal(to_host(out).view(np.uint32), want.view(np.uint32))
+
+
+def test_dequant_row_chunks_of_lm_head_9b(q4k):
+    """Rows of the 9B lm_head (248320 x 4096, 572 MB) through pointer offsets:
+    the first rows, a middle range and the last rows."""
+    import torch
+
+    n, k = inputs.SHAPES["lm_head_9b"]
+    w = inputs.make_q4k(n, k, config_id=3, tensor_id=0)
+    wd = to_dev(w.reshape(-1))
+    rb = inputs.row_bytes(k)
+    for r0, cnt in ((0, 1024), (131_071, 2049), (n - 1000, 1000)):
+        out = torch.empty((cnt, k), dtype=torch.float32, device="cuda")
+        q4k.dequant(wd[r0 * rb:(r0 + cnt) * rb], k, out=out)
+        want = oracle.dequant(w[r0:r0 + cnt], k, threads=THREADS)
+        np.testing.assert_array_equal(to_host(out).view(np.uint32), want.view(np.uint32))
+
+
 # --------------------------------------------------------------------- gemv
 def _gemv_case(q4k, w, x, rows=None):
     y = to_host(q4k.gemv(to_dev(w.reshape(-1)), to_dev(x)))
