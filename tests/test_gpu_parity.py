@@ -158,11 +158,11 @@ def test_gemv_full_size_sampled(q4k, name, cfg, tid):
     _report(name, check_bound(got[rows], yr, ar, name))
 
 
-def test_gemv_work_counter_across_streams(q4k):
-    """Large matrices hand rows out through a per-stream work counter that
-    each launch leaves at zero: repeated launches on one stream, and launches
-    on two streams running at the same time, all write every row with the
-    same bits (each row is still summed by one wave in a fixed order)."""
+def test_gemv_concurrent_streams_bitwise(q4k):
+    """Repeated launches on one stream, and launches on two streams running
+    at the same time, all write every row with the same bits: rows are
+    assigned to waves statically and each row is summed by one wave in a
+    fixed order, so nothing depends on timing or on another launch."""
     import torch
 
     n, k = inputs.SHAPES["lm_head_0p8b"]
