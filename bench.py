@@ -84,7 +84,8 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this path runs on one GPU; multi-GPU runs are not part of this benchmark "
-              "(rows shard across GPUs without communication, see DESIGN.md)", file=sys.stderr)
+              "(row shards need no communication between GPUs; only one GPU's share is built and timed)",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
