@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-batched", action="store_true", help="skip the skinny-GEMM timings")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time only the decode step and its three kernels (no batched, block, Q8_0, f16, prefill, "
+                         "small-config or streaming-ceiling timings, no CPU baseline): for kernel traces")
     ap.add_argument("--eager", action="store_true",
                     help="time the steps as eager launches instead of one captured HIP graph")
     ap.add_argument("--sweep", action="store_true",
@@ -218,6 +221,9 @@ def main():
     # The skinny-GEMM workload over the same FFN weights (m tokens): one call
     # per launch, weights rotated over >= 512 MiB of copies.
     batched = {}
+    if args.step_only:
+        args.no_batched = True
+        args.no_cpu_baseline = True
     if not args.no_batched:
         for nm in ("gate_9b", "down_9b"):
             n_, k_ = shapes[nm]
@@ -240,12 +246,15 @@ def main():
                 del ws
             del sets_b
 
-    blocks = decode_blocks(q4k, inputs, torch, dev, stream, args.steps, args.warmup)
-    q8 = q8_0_kernels(q4k, inputs, torch, dev, stream, args.steps, args.warmup)
-    f16io = f16_variants(q4k, inputs, torch, dev, stream, args.steps, args.warmup, not args.no_batched)
-    prefill = prefill_kernels(q4k, inputs, torch, dev, stream) if not args.no_batched else {}
-    ceiling = stream_read_ceiling(torch, dev, stream, kernels["gemv_lm_head"]["GB/s"])
-    small = small_configs(q4k, inputs, torch, dev, stream)
+    blocks = q8 = f16io = prefill = small = {}
+    ceiling = None
+    if not args.step_only:
+        blocks = decode_blocks(q4k, inputs, torch, dev, stream, args.steps, args.warmup)
+        q8 = q8_0_kernels(q4k, inputs, torch, dev, stream, args.steps, args.warmup)
+        f16io = f16_variants(q4k, inputs, torch, dev, stream, args.steps, args.warmup, not args.no_batched)
+        prefill = prefill_kernels(q4k, inputs, torch, dev, stream) if not args.no_batched else {}
+        ceiling = stream_read_ceiling(torch, dev, stream, kernels["gemv_lm_head"]["GB/s"])
+        small = small_configs(q4k, inputs, torch, dev, stream)
 
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s; per kernel {kernels}; "
         f"batched {batched}; decode blocks {blocks}; q8_0 {q8}; f16 i/o {f16io}; prefill {prefill}; "
