@@ -66,3 +66,63 @@ def test_decode_step_graph_replays_equal_eager():
         step()  # the program's own eager work between replays
         torch.cuda.synchronize()
         assert np.isfinite(lg.cpu().numpy()).all()
+
+
+def test_full_size_9b_step_in_a_graph():
+    """The decode step at its full 9B sizes, in the launch configuration the
+    benchmark times (a HIP graph of whole steps): fused gate+up SwiGLU
+    (2 x 12288 x 4096), down (4096 x 12288), lm_head (248320 x 4096).
+    Replays equal the eager step bit for bit; each stage is checked against
+    the oracle on the GPU's own input to that stage (h, y), on sampled rows."""
+    import torch
+
+    import oracle
+    from gpu_helpers import THREADS, check_bound, check_swiglu_bound, to_host
+    from q4_dequant_gemv_amd import q4k
+
+    torch.cuda.init()
+    oracle.build(force=False)
+    nff, k = inputs.SHAPES["gate_9b"]
+    nv = inputs.SHAPES["lm_head_9b"][0]
+    print("[case] full-size 9B step in a graph", flush=True)
+    wg_h = inputs.make_q4k(nff, k, config_id=2, tensor_id=0)
+    wu_h = inputs.make_q4k(nff, k, config_id=2, tensor_id=1)
+    wd_h = inputs.make_q4k(k, nff, config_id=2, tensor_id=2)
+    wl_h = inputs.make_q4k(nv, k, config_id=3, tensor_id=0)
+    x_h = inputs.make_x(1, k, config_id=2)[0]
+    wg, wu, wd, wl = (to_dev(a.reshape(-1)) for a in (wg_h, wu_h, wd_h, wl_h))
+    x = to_dev(x_h)
+    h = torch.empty(nff, device="cuda")
+    y = torch.empty(k, device="cuda")
+    logits = torch.empty(nv, device="cuda")
+
+    def step():
+        q4k.fused_swiglu(wg, wu, x, h=h)
+        q4k.gemv(wd, h, y=y)
+        q4k.gemv(wl, y, y=logits)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (h, y, logits)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(3):
+            step()
+    for rep in range(3):
+        for t in (h, y, logits):
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for t, e, nm in zip((h, y, logits), ref, ("h", "y", "logits")):
+            assert torch.equal(t, e), f"replay {rep}: {nm} differs from the eager step"
+        step()
+        torch.cuda.synchronize()
+    hh, yy, lg = (to_host(t) for t in ref)
+    rows = np.unique(np.r_[0:64, nff - 64:nff, np.random.default_rng(1).choice(nff, 1500, replace=False)])
+    sw = oracle.fused_swiglu(wg_h[rows], wu_h[rows], x_h, threads=THREADS)
+    check_swiglu_bound(hh[rows], sw, "9B step: SwiGLU")
+    yr, ar = oracle.gemv(wd_h, hh, threads=THREADS)
+    check_bound(yy, yr, ar, "9B step: down")
+    rows = np.unique(np.r_[0:64, nv - 64:nv, np.random.default_rng(2).choice(nv, 3000, replace=False)])
+    lr, la = oracle.gemv(wl_h[rows], yy, threads=THREADS)
+    check_bound(lg[rows], lr, la, "9B step: lm_head")
