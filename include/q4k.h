@@ -124,9 +124,11 @@ Q4K_API q4k_status q4k_gemv_residual(const void *w, const float *x, const float 
 
 /* One matrix of q4k_gemv_multi. */
 typedef struct {
-    const void *w; /* Q4_K matrix [n, k], 16-byte aligned */
-    float *y;      /* f32 [n] output */
-    int64_t n;     /* rows (0: skipped) */
+    const void *w;    /* Q4_K matrix [n, k], 16-byte aligned */
+    float *y;         /* f32 [n] output (the q half, [n/2], with y_gate) */
+    int64_t n;        /* rows (0: skipped) */
+    float *y_gate;    /* NULL, or the gate half [n/2] of a per-head interleaved q projection */
+    int64_t head_dim; /* with y_gate: rows per half head (a power of two dividing n/2) */
 } q4k_gemv_item;
 
 /* Largest number of matrices in one q4k_gemv_multi call. */
@@ -140,6 +142,15 @@ typedef struct {
  *   items : host array of `count` items, 0 <= count <= Q4K_MAX_MULTI
  * No output may overlap another output, any weight matrix, or x.  Each
  * result equals what q4k_gemv gives for that matrix.
+ *
+ * An item with y_gate set has its output de-interleaved per head as it is
+ * stored (the split of an attention-output-gate q projection, "@simulatte/
+ * doppler 0.1.7 -> 0.1.8", kernels/split_qg: q_proj rows interleave each
+ * head's q rows and gate rows).  With D = head_dim, row h*2D + j goes to
+ * y[h*D + j] for j < D and to y_gate[h*D + j - D] otherwise; the values are
+ * those q4k_gemv gives for the rows.  head_dim must be a power of two with
+ * n % (2*head_dim) == 0 (else Q4K_ERR_INVALID_ARG), and k <= 4096 (else
+ * Q4K_ERR_UNSUPPORTED_SHAPE).  Without y_gate, head_dim is ignored.
  */
 Q4K_API q4k_status q4k_gemv_multi(const q4k_gemv_item *items, int count, const float *x, int64_t k, void *stream);
 

@@ -218,6 +218,26 @@ def gemv_multi(ws, x: np.ndarray, threads: int = 1):
     return [gemv(w, x, threads=threads) for w in ws]
 
 
+def split_qg(y: np.ndarray, head_dim: int):
+    """(q, gate): the per-head de-interleave of a q projection's output
+    ("@simulatte/doppler 0.1.7 -> 0.1.8", kernels/split_qg.wgsl): the rows
+    of head h are 2*head_dim apart, its first head_dim rows are q and the
+    next head_dim the gate, so q[h*D + d] = y[h*2D + d] and
+    gate[h*D + d] = y[h*2D + D + d] with D = head_dim."""
+    y = np.asarray(y)
+    n = y.shape[0]
+    d2 = 2 * head_dim
+    if head_dim <= 0 or n % d2 != 0:
+        raise ValueError("the output length must be a multiple of 2 * head_dim")
+    q = np.empty(n // 2, dtype=y.dtype)
+    g = np.empty(n // 2, dtype=y.dtype)
+    for h in range(n // d2):
+        for d in range(head_dim):
+            q[h * head_dim + d] = y[h * d2 + d]
+            g[h * head_dim + d] = y[h * d2 + head_dim + d]
+    return q, g
+
+
 # ------------------------------------------------------------------- Q8_0
 def _q8_rows(w: np.ndarray, k: int) -> np.ndarray:
     if k % Q8_0_BLOCK_WEIGHTS != 0:

@@ -177,12 +177,24 @@ q4k_status q4k_gemv_multi(const q4k_gemv_item *items, int count, const float *x,
     for (int i = 0; i < count; ++i) {
         const q4k_status s = check_shape(items[i].n, k, &wbytes[i]);
         if (s != Q4K_OK) return s;
-        rows += items[i].n;
+        const q4k_gemv_item &it = items[i];
+        if (it.y_gate != nullptr && it.n != 0) {
+            // per-head de-interleave: a power-of-two head size dividing n / 2
+            const int64_t hd = it.head_dim;
+            if (hd <= 0 || hd > (int64_t{1} << 30) || (hd & (hd - 1)) != 0) return Q4K_ERR_INVALID_ARG;
+            if (it.n % (2 * hd) != 0) return Q4K_ERR_INVALID_ARG;
+            if (k > 4096) return Q4K_ERR_UNSUPPORTED_SHAPE;  // one launch only up to k = 4096
+        }
+        rows += it.n;
     }
     if (rows == 0) return Q4K_OK;
     if (k > 0 && x == nullptr) return Q4K_ERR_INVALID_ARG;
     if (!aligned(x, 4)) return Q4K_ERR_MISALIGNED;
     const uint64_t xb = static_cast<uint64_t>(k) * 4;
+    // every output range: y (all n rows, or the q half) and the gate half
+    const void *out_p[2 * Q4K_MAX_MULTI];
+    uint64_t out_b[2 * Q4K_MAX_MULTI];
+    int nout = 0;
     q4k::GemvJob jobs[Q4K_MAX_MULTI];
     for (int i = 0; i < count; ++i) {
         const q4k_gemv_item &it = items[i];
@@ -190,16 +202,33 @@ q4k_status q4k_gemv_multi(const q4k_gemv_item *items, int count, const float *x,
             jobs[i] = q4k::GemvJob{nullptr, nullptr, nullptr, 0};
             continue;
         }
+        const bool split = it.y_gate != nullptr;
         if (it.y == nullptr || (k > 0 && it.w == nullptr)) return Q4K_ERR_INVALID_ARG;
-        if (!aligned(it.w, 16) || !aligned(it.y, 4)) return Q4K_ERR_MISALIGNED;
-        const uint64_t yb = static_cast<uint64_t>(it.n) * 4;
-        if (overlap(it.y, yb, x, xb)) return Q4K_ERR_INVALID_ARG;
-        for (int j = 0; j < count; ++j) {
-            if (items[j].n == 0) continue;
-            if (overlap(it.y, yb, items[j].w, wbytes[j])) return Q4K_ERR_INVALID_ARG;
-            if (j != i && overlap(it.y, yb, items[j].y, static_cast<uint64_t>(items[j].n) * 4)) return Q4K_ERR_INVALID_ARG;
+        if (!aligned(it.w, 16) || !aligned(it.y, 4) || !aligned(it.y_gate, 4)) return Q4K_ERR_MISALIGNED;
+        const uint64_t yb = static_cast<uint64_t>(split ? it.n / 2 : it.n) * 4;
+        out_p[nout] = it.y;
+        out_b[nout++] = yb;
+        if (split) {
+            out_p[nout] = it.y_gate;
+            out_b[nout++] = yb;
         }
         jobs[i] = q4k::GemvJob{static_cast<const uint8_t *>(it.w), it.y, nullptr, it.n};
+        if (split) {
+            jobs[i].y_gate = it.y_gate;
+            int lg = 0;
+            while ((int64_t{1} << lg) < it.head_dim) ++lg;
+            jobs[i].head_log2 = lg;
+        }
+    }
+    // no output may overlap x, any weight matrix or another output
+    for (int a = 0; a < nout; ++a) {
+        if (overlap(out_p[a], out_b[a], x, xb)) return Q4K_ERR_INVALID_ARG;
+        for (int j = 0; j < count; ++j) {
+            if (items[j].n != 0 && overlap(out_p[a], out_b[a], items[j].w, wbytes[j])) return Q4K_ERR_INVALID_ARG;
+        }
+        for (int b = a + 1; b < nout; ++b) {
+            if (overlap(out_p[a], out_b[a], out_p[b], out_b[b])) return Q4K_ERR_INVALID_ARG;
+        }
     }
     return from_hip(q4k::launch_gemv_multi(jobs, count, nullptr, x, k, static_cast<hipStream_t>(stream)));
 }
@@ -441,6 +470,6 @@ const char *q4k_status_string(q4k_status s) {
     return "unknown status";
 }
 
-int q4k_abi_version(void) { return 106; }
+int q4k_abi_version(void) { return 107; }
 
 }  // extern "C"

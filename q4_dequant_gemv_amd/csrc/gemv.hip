@@ -195,6 +195,8 @@ struct MatTable {
     void *y[kMaxMats];  // YT [n] each
     const float *r[kMaxMats];
     int64_t n[kMaxMats];
+    void *y_gate[kMaxMats];  // with head_log2: the gate half of each head's rows
+    int head_log2[kMaxMats];
     int it_begin[kMaxMats + 1];
     int tail_bytes[kMaxMats];
     int count;
@@ -206,9 +208,10 @@ struct MatTable {
 // counts in the streaming loop more conservative.  RPG: rows per lane group
 // and iteration (the lane takes its group of RPG rows, 64/LPR rows apart),
 // which puts RPG rows per buffer in flight with the same activation
-// registers.
+// registers.  QG: some matrix of the table de-interleaves its output per
+// head (y_gate set); only then does the store path remap rows.
 template <class F, typename XT, typename YT, int LPR, bool SWIGLU, bool RES, int NB, int BLOCK, int MIN_WAVES,
-          int RPG>
+          int RPG, bool QG = false>
 __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable mt, const uint8_t *__restrict__ wu,
                                                                 const XT *x, int ngroups, int64_t row_bytes) {
     static_assert(NB >= 2, "at least one row in flight");
@@ -247,9 +250,12 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
         int64_t n;
         YT *y;
         const float *r;
+        YT *yg;
+        int hl;
     };
     LoadCursor lc{0, 0, mt.it_begin[1], mt.tail_bytes[0], mt.w[0]};
-    RowCursor rc{0, 0, mt.it_begin[1], mt.n[0], static_cast<YT *>(mt.y[0]), mt.r[0]};
+    RowCursor rc{0, 0, mt.it_begin[1], mt.n[0], static_cast<YT *>(mt.y[0]), mt.r[0], static_cast<YT *>(mt.y_gate[0]),
+                 mt.head_log2[0]};
     auto issue = [&](RowLoads<F, NMAT> (&b)[RPG], int it) {
         while (it >= lc.end && lc.mi + 1 < count) {
             ++lc.mi;
@@ -281,7 +287,21 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
             rc.n = mt.n[rc.mi];
             rc.y = static_cast<YT *>(mt.y[rc.mi]);
             rc.r = mt.r[rc.mi];
+            if constexpr (QG) {
+                rc.yg = static_cast<YT *>(mt.y_gate[rc.mi]);
+                rc.hl = mt.head_log2[rc.mi];
+            }
         }
+    };
+    // Where row `row` of the current matrix goes: rows of head h are 2D
+    // apart (D = 2^hl), the first D of them to y, the next D to the gate
+    // output.  A plain matrix has hl so large that every row is in head 0's
+    // first half: y + row.
+    auto dest = [&](int64_t row) -> YT * {
+        const int64_t d = int64_t{1} << rc.hl;
+        const int64_t h = row >> (rc.hl + 1);
+        const int64_t j = row - (h << (rc.hl + 1));
+        return j < d ? rc.y + (h << rc.hl) + j : rc.yg + (h << rc.hl) + (j - d);
     };
 
     const int nwaves = static_cast<int>(gridDim.x) * kWavesPerBlock;
@@ -363,7 +383,8 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
                     const float out = SWIGLU ? silu(acc[0]) * acc[1] : acc[0];
                     const bool mine = sub == win;
                     yv = mine ? out : yv;
-                    yp = mine ? (rok ? rc.y + row : nullptr) : yp;
+                    if constexpr (QG) yp = mine ? (rok ? dest(row) : nullptr) : yp;
+                    else yp = mine ? (rok ? rc.y + row : nullptr) : yp;
                     if constexpr (RES) rp = mine ? (rc.r != nullptr ? rc.r + row : nullptr) : rp;
                     if (++win == LPR) flush();
                 }
@@ -570,10 +591,10 @@ int resident_blocks_per_cu(Kernel kern, int block, size_t lds, std::atomic<int> 
 
 // One launch of the batch-1 kernel over `count` matrices (all with k columns).
 template <class F, typename XT, typename YT, int LPR, bool SWIGLU, bool RES, int NB, int BLOCK, int MIN_WAVES,
-          int RPG>
+          int RPG, bool QG = false>
 hipError_t launch_fast_kernel(const GemvJob *jobs, int count, const uint8_t *wu, const void *x, int64_t k,
                               hipStream_t stream) {
-    auto kern = gemv_kernel<F, XT, YT, LPR, SWIGLU, RES, NB, BLOCK, MIN_WAVES, RPG>;
+    auto kern = gemv_kernel<F, XT, YT, LPR, SWIGLU, RES, NB, BLOCK, MIN_WAVES, RPG, QG>;
     const int ngroups = static_cast<int>(k / 64);
     const int64_t row_bytes = F::row_bytes(k);
     const size_t lds = static_cast<size_t>(ngroups) * sizeof(XGroup);
@@ -589,6 +610,8 @@ hipError_t launch_fast_kernel(const GemvJob *jobs, int count, const uint8_t *wu,
         mt.y[i] = jobs[i].y;
         mt.r[i] = jobs[i].r;
         mt.n[i] = jobs[i].n;
+        mt.y_gate[i] = jobs[i].y_gate;
+        mt.head_log2[i] = jobs[i].head_log2;
         mt.it_begin[i] = static_cast<int>(total);
         mt.tail_bytes[i] = static_cast<int>((jobs[i].n - (iters - 1) * kRowsPerWave) * row_bytes);
         total += iters;
@@ -608,9 +631,18 @@ hipError_t launch_fast_kernel(const GemvJob *jobs, int count, const uint8_t *wu,
 template <class F, typename XT, typename YT, int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES, int RPG = 1>
 hipError_t launch_fast(const GemvJob *jobs, int count, const uint8_t *wu, const void *x, int64_t k,
                        hipStream_t stream) {
-    bool res = false;
-    for (int i = 0; i < count; ++i) res = res || jobs[i].r != nullptr;
+    bool res = false, qg = false;
+    for (int i = 0; i < count; ++i) {
+        res = res || jobs[i].r != nullptr;
+        qg = qg || jobs[i].y_gate != nullptr;
+    }
     if constexpr (std::is_same_v<XT, float> && std::is_same_v<YT, float> && !SWIGLU) {
+        // a per-head de-interleave comes only from the multi-matrix call,
+        // which has no residual
+        if (qg) {
+            return launch_fast_kernel<F, XT, YT, LPR, SWIGLU, false, NB, BLOCK, MIN_WAVES, RPG, true>(jobs, count, wu, x,
+                                                                                                    k, stream);
+        }
         if (res) {
             return launch_fast_kernel<F, XT, YT, LPR, SWIGLU, true, NB, BLOCK, MIN_WAVES, RPG>(jobs, count, wu, x, k,
                                                                                               stream);
@@ -771,8 +803,11 @@ hipError_t launch_gemv_multi(const GemvJob *jobs, int count, const uint8_t *w_up
         if (jobs[i].n == 0) continue;
         if (k == 0) {
             float *y = static_cast<float *>(jobs[i].y);
-            const hipError_t e = jobs[i].r != nullptr ? launch_copy(y, jobs[i].r, jobs[i].n, stream)
-                                                      : launch_fill_zero(y, jobs[i].n, stream);
+            const bool split = jobs[i].y_gate != nullptr;
+            const int64_t ny = split ? jobs[i].n / 2 : jobs[i].n;
+            hipError_t e = jobs[i].r != nullptr ? launch_copy(y, jobs[i].r, ny, stream)
+                                                : launch_fill_zero(y, ny, stream);
+            if (e == hipSuccess && split) e = launch_fill_zero(static_cast<float *>(jobs[i].y_gate), ny, stream);
             if (e != hipSuccess) return e;
             continue;
         }

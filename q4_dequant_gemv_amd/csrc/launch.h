@@ -37,6 +37,12 @@ struct GemvJob {
     void *y;  // f32 [n] (f16 for launch_gemv_dt with y_f16)
     const float *r;
     int64_t n;
+    // Per-head de-interleave of the output (q and gate halves of each head):
+    // with y_gate set, row r = h*2D + j (D = 2^head_log2) goes to y[h*D + j]
+    // if j < D, else to y_gate[h*D + j - D].  kPlainHead: every row r to y[r].
+    void *y_gate = nullptr;
+    int head_log2 = kPlainHead;
+    static constexpr int kPlainHead = 61;
 };
 
 // y[i] = sum_c W[i,c] x[c] (+ r[i]); with w_up != nullptr computes

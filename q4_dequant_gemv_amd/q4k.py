@@ -44,7 +44,8 @@ MAX_MULTI = 8
 class GemvItem(ctypes.Structure):
     """q4k_gemv_item: one matrix of a gemv_multi call."""
 
-    _fields_ = [("w", ctypes.c_void_p), ("y", ctypes.c_void_p), ("n", ctypes.c_int64)]
+    _fields_ = [("w", ctypes.c_void_p), ("y", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("y_gate", ctypes.c_void_p), ("head_dim", ctypes.c_int64)]
 
 
 class Q4KError(RuntimeError):
@@ -299,25 +300,49 @@ def gemv_residual(w, x, r, y=None, n: int | None = None, stream=None):
     return y
 
 
-def gemv_multi(ws, x, ys=None, ns=None, stream=None):
-    """ys[j][i] = sum_c W_j[i,c] x[c] for up to MAX_MULTI matrices sharing ``x``, in one launch."""
+def gemv_multi(ws, x, ys=None, ns=None, gates=None, head_dims=None, stream=None):
+    """ys[j][i] = sum_c W_j[i,c] x[c] for up to MAX_MULTI matrices sharing ``x``, in one launch.
+
+    ``gates[j]`` (a tensor, or None) with ``head_dims[j]`` de-interleaves matrix
+    j's output per head: its q rows go to ``ys[j]`` and its gate rows to
+    ``gates[j]`` (n/2 each)."""
     import torch
 
     k = x.numel()
     ws = list(ws)
     ns = [rows_of(w, k) for w in ws] if ns is None else list(ns)
+    gates = [None] * len(ws) if gates is None else list(gates)
+    head_dims = [0] * len(ws) if head_dims is None else list(head_dims)
     if ys is None:
-        ys = [torch.empty(n, dtype=torch.float32, device=x.device) for n in ns]
+        ys = [torch.empty(n // 2 if g is not None else n, dtype=torch.float32, device=x.device)
+              for n, g in zip(ns, gates)]
     ys = list(ys)
-    if not (len(ws) == len(ys) == len(ns)):
-        raise ValueError("ws, ys and ns must have the same length")
+    if not (len(ws) == len(ys) == len(ns) == len(gates) == len(head_dims)):
+        raise ValueError("ws, ys, ns, gates and head_dims must have the same length")
     items = (GemvItem * max(len(ws), 1))()
-    for i, (w, y, n) in enumerate(zip(ws, ys, ns)):
+    for i, (w, y, n, g, hd) in enumerate(zip(ws, ys, ns, gates, head_dims)):
         items[i].w = _dev(w, f"ws[{i}]", torch.uint8).value
         items[i].y = _dev(y, f"ys[{i}]", torch.float32).value
         items[i].n = n
+        items[i].y_gate = _dev(g, f"gates[{i}]", torch.float32).value if g is not None else None
+        items[i].head_dim = hd
     _check(lib().q4k_gemv_multi(items, len(ws), _dev(x, "x", torch.float32), k, _stream(stream)), "q4k_gemv_multi")
     return ys
+
+
+def gemv_split_qg(w, x, head_dim: int, q=None, g=None, n: int | None = None, stream=None):
+    """The q projection of an attention-output-gate model with its output
+    de-interleaved per head as it is stored: returns (q, gate), n/2 each."""
+    import torch
+
+    k = x.numel()
+    n = rows_of(w, k) if n is None else n
+    if q is None:
+        q = torch.empty(n // 2, dtype=torch.float32, device=x.device)
+    if g is None:
+        g = torch.empty(n // 2, dtype=torch.float32, device=x.device)
+    gemv_multi([w], x, ys=[q], ns=[n], gates=[g], head_dims=[head_dim], stream=stream)
+    return q, g
 
 
 def q8_0_rows_of(w, k: int) -> int:

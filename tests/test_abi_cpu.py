@@ -57,7 +57,7 @@ def test_only_the_abi_is_exported():
 
 
 def test_status_strings(L):
-    assert L.q4k_abi_version() == 106
+    assert L.q4k_abi_version() == 107
     for s in range(5):
         assert len(L.q4k_status_string(s)) > 0
     assert L.q4k_status_string(99) == b"unknown status"
@@ -239,11 +239,14 @@ def test_workspace_size_queries(L):
 
 
 def _items(*triples):
+    """(w, y, n) or (w, y, n, y_gate, head_dim) per item."""
     from q4_dequant_gemv_amd import q4k
 
     items = (q4k.GemvItem * max(len(triples), 1))()
-    for i, (w, y, n) in enumerate(triples):
-        items[i].w, items[i].y, items[i].n = w, y, n
+    for i, t in enumerate(triples):
+        items[i].w, items[i].y, items[i].n = t[:3]
+        if len(t) == 5:
+            items[i].y_gate, items[i].head_dim = t[3:]
     return items
 
 
@@ -265,6 +268,24 @@ def _items(*triples):
 ])
 def test_multi_validation(L, triples, count, x, k, status):
     assert L.q4k_gemv_multi(_items(*triples), count, ctypes.c_void_p(x), k, None) == status
+
+
+Y3 = A + 0x50000000
+
+
+@pytest.mark.parametrize("triples,k,status", [
+    ([(W, Y, 4096, Y3, 0)], 1024, INVALID),                     # head_dim must be positive
+    ([(W, Y, 4096, Y3, 96)], 1024, INVALID),                    # not a power of two
+    ([(W, Y, 4000, Y3, 256)], 1024, INVALID),                   # n not a multiple of 2 * head_dim
+    ([(W, Y, 4096, Y3, 256)], 8192, SHAPE),                     # one launch only up to k = 4096
+    ([(W, Y, 4096, Y + 8000, 256)], 1024, INVALID),             # gate half overlaps the q half
+    ([(W, Y, 4096, Y3, 256), (Y2, Y3 + 4096, 16)], 1024, INVALID),  # another output inside the gate half
+    ([(W, Y, 4096, W + 64, 256)], 1024, INVALID),               # gate output overlaps the matrix
+    ([(W, Y, 4096, Y3 + 2, 256)], 1024, MISALIGNED),
+    ([(W, Y, 0, Y3, 96)], 1024, OK),                            # empty item: nothing checked beyond the shape
+])
+def test_multi_split_qg_validation(L, triples, k, status):
+    assert L.q4k_gemv_multi(_items(*triples), len(triples), ctypes.c_void_p(X), k, None) == status
 
 
 def test_multi_null_items(L):

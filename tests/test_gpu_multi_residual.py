@@ -9,6 +9,8 @@ oracle on the same seeded inputs.
     the oracle's f64 W x + r (the GPU adds r to its f32 sum: one more rounding,
     at most 2^-24 of that magnitude); in place (y is r) and out of place give
     the same bits.
+  * q4k_gemv_multi with a gate output: the per-head de-interleave of a q
+    projection's rows, bitwise the plain GEMV's values in their new places.
 """
 
 from __future__ import annotations
@@ -113,6 +115,69 @@ def test_multi_repeated_launches_bitwise(q4k):
             s.synchronize()
             for y, b in zip(ys, base):
                 np.testing.assert_array_equal(to_host(y), b)
+
+
+def _split_case(q4k, shapes, split, k, cfg, label):
+    """gemv_multi where matrix i (split[i] = head_dim, or 0) writes its output
+    de-interleaved per head into q and gate halves: bitwise the plain GEMV's
+    values reordered, and inside the oracle's bound after the oracle's own
+    de-interleave."""
+    import torch
+
+    ws = [inputs.make_q4k(n, k, config_id=cfg, tensor_id=i) for i, n in enumerate(shapes)]
+    x = inputs.make_x(1, k, config_id=cfg, tensor_id=100)[0]
+    wds = [to_dev(w.reshape(-1)) for w in ws]
+    xd = to_dev(x)
+    ys = [_nan(n // 2 if hd else n) for n, hd in zip(shapes, split)]
+    gs = [_nan(n // 2) if hd else None for n, hd in zip(shapes, split)]
+    print(f"[case] {label}: multi rows={list(shapes)} heads={list(split)} k={k}", flush=True)
+    q4k.gemv_multi(wds, xd, ys=ys, ns=list(shapes), gates=gs, head_dims=list(split))
+    torch.cuda.synchronize()
+    for i, (w, n, hd) in enumerate(zip(ws, shapes, split)):
+        alone = to_host(q4k.gemv(wds[i], xd, n=n))
+        yr, ar = oracle.gemv(w, x, threads=THREADS)
+        if not hd:
+            np.testing.assert_array_equal(to_host(ys[i]), alone)
+            continue
+        q, g = to_host(ys[i]), to_host(gs[i])
+        aq, ag = oracle.split_qg(alone, hd)
+        np.testing.assert_array_equal(q, aq)
+        np.testing.assert_array_equal(g, ag)
+        rq, rg = oracle.split_qg(yr, hd)
+        sq, sg = oracle.split_qg(ar, hd)
+        _report(f"{label}[{i}] q", check_bound(q, rq, sq, f"{label}[{i}] q"))
+        _report(f"{label}[{i}] gate", check_bound(g, rg, sg, f"{label}[{i}] gate"))
+
+
+def test_multi_split_qg_q_proj_0p8b(q4k):
+    """The 0.8B q projection (8 heads x 256, q and gate interleaved per head:
+    4096 x 1024) de-interleaved in the launch that also carries two other
+    matrices."""
+    _split_case(q4k, (4096, 512, 512), (256, 0, 0), 1024, 71, "q_proj 0.8B split")
+
+
+@pytest.mark.parametrize("shapes,split,k", [
+    ((24,), (4,), 256), ((2,), (1,), 512), ((64, 7), (32, 0), 2048), ((512, 256), (128, 64), 4096),
+    ((8192,), (1024,), 1024), ((4,), (2,), 3072)])
+def test_multi_split_qg_shapes(q4k, shapes, split, k):
+    _split_case(q4k, shapes, split, k, 72, f"split {shapes}")
+
+
+def test_gemv_split_qg_helper_and_k_zero(q4k):
+    import torch
+
+    n, k, hd = 1024, 2048, 64
+    w = to_dev(inputs.make_q4k(n, k, config_id=73).reshape(-1))
+    x = to_dev(inputs.make_x(1, k, config_id=73)[0])
+    q, g = q4k.gemv_split_qg(w, x, hd)
+    aq, ag = oracle.split_qg(to_host(q4k.gemv(w, x)), hd)
+    np.testing.assert_array_equal(to_host(q), aq)
+    np.testing.assert_array_equal(to_host(g), ag)
+    q0 = torch.full((8,), 5.0, device="cuda")
+    g0 = torch.full((8,), 5.0, device="cuda")
+    q4k.gemv_split_qg(torch.empty(0, dtype=torch.uint8, device="cuda"), torch.empty(0, device="cuda"), 4, q=q0, g=g0,
+                      n=16)
+    assert np.all(to_host(q0) == 0) and np.all(to_host(g0) == 0)
 
 
 def test_multi_k_zero_writes_zeros(q4k):

@@ -311,6 +311,28 @@ def test_threads_do_not_change_results(oracle_mod):
     np.testing.assert_array_equal(yb[1], -y1)
 
 
+def test_split_qg_pins(oracle_mod):
+    """The per-head de-interleave ("@simulatte/doppler 0.1.7 -> 0.1.8",
+    kernels/split_qg.wgsl): q[h*D + d] = y[h*2D + d], gate[h*D + d] =
+    y[h*2D + D + d]."""
+    # worked by hand: two heads of D = 2 over y = 0..7
+    q, g = oracle_mod.split_qg(np.arange(8.0), 2)
+    np.testing.assert_array_equal(q, [0, 1, 4, 5])
+    np.testing.assert_array_equal(g, [2, 3, 6, 7])
+    # one head: q is the first half of the rows, the gate the second
+    y = np.random.default_rng(0).standard_normal(512)
+    q, g = oracle_mod.split_qg(y, 256)
+    np.testing.assert_array_equal(q, y[:256])
+    np.testing.assert_array_equal(g, y[256:])
+    # the split is a bijection: interleaving q and gate head by head gives y back
+    y = np.random.default_rng(1).standard_normal(8 * 2 * 64)
+    q, g = oracle_mod.split_qg(y, 64)
+    back = np.stack([q.reshape(8, 64), g.reshape(8, 64)], axis=1).reshape(-1)
+    np.testing.assert_array_equal(back, y)
+    with pytest.raises(ValueError):
+        oracle_mod.split_qg(np.zeros(300), 64)
+
+
 def test_silu_special_cases(oracle_mod):
     # one-row matrices whose g is fixed: silu(0) = 0, silu(t) ~ t, silu(-t) ~ 0
     blocks = _integer_blocks(1, 15)
