@@ -40,7 +40,8 @@
  *    offsets (w + r0*(k/256)*144, y + r0), which keep 16-byte alignment.
  *  - n == 0 or m == 0 is an empty call: Q4K_OK, nothing launched.  k == 0 is
  *    a valid empty sum: outputs are written as 0 (dequant writes nothing).
- *  - Activations and outputs are f32.  The products use the factored form
+ *  - Activations and outputs are f32, except where a call takes a q4k_dtype
+ *    (and the prefill GEMM, whose activations are f16).  The products use the factored form
  *    sum_j [d*sc_j * sum_{e in j} q_e x_e - dmin*m_j * sum_{e in j} x_e]
  *    in f32; each result satisfies |y - y_exact| <= 2e-4 * sum_k |w_k x_k|
  *    for finite inputs (non-finite x gives NaN in the affected outputs).
@@ -64,7 +65,7 @@ extern "C" {
 typedef enum {
     Q4K_OK = 0,
     Q4K_ERR_INVALID_ARG = 1,       /* null pointer, negative size, overlap, size overflow */
-    Q4K_ERR_UNSUPPORTED_SHAPE = 2, /* k % 256 != 0 */
+    Q4K_ERR_UNSUPPORTED_SHAPE = 2, /* k % 256 != 0, or a shape beyond a call's stated limits */
     Q4K_ERR_MISALIGNED = 3,        /* w not 16-B aligned, or x/y not 4-B aligned */
     Q4K_ERR_LAUNCH = 4             /* the HIP runtime refused a launch */
 } q4k_status;
@@ -271,7 +272,9 @@ Q4K_API q4k_status q4k_dequant(const void *w, float *out, int64_t n, int64_t k, 
 /* Static, NUL-terminated description of a status code. */
 Q4K_API const char *q4k_status_string(q4k_status s);
 
-/* ABI version of this header (major*100 + minor). */
+/* ABI version of this header (major*100 + minor); q4k_abi_version() of the
+ * library it was built with returns the same number. */
+#define Q4K_ABI_VERSION 107
 Q4K_API int q4k_abi_version(void);
 
 #ifdef __cplusplus
