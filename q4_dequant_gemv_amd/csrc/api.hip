@@ -470,6 +470,6 @@ const char *q4k_status_string(q4k_status s) {
     return "unknown status";
 }
 
-int q4k_abi_version(void) { return 107; }
+int q4k_abi_version(void) { return Q4K_ABI_VERSION; }
 
 }  // extern "C"
