@@ -561,8 +561,9 @@ F16_DENSE_PEAK_TFLOPS = 2500.0
 
 def prefill_kernels(q4k, inputs, torch, dev, stream):
     """The prefill GEMM (q4k_prefill_gemm, f16 activations, f32 outputs) on
-    the 9B gate and down projections at m = 128 .. 2048 tokens, and the
-    batched call on the same f16 activations for comparison."""
+    the 9B gate and down projections at m = 128 .. 2048 tokens, and, for
+    comparison, the skinny-GEMM path on the same activations widened to f32
+    (an f16 batched call of these sizes runs the prefill GEMM itself)."""
     out = {}
     for nm in ("gate_9b", "down_9b"):
         n, k = inputs.SHAPES[nm]
@@ -575,8 +576,10 @@ def prefill_kernels(q4k, inputs, torch, dev, stream):
             rec = {"mean_us": round(t * 1e6, 2), "TFLOP/s": round(tf, 1),
                    "frac_f16_peak": round(tf / F16_DENSE_PEAK_TFLOPS, 4)}
             if m <= 512:
-                tb = _time_launches(lambda i: q4k.gemv_batched_dt(w, xh, y=y, stream=stream), torch, stream, 10, 2)
-                rec["batched_call_us"] = round(tb * 1e6, 2)
+                xf = xh.float()
+                tb = _time_launches(lambda i: q4k.gemv_batched_dt(w, xf, y=y, stream=stream), torch, stream, 10, 2)
+                rec["batched_f32_call_us"] = round(tb * 1e6, 2)
+                del xf
             out[f"{nm} m={m}"] = rec
         del w
     return out

@@ -192,7 +192,10 @@ Q4K_API q4k_status q4k_gemv_batched(const void *w, const float *x, float *y, int
  * skinny-GEMM side of selectQ4KFusedVariant's aDtype / wantF16Output choice
  * ("@simulatte/doppler 0.1.7 -> 0.1.8", matmul-selection.js).  Computes what
  * q4k_gemv_batched computes on the activations widened to f32; f16 outputs
- * are rounded to nearest even.  The scratch is that of q4k_gemv_batched,
+ * are rounded to nearest even.  With f16 activations, m >= 128 and a
+ * 16-byte aligned x the call runs q4k_prefill_gemm instead (the kernel for
+ * prefill sizes): the same bound and bitwise reproducible, but not bit for
+ * bit the f32 path's result.  The scratch is that of q4k_gemv_batched,
  * plus 4*m*n bytes for an f16 output when K is split across workgroups (the
  * partial sums are added in f32 first).  Errors and aliasing as
  * q4k_gemv_batched; an unknown dtype is Q4K_ERR_INVALID_ARG.

@@ -573,6 +573,18 @@ hipError_t launch_gemv_batched_dt(const uint8_t *w, const void *x, bool x_f16, v
                      : launch_fill_zero(static_cast<float *>(y), m * n, stream);
     }
     if (m == 1) return launch_gemv_dt(w, x, x_f16, y, y_f16, n, k, stream);
+    // Prefill sizes with f16 activations: the prefill GEMM (exact f16
+    // operands, 128-token tiles) is the faster kernel there.  It reads x in
+    // 16-byte pieces, so it takes only a 16-byte aligned x; a size query,
+    // which does not know x, makes room for either path.
+    if (x_f16 && m >= kPrefillMinTokens && k <= kPrefillMaxK) {
+        if (ws.query) {
+            const hipError_t e = launch_prefill(w, static_cast<const _Float16 *>(x), y, y_f16, m, n, k, ws, stream);
+            if (e != hipSuccess) return e;
+        } else if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+            return launch_prefill(w, static_cast<const _Float16 *>(x), y, y_f16, m, n, k, ws, stream);
+        }
+    }
     using H = _Float16;
     if (x_f16 && y_f16) return batched_slices(w, static_cast<const H *>(x), static_cast<H *>(y), m, n, k, ws, stream);
     if (x_f16) return batched_slices(w, static_cast<const H *>(x), static_cast<float *>(y), m, n, k, ws, stream);

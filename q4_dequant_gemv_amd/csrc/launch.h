@@ -76,6 +76,10 @@ hipError_t launch_gemv_batched_dt(const uint8_t *w, const void *x, bool x_f16, v
 // x f16 [m, k] (16-byte aligned), y f32 or f16 [m, n].
 hipError_t launch_prefill(const uint8_t *w, const _Float16 *x, void *y, bool y_f16, int64_t m, int64_t n, int64_t k,
                           Workspace &ws, hipStream_t stream);
+// The batched call with f16 activations hands m >= kPrefillMinTokens tokens
+// (16-byte aligned x, k <= kPrefillMaxK) to the prefill GEMM.
+constexpr int64_t kPrefillMinTokens = 128;
+constexpr int64_t kPrefillMaxK = int64_t{1} << 24;
 
 // Writes zeros to y[0..count) (the k == 0 empty sum).
 hipError_t launch_fill_zero(float *y, int64_t count, hipStream_t stream);

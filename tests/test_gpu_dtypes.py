@@ -137,6 +137,40 @@ def test_batched_dt_all_combinations(q4k, m, n, k):
             assert torch.equal(y16, y32.half()), f"{xd}: f16 output is not the rounded f32 result"
 
 
+@pytest.mark.parametrize("m,n,k", [(128, 1024, 2048), (300, 700, 4096), (129, 96, 12288)])
+def test_batched_dt_f16_prefill_sizes_route_to_prefill(q4k, m, n, k):
+    """f16 activations at m >= 128 (16-byte aligned): the batched call runs the
+    prefill GEMM, so it equals q4k_prefill_gemm bit for bit (also through a
+    workspace of the queried size), and stays inside the oracle's bound.  An
+    x that is only 2-byte aligned takes the skinny-GEMM path, also inside the
+    bound, with the same workspace size."""
+    import torch
+
+    w = inputs.make_q4k(n, k, config_id=64, tensor_id=k)
+    x16 = _f16_x(m, k, 64, m)
+    wd, xh = to_dev(w.reshape(-1)), to_dev(x16)
+    assert xh.data_ptr() % 16 == 0
+    print(f"[case] batched_dt f16 m={m} {n}x{k}", flush=True)
+    for yd in (torch.float32, torch.float16):
+        yb = q4k.gemv_batched_dt(wd, xh, out_dtype=yd)
+        yp = q4k.prefill_gemm(wd, xh, out_dtype=yd)
+        torch.cuda.synchronize()
+        assert torch.equal(yb, yp), "f16 batched call at prefill sizes differs from the prefill GEMM"
+    need = q4k.gemv_batched_workspace_size(m, n, k, x_dtype=torch.float16, out_dtype=torch.float32)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    yw = q4k.gemv_batched_ws(wd, xh, ws, out_dtype=torch.float32)
+    assert torch.equal(yw, q4k.prefill_gemm(wd, xh, out_dtype=torch.float32))
+    yr, ar = oracle.gemv_batched(w, x16.astype(np.float32), threads=THREADS)
+    check_bound(to_host(yw), yr, ar, f"batched_dt f16 m={m} {n}x{k} (prefill)")
+    # the same activations 2 bytes into an allocation: the skinny-GEMM path
+    big = torch.empty(m * k + 1, dtype=torch.float16, device="cuda")
+    xv = big[1:].view(m, k)
+    xv.copy_(xh)
+    assert xv.data_ptr() % 16 == 2
+    y2 = q4k.gemv_batched_ws(wd, xv, ws, out_dtype=torch.float32)
+    check_bound(to_host(y2), yr, ar, f"batched_dt f16 m={m} {n}x{k} (2-byte aligned x)")
+
+
 def test_batched_dt_k_zero(q4k):
     import torch
 
