@@ -573,6 +573,12 @@ hipError_t launch_gemv_batched_dt(const uint8_t *w, const void *x, bool x_f16, v
                      : launch_fill_zero(static_cast<float *>(y), m * n, stream);
     }
     if (m == 1) return launch_gemv_dt(w, x, x_f16, y, y_f16, n, k, stream);
+    // A few tokens: the streaming GEMV with the codes decoded once per token
+    // pair, no scratch.
+    if ((m <= kTokensMax && k <= kTokensMaxK) || (m == 2 && k <= kTokensSplitMaxK)) {
+        if (ws.query) return hipSuccess;
+        return launch_gemv_tokens(w, x, x_f16, y, y_f16, m, n, k, stream);
+    }
     // Prefill sizes with f16 activations: the prefill GEMM (exact f16
     // operands, 128-token tiles) is the faster kernel there.  It reads x in
     // 16-byte pieces, so it takes only a 16-byte aligned x; a size query,

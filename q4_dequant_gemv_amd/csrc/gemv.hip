@@ -85,6 +85,18 @@ struct Q4KFormat {
         decode_group(l.hdr, l.qa, l.qb, g.ps, c);
         return group_dot(c, xr);
     }
+    // the same for MT tokens, the codes decoded once; acc[t] in units of 1
+    template <int MT>
+    static __device__ __forceinline__ void dot_tokens(const Loads &l, const Lane &g, const XRegs (&xr)[MT], bool active,
+                                                      float (&acc)[MT]) {
+        GroupCodes c;
+        decode_group(l.hdr, l.qa, l.qb, g.ps, c);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            acc[t] = 0.0f;
+            if (active) acc[t] = xr[t].scale * group_dot(c, xr[t]);
+        }
+    }
 };
 
 // Q8_0: 34-byte blocks of 32 weights, an f16 scale d then 32 signed bytes q,
@@ -210,15 +222,27 @@ struct MatTable {
 // which puts RPG rows per buffer in flight with the same activation
 // registers.  QG: some matrix of the table de-interleaves its output per
 // head (y_gate set); only then does the store path remap rows.
+//
+// MT, TP: several tokens (a small batch, x [ntok][K], y [ntok][n], one
+// matrix).  A wave holds the activation registers of MT tokens and decodes
+// each weight group once for all of them; TP waves of a workgroup (adjacent
+// wave indices) take the same wave iteration for token tiles 0 .. TP-1, so a
+// row's bytes come from HBM once and reach the other waves from the caches.
+// Tokens past ntok in the last tile repeat token ntok-1 and are not stored.
 template <class F, typename XT, typename YT, int LPR, bool SWIGLU, bool RES, int NB, int BLOCK, int MIN_WAVES,
-          int RPG, bool QG = false>
+          int RPG, bool QG = false, int MT = 1, int TP = 1>
 __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable mt, const uint8_t *__restrict__ wu,
-                                                                const XT *x, int ngroups, int64_t row_bytes) {
+                                                                const XT *x, int ngroups, int64_t row_bytes,
+                                                                int ntok) {
     static_assert(NB >= 2, "at least one row in flight");
+    static_assert(MT * TP == 1 || (!SWIGLU && !RES && !QG && RPG == 1), "token tiles: plain single-matrix GEMV");
     constexpr int NMAT = SWIGLU ? 2 : 1;
     constexpr int kRowsPerGroup = kWave / LPR;  // rows per wave and row slot q
     constexpr int kRowsPerWave = RPG * kRowsPerGroup;
     constexpr int kWavesPerBlock = BLOCK / kWave;
+    static_assert(kWavesPerBlock % TP == 0, "whole token-tile groups per workgroup");
+    constexpr int kIterWaves = kWavesPerBlock / TP;  // waves of a workgroup with distinct iterations
+    constexpr int kTok = MT * TP;
     extern __shared__ __align__(16) unsigned char smem[];
     XGroup *xg = reinterpret_cast<XGroup *>(smem);
 
@@ -304,14 +328,22 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
         return j < d ? rc.y + (h << rc.hl) + j : rc.yg + (h << rc.hl) + (j - d);
     };
 
-    const int nwaves = static_cast<int>(gridDim.x) * kWavesPerBlock;
-    const int it0 = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWavesPerBlock +
-                                                   static_cast<int>(threadIdx.x >> 6));
+    const int nwaves = static_cast<int>(gridDim.x) * kIterWaves;
+    const int wave = static_cast<int>(threadIdx.x >> 6);
+    const int it0 = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kIterWaves + wave / TP);
+    const int tile = __builtin_amdgcn_readfirstlane(wave % TP);
 
     // activations first, then the first rows' weights: waiting for the
     // activations (in issue order) then leaves the weight loads in flight
     constexpr int kXChunks = (LPR * 16 + BLOCK - 1) / BLOCK;
-    const XLoaded<kXChunks> xl = load_x<BLOCK, kXChunks, XT>(x, ngroups);
+    const int64_t xstride = static_cast<int64_t>(ngroups) * 64;
+    XLoaded<kXChunks> xl[kTok];
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) {
+        const XT *xt = x;
+        if constexpr (kTok > 1) xt = x + (t < ntok ? t : ntok - 1) * xstride;
+        xl[t] = load_x<BLOCK, kXChunks, XT>(xt, ngroups);
+    }
     // keep the activation loads ahead of the weight loads (an empty asm with a
     // memory clobber: no instruction, only an ordering point for the compiler;
     // x is deliberately not __restrict__ so its loads cannot move across it)
@@ -320,10 +352,25 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
 #pragma unroll
     for (int b = 0; b + 1 < NB; ++b) issue(buf[b], it0 + b * nwaves);
 
-    prepare_x<BLOCK, kXChunks>(xl, ngroups, xg);
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) {
+        if (kTok == 1 || t < ntok) prepare_x<BLOCK, kXChunks>(xl[t], ngroups, xg + t * ngroups);
+    }
     __syncthreads();
-    XRegs xr;
-    load_xregs(xg[g.j], xr);
+    XRegs xr[MT];
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+        int tok = 0;
+        if constexpr (kTok > 1) {
+            tok = tile * MT + j;
+            tok = tok < ntok ? tok : ntok - 1;
+        }
+        load_xregs(xg[tok * ngroups + g.j], xr[j]);
+    }
+    // token tiles: outputs of token tile*MT + j sit j*ystride after the
+    // tile's first; nvalid of the tile's tokens exist
+    const int64_t ystride = mt.n[0];
+    const int nvalid = ntok - tile * MT;
 
     // The loads are never inside a branch: at a control-flow join the wait
     // counters would have to assume the fewest loads in flight and drain the
@@ -335,14 +382,23 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     // keeps the group's k-th result of the current window of LPR rows (and
     // where it goes); the window is stored in one go when it is full (a wave
     // streaming fewer than LPR rows per group stores only after the loop).
-    float yv = 0.0f;
+    float yv[MT];
+#pragma unroll
+    for (int j = 0; j < MT; ++j) yv[j] = 0.0f;
     YT *yp = nullptr;
     const float *rp = nullptr;
     int win = 0;
     auto flush = [&]() {
         if (yp != nullptr) {
-            if constexpr (RES) *yp = static_cast<YT>(rp != nullptr ? yv + *rp : yv);
-            else *yp = static_cast<YT>(yv);
+            if constexpr (RES) {
+                *yp = static_cast<YT>(rp != nullptr ? yv[0] + *rp : yv[0]);
+            } else {
+                *yp = static_cast<YT>(yv[0]);
+#pragma unroll
+                for (int j = 1; j < MT; ++j) {
+                    if (j < nvalid) yp[j * ystride] = static_cast<YT>(yv[j]);
+                }
+            }
         }
         yp = nullptr;
         win = 0;
@@ -376,14 +432,26 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
                     const int64_t row =
                         static_cast<int64_t>(cur - rc.begin) * kRowsPerWave + q * kRowsPerGroup + slot;
                     const bool rok = row < rc.n;
-                    float acc[NMAT];
-                    lane_dot(buf[b][q], g, xr, rok && g.ok, acc);
-#pragma unroll
-                    for (int m2 = 0; m2 < NMAT; ++m2) acc[m2] = lane_group_sum<LPR>(acc[m2]);
-                    const float out = SWIGLU ? silu(acc[0]) * acc[1] : acc[0];
                     const bool mine = sub == win;
-                    yv = mine ? out : yv;
+                    if constexpr (MT == 1) {
+                        float acc[NMAT];
+                        lane_dot(buf[b][q], g, xr[0], rok && g.ok, acc);
+#pragma unroll
+                        for (int m2 = 0; m2 < NMAT; ++m2) acc[m2] = lane_group_sum<LPR>(acc[m2]);
+                        const float out = SWIGLU ? silu(acc[0]) * acc[1] : acc[0];
+                        yv[0] = mine ? out : yv[0];
+                    } else {
+                        // one decode of the group for the wave's MT tokens
+                        float acc[MT];
+                        F::dot_tokens(buf[b][q].m[0], g, xr, rok && g.ok, acc);
+#pragma unroll
+                        for (int j = 0; j < MT; ++j) {
+                            acc[j] = lane_group_sum<LPR>(acc[j]);
+                            yv[j] = mine ? acc[j] : yv[j];
+                        }
+                    }
                     if constexpr (QG) yp = mine ? (rok ? dest(row) : nullptr) : yp;
+                    else if constexpr (kTok > 1) yp = mine ? (rok ? rc.y + tile * MT * ystride + row : nullptr) : yp;
                     else yp = mine ? (rok ? rc.y + row : nullptr) : yp;
                     if constexpr (RES) rp = mine ? (rc.r != nullptr ? rc.r + row : nullptr) : rp;
                     if (++win == LPR) flush();
@@ -407,19 +475,26 @@ done:
 // stretch of iterations writes while the last one is read.  res, if set, is
 // added to each result (it may be y itself: each thread reads a row's
 // residual before it writes that row).
+//
+// MT > 1: MT tokens (x [ntok][K], y [ntok][n], ntok <= MT; a missing token
+// repeats the last and is not stored), each wave holding the activation
+// registers of all of them and decoding each weight group once.
 constexpr int kFlush = 8;
 
-template <class F, typename XT, typename YT, int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
+template <class F, typename XT, typename YT, int S, int R, bool SWIGLU, int NB, int MIN_WAVES, int MT = 1>
 __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const uint8_t *__restrict__ w,
                                                                            const uint8_t *__restrict__ wu,
                                                                            const XT *x, YT *y,
                                                                            const float *res, int64_t n, int ngroups,
-                                                                           int64_t row_bytes) {
+                                                                           int64_t row_bytes, int ntok) {
+    static_assert(MT == 1 || !SWIGLU, "token tiles: plain GEMV");
     constexpr int BLOCK = 64 * S * R;
     constexpr int NMAT = SWIGLU ? 2 : 1;
+    constexpr int NV = NMAT * MT;  // partial sums per row and slice
     extern __shared__ __align__(16) unsigned char smem[];
     XGroup *xg = reinterpret_cast<XGroup *>(smem);
-    float *part = reinterpret_cast<float *>(smem + static_cast<size_t>(ngroups) * sizeof(XGroup));  // [2][kFlush][R][S][NMAT]
+    // [2][kFlush][R][S][NV]
+    float *part = reinterpret_cast<float *>(smem + static_cast<size_t>(MT) * ngroups * sizeof(XGroup));
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -440,16 +515,30 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
     };
 
     constexpr int kXChunks = (S * kWave * 16 + BLOCK - 1) / BLOCK;
-    const XLoaded<kXChunks> xl = load_x<BLOCK, kXChunks, XT>(x, ngroups);
+    const int64_t xstride = static_cast<int64_t>(ngroups) * 64;
+    XLoaded<kXChunks> xl[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        const XT *xt = x;
+        if constexpr (MT > 1) xt = x + (t < ntok ? t : ntok - 1) * xstride;
+        xl[t] = load_x<BLOCK, kXChunks, XT>(xt, ngroups);
+    }
     asm volatile("" ::: "memory");
     RowLoads<F, NMAT> buf[NB];
 #pragma unroll
     for (int b = 0; b + 1 < NB; ++b) issue(buf[b], b);
 
-    prepare_x<BLOCK, kXChunks>(xl, ngroups, xg);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        if (MT == 1 || t < ntok) prepare_x<BLOCK, kXChunks>(xl[t], ngroups, xg + t * ngroups);
+    }
     __syncthreads();
-    XRegs xr;
-    load_xregs(xg[g.j], xr);
+    XRegs xr[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        const int tok = MT == 1 ? 0 : (t < ntok ? t : ntok - 1);
+        load_xregs(xg[tok * ngroups + g.j], xr[t]);
+    }
 
     for (int c = 0; c < my_iters; c += NB) {
         {
@@ -464,15 +553,22 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
         for (int b = 0; b < NB; ++b) {
             const int cur = c + b;
             issue(buf[(b + NB - 1) % NB], cur + NB - 1);
-            float acc[NMAT];
-            lane_dot(buf[b], g, xr, g.ok, acc);
+            float acc[NV];
+            if constexpr (MT == 1) {
+                lane_dot(buf[b], g, xr[0], g.ok, acc);
+            } else {
+                float at[MT];
+                F::dot_tokens(buf[b].m[0], g, xr, g.ok, at);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[t] = at[t];
+            }
             const int d = cur % kFlush;
             const int half = (cur / kFlush) & 1;
-            float *pp = part + (((half * kFlush + d) * R + rslot) * S + slice) * NMAT;
+            float *pp = part + (((half * kFlush + d) * R + rslot) * S + slice) * NV;
 #pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt) {
-                acc[mt] = lane_group_sum<kWave>(acc[mt]);
-                if (lane == 0) pp[mt] = acc[mt];
+            for (int v = 0; v < NV; ++v) {
+                acc[v] = lane_group_sum<kWave>(acc[v]);
+                if (lane == 0) pp[v] = acc[v];
             }
             if (d == kFlush - 1 || cur + 1 == my_iters) {
                 __syncthreads();
@@ -482,17 +578,24 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
                     const int r = t % R;
                     const int64_t row = row_of(cur - d + dd, r);
                     if (row < n) {
-                        const float *q = part + ((half * kFlush + dd) * R + r) * S * NMAT;
-                        float sum[NMAT];
+                        const float *q = part + ((half * kFlush + dd) * R + r) * S * NV;
+                        float sum[NV];
 #pragma unroll
-                        for (int mt = 0; mt < NMAT; ++mt) sum[mt] = q[mt];
+                        for (int v = 0; v < NV; ++v) sum[v] = q[v];
 #pragma unroll
                         for (int s = 1; s < S; ++s) {
 #pragma unroll
-                            for (int mt = 0; mt < NMAT; ++mt) sum[mt] += q[s * NMAT + mt];
+                            for (int v = 0; v < NV; ++v) sum[v] += q[s * NV + v];
                         }
-                        const float v = SWIGLU ? silu(sum[0]) * sum[1] : sum[0];
-                        y[row] = static_cast<YT>(res != nullptr ? v + res[row] : v);
+                        if constexpr (MT == 1) {
+                            const float v = SWIGLU ? silu(sum[0]) * sum[1] : sum[0];
+                            y[row] = static_cast<YT>(res != nullptr ? v + res[row] : v);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < MT; ++j) {
+                                if (j < ntok) y[j * n + row] = static_cast<YT>(sum[j]);
+                            }
+                        }
                     }
                 }
             }
@@ -624,8 +727,110 @@ hipError_t launch_fast_kernel(const GemvJob *jobs, int count, const uint8_t *wu,
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
     const int grid = static_cast<int>(need < cap ? need : cap);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, mt, wu, static_cast<const XT *>(x), ngroups,
-                       row_bytes);
+                       row_bytes, 1);
     return hipGetLastError();
+}
+
+template <class F, typename XT, typename YT, int S, int R, bool SWIGLU, int NB, int MIN_WAVES, int MT = 1>
+hipError_t launch_split(const uint8_t *w, const uint8_t *wu, const void *x, const float *r, void *y, int64_t n,
+                        int64_t k, hipStream_t stream, int ntok = 1) {
+    auto kern = gemv_split_kernel<F, XT, YT, S, R, SWIGLU, NB, MIN_WAVES, MT>;
+    constexpr int BLOCK = 64 * S * R;
+    const int ngroups = static_cast<int>(k / 64);
+    const size_t lds = static_cast<size_t>(MT) * ngroups * sizeof(XGroup) +
+                       sizeof(float) * 2 * kFlush * R * S * (SWIGLU ? 2 : 1) * MT;
+    static std::atomic<int> cache[kMaxDevices];
+    const int per_cu = resident_blocks_per_cu(kern, BLOCK, lds, cache);
+    const int64_t need = (n + R - 1) / R;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
+    const int grid = static_cast<int>(need < cap ? need : cap);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, w, wu, static_cast<const XT *>(x),
+                       static_cast<YT *>(y), r, n, ngroups, F::row_bytes(k), ntok);
+    return hipGetLastError();
+}
+
+// One launch of the token-tile kernel: m tokens (MT * (TP - 1) < m <= MT * TP)
+// against one matrix of n rows.
+template <typename XT, typename YT, int LPR, int MT, int TP, int NB, int BLOCK, int MIN_WAVES>
+hipError_t launch_tokens_kernel(const uint8_t *w, const void *x, void *y, int m, int64_t n, int64_t k,
+                                hipStream_t stream) {
+    auto kern = gemv_kernel<Q4KFormat, XT, YT, LPR, false, false, NB, BLOCK, MIN_WAVES, 1, false, MT, TP>;
+    const int ngroups = static_cast<int>(k / 64);
+    const int64_t row_bytes = Q4KFormat::row_bytes(k);
+    // every token's activation groups; the occupancy query takes the largest
+    const size_t lds = static_cast<size_t>(m) * ngroups * sizeof(XGroup);
+    static std::atomic<int> cache[kMaxDevices];
+    const int per_cu = resident_blocks_per_cu(kern, BLOCK, static_cast<size_t>(MT * TP) * ngroups * sizeof(XGroup),
+                                              cache);
+    constexpr int kRowsPerWave = kWave / LPR;
+    constexpr int kIterWaves = BLOCK / kWave / TP;
+    const int64_t iters = (n + kRowsPerWave - 1) / kRowsPerWave;
+    if (iters >= (int64_t{1} << 30)) return hipErrorInvalidValue;
+    MatTable mt{};
+    mt.count = 1;
+    mt.w[0] = w;
+    mt.y[0] = y;
+    mt.n[0] = n;
+    mt.head_log2[0] = GemvJob::kPlainHead;
+    for (int i = 1; i <= kMaxMats; ++i) mt.it_begin[i] = static_cast<int>(iters);
+    mt.tail_bytes[0] = static_cast<int>((n - (iters - 1) * kRowsPerWave) * row_bytes);
+    const int64_t need = (iters + kIterWaves - 1) / kIterWaves;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
+    const int grid = static_cast<int>(need < cap ? need : cap);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, mt, nullptr, static_cast<const XT *>(x), ngroups,
+                       row_bytes, m);
+    return hipGetLastError();
+}
+
+// Launch shape of the token-tile kernel: two tokens' activation registers
+// (102 VGPRs) per wave.
+#ifndef Q4K_TOK_BLOCK
+#define Q4K_TOK_BLOCK 768
+#endif
+#ifndef Q4K_TOK_MINW
+#define Q4K_TOK_MINW 3
+#endif
+#ifndef Q4K_TOK_NB
+#define Q4K_TOK_NB 2
+#endif
+
+template <typename XT, typename YT, int LPR>
+hipError_t dispatch_tokens_lpr(const uint8_t *w, const void *x, void *y, int m, int64_t n, int64_t k,
+                               hipStream_t stream) {
+    constexpr int B = Q4K_TOK_BLOCK, W = Q4K_TOK_MINW, NB = Q4K_TOK_NB;
+    if (m <= 2) return launch_tokens_kernel<XT, YT, LPR, 2, 1, NB, B, W>(w, x, y, m, n, k, stream);
+    return launch_tokens_kernel<XT, YT, LPR, 2, 2, NB, B, W>(w, x, y, m, n, k, stream);
+}
+
+// K-split shapes for two tokens (4096 < K <= 16384)
+#ifndef Q4K_TOK_SPLIT_R
+#define Q4K_TOK_SPLIT_R 4
+#endif
+#ifndef Q4K_TOK_SPLIT_NB
+#define Q4K_TOK_SPLIT_NB 2
+#endif
+#ifndef Q4K_TOK_SPLIT_MINW
+#define Q4K_TOK_SPLIT_MINW 2
+#endif
+
+template <typename XT, typename YT>
+hipError_t dispatch_tokens(const uint8_t *w, const void *x, void *y, int m, int64_t n, int64_t k,
+                           hipStream_t stream) {
+    const int64_t ngroups = k / 64;
+    if (ngroups > 64) {
+        constexpr int R = Q4K_TOK_SPLIT_R, NB = Q4K_TOK_SPLIT_NB, W = Q4K_TOK_SPLIT_MINW;
+        if (ngroups <= 128)
+            return launch_split<Q4KFormat, XT, YT, 2, R, false, NB, W, 2>(w, nullptr, x, nullptr, y, n, k, stream, m);
+        if (ngroups <= 192)
+            return launch_split<Q4KFormat, XT, YT, 3, R, false, NB, W, 2>(w, nullptr, x, nullptr, y, n, k, stream, m);
+        // four slices: two rows per workgroup keep it at 512 threads (registers)
+        return launch_split<Q4KFormat, XT, YT, 4, 2, false, NB, W, 2>(w, nullptr, x, nullptr, y, n, k, stream, m);
+    }
+    if (ngroups <= 4) return dispatch_tokens_lpr<XT, YT, 4>(w, x, y, m, n, k, stream);
+    if (ngroups <= 8) return dispatch_tokens_lpr<XT, YT, 8>(w, x, y, m, n, k, stream);
+    if (ngroups <= 16) return dispatch_tokens_lpr<XT, YT, 16>(w, x, y, m, n, k, stream);
+    if (ngroups <= 32) return dispatch_tokens_lpr<XT, YT, 32>(w, x, y, m, n, k, stream);
+    return dispatch_tokens_lpr<XT, YT, 64>(w, x, y, m, n, k, stream);
 }
 
 template <class F, typename XT, typename YT, int LPR, bool SWIGLU, int NB, int BLOCK, int MIN_WAVES, int RPG = 1>
@@ -649,24 +854,6 @@ hipError_t launch_fast(const GemvJob *jobs, int count, const uint8_t *wu, const 
         }
     }
     return launch_fast_kernel<F, XT, YT, LPR, SWIGLU, false, NB, BLOCK, MIN_WAVES, RPG>(jobs, count, wu, x, k, stream);
-}
-
-template <class F, typename XT, typename YT, int S, int R, bool SWIGLU, int NB, int MIN_WAVES>
-hipError_t launch_split(const uint8_t *w, const uint8_t *wu, const void *x, const float *r, void *y, int64_t n,
-                        int64_t k, hipStream_t stream) {
-    auto kern = gemv_split_kernel<F, XT, YT, S, R, SWIGLU, NB, MIN_WAVES>;
-    constexpr int BLOCK = 64 * S * R;
-    const int ngroups = static_cast<int>(k / 64);
-    const size_t lds = static_cast<size_t>(ngroups) * sizeof(XGroup) +
-                       sizeof(float) * 2 * kFlush * R * S * (SWIGLU ? 2 : 1);
-    static std::atomic<int> cache[kMaxDevices];
-    const int per_cu = resident_blocks_per_cu(kern, BLOCK, lds, cache);
-    const int64_t need = (n + R - 1) / R;
-    const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
-    const int grid = static_cast<int>(need < cap ? need : cap);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(BLOCK), lds, stream, w, wu, static_cast<const XT *>(x),
-                       static_cast<YT *>(y), r, n, ngroups, F::row_bytes(k));
-    return hipGetLastError();
 }
 
 template <class F, typename XT, typename YT, bool SWIGLU>
@@ -830,6 +1017,19 @@ hipError_t launch_gemv_dt(const uint8_t *w, const void *x, bool x_f16, void *y, 
     if (x_f16) return dispatch<Q4KFormat, _Float16, float, false>(&job, 1, nullptr, x, k, stream);
     if (y_f16) return dispatch<Q4KFormat, float, _Float16, false>(&job, 1, nullptr, x, k, stream);
     return dispatch<Q4KFormat, float, float, false>(&job, 1, nullptr, x, k, stream);
+}
+
+hipError_t launch_gemv_tokens(const uint8_t *w, const void *x, bool x_f16, void *y, bool y_f16, int64_t m, int64_t n,
+                              int64_t k, hipStream_t stream) {
+    if (m < 2 || m > (k <= kTokensMaxK ? kTokensMax : 2) || k <= 0 || k > kTokensSplitMaxK || n == 0) {
+        return hipErrorInvalidValue;
+    }
+    const int mi = static_cast<int>(m);
+    using H = _Float16;
+    if (x_f16 && y_f16) return dispatch_tokens<H, H>(w, x, y, mi, n, k, stream);
+    if (x_f16) return dispatch_tokens<H, float>(w, x, y, mi, n, k, stream);
+    if (y_f16) return dispatch_tokens<float, H>(w, x, y, mi, n, k, stream);
+    return dispatch_tokens<float, float>(w, x, y, mi, n, k, stream);
 }
 
 hipError_t launch_q8_0_gemv(const uint8_t *w, const float *x, const float *r, float *y, int64_t n, int64_t k,

@@ -64,6 +64,15 @@ hipError_t launch_gemv_dt(const uint8_t *w, const void *x, bool x_f16, void *y, 
 hipError_t launch_q8_0_gemv(const uint8_t *w, const float *x, const float *r, float *y, int64_t n, int64_t k,
                             hipStream_t stream);
 
+// Small batches on the streaming GEMV kernels: y[t, r] = sum_c W[r,c] x[t,c]
+// for 2 <= m <= kTokensMax tokens with k <= kTokensMaxK, or m == 2 with
+// k <= kTokensSplitMaxK (the K-split kernel); f16 or f32 x and y.
+constexpr int64_t kTokensMax = 4;
+constexpr int64_t kTokensMaxK = 4096;
+constexpr int64_t kTokensSplitMaxK = 16384;
+hipError_t launch_gemv_tokens(const uint8_t *w, const void *x, bool x_f16, void *y, bool y_f16, int64_t m, int64_t n,
+                              int64_t k, hipStream_t stream);
+
 // y[t, r] = sum_c W[r,c] x[t,c] for t < m.
 hipError_t launch_gemv_batched(const uint8_t *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
                                hipStream_t stream);

@@ -112,7 +112,8 @@ def test_gemv_dt_two_byte_aligned_f16_and_overflow(q4k):
 
 
 @pytest.mark.parametrize("m,n,k", [(2, 300, 2048), (16, 4096, 1024), (33, 513, 1024), (64, 4100, 2048),
-                                   (100, 700, 2304), (4, 70, 12288), (40, 70, 4096), (17, 4096, 4096)])
+                                   (100, 700, 2304), (4, 70, 12288), (40, 70, 4096), (17, 4096, 4096),
+                                   (2, 70, 12288), (3, 513, 1024), (4, 1000, 4096)])
 def test_batched_dt_all_combinations(q4k, m, n, k):
     import torch
 
@@ -123,8 +124,10 @@ def test_batched_dt_all_combinations(q4k, m, n, k):
     xf = xh.float()
     print(f"[case] batched_dt m={m} {n}x{k}", flush=True)
     yr, ar = oracle.gemv_batched(w, x16.astype(np.float32), threads=THREADS)
-    # few rows per CU: K is split across workgroups and added with atomics
-    split = n < 16 * torch.cuda.get_device_properties(0).multi_processor_count and k >= 512
+    # few rows per CU on the matrix-core kernel: K is split across workgroups
+    # and added with atomics (a few tokens run on the streaming kernels instead)
+    streaming = (m <= 4 and k <= 4096) or (m == 2 and k <= 16384)
+    split = not streaming and n < 16 * torch.cuda.get_device_properties(0).multi_processor_count and k >= 512
     for xd in ("f16", "f32"):
         xin = xh if xd == "f16" else xf
         y32 = q4k.gemv_batched_dt(wd, xin, out_dtype=torch.float32)

@@ -352,7 +352,8 @@ def test_batched_small(q4k, m):
 
 
 @pytest.mark.parametrize("m,n,k", [(4, 70, 12288), (16, 70, 12288), (64, 70, 12288), (3, 10, 256), (20, 10, 256),
-                                   (7, 129, 20480), (40, 129, 1280)])
+                                   (7, 129, 20480), (40, 129, 1280), (2, 70, 12288), (2, 129, 8192), (2, 33, 16384),
+                                   (2, 300, 4352), (4, 4097, 1024), (3, 1, 256), (2, 5, 20480)])
 def test_batched_shapes(q4k, m, n, k):
     w = inputs.make_q4k(n, k, config_id=97, tensor_id=k)
     xs = inputs.make_x(m, k, config_id=97, tensor_id=m)
@@ -362,7 +363,7 @@ def test_batched_shapes(q4k, m, n, k):
 
 
 @pytest.mark.parametrize("name,tid", [("gate_9b", 0), ("down_9b", 2)])
-@pytest.mark.parametrize("m", [1, 4, 16, 32, 64])
+@pytest.mark.parametrize("m", [1, 2, 4, 16, 32, 64])
 def test_batched_ffn_9b_sampled(q4k, name, tid, m):
     """Whole matrix on the GPU (y pre-filled with NaN: every output must be
     written), sampled rows against the oracle."""
@@ -380,10 +381,33 @@ def test_batched_ffn_9b_sampled(q4k, name, tid, m):
     _report(f"batched 9b {name} m={m}", check_bound(y[:, rows], yr, ar, f"batched {name} m={m}"))
 
 
+@pytest.mark.parametrize("m,n,k", [(2, 4096, 4096), (3, 1000, 4096), (4, 4097, 1024), (2, 777, 2048), (4, 300, 256),
+                                   (2, 4096, 12288), (2, 1000, 8192), (2, 515, 16384)])
+def test_batched_few_tokens_equal_batch1_bitwise(q4k, m, n, k):
+    """Up to four tokens (two at K > 4096) run on the streaming GEMV kernels,
+    which decode each weight group once for a pair of tokens and otherwise do
+    per token exactly the arithmetic of the batch-1 call: every token's row
+    equals q4k_gemv on that token bit for bit, and is inside the oracle's
+    bound."""
+    import torch
+
+    print(f"[case] few tokens m={m} {n}x{k}", flush=True)
+    w = inputs.make_q4k(n, k, config_id=95, tensor_id=k)
+    xs = inputs.make_x(m, k, config_id=95, tensor_id=m)
+    wd, xd = to_dev(w.reshape(-1)), to_dev(xs)
+    yd = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    q4k.gemv_batched(wd, xd, y=yd)
+    for t in range(m):
+        assert torch.equal(yd[t], q4k.gemv(wd, xd[t])), f"token {t} differs from the batch-1 call"
+    rows = _sample_rows(n, 300, seed=k)
+    yr, ar = oracle.gemv_batched(w[rows], xs, threads=THREADS)
+    _report(f"few tokens m={m} {n}x{k}", check_bound(to_host(yd)[:, rows], yr, ar, f"few tokens m={m} {n}x{k}"))
+
+
 def test_batched_special_values(q4k):
     n, k = 64, 1024
     w = inputs.make_q4k(n, k, config_id=98, tensor_id=0)
-    for m in (4, 16):
+    for m in (4, 16):  # the streaming kernels (two token pairs), the matrix cores
         xs = inputs.make_x(m, k, config_id=98, tensor_id=m)
         xs[1] = 0.0
         xs[2] *= np.float32(1e-30)
