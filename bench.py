@@ -228,7 +228,7 @@ def main():
         for nm in ("gate_9b", "down_9b"):
             n_, k_ = shapes[nm]
             sets_b = rotated([nm])
-            for mtok in (4, 16, 32, 64):
+            for mtok in (2, 4, 16, 32, 64):
                 xs = torch.from_numpy(inputs.make_x(mtok, k_, config_id=4, tensor_id=100 + mtok)).to(dev)
                 yb = torch.empty((mtok, n_), dtype=torch.float32, device=dev)
                 t = _time_launches(lambda i: q4k.gemv_batched(sets_b[i % len(sets_b)][0], xs, y=yb, stream=stream),

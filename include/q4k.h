@@ -25,12 +25,13 @@
  *  - All pointers except `stream` are DEVICE pointers owned by the caller.
  *    Every call only enqueues work on `stream` (a hipStream_t passed as
  *    void*; NULL means the null stream) and returns; it never synchronises.
- *    Results are ready when the stream is.  Only the batched calls with
- *    m >= 2 and the prefill GEMM need device scratch: they take it
- *    stream-ordered from the device's default memory pool (hipMallocAsync /
- *    hipFreeAsync on `stream`), 536 * ceil(m'/16) * k/8 bytes for the batched
- *    call with m' = min(m, 64) tokens (about 1.1 MB at m = 64, k = 4096), or,
- *    through their *_ws forms, from a workspace the caller passes in.
+ *    Results are ready when the stream is.  Only the batched calls on the
+ *    matrix cores (see q4k_gemv_batched) and the prefill GEMM need device
+ *    scratch: they take it stream-ordered from the device's default memory
+ *    pool (hipMallocAsync / hipFreeAsync on `stream`), 536 * ceil(m'/16) *
+ *    k/8 bytes for the batched call with m' = min(m, 64) tokens (about 1.1 MB
+ *    at m = 64, k = 4096), or, through their *_ws forms, from a workspace the
+ *    caller passes in.
  *  - Arguments are validated on the host before anything is enqueued; on any
  *    error nothing is launched and the status says why.  Launch failures are
  *    reported as Q4K_ERR_LAUNCH.
@@ -175,13 +176,16 @@ Q4K_API q4k_status q4k_q8_0_gemv(const void *w, const float *x, float *y, int64_
  * non-M1 variant; "Module qwen3_attention" names a W4A16 batched path).
  *   x : f32 [m, k] row-major (token-major), y : f32 [m, n] row-major:
  *   y[t, r] = sum_c W[r,c] x[t,c].
- * m >= 2 runs on the matrix cores (each weight decoded once per 64
- * tokens).  With n >= 16 * (compute units of the device) every output is
- * summed by one workgroup in a fixed order and the call is bitwise
- * reproducible; with fewer rows the K range is split across workgroups whose
- * partial sums are added into y with f32 atomics, so the last bits may
- * differ between runs (every run is inside the error bound).  y is
- * overwritten, not accumulated.
+ * A few tokens (2 <= m <= 4 with k <= 4096, and m == 2 with k <= 16384) run
+ * on the streaming GEMV kernels, which decode each weight group once per
+ * pair of tokens and need no scratch: every token's row is bit for bit what
+ * q4k_gemv computes for that token.  Every other m >= 2 runs on the matrix
+ * cores (each weight decoded once per 64 tokens).  There, with n >= 16 *
+ * (compute units of the device), every output is summed by one workgroup in
+ * a fixed order and the call is bitwise reproducible; with fewer rows the K
+ * range is split across workgroups whose partial sums are added into y with
+ * f32 atomics, so the last bits may differ between runs (every run is inside
+ * the error bound).  y is overwritten, not accumulated.
  */
 Q4K_API q4k_status q4k_gemv_batched(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
                             void *stream);
@@ -233,7 +237,8 @@ Q4K_API q4k_status q4k_prefill_gemm(const void *w, const void *x, void *y, q4k_d
  * *bytes the scratch that q4k_gemv_batched_dt / q4k_prefill_gemm need for
  * these dtypes and sizes on the CURRENT device (the split of K follows the
  * device's compute-unit count); 0 where none is needed (m <= 1, k == 0, an
- * empty call).  Same shape checks and status codes as the calls themselves;
+ * empty call, the few-token sizes that q4k_gemv_batched runs on the
+ * streaming kernels).  Same shape checks and status codes as the calls themselves;
  * bytes == NULL is Q4K_ERR_INVALID_ARG.  Nothing is enqueued.
  *
  * q4k_gemv_batched_ws / q4k_prefill_gemm_ws compute exactly what
@@ -277,7 +282,7 @@ Q4K_API const char *q4k_status_string(q4k_status s);
 
 /* ABI version of this header (major*100 + minor); q4k_abi_version() of the
  * library it was built with returns the same number. */
-#define Q4K_ABI_VERSION 107
+#define Q4K_ABI_VERSION 108
 Q4K_API int q4k_abi_version(void);
 
 #ifdef __cplusplus

@@ -3,8 +3,10 @@
 // selectQ4KFusedVariant ("@simulatte/doppler 0.1.7 -> 0.1.8",
 // matmul-selection.js) picks a fused Q4K kernel by whether M == 1; this file
 // is the M > 1 side ("Module qwen3_attention" names a W4A16 batched path).
+// A few tokens (launch_gemv_tokens) stay on the streaming GEMV kernels, and
+// f16 activations at prefill sizes go to the prefill GEMM; the rest is here.
 //
-// Once several tokens share each weight the work is a dense contraction, so
+// Once enough tokens share each weight the work is a dense contraction, so
 // it runs on the matrix cores (v_mfma_f32_16x16x32_f16: 16 tokens x 16 rows x
 // 32 weights per instruction; fewer than 16 tokens leave the other rows of the
 // activation operand zero).  Exactness of the operands:

@@ -34,6 +34,11 @@
 // Row partial sums are reduced across the LPR lanes of the row with DPP and
 // permlane swaps (no LDS); the workgroup's activations are converted once into
 // LDS and then held in registers for the whole row stream.
+//
+// The same kernels serve a batched call of a few tokens: each wave holds two
+// tokens' activation registers and decodes every weight group once for both,
+// and waves of one workgroup that take the same rows for different token
+// pairs share the row's bytes through the caches.
 #include <float.h>
 #include <math.h>
 

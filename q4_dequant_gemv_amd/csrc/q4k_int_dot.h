@@ -1,6 +1,6 @@
 // Integer dot products of Q4_K codes with activations on the vector ALUs
 // (v_dot4_i32_i8), shared by the batch-1 GEMV, the SwiGLU GEMV and the
-// small-batch (m < 16) kernel.
+// few-token form of the batched call (the same kernels with token tiles).
 //
 // A 64-weight group is one sub-block pair (2g, 2g+1) of a super-block: its 32
 // code bytes hold the 32 weights of sub-block 2g in their low nibbles and the

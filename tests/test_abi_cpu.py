@@ -57,8 +57,8 @@ def test_only_the_abi_is_exported():
 
 
 def test_status_strings(L):
-    assert L.q4k_abi_version() == 107
-    assert re.search(r"#define Q4K_ABI_VERSION (\d+)", open(HEADER).read()).group(1) == "107"
+    assert L.q4k_abi_version() == 108
+    assert re.search(r"#define Q4K_ABI_VERSION (\d+)", open(HEADER).read()).group(1) == "108"
     for s in range(5):
         assert len(L.q4k_status_string(s)) > 0
     assert L.q4k_status_string(99) == b"unknown status"
