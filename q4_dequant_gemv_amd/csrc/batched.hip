@@ -444,6 +444,145 @@ __global__ __launch_bounds__(128 * S, 1) void batched_mfma_kernel(const uint8_t 
     }
 }
 
+// ---- up to 16 tokens, K <= 4096: a weight stream into the matrix cores ------
+// Wave w of the workgroup owns half super-blocks [H*w, H*w + H) of every row
+// and keeps their activation fragments (one 16-token tile, from the
+// preparation kernel's scratch) in registers for the whole call, and their
+// per-token sums and scales in LDS (read per tile).  The
+// workgroup streams 16-row tiles (tile blockIdx.x + c*gridDim.x); each wave
+// loads its part of a tile straight into registers NB tiles ahead (per lane:
+// row `col`'s super-block header and 16 code bytes per half), builds the B
+// operands and runs the same half super-block products as the staged kernel.
+// Each wave's tile sums go to LDS; every kStreamFlush tiles, after a barrier,
+// one thread per (tile, lane) adds the W waves' sums in wave order and stores
+// them, so the result does not depend on timing.  A wave whose last half is
+// past the row (an odd number of halves) skips it.
+constexpr int kStreamFlush = 2;
+constexpr int kStreamMaxWaves = 16;
+constexpr int kStreamMaxHalves = 32;
+constexpr int64_t kStreamMaxK = kStreamMaxHalves * kStageK;
+// Waves per workgroup at most: 16 with one or two halves per wave (128
+// registers each), 8 with four (256 registers: two waves per SIMD).
+template <int H>
+constexpr int stream_max_waves() { return H <= 2 ? 16 : 8; }
+
+template <int H, int NB, typename YT>
+__global__ __launch_bounds__(64 * stream_max_waves<H>(), 1) void stream_mfma_kernel(
+    const uint8_t *__restrict__ w, const uint8_t *__restrict__ xc, YT *__restrict__ y, int m, int64_t n, int64_t k,
+    int64_t row_bytes, int64_t xc_bytes) {
+    static_assert(H == 1 || H == 2 || H == 4, "a wave's halves start a super-block (H even) or are one half");
+    constexpr int NH = (H + 1) / 2;  // super-blocks (headers) per wave
+    __shared__ __align__(16) float4_t part[2][kStreamFlush][stream_max_waves<H>()][64];
+    // per half: the scratch block's tail from kSubOff (sub-block sums, bias,
+    // 2^e), 24 pieces of 16 bytes
+    constexpr int kTail = (kTileStageBytes - kSubOff) / 16;
+    __shared__ __align__(16) uint4 tails[kStreamMaxHalves][kTail];
+    const int nw = static_cast<int>(blockDim.x) >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+    const int nhalf = static_cast<int>(k / kStageK);
+    const int hw0 = wave * H;  // the wave's first half (even when H >= 2)
+    const int sb = hw0 >> 1;   // its first super-block
+
+    // activations of the wave's halves (a lane whose token is past m reads
+    // zeros; a half past the row reads the last one and is skipped)
+    const __amdgpu_buffer_rsrc_t ar = stream_rsrc(xc, static_cast<int>(xc_bytes));
+    const uint32_t a_off = col < m ? 0u : 0x40000000u;
+    uint4 af[H][8];
+    PairSelect ps[H];
+    int hl[H];  // the half's row of `tails`
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+        hl[h] = hw0 + h < nhalf ? hw0 + h : nhalf - 1;
+        const int soff = hl[h] * kTileStageBytes;
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+            af[h][f] = as_uint4(
+                __builtin_amdgcn_raw_buffer_load_b128(ar, static_cast<int>(a_off + f * 1024 + lane * 16), soff, 0));
+        if (lane < kTail) tails[hl[h]][lane] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(ar, kSubOff + lane * 16, soff, 0));
+        ps[h] = pair_select(2 * ((hw0 + h) & 1) + (kq >> 1));
+    }
+    __syncthreads();
+
+    // the host keeps gridDim.x <= the number of tiles: every workgroup has one
+    const int64_t ntiles = (n + 15) / 16;
+    const int my_tiles = static_cast<int>((ntiles - 1 - blockIdx.x) / gridDim.x) + 1;
+    // byte offset of the lane's header inside a tile (< 16 * 2304 + 2304)
+    const uint32_t lane_off = static_cast<uint32_t>(col * row_bytes + sb * kBlockBytes);
+    struct TileLoads {
+        uint4 hdr[NH];
+        uint4 q[H];
+    };
+    // loads of tile c of this workgroup (none past the last: a 0-byte
+    // descriptor, so the loads read zeros without a fetch)
+    auto issue = [&](TileLoads &L, int c) {
+        const bool live = c < my_tiles;
+        const int64_t row0 = live ? (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(c) * gridDim.x) * 16 : 0;
+        const int64_t rows = n - row0 < 16 ? n - row0 : 16;
+        const int nrec = __builtin_amdgcn_readfirstlane(live ? static_cast<int>(rows * row_bytes) : 0);
+        const uint8_t *base = reinterpret_cast<const uint8_t *>(wave_uniform(reinterpret_cast<int64_t>(w + row0 * row_bytes)));
+        const __amdgpu_buffer_rsrc_t r = stream_rsrc(base, nrec);
+#pragma unroll
+        for (int j = 0; j < NH; ++j) L.hdr[j] = buffer_load16(r, lane_off + j * kBlockBytes);
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            L.q[h] = buffer_load16(r, lane_off + (h >> 1) * kBlockBytes + 16u + 64u * ((hw0 + h) & 1) + 16u * kq);
+        }
+    };
+
+    TileLoads ring[NB];
+#pragma unroll
+    for (int b = 0; b + 1 < NB; ++b) issue(ring[b], b);
+    for (int c = 0; c < my_tiles; c += NB) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int cur = c + u;
+            issue(ring[(u + NB - 1) % NB], cur + NB - 1);
+            float4_t out = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+                if (H == 1 || hw0 + h < nhalf) {
+                    AStep a;
+#pragma unroll
+                    for (int f = 0; f < 8; ++f) a.f[f] = af[h][f];
+                    a.sub = tails[hl[h]][col];
+                    a.bias = __builtin_bit_cast(float4_t, tails[hl[h]][(kBiasOff - kSubOff) / 16 + kq]);
+                    a.esc = __builtin_bit_cast(float4_t, tails[hl[h]][(kEscOff - kSubOff) / 16 + kq]);
+                    BOps bo;
+                    build_b_ops(bo, ring[u].hdr[h >> 1], ring[u].q[h], ps[h], kq);
+                    mfma_half(bo, a, out, kq);
+                }
+            }
+            const int d = cur % kStreamFlush;
+            const int half = (cur / kStreamFlush) & 1;
+            part[half][d][wave][lane] = out;
+            if (d == kStreamFlush - 1 || cur + 1 == my_tiles) {
+                __syncthreads();
+                const int t = static_cast<int>(threadIdx.x);
+                if (t < (d + 1) * 64) {
+                    const int dd = t >> 6;
+                    const int ln = t & 63;
+                    float4_t sum = part[half][dd][0][ln];
+                    for (int v = 1; v < nw; ++v) sum += part[half][dd][v][ln];
+                    const int64_t row =
+                        (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(cur - d + dd) * gridDim.x) * 16 +
+                        (ln & 15);
+                    if (row < n) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int tok = 4 * (ln >> 4) + r;
+                            if (tok < m) y[static_cast<int64_t>(tok) * n + row] = static_cast<YT>(sum[r]);
+                        }
+                    }
+                }
+            }
+            if (cur + 1 >= my_tiles) break;
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void f32_to_f16_kernel(const float *__restrict__ src, _Float16 *__restrict__ dst,
                                                           int64_t count) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
@@ -512,6 +651,52 @@ hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, i
     return e != hipSuccess ? e : f;
 }
 
+#ifndef Q4K_STREAM_NB
+#define Q4K_STREAM_NB 2
+#endif
+
+// m <= 16 tokens, k <= kStreamMaxK: the activation operands prepared once,
+// then the weight-streaming kernel (no split of K, no atomics).
+template <typename XT, typename YT>
+hipError_t launch_stream(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, Workspace &ws,
+                         hipStream_t stream) {
+    const int64_t nhalf = k / kStageK;
+    const int64_t bytes = nhalf * kTileStageBytes;
+    if (ws.query) {
+        if (bytes > ws.need) ws.need = bytes;
+        return hipSuccess;
+    }
+    uint8_t *xc = nullptr;
+    bool owned = false;
+    hipError_t e = ws_acquire(ws, bytes, stream, &xc, &owned);
+    if (e != hipSuccess) return e;
+    const int64_t prep_blocks = (nhalf * 16 * 32 + 255) / 256;
+    hipLaunchKernelGGL(x_prep_kernel<XT>, dim3(static_cast<unsigned>(prep_blocks)), dim3(256), 0, stream, x, xc,
+                       static_cast<uint32_t *>(nullptr), m, 1, k, int64_t{0});
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+        // halves per wave: one up to 16 halves (K = 2048), then four (eight
+        // waves of 256 registers); two spill at the 128 registers of 16 waves
+        const int H = nhalf <= kStreamMaxWaves ? 1 : 4;
+        const int nw = static_cast<int>((nhalf + H - 1) / H);
+        const int64_t ntiles = (n + 15) / 16;
+        const int64_t cap = static_cast<int64_t>(device_cu_count()) * (H == 1 && nw <= 8 ? 2 : 1);
+        const dim3 grid(static_cast<unsigned>(ntiles < cap ? ntiles : cap));
+        const int64_t rb = (k / kBlockWeights) * kBlockBytes;
+        constexpr int NB = Q4K_STREAM_NB;
+        if (H == 1) {
+            hipLaunchKernelGGL((stream_mfma_kernel<1, NB, YT>), grid, dim3(64 * nw), 0, stream, w, xc, y, m, n, k, rb,
+                               bytes);
+        } else {
+            hipLaunchKernelGGL((stream_mfma_kernel<4, NB, YT>), grid, dim3(64 * nw), 0, stream, w, xc, y, m, n, k, rb,
+                               bytes);
+        }
+        e = hipGetLastError();
+    }
+    const hipError_t f = ws_release(xc, owned, stream);
+    return e != hipSuccess ? e : f;
+}
+
 // Rows per workgroup (16*NT) and the split of K across workgroups.  Each
 // workgroup reads its whole K range of activations (16*MT tokens x 4 bytes
 // per activation) besides its weights (0.5625 bytes per weight), so when
@@ -530,6 +715,10 @@ hipError_t dispatch_mt(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, i
     constexpr int kNtMax0 = MT == 1 ? 4 : (MT == 2 ? 3 : 2);
     constexpr int kNtMax = kNtMax0 < Q4K_BATCH_NT_CAP ? kNtMax0 : Q4K_BATCH_NT_CAP;
     const int64_t cus = device_cu_count();
+    if constexpr (MT == 1) {
+        // a row tile for every CU: the weight-streaming kernel
+        if (k <= kStreamMaxK && (n + 15) / 16 >= cus) return launch_stream(w, x, y, m, n, k, ws, stream);
+    }
     const int64_t nsb = k / kBlockWeights;
     const int64_t per = n / (16 * cus);  // row tiles per CU with one row block each
     if (per >= 1 || nsb < 2) {

@@ -113,7 +113,8 @@ def test_gemv_dt_two_byte_aligned_f16_and_overflow(q4k):
 
 @pytest.mark.parametrize("m,n,k", [(2, 300, 2048), (16, 4096, 1024), (33, 513, 1024), (64, 4100, 2048),
                                    (100, 700, 2304), (4, 70, 12288), (40, 70, 4096), (17, 4096, 4096),
-                                   (2, 70, 12288), (3, 513, 1024), (4, 1000, 4096)])
+                                   (2, 70, 12288), (3, 513, 1024), (4, 1000, 4096), (16, 4100, 2304),
+                                   (6, 4096, 1024)])
 def test_batched_dt_all_combinations(q4k, m, n, k):
     import torch
 

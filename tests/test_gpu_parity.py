@@ -404,10 +404,37 @@ def test_batched_few_tokens_equal_batch1_bitwise(q4k, m, n, k):
     _report(f"few tokens m={m} {n}x{k}", check_bound(to_host(yd)[:, rows], yr, ar, f"few tokens m={m} {n}x{k}"))
 
 
-def test_batched_special_values(q4k):
-    n, k = 64, 1024
+@pytest.mark.parametrize("m,n,k", [(5, 4096, 256), (16, 4100, 1024), (9, 4096, 2048), (16, 4111, 2304),
+                                   (12, 5000, 3328), (7, 4097, 4096), (16, 8192, 4096)])
+def test_batched_streamed_tiles(q4k, m, n, k):
+    """5 to 16 tokens, k <= 4096, a 16-row tile for every CU: the matrix-core
+    kernel that streams the weights (each wave holding its K slice's
+    activation operands), including waves whose last halves are past the row
+    (k = 2304, 3328) and a ragged last tile.  Every output is written, inside
+    the bound, and the same bits on a second run."""
+    import torch
+
+    print(f"[case] streamed tiles m={m} {n}x{k}", flush=True)
+    w = inputs.make_q4k(n, k, config_id=94, tensor_id=k)
+    xs = inputs.make_x(m, k, config_id=94, tensor_id=m)
+    wd, xd = to_dev(w.reshape(-1)), to_dev(xs)
+    yd = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    q4k.gemv_batched(wd, xd, y=yd)
+    y = to_host(yd)
+    assert np.isfinite(y).all(), f"{int((~np.isfinite(y)).sum())} outputs not written"
+    assert torch.equal(q4k.gemv_batched(wd, xd), yd), "not reproducible"
+    rows = _sample_rows(n, 400, seed=m)
+    yr, ar = oracle.gemv_batched(w[rows], xs, threads=THREADS)
+    _report(f"streamed m={m} {n}x{k}", check_bound(y[:, rows], yr, ar, f"streamed m={m} {n}x{k}"))
+
+
+@pytest.mark.parametrize("n", [64, 4096])
+def test_batched_special_values(q4k, n):
+    """m = 4: the streaming GEMV kernels (two token pairs); m = 16: the staged
+    matrix-core kernel at n = 64, the weight-streaming one at n = 4096."""
+    k = 1024
     w = inputs.make_q4k(n, k, config_id=98, tensor_id=0)
-    for m in (4, 16):  # the streaming kernels (two token pairs), the matrix cores
+    for m in (4, 16):
         xs = inputs.make_x(m, k, config_id=98, tensor_id=m)
         xs[1] = 0.0
         xs[2] *= np.float32(1e-30)
