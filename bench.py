@@ -246,7 +246,7 @@ def main():
                 del ws
             del sets_b
 
-    blocks = q8 = f16io = prefill = small = {}
+    blocks = q8 = f16io = prefill = small = shards = {}
     ceiling = None
     if not args.step_only:
         blocks = decode_blocks(q4k, inputs, torch, dev, stream, args.steps, args.warmup)
@@ -255,6 +255,7 @@ def main():
         prefill = prefill_kernels(q4k, inputs, torch, dev, stream) if not args.no_batched else {}
         ceiling = stream_read_ceiling(torch, dev, stream, kernels["gemv_lm_head"]["GB/s"])
         small = small_configs(q4k, inputs, torch, dev, stream)
+        shards = shard_shapes(q4k, inputs, torch, dev, stream)
 
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s; per kernel {kernels}; "
         f"batched {batched}; decode blocks {blocks}; q8_0 {q8}; f16 i/o {f16io}; prefill {prefill}; "
@@ -321,6 +322,7 @@ def main():
             "prefill_9b_ffn": prefill,
             "stream_read_1GiB": ceiling,
             "configs_0_1": small,
+            "shard_of_8_9b": shards,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -330,17 +332,33 @@ def main():
 
 def small_configs(q4k, inputs, torch, dev, stream):
     """The GEMV and dequant calls at the small config shapes (the 1024 x 1024
-    square; the 0.8B q-proj, out-proj and lm_head), weights rotated over
-    >= 512 MiB of copies: the launches captured in a HIP graph (the rate a
-    decode loop sees; eager Python calls of these sizes are bound by the host),
-    the same launches eager back to back, and single-launch percentiles."""
+    square; the 0.8B q-proj, out-proj and lm_head): see graph_timed_calls."""
+    return graph_timed_calls(q4k, inputs, torch, dev, stream,
+                             (("gemv", "square_1k"), ("dequant", "square_1k"), ("gemv", "q_proj_0p8b"),
+                              ("gemv", "out_proj_0p8b"), ("gemv", "lm_head_0p8b")))
+
+
+def shard_shapes(q4k, inputs, torch, dev, stream):
+    """One GPU's share of the 9B decode matrices split eight ways: a
+    vocabulary shard of the lm_head (31,040 rows), a row shard of gate and up
+    (SwiGLU over 1536 rows) and a split-K shard of down (K = 1536, a partial
+    y that an all-reduce would sum)."""
+    return graph_timed_calls(q4k, inputs, torch, dev, stream,
+                             (("gemv", "lm_head_9b_shard8"), ("swiglu", "gate_9b_shard8"), ("gemv", "down_9b_kshard8")))
+
+
+def graph_timed_calls(q4k, inputs, torch, dev, stream, cases):
+    """GEMV, SwiGLU or dequant calls, weights rotated over >= 512 MiB of
+    copies: the launches captured in a HIP graph (the rate a decode loop sees;
+    eager Python calls of small sizes are bound by the host), the same
+    launches eager back to back, and single-launch percentiles."""
     out = {}
-    for kind, name in (("gemv", "square_1k"), ("dequant", "square_1k"), ("gemv", "q_proj_0p8b"),
-                       ("gemv", "out_proj_0p8b"), ("gemv", "lm_head_0p8b")):
+    for kind, name in cases:
         n, k = inputs.SHAPES[name]
+        mats = 2 if kind == "swiglu" else 1
         w0 = torch.from_numpy(inputs.make_q4k(n, k, config_id=7, tensor_id=1).reshape(-1)).to(dev)
-        copies = max(1, -(-(512 << 20) // w0.numel()))
-        ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+        copies = max(1, -(-(512 << 20) // (mats * w0.numel())))
+        ws = [w0] + [w0.clone() for _ in range(mats * copies - 1)]
         x = torch.from_numpy(inputs.make_x(1, k, config_id=7)[0]).to(dev)
         if kind == "gemv":
             y = torch.empty(n, dtype=torch.float32, device=dev)
@@ -349,6 +367,14 @@ def small_configs(q4k, inputs, torch, dev, stream):
                 q4k.gemv(ws[i % copies], x, y=y, stream=s)
 
             nbytes = w0.numel() + 4 * (n + k)
+        elif kind == "swiglu":
+            y = torch.empty(n, dtype=torch.float32, device=dev)
+
+            def fn(i, s=stream):
+                c = i % copies
+                q4k.fused_swiglu(ws[2 * c], ws[2 * c + 1], x, h=y, stream=s)
+
+            nbytes = 2 * w0.numel() + 4 * (n + k)
         else:
             y = torch.empty((n, k), dtype=torch.float32, device=dev)
 

@@ -36,6 +36,12 @@ SHAPES = {
     "up_9b": (12288, 4096),
     "down_9b": (4096, 12288),
     "lm_head_9b": (248320, 4096),
+    # one GPU's share of the 9B decode matrices split eight ways: a
+    # vocabulary (row) shard of the lm_head, a row shard of gate/up, and a
+    # split-K shard of down (1536 columns: 6 super-blocks of each row)
+    "lm_head_9b_shard8": (31040, 4096),
+    "gate_9b_shard8": (1536, 4096),
+    "down_9b_kshard8": (4096, 1536),
     # input projections of a Qwen3.5-0.8B linear-attention (GatedDeltaNet)
     # layer, all read against the same normed hidden state (the
     # hf_qwen35_linear_attn_debug.py trace: qkv is 6144 wide, 16 heads of 128;

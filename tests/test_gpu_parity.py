@@ -246,6 +246,58 @@ def test_gemv_row_subrange_matches_whole(q4k):
     np.testing.assert_array_equal(to_host(part), full[517:817])
 
 
+def test_eight_way_shards_of_the_9b_decode_matrices(q4k):
+    """One GPU's share of an eight-way split, at its real shapes:
+    * lm_head and gate/up by rows (pointer offsets): each shard's outputs are
+      the whole call's rows, bit for bit (31,040 and 1536 rows);
+    * down by K: each GPU holds its 1536 columns (6 super-blocks of every row)
+      as a matrix of its own and produces a partial y; the eight partials,
+      summed as an all-reduce would, are inside the whole product's bound."""
+    import torch
+
+    print("[case] eight-way shards", flush=True)
+    g = 8
+    # lm_head 9B: rows
+    n, k = inputs.SHAPES["lm_head_9b"]
+    ns = inputs.SHAPES["lm_head_9b_shard8"][0]
+    assert ns * g == n
+    wl = to_dev(inputs.make_q4k(n, k, config_id=3, tensor_id=0).reshape(-1))
+    x = to_dev(inputs.make_x(1, k, config_id=3)[0])
+    full = q4k.gemv(wl, x)
+    rb = inputs.row_bytes(k)
+    for s in (0, 3, 7):
+        part = q4k.gemv(wl[s * ns * rb:(s + 1) * ns * rb], x)
+        assert torch.equal(part, full[s * ns:(s + 1) * ns]), f"lm_head shard {s}"
+    del wl, full
+    # gate/up 9B: rows, through the fused SwiGLU
+    n, k = inputs.SHAPES["gate_9b"]
+    ns = inputs.SHAPES["gate_9b_shard8"][0]
+    wg = to_dev(inputs.make_q4k(n, k, config_id=2, tensor_id=0).reshape(-1))
+    wu = to_dev(inputs.make_q4k(n, k, config_id=2, tensor_id=1).reshape(-1))
+    x = to_dev(inputs.make_x(1, k, config_id=2)[0])
+    full = q4k.fused_swiglu(wg, wu, x)
+    rb = inputs.row_bytes(k)
+    for s in range(g):
+        sl = slice(s * ns * rb, (s + 1) * ns * rb)
+        assert torch.equal(q4k.fused_swiglu(wg[sl], wu[sl], x), full[s * ns:(s + 1) * ns]), f"gate/up shard {s}"
+    del wg, wu, full
+    # down 9B: split K
+    n, k = inputs.SHAPES["down_9b"]
+    ks = inputs.SHAPES["down_9b_kshard8"][1]
+    assert ks * g == k
+    w = inputs.make_q4k(n, k, config_id=2, tensor_id=2)
+    xh = inputs.make_x(1, k, config_id=2, tensor_id=5)[0]
+    sb = ks // 256
+    w_rows = w.reshape(n, -1)
+    acc = np.zeros(n, dtype=np.float64)
+    for s in range(g):
+        shard = np.ascontiguousarray(w_rows[:, s * sb * 144:(s + 1) * sb * 144])
+        ys = q4k.gemv(to_dev(shard.reshape(-1)), to_dev(np.ascontiguousarray(xh[s * ks:(s + 1) * ks])))
+        acc += to_host(ys).astype(np.float64)
+    yr, ar = oracle.gemv(w, xh, threads=THREADS)
+    _report("down split-K 8 ways", check_bound(acc, yr, ar, "down split-K sum"))
+
+
 def test_gemv_special_values(q4k):
     n, k = 64, 1024
     x = inputs.make_x(1, k, config_id=93)[0]
