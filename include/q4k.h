@@ -179,8 +179,10 @@ Q4K_API q4k_status q4k_q8_0_gemv(const void *w, const float *x, float *y, int64_
  * A few tokens (2 <= m <= 4 with k <= 4096, and m == 2 with k <= 16384) run
  * on the streaming GEMV kernels, which decode each weight group once per
  * pair of tokens and need no scratch: every token's row is bit for bit what
- * q4k_gemv computes for that token.  Every other m >= 2 runs on the matrix
- * cores (each weight decoded once per 64 tokens).  There, with n >= 16 *
+ * q4k_gemv computes for that token.  The exception is 3 or 4 tokens with
+ * k <= 4096 over n >= 64 * (compute units) rows, which the matrix cores do
+ * faster.  Every other m >= 2 runs on the matrix cores (each weight decoded
+ * once per 64 tokens).  There, with n >= 16 *
  * (compute units of the device), every output is summed by one workgroup in
  * a fixed order and the call is bitwise reproducible; with fewer rows the K
  * range is split across workgroups whose partial sums are added into y with

@@ -765,8 +765,13 @@ hipError_t launch_gemv_batched_dt(const uint8_t *w, const void *x, bool x_f16, v
     }
     if (m == 1) return launch_gemv_dt(w, x, x_f16, y, y_f16, n, k, stream);
     // A few tokens: the streaming GEMV with the codes decoded once per token
-    // pair, no scratch.
-    if ((m <= kTokensMax && k <= kTokensMaxK) || (m == 2 && k <= kTokensSplitMaxK)) {
+    // pair, no scratch.  Three or four tokens over many rows (four 16-row
+    // tiles per CU or more) go to the weight-streaming matrix-core kernel
+    // instead: there the decode work of a second token pair outweighs its
+    // activation preparation.
+    const bool few = (m <= kTokensMax && k <= kTokensMaxK) || (m == 2 && k <= kTokensSplitMaxK);
+    const bool many_rows = m > 2 && k <= kStreamMaxK && (n + 15) / 16 >= 4 * static_cast<int64_t>(device_cu_count());
+    if (few && !many_rows) {
         if (ws.query) return hipSuccess;
         return launch_gemv_tokens(w, x, x_f16, y, y_f16, m, n, k, stream);
     }

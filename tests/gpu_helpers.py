@@ -87,3 +87,15 @@ def check_bound_f16(y16, y_ref, a_ref, what):
         raise AssertionError(f"{what}: {int((~ok).sum())} of {y.size} f16 outputs outside the bound; first at "
                              f"{i.tolist()}: gpu {y[tuple(i)]!r} oracle {y_ref[tuple(i)]!r} bound {bound[tuple(i)]!r}")
     return float(np.max(err / bound)) if err.size else 0.0
+
+
+def batched_on_gemv_kernels(m: int, n: int, k: int) -> bool:
+    """Whether q4k_gemv_batched runs m tokens on the streaming GEMV kernels
+    (token pairs, no scratch, each token bitwise equal to q4k_gemv) rather
+    than on the matrix cores."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    few = (m <= 4 and k <= 4096) or (m == 2 and k <= 16384)
+    many_rows = m > 2 and k <= 4096 and (n + 15) // 16 >= 4 * cus
+    return m >= 2 and few and not many_rows

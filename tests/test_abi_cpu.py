@@ -220,7 +220,7 @@ def test_workspace_size_queries(L):
     out = ctypes.c_int64(-1)
     # sizes that need no device: empty calls, one token, k == 0,
     # and up to 4 tokens with k <= 4096 (the streaming GEMV kernel)
-    for m, n, k in ((0, 16, 256), (4, 0, 256), (1, 4096, 4096), (8, 16, 0), (2, 16, 256), (4, 12288, 4096)):
+    for m, n, k in ((0, 16, 256), (4, 0, 256), (1, 4096, 4096), (8, 16, 0), (2, 16, 256), (4, 48, 4096)):
         for xd in (0, 1):
             for yd in (0, 1):
                 out.value = -1

@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import REL, THREADS, check_bound, check_bound_f16, to_dev, to_host
+from gpu_helpers import REL, THREADS, batched_on_gemv_kernels, check_bound, check_bound_f16, to_dev, to_host
 from q4_dequant_gemv_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -127,7 +127,7 @@ def test_batched_dt_all_combinations(q4k, m, n, k):
     yr, ar = oracle.gemv_batched(w, x16.astype(np.float32), threads=THREADS)
     # few rows per CU on the matrix-core kernel: K is split across workgroups
     # and added with atomics (a few tokens run on the streaming kernels instead)
-    streaming = (m <= 4 and k <= 4096) or (m == 2 and k <= 16384)
+    streaming = batched_on_gemv_kernels(m, n, k)
     split = not streaming and n < 16 * torch.cuda.get_device_properties(0).multi_processor_count and k >= 512
     for xd in ("f16", "f32"):
         xin = xh if xd == "f16" else xf

@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import THREADS, check_bound, check_swiglu_bound, to_dev, to_host
+from gpu_helpers import THREADS, batched_on_gemv_kernels, check_bound, check_swiglu_bound, to_dev, to_host
 from q4_dequant_gemv_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -444,6 +444,7 @@ def test_batched_few_tokens_equal_batch1_bitwise(q4k, m, n, k):
     import torch
 
     print(f"[case] few tokens m={m} {n}x{k}", flush=True)
+    assert batched_on_gemv_kernels(m, n, k)
     w = inputs.make_q4k(n, k, config_id=95, tensor_id=k)
     xs = inputs.make_x(m, k, config_id=95, tensor_id=m)
     wd, xd = to_dev(w.reshape(-1)), to_dev(xs)
@@ -457,13 +458,16 @@ def test_batched_few_tokens_equal_batch1_bitwise(q4k, m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(5, 4096, 256), (16, 4100, 1024), (9, 4096, 2048), (16, 4111, 2304),
-                                   (12, 5000, 3328), (7, 4097, 4096), (16, 8192, 4096)])
+                                   (12, 5000, 3328), (7, 4097, 4096), (16, 8192, 4096), (4, 16400, 1024),
+                                   (3, 16384, 2048)])
 def test_batched_streamed_tiles(q4k, m, n, k):
-    """5 to 16 tokens, k <= 4096, a 16-row tile for every CU: the matrix-core
-    kernel that streams the weights (each wave holding its K slice's
-    activation operands), including waves whose last halves are past the row
-    (k = 2304, 3328) and a ragged last tile.  Every output is written, inside
-    the bound, and the same bits on a second run."""
+    """5 to 16 tokens with k <= 4096 and a 16-row tile for every CU, or 3 and
+    4 tokens with four tiles per CU: the matrix-core kernel that streams the
+    weights (each wave holding its K slice's activation operands), including
+    waves whose last halves are past the row (k = 2304, 3328) and a ragged
+    last tile.  Every output is written, inside the bound, and the same bits
+    on a second run."""
+    assert not batched_on_gemv_kernels(m, n, k)
     import torch
 
     print(f"[case] streamed tiles m={m} {n}x{k}", flush=True)

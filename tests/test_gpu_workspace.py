@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import THREADS, check_bound, check_bound_f16, to_dev, to_host
+from gpu_helpers import THREADS, batched_on_gemv_kernels, check_bound, check_bound_f16, to_dev, to_host
 from q4_dequant_gemv_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -60,7 +60,7 @@ def _workspace(nbytes, offset=0):
 
 @pytest.mark.parametrize("m,n,k", [(2, 4096, 2048), (16, 8192, 1024), (64, 4100, 2048), (100, 4096, 2304),
                                    (33, 513, 1024), (4, 70, 12288), (17, 300, 4096), (3, 1000, 4096),
-                                   (5, 4096, 1024)])
+                                   (5, 4096, 1024), (4, 20000, 1024)])
 @pytest.mark.parametrize("xd,yd", [("f32", "f32"), ("f16", "f16"), ("f16", "f32")])
 def test_batched_ws_matches_allocating_call(q4k, m, n, k, xd, yd):
     import torch
@@ -73,8 +73,8 @@ def test_batched_ws_matches_allocating_call(q4k, m, n, k, xd, yd):
         x = x.astype(np.float16)
     wd, xt = to_dev(w.reshape(-1)), to_dev(x)
     need = q4k.gemv_batched_workspace_size(m, n, k, x_dtype=dt[xd], out_dtype=dt[yd])
-    # up to 4 tokens with k <= 4096 run on the streaming kernel, which needs none
-    small = m <= 4 and k <= 4096
+    # a few tokens run on the streaming GEMV kernels, which need none
+    small = batched_on_gemv_kernels(m, n, k)
     assert (need == 0) == small
     y_ws = q4k.gemv_batched_ws(wd, xt, None if small else _workspace(need), out_dtype=dt[yd])
     y_al = q4k.gemv_batched_dt(wd, xt, out_dtype=dt[yd])
