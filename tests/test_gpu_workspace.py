@@ -169,14 +169,25 @@ def test_workspace_calls_in_a_graph_replay_equal_eager(q4k):
     ws_p = _workspace(q4k.prefill_workspace_size(200, 512, k))
     yb = torch.empty((24, nb), dtype=torch.float16, device="cuda")
     yp = torch.empty((200, 512), dtype=torch.float32, device="cuda")
+    # two tokens (the streaming GEMV, no workspace) and sixteen (the streamed
+    # matrix-core kernel) over the same rows
+    x2 = to_dev(inputs.make_x(2, k, config_id=94, tensor_id=3))
+    x16 = to_dev(inputs.make_x(16, k, config_id=94, tensor_id=4))
+    assert batched_on_gemv_kernels(2, nb, k) and not batched_on_gemv_kernels(16, nb, k)
+    assert q4k.gemv_batched_workspace_size(2, nb, k) == 0
+    ws_16 = _workspace(q4k.gemv_batched_workspace_size(16, nb, k))
+    y2 = torch.empty((2, nb), dtype=torch.float32, device="cuda")
+    y16 = torch.empty((16, nb), dtype=torch.float32, device="cuda")
 
     def step():
         q4k.gemv_batched_ws(wb, xb, ws_b, y=yb)
         q4k.prefill_gemm_ws(wp, xp, ws_p, y=yp)
+        q4k.gemv_batched_ws(wb, x2, None, y=y2)
+        q4k.gemv_batched_ws(wb, x16, ws_16, y=y16)
 
     step()
     torch.cuda.synchronize()
-    ref = [yb.clone(), yp.clone()]
+    ref = [yb.clone(), yp.clone(), y2.clone(), y16.clone()]
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -187,13 +198,16 @@ def test_workspace_calls_in_a_graph_replay_equal_eager(q4k):
     with torch.cuda.graph(g):
         step()
     for rep in range(4):
-        yb.fill_(float("nan"))
-        yp.fill_(float("nan"))
+        for t in (yb, yp, y2, y16):
+            t.fill_(float("nan"))
         ws_b.fill_(0xAB)
         ws_p.fill_(0xCD)      # stale workspace contents must not matter
+        ws_16.fill_(0xEF)
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(yb, ref[0]), f"replay {rep}: batched output differs"
         assert torch.equal(yp, ref[1]), f"replay {rep}: prefill output differs"
+        assert torch.equal(y2, ref[2]), f"replay {rep}: two-token output differs"
+        assert torch.equal(y16, ref[3]), f"replay {rep}: sixteen-token output differs"
         step()
         torch.cuda.synchronize()
