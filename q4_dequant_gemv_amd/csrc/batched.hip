@@ -205,7 +205,11 @@ __device__ __forceinline__ void build_b_ops(BOps &o, uint4 hdr, uint4 qv, const 
 
 // One (row tile, token tile) product of a half super-block and its epilogue:
 // out[r] += 2^e * (d * (P - 1024 * sum(hi + lo)) - dmin * Q) for the lane's
-// tokens 4*kq + r.
+// tokens 4*kq + r.  TWO_CHAINS: the hi and lo products accumulate into two
+// independent tiles, added at the end, so consecutive matrix-core
+// instructions do not wait on each other (faster when a wave has many
+// token tiles to multiply; one chain is as fast otherwise).
+template <bool TWO_CHAINS = false>
 __device__ __forceinline__ void mfma_half(const BOps &bo, const AStep &a, float4_t &out, int kq) {
     // the lane's token's sums of its quarter's two sub-blocks, hi and lo
     const int gg = kq >> 1;
@@ -214,12 +218,15 @@ __device__ __forceinline__ void mfma_half(const BOps &bo, const AStep &a, float4
     const half8_t amin_hi = __builtin_bit_cast(half8_t, u32x4_t{shi, 0u, 0u, 0u});
     const half8_t amin_lo = __builtin_bit_cast(half8_t, u32x4_t{slo, 0u, 0u, 0u});
     float4_t pacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float4_t lacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a.f[2 * i]), bo.b[i], pacc, 0, 0, 0);
-        pacc =
-            __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a.f[2 * i + 1]), bo.b[i], pacc, 0, 0, 0);
+        float4_t &second = TWO_CHAINS ? lacc : pacc;
+        second =
+            __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a.f[2 * i + 1]), bo.b[i], second, 0, 0, 0);
     }
+    if constexpr (TWO_CHAINS) pacc += lacc;
     float4_t qacc = {0.0f, 0.0f, 0.0f, 0.0f};
     qacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(amin_hi, bo.bmin, qacc, 0, 0, 0);
     qacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(amin_lo, bo.bmin, qacc, 0, 0, 0);
@@ -363,7 +370,7 @@ __global__ __launch_bounds__(128 * S, 1) void batched_mfma_kernel(const uint8_t 
 #pragma unroll
         for (int p = 0; p < MT; ++p) acc[t][p] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto multiply = [&](const BOps &bo, const AStep &a, float4_t &out) { mfma_half(bo, a, out, kq); };
+    auto multiply = [&](const BOps &bo, const AStep &a, float4_t &out) { mfma_half<(MT >= 4)>(bo, a, out, kq); };
 
     // ---- pipeline: weights P stages ahead (register ring -> LDS), the wave's
     // activations one step ahead.  Unrolled by P so every ring slot, LDS
