@@ -484,6 +484,43 @@ def test_batched_streamed_tiles(q4k, m, n, k):
     _report(f"streamed m={m} {n}x{k}", check_bound(y[:, rows], yr, ar, f"streamed m={m} {n}x{k}"))
 
 
+def _boundary_cases():
+    # the batched call's kernel choice switches at m = 2 | 3..4 | 5..16 | 17+,
+    # at K = 4096 (token pairs, streamed tiles) and 16384 (two-token K split),
+    # and at 16 and 64 rows per CU (rows as multiples of 16 * CUs, here for up
+    # to 256 CUs: each side of each switch appears for any CU count <= 256)
+    out = []
+    for m in (2, 3, 4, 5, 16, 17):
+        for n in (4080, 4096, 16368, 16384):
+            out.append((m, n, 4096))
+        out.append((m, 16384, 4352))
+    out += [(2, 512, 16384), (2, 512, 16640), (3, 512, 16384)]
+    return out
+
+
+@pytest.mark.parametrize("m,n,k", _boundary_cases())
+def test_batched_kernel_choice_boundaries(q4k, m, n, k):
+    """Both sides of every switch in the batched call's kernel choice: every
+    output written, sampled rows inside the oracle's bound, and the few-token
+    path's rows equal to q4k_gemv per token."""
+    import torch
+
+    print(f"[case] boundary m={m} {n}x{k} gemv-kernels={batched_on_gemv_kernels(m, n, k)}", flush=True)
+    w = inputs.make_q4k(n, k, config_id=93, tensor_id=n + k)
+    xs = inputs.make_x(m, k, config_id=93, tensor_id=m)
+    wd, xd = to_dev(w.reshape(-1)), to_dev(xs)
+    yd = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    q4k.gemv_batched(wd, xd, y=yd)
+    y = to_host(yd)
+    assert np.isfinite(y).all(), f"{int((~np.isfinite(y)).sum())} outputs not written"
+    if batched_on_gemv_kernels(m, n, k):
+        for t in range(m):
+            assert torch.equal(yd[t], q4k.gemv(wd, xd[t])), f"token {t} differs from the batch-1 call"
+    rows = _sample_rows(n, 200, seed=m * 7 + n)
+    yr, ar = oracle.gemv_batched(w[rows], xs, threads=THREADS)
+    check_bound(y[:, rows], yr, ar, f"boundary m={m} {n}x{k}")
+
+
 @pytest.mark.parametrize("n", [64, 4096])
 def test_batched_special_values(q4k, n):
     """m = 4: the streaming GEMV kernels (two token pairs); m = 16: the staged
