@@ -63,18 +63,29 @@ extern "C" {
 #define Q4K_API
 #endif
 
+/*
+ * The two enums below also name the ends of the int range (the *_INT_MIN_ and
+ * *_INT_MAX_ members, never returned or accepted as values): every int is
+ * then a value of the type, also in C++, so a caller may pass any code and
+ * an unknown one is rejected (Q4K_ERR_INVALID_ARG; "unknown status" from
+ * q4k_status_string) rather than being out of the type's range.
+ */
 typedef enum {
     Q4K_OK = 0,
     Q4K_ERR_INVALID_ARG = 1,       /* null pointer, negative size, overlap, size overflow */
     Q4K_ERR_UNSUPPORTED_SHAPE = 2, /* k % 256 != 0, or a shape beyond a call's stated limits */
     Q4K_ERR_MISALIGNED = 3,        /* w not 16-B aligned, or x/y not 4-B aligned */
-    Q4K_ERR_LAUNCH = 4             /* the HIP runtime refused a launch */
+    Q4K_ERR_LAUNCH = 4,            /* the HIP runtime refused a launch */
+    Q4K_STATUS_INT_MIN_ = -2147483647 - 1,
+    Q4K_STATUS_INT_MAX_ = 2147483647
 } q4k_status;
 
 /* Element type of activations and outputs in the *_dt calls. */
 typedef enum {
     Q4K_F32 = 0, /* IEEE binary32 */
-    Q4K_F16 = 1  /* IEEE binary16: inputs widened exactly, outputs rounded to nearest even */
+    Q4K_F16 = 1, /* IEEE binary16: inputs widened exactly, outputs rounded to nearest even */
+    Q4K_DTYPE_INT_MIN_ = -2147483647 - 1,
+    Q4K_DTYPE_INT_MAX_ = 2147483647
 } q4k_dtype;
 
 /* Bytes of one Q4_K super-block and weights per super-block. */
@@ -247,9 +258,9 @@ Q4K_API q4k_status q4k_prefill_gemm(const void *w, const void *x, void *y, q4k_d
  * q4k_gemv_batched_dt / q4k_prefill_gemm compute (the same kernels, the same
  * order of sums) with `workspace`, a device buffer of workspace_bytes owned by
  * the caller, in place of the stream-ordered allocation.  The workspace must
- * be 256-byte aligned, hold at least the queried size (else
- * Q4K_ERR_INVALID_ARG; it may be NULL when that size is 0) and overlap none of
- * w, x, y (Q4K_ERR_INVALID_ARG).  Its contents are garbage before and after
+ * be 256-byte aligned (else Q4K_ERR_MISALIGNED), hold at least the queried
+ * size (else Q4K_ERR_INVALID_ARG; it may be NULL when that size is 0) and
+ * overlap none of w, x, y (Q4K_ERR_INVALID_ARG).  Its contents are garbage before and after
  * the call; the call uses it until the stream reaches the end of the call's
  * work, so calls in flight at the same time need separate workspaces.
  */

@@ -463,9 +463,13 @@ const char *q4k_status_string(q4k_status s) {
     switch (s) {
         case Q4K_OK: return "ok";
         case Q4K_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size, overlapping buffers or size overflow)";
-        case Q4K_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (k must be a multiple of 256)";
-        case Q4K_ERR_MISALIGNED: return "misaligned pointer (w needs 16-byte alignment, activations/outputs 4-byte; dequant output 16-byte)";
+        case Q4K_ERR_UNSUPPORTED_SHAPE:
+            return "unsupported shape (k not a multiple of 256, or of 32 for Q8_0, or beyond a call's stated limits)";
+        case Q4K_ERR_MISALIGNED:
+            return "misaligned pointer (w needs 16-byte alignment, activations/outputs their element size; dequant "
+                   "output and workspaces as documented)";
         case Q4K_ERR_LAUNCH: return "kernel launch failed";
+        default: break;  // any other int: the type spans the whole int range
     }
     return "unknown status";
 }
