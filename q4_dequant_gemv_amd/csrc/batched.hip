@@ -457,13 +457,14 @@ __global__ __launch_bounds__(128 * S, 1) void batched_mfma_kernel(const uint8_t 
 // preparation kernel's scratch) in registers for the whole call, and their
 // per-token sums and scales in LDS (read per tile).  The
 // workgroup streams 16-row tiles (tile blockIdx.x + c*gridDim.x); each wave
-// loads its part of a tile straight into registers NB tiles ahead (per lane:
-// row `col`'s super-block header and 16 code bytes per half), builds the B
-// operands and runs the same half super-block products as the staged kernel.
-// Each wave's tile sums go to LDS; every kStreamFlush tiles, after a barrier,
-// one thread per (tile, lane) adds the W waves' sums in wave order and stores
-// them, so the result does not depend on timing.  A wave whose last half is
-// past the row (an odd number of halves) skips it.
+// loads its part of a tile straight into registers, NB - 1 tiles ahead of the
+// one it multiplies (per lane: row `col`'s super-block headers and 16 code
+// bytes per half), builds the B operands and runs the same half super-block
+// products as the staged kernel.  Each wave's tile sums go to LDS; every
+// kStreamFlush tiles, after a barrier, one thread per (tile, lane) adds the
+// waves' sums in wave order and stores them, so the result does not depend on
+// timing.  Halves past the row (the half count not a multiple of H) are
+// skipped.
 constexpr int kStreamFlush = 2;
 constexpr int kStreamMaxWaves = 16;
 constexpr int kStreamMaxHalves = 32;
