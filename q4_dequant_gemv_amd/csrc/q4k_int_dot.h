@@ -92,20 +92,27 @@ __device__ __forceinline__ void prepare_x(const XLoaded<NCH> &f, int ngroups, XG
             sexp = 21 - e;
             scale = ldexpf(1.0f, e - 21);
         }
-        uint32_t l0 = 0, l1 = 0, l2 = 0;
+        // Balanced digits by a bias: with X = X2*2^16 + X1*2^8 + X0 and every
+        // Xj in [-128, 127], byte j of B = X + 0x808080 is Xj + 128 (B stays
+        // below 2^24), so gathering byte j of the four values into one dword
+        // (two rounds of byte permutes) and flipping each byte's top bit
+        // gives the four Xj as signed bytes.
+        uint32_t bx[4];
         int s = 0;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int X = (finite && !zero) ? static_cast<int>(rintf(ldexpf(v[b], sexp))) : 0;
             s += X;
-            const int x0 = static_cast<int>(static_cast<int8_t>(X & 0xff));
-            const int r = (X - x0) >> 8;
-            const int x1 = static_cast<int>(static_cast<int8_t>(r & 0xff));
-            const int x2 = (r - x1) >> 8;
-            l0 |= static_cast<uint32_t>(x0 & 0xff) << (8 * b);
-            l1 |= static_cast<uint32_t>(x1 & 0xff) << (8 * b);
-            l2 |= static_cast<uint32_t>(x2 & 0xff) << (8 * b);
+            bx[b] = static_cast<uint32_t>(X + 0x808080);
         }
+        // v_perm_b32: byte i of the result is byte sel_i of {first (bytes 4-7), second (bytes 0-3)}
+        const uint32_t t01 = __builtin_amdgcn_perm(bx[1], bx[0], 0x05010400u);  // bytes 0 and 1 of values 0, 1
+        const uint32_t t23 = __builtin_amdgcn_perm(bx[3], bx[2], 0x05010400u);
+        const uint32_t u01 = __builtin_amdgcn_perm(bx[1], bx[0], 0x07030602u);  // bytes 2 and 3 of values 0, 1
+        const uint32_t u23 = __builtin_amdgcn_perm(bx[3], bx[2], 0x07030602u);
+        const uint32_t l0 = __builtin_amdgcn_perm(t23, t01, 0x05040100u) ^ 0x80808080u;
+        const uint32_t l1 = __builtin_amdgcn_perm(t23, t01, 0x07060302u) ^ 0x80808080u;
+        const uint32_t l2 = __builtin_amdgcn_perm(u23, u01, 0x05040100u) ^ 0x80808080u;
         s = lane_group_sum_int<8>(s);
         xg[j].limb[half][0][i] = l0;
         xg[j].limb[half][1][i] = l1;
