@@ -134,14 +134,49 @@ def rows_of(w, k: int) -> int:
     return w.numel() // rb
 
 
+def _tensor(t, name):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    return t
+
+
+def _sizes(device, weights=(), exact=()):
+    """Host-side size and placement checks made before anything reaches the
+    library, which sees only pointers: every tensor on ``device``; each
+    ``(w, name, bytes)`` of ``weights`` holds at least ``bytes`` bytes; each
+    ``(t, name, count)`` of ``exact`` has exactly ``count`` elements.  A
+    mismatch raises ValueError and nothing is launched."""
+    for t, name, need in weights:
+        _tensor(t, name)
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the activations on {device}")
+        if t.numel() < need:
+            raise ValueError(f"{name} holds {t.numel()} bytes; the call reads {need}")
+    for t, name, count in exact:
+        _tensor(t, name)
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the activations on {device}")
+        if t.numel() != count:
+            raise ValueError(f"{name} has {t.numel()} elements; the call needs {count}")
+
+
+def _q4k_bytes(n: int, k: int) -> int:
+    if n < 0 or k < 0:
+        raise ValueError(f"negative size (n={n}, k={k})")
+    return n * (k // BLOCK_WEIGHTS) * BLOCK_BYTES
+
+
 def gemv(w, x, y=None, n: int | None = None, stream=None):
     """y[r] = sum_c W[r,c] x[c] for a Q4_K matrix ``w`` (uint8) and f32 ``x`` [k]."""
     import torch
 
-    k = x.numel()
+    k = _tensor(x, "x").numel()
     n = rows_of(w, k) if n is None else n
     if y is None:
         y = torch.empty(n, dtype=torch.float32, device=x.device)
+    _sizes(x.device, [(w, "w", _q4k_bytes(n, k))], [(y, "y", n)])
     _check(lib().q4k_gemv(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float32), _dev(y, "y", torch.float32),
                           n, k, _stream(stream)), "q4k_gemv")
     return y
@@ -173,10 +208,11 @@ def gemv_dt(w, x, y=None, n: int | None = None, out_dtype=None, stream=None):
     """``gemv`` with f16 or f32 ``x`` and ``y`` (the tensors' dtypes say which)."""
     import torch
 
-    k = x.numel()
+    k = _tensor(x, "x").numel()
     n = rows_of(w, k) if n is None else n
     if y is None:
         y = torch.empty(n, dtype=out_dtype or x.dtype, device=x.device)
+    _sizes(x.device, [(w, "w", _q4k_bytes(n, k))], [(y, "y", n)])
     _check(lib().q4k_gemv_dt(_dev(w, "w", torch.uint8), _dev_any(x, "x"), _dtype_code(x, "x"), _dev_any(y, "y"),
                              _dtype_code(y, "y"), n, k, _stream(stream)), "q4k_gemv_dt")
     return y
@@ -186,12 +222,13 @@ def gemv_batched_dt(w, x, y=None, n: int | None = None, out_dtype=None, stream=N
     """``gemv_batched`` with f16 or f32 ``x`` [m, k] and ``y`` [m, n]."""
     import torch
 
-    if x.dim() != 2:
+    if _tensor(x, "x").dim() != 2:
         raise ValueError("x must be [m, k]")
     m, k = x.shape
     n = rows_of(w, k) if n is None else n
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype or x.dtype, device=x.device)
+    _sizes(x.device, [(w, "w", _q4k_bytes(n, k))], [(y, "y", m * n)])
     _check(lib().q4k_gemv_batched_dt(_dev(w, "w", torch.uint8), _dev_any(x, "x"), _dtype_code(x, "x"),
                                      _dev_any(y, "y"), _dtype_code(y, "y"), m, n, k, _stream(stream)),
            "q4k_gemv_batched_dt")
@@ -202,12 +239,13 @@ def prefill_gemm(w, x, y=None, n: int | None = None, out_dtype=None, stream=None
     """y[t, r] = sum_c W[r,c] x[t,c] for f16 ``x`` [m, k] (prefill sizes); ``y`` f32 or f16 [m, n]."""
     import torch
 
-    if x.dim() != 2:
+    if _tensor(x, "x").dim() != 2:
         raise ValueError("x must be [m, k]")
     m, k = x.shape
     n = rows_of(w, k) if n is None else n
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype or torch.float32, device=x.device)
+    _sizes(x.device, [(w, "w", _q4k_bytes(n, k))], [(y, "y", m * n)])
     _check(lib().q4k_prefill_gemm(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float16), _dev_any(y, "y"),
                                   _dtype_code(y, "y"), m, n, k, _stream(stream)), "q4k_prefill_gemm")
     return y
@@ -257,12 +295,14 @@ def gemv_batched_ws(w, x, workspace, y=None, n: int | None = None, out_dtype=Non
     """``gemv_batched_dt`` with scratch taken from ``workspace`` (uint8, 256-byte aligned)."""
     import torch
 
-    if x.dim() != 2:
+    if _tensor(x, "x").dim() != 2:
         raise ValueError("x must be [m, k]")
     m, k = x.shape
     n = rows_of(w, k) if n is None else n
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype or x.dtype, device=x.device)
+    _sizes(x.device, [(w, "w", _q4k_bytes(n, k))] + ([] if workspace is None else [(workspace, "workspace", 0)]),
+           [(y, "y", m * n)])
     wp, wb = _workspace(workspace)
     _check(lib().q4k_gemv_batched_ws(_dev(w, "w", torch.uint8), _dev_any(x, "x"), _dtype_code(x, "x"),
                                      _dev_any(y, "y"), _dtype_code(y, "y"), m, n, k, wp, wb, _stream(stream)),
@@ -274,12 +314,14 @@ def prefill_gemm_ws(w, x, workspace, y=None, n: int | None = None, out_dtype=Non
     """``prefill_gemm`` with scratch taken from ``workspace`` (uint8, 256-byte aligned)."""
     import torch
 
-    if x.dim() != 2:
+    if _tensor(x, "x").dim() != 2:
         raise ValueError("x must be [m, k]")
     m, k = x.shape
     n = rows_of(w, k) if n is None else n
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype or torch.float32, device=x.device)
+    _sizes(x.device, [(w, "w", _q4k_bytes(n, k))] + ([] if workspace is None else [(workspace, "workspace", 0)]),
+           [(y, "y", m * n)])
     wp, wb = _workspace(workspace)
     _check(lib().q4k_prefill_gemm_ws(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float16), _dev_any(y, "y"),
                                      _dtype_code(y, "y"), m, n, k, wp, wb, _stream(stream)), "q4k_prefill_gemm_ws")
@@ -290,10 +332,11 @@ def gemv_residual(w, x, r, y=None, n: int | None = None, stream=None):
     """y[i] = sum_c W[i,c] x[c] + r[i]; ``y`` may be ``r`` itself (in-place residual add)."""
     import torch
 
-    k = x.numel()
+    k = _tensor(x, "x").numel()
     n = rows_of(w, k) if n is None else n
     if y is None:
         y = torch.empty(n, dtype=torch.float32, device=x.device)
+    _sizes(x.device, [(w, "w", _q4k_bytes(n, k))], [(r, "r", n), (y, "y", n)])
     _check(lib().q4k_gemv_residual(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float32),
                                    _dev(r, "r", torch.float32), _dev(y, "y", torch.float32), n, k, _stream(stream)),
            "q4k_gemv_residual")
@@ -308,7 +351,7 @@ def gemv_multi(ws, x, ys=None, ns=None, gates=None, head_dims=None, stream=None)
     ``gates[j]`` (n/2 each)."""
     import torch
 
-    k = x.numel()
+    k = _tensor(x, "x").numel()
     ws = list(ws)
     ns = [rows_of(w, k) for w in ws] if ns is None else list(ns)
     gates = [None] * len(ws) if gates is None else list(gates)
@@ -319,6 +362,10 @@ def gemv_multi(ws, x, ys=None, ns=None, gates=None, head_dims=None, stream=None)
     ys = list(ys)
     if not (len(ws) == len(ys) == len(ns) == len(gates) == len(head_dims)):
         raise ValueError("ws, ys, ns, gates and head_dims must have the same length")
+    for i, (w, y, n, g) in enumerate(zip(ws, ys, ns, gates)):
+        ny = n // 2 if g is not None else n
+        outs = [(y, f"ys[{i}]", ny)] + ([(g, f"gates[{i}]", ny)] if g is not None else [])
+        _sizes(x.device, [(w, f"ws[{i}]", _q4k_bytes(n, k))], outs)
     items = (GemvItem * max(len(ws), 1))()
     for i, (w, y, n, g, hd) in enumerate(zip(ws, ys, ns, gates, head_dims)):
         items[i].w = _dev(w, f"ws[{i}]", torch.uint8).value
@@ -360,10 +407,13 @@ def q8_0_gemv(w, x, y=None, n: int | None = None, stream=None):
     """y[r] = sum_c W[r,c] x[c] for a Q8_0 matrix ``w`` (uint8) and f32 ``x`` [k]."""
     import torch
 
-    k = x.numel()
+    k = _tensor(x, "x").numel()
     n = q8_0_rows_of(w, k) if n is None else n
     if y is None:
         y = torch.empty(n, dtype=torch.float32, device=x.device)
+    if n < 0:
+        raise ValueError(f"negative size (n={n})")
+    _sizes(x.device, [(w, "w", n * (k // Q8_0_BLOCK_WEIGHTS) * Q8_0_BLOCK_BYTES)], [(y, "y", n)])
     _check(lib().q4k_q8_0_gemv(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float32), _dev(y, "y", torch.float32),
                                n, k, _stream(stream)), "q4k_q8_0_gemv")
     return y
@@ -373,12 +423,13 @@ def gemv_batched(w, x, y=None, n: int | None = None, stream=None):
     """y[t, r] = sum_c W[r,c] x[t,c]; ``x`` f32 [m, k] -> ``y`` f32 [m, n]."""
     import torch
 
-    if x.dim() != 2:
+    if _tensor(x, "x").dim() != 2:
         raise ValueError("x must be [m, k]")
     m, k = x.shape
     n = rows_of(w, k) if n is None else n
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _sizes(x.device, [(w, "w", _q4k_bytes(n, k))], [(y, "y", m * n)])
     _check(lib().q4k_gemv_batched(_dev(w, "w", torch.uint8), _dev(x, "x", torch.float32),
                                   _dev(y, "y", torch.float32), m, n, k, _stream(stream)), "q4k_gemv_batched")
     return y
@@ -388,10 +439,11 @@ def fused_swiglu(w_gate, w_up, x, h=None, n: int | None = None, stream=None):
     """h[r] = silu((W_gate x)[r]) * (W_up x)[r]."""
     import torch
 
-    k = x.numel()
+    k = _tensor(x, "x").numel()
     n = rows_of(w_gate, k) if n is None else n
     if h is None:
         h = torch.empty(n, dtype=torch.float32, device=x.device)
+    _sizes(x.device, [(w_gate, "w_gate", _q4k_bytes(n, k)), (w_up, "w_up", _q4k_bytes(n, k))], [(h, "h", n)])
     _check(lib().q4k_fused_swiglu(_dev(w_gate, "w_gate", torch.uint8), _dev(w_up, "w_up", torch.uint8),
                                   _dev(x, "x", torch.float32), _dev(h, "h", torch.float32), n, k,
                                   _stream(stream)), "q4k_fused_swiglu")
@@ -402,9 +454,10 @@ def dequant(w, k: int, out=None, n: int | None = None, stream=None):
     """W as dense f32 [n, k], bit-exact."""
     import torch
 
-    n = rows_of(w, k) if n is None else n
+    n = rows_of(_tensor(w, "w"), k) if n is None else n
     if out is None:
         out = torch.empty((n, k), dtype=torch.float32, device=w.device)
+    _sizes(w.device, [(w, "w", _q4k_bytes(n, k))], [(out, "out", n * k)])
     _check(lib().q4k_dequant(_dev(w, "w", torch.uint8), _dev(out, "out", torch.float32), n, k, _stream(stream)),
            "q4k_dequant")
     return out

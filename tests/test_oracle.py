@@ -207,6 +207,58 @@ def check_residual(orc):
     np.testing.assert_array_equal(outs[1][0], (q2 @ x).astype(np.float64))
 
 
+def check_row_ranges(orc):
+    # rows [r0, r1) of a matrix with several super-blocks per row, r0 > 0:
+    # the output starts at the first requested row, each block lands at its
+    # own columns, and nothing is written past the requested rows (a guard
+    # region after them keeps its sentinel)
+    lib = orc._load()
+    for k, seed in ((512, 40), (4096, 41)):
+        n, r0, r1 = 11, 3, 9
+        blocks = _random_blocks(n * k // 256, seed)
+        rows = np.ascontiguousarray(blocks.reshape(n, -1))
+        want = ind_dequant(blocks).reshape(n, k)
+        buf = np.full((r1 + 1) * k, np.float32(-12345.5), dtype=np.float32)
+        lib.q4k_oracle_dequant_rows(rows.ctypes.data, k, r0, r1, buf.ctypes.data)
+        got = buf[:(r1 - r0) * k].reshape(r1 - r0, k)
+        np.testing.assert_array_equal(got.view(np.uint32), want[r0:r1].view(np.uint32))
+        assert np.all(buf[(r1 - r0) * k:] == np.float32(-12345.5)), "rows written past the requested range"
+        # the threaded wrapper splits the rows into ranges with r0 > 0
+        np.testing.assert_array_equal(orc.dequant(rows.reshape(-1), k, threads=3).view(np.uint32),
+                                      want.view(np.uint32))
+
+
+def check_batched_magnitudes(orc):
+    # Y and the magnitude sums A of the batched call against a dense f64
+    # product of independently decoded weights, token by token
+    n, k, m = 24, 1024, 3
+    blocks = _random_blocks(n * k // 256, 42)
+    xs = np.random.default_rng(43).standard_normal((m, k)).astype(np.float32)
+    y, a = orc.gemv_batched(blocks.reshape(-1), xs)
+    wd = ind_dequant(blocks).reshape(n, k).astype(np.float64)
+    xd = xs.astype(np.float64)
+    want_a = np.abs(wd[None, :, :] * xd[:, None, :]).sum(axis=-1)
+    assert a.shape == (m, n)
+    np.testing.assert_allclose(a, want_a, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(y, xd @ wd.T, rtol=0, atol=1e-12 * want_a.max())
+
+
+def check_swiglu_magnitudes(orc):
+    # g, u and their magnitude sums ag, au against dense f64 products of two
+    # different, independently decoded matrices (a swap of the two is caught)
+    n, k = 20, 1024
+    bg = _random_blocks(n * k // 256, 44)
+    bu = _random_blocks(n * k // 256, 45)
+    x = np.random.default_rng(46).standard_normal(k).astype(np.float32)
+    out = orc.fused_swiglu(bg.reshape(-1), bu.reshape(-1), x)
+    xd = x.astype(np.float64)
+    for mat, val, mag in ((bg, "g", "ag"), (bu, "u", "au")):
+        wd = ind_dequant(mat).reshape(n, k).astype(np.float64)
+        want_a = np.abs(wd * xd[None, :]).sum(axis=1)
+        np.testing.assert_allclose(out[mag], want_a, rtol=1e-13, atol=0)
+        np.testing.assert_allclose(out[val], wd @ xd, rtol=0, atol=1e-12 * want_a.max())
+
+
 # ------------------------------------------------------------------- Q8_0
 def _q8_numpy_dequant(blocks):
     # independent of the oracle: numpy's binary16 and int8 views of the bytes
@@ -259,7 +311,8 @@ def check_q8_integer_matrix(orc):
 
 
 ALL_PINS = [check_golden_block, check_independent_decoder, check_zero_codes, check_linearity,
-            check_integer_matrix, check_closed_form, check_one_hot, check_residual,
+            check_integer_matrix, check_closed_form, check_one_hot, check_residual, check_row_ranges,
+            check_batched_magnitudes, check_swiglu_magnitudes,
             check_q8_golden, check_q8_independent_decoder, check_q8_integer_matrix]
 
 
@@ -379,6 +432,12 @@ MUTATIONS = {
                         "q8_0_oracle_dequant_block(w + r * row_bytes + b * Q8_0_BLOCK_WEIGHTS, wblk);"),
     "q8_x_index": ("x[b * Q8_0_BLOCK_WEIGHTS + e]", "x[e * nb + b]"),
     "q8_abs_signed": ("mag += p < 0.0 ? -p : p;", "mag += p;"),
+    "rows_block_offset_in_bytes": ("out + (r - r0) * k + b * Q4K_BLOCK_WEIGHTS);",
+                                   "out + (r - r0) * k + b * Q4K_BLOCK_BYTES);"),
+    "rows_output_not_relative": ("out + (r - r0) * k + b * Q4K_BLOCK_WEIGHTS);", "out + r * k + b * Q4K_BLOCK_WEIGHTS);"),
+    "batched_magnitude_transposed": ("&a[t * nr + (r - r0)]", "&a[(r - r0) * m + t]"),
+    "swiglu_magnitudes_swapped": ("&g[i], &ag[i]);\n        q4k_oracle_row_dot(wu + r * row_bytes, k, x, &u[i], &au[i]);",
+                                  "&g[i], &au[i]);\n        q4k_oracle_row_dot(wu + r * row_bytes, k, x, &u[i], &ag[i]);"),
 }
 
 
