@@ -28,10 +28,11 @@
  *    Results are ready when the stream is.  Only the batched calls on the
  *    matrix cores (see q4k_gemv_batched) and the prefill GEMM need device
  *    scratch: they take it stream-ordered from the device's default memory
- *    pool (hipMallocAsync / hipFreeAsync on `stream`), 536 * ceil(m'/16) *
- *    k/8 bytes for the batched call with m' = min(m, 64) tokens (about 1.1 MB
- *    at m = 64, k = 4096), or, through their *_ws forms, from a workspace the
- *    caller passes in.
+ *    pool (hipMallocAsync / hipFreeAsync on `stream`), about 67 *
+ *    ceil(m'/16) * k bytes for the batched call with m' = min(m, 64) tokens
+ *    (about 1.1 MB at m = 64, k = 4096; the size queries below give it
+ *    exactly), or, through their *_ws forms, from a workspace the caller
+ *    passes in.
  *  - Arguments are validated on the host before anything is enqueued; on any
  *    error nothing is launched and the status says why.  Launch failures are
  *    reported as Q4K_ERR_LAUNCH.
@@ -42,10 +43,32 @@
  *  - n == 0 or m == 0 is an empty call: Q4K_OK, nothing launched.  k == 0 is
  *    a valid empty sum: outputs are written as 0 (dequant writes nothing).
  *  - Activations and outputs are f32, except where a call takes a q4k_dtype
- *    (and the prefill GEMM, whose activations are f16).  The products use the factored form
- *    sum_j [d*sc_j * sum_{e in j} q_e x_e - dmin*m_j * sum_{e in j} x_e]
- *    in f32; each result satisfies |y - y_exact| <= 2e-4 * sum_k |w_k x_k|
- *    for finite inputs (non-finite x gives NaN in the affected outputs).
+ *    (and the prefill GEMM, whose activations are f16).  The products use the
+ *    factored form sum_j [d*sc_j * sum_{e in j} q_e x_e - dmin*m_j * sum_{e in
+ *    j} x_e], with the activations of each token in block fixed point.
+ *  - Accuracy.  For one output write A = sum_k |w_k x_k| and B = sum_k
+ *    (|d| sc_k q_k + |dmin| m_k) |x_k| (the two factored terms of each weight
+ *    counted apart).  Each group of 64 consecutive activations of a token
+ *    (128 on the matrix cores) is held to about 22 bits relative to its
+ *    largest |x|.  Before any product the kernels compare each group's total
+ *    rounding E with S4, the sum of the group's |x| other than its four
+ *    largest; where E exceeds 2^-15 S4 (a few outliers far above the rest of
+ *    their group, say) that group is multiplied in f32 instead, every weight
+ *    dequantized on its own and every product rounded once.  Every result
+ *    therefore satisfies
+ *        |y - y_exact| <= 2^-15 sum_g max_{k in g} |w_k| S4_g + cB B + cA A
+ *    with cB = 2^-22, cA = 2^-18 on the batch-1 and few-token kernels
+ *    (groups of 64), and cB = 2^-18 with |d| (1024 + sc_k q_k) in place of
+ *    |d| sc_k q_k, cA = 2^-17 on the matrix cores (groups of 128).  The
+ *    prefill GEMM multiplies its f16 activations exactly (no first term).
+ *    The method's bound |y - y_exact| <= 2e-4 A follows whenever
+ *    sum_g max|w| S4_g <= 4 A and B <= 200 A (B <= 15 A on the matrix cores):
+ *    weights spread within each group (a group whose weights sit only on its
+ *    smallest activations is outside it) and factored terms that do not
+ *    cancel.  Outliers of any size, up to four per group, with zero weights
+ *    included, stay inside it.  An f16 output adds its rounding to nearest.
+ *    Non-finite x gives NaN in every output of its token.  The statements
+ *    assume no product or partial sum overflows or underflows f32.
  *  - Calls are stateless and may be made from several host threads.
  */
 #ifndef Q4K_H

@@ -24,6 +24,18 @@
 // hold sc*q exactly (8 significant bits), and a bf16 dequantized weight misses
 // the 2e-4 * sum|w x| bound at K = 4096.
 //
+// The hi/lo split carries about 22 bits relative to the largest |x| of its
+// (token, half super-block), not of each activation, and a few outliers far
+// above the rest (whose weights may be zero) would leave the others coarse.
+// The preparation kernel compares, per (half, token) block, the split's total
+// remainder E = sum |x - 2^e (hi + lo)| (each remainder exact in f32) with
+// S4, the sum of the block's |x| other than its four largest (through a lower
+// bound formed without cancellation, lane_group_rest_bound), and flags the
+// block if E exceeds 2^-15 times that bound.  A
+// workgroup whose range holds a flagged block computes its whole tile in f32
+// instead (exact_tile: every weight dequantized on its own, every product
+// rounded once), so every activation keeps its full precision.
+//
 // Data flow (gfx950).  A preparation kernel converts x once per call into
 // scratch, already in the lane order of the MFMA operand fragments, so each
 // wave reads its activations with fully coalesced 1 KB loads straight into
@@ -63,6 +75,11 @@ constexpr int kBiasOff = 8448;
 constexpr int kEscOff = 8512;
 constexpr int kTileStageBytes = 8576;
 
+// After the stage blocks, the scratch holds one flag byte per (half
+// super-block, padded token): [k/128][16*mt], 1 if that block needs the f32
+// path.  Its size, rounded to 16 bytes.
+__host__ __device__ constexpr int64_t flag_bytes(int64_t nst, int mt) { return (nst * 16 * mt + 15) / 16 * 16; }
+
 // Position of in-stage activation kk (0..127) in the operand order: the order
 // in which the B operand below consumes the codes.  A lane-quarter kq (lanes
 // 16kq..16kq+15) owns code bytes [16kq, 16kq+16) of the half block's 64 code
@@ -92,8 +109,8 @@ __device__ __forceinline__ int stage_pos(int kk) {
 // activations (widened exactly).
 template <typename XT>
 __global__ __launch_bounds__(256) void x_prep_kernel(const XT *x, uint8_t *__restrict__ xc,
-                                                      uint32_t *__restrict__ zero, int m, int mt, int64_t k,
-                                                      int64_t nzero) {
+                                                      uint8_t *__restrict__ flags, uint32_t *__restrict__ zero,
+                                                      int m, int mt, int64_t k, int64_t nzero) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     for (int64_t i = gid; i < nzero; i += static_cast<int64_t>(gridDim.x) * 256) zero[i] = 0u;
 
@@ -123,16 +140,25 @@ __global__ __launch_bounds__(256) void x_prep_kernel(const XT *x, uint8_t *__res
     const int e = nz ? ilogbf(amax) : 0;
     _Float16 hi[4], lo[4];
     float part = 0.0f;
+    // remainder and magnitudes in units of 2^e
+    float round_sum = 0.0f;
+    float mag[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         const float sv = nz ? ldexpf(v[b], -e) : 0.0f;
         hi[b] = static_cast<_Float16>(sv);
-        lo[b] = static_cast<_Float16>(sv - static_cast<float>(hi[b]));
+        const float rem = sv - static_cast<float>(hi[b]);  // exact in f32
+        lo[b] = static_cast<_Float16>(rem);
+        round_sum += fabsf(rem - static_cast<float>(lo[b]));  // exact: what the split leaves out
+        mag[b] = fabsf(sv);
         part += static_cast<float>(hi[b]) + static_cast<float>(lo[b]);
     }
     const float sub8 = lane_group_sum<8>(part);
     const float tot = lane_group_sum<32>(part);
+    round_sum = lane_group_sum<32>(round_sum);
+    const float rest = lane_group_rest_bound<32>(mag);
     if (!live) return;
+    if (c == 0) flags[st * tpad + tok] = round_sum * 32768.0f > rest ? 1 : 0;
     uint8_t *blk = xc + (st * mt + tok / 16) * kTileStageBytes;
     const int col = tok & 15;
     // activations 4c..4c+3 land at positions pos + {0, 2, 1, 3} of one lane
@@ -155,6 +181,103 @@ __global__ __launch_bounds__(256) void x_prep_kernel(const XT *x, uint8_t *__res
         reinterpret_cast<float *>(blk + kBiasOff)[col] = tot;
         reinterpret_cast<float *>(blk + kEscOff)[col] = finite ? (nz ? ldexpf(1.0f, e) : 0.0f) : NAN;
     }
+}
+
+// ---- the f32 path -------------------------------------------------------------
+// Rows [row0, row1) of W times tokens [0, m) of x over super-blocks
+// [sb0, sb1), in f32 with every weight on its own: w = fma(d*sc, q, -dmin*m)
+// (d*sc*q is exact in f32, so this is the correctly rounded weight the
+// dequant kernel writes) and every product rounded once.  Wave `wave` of
+// `nwaves` takes rows row0 + wave, row0 + wave + nwaves, ...; for each row and
+// four tokens at a time, lane l multiplies weights 4l .. 4l+3 of each
+// super-block (four products summed in f32), adds them into an f64 sum over
+// the super-blocks (any K range without a long chain of f32 roundings), and
+// the lane sums are added across the wave.  The results are
+// stored (ADD false: y = YT of the sum) or added into f32 y with atomics.  A
+// non-finite activation makes its token's results NaN, as on the matrix
+// cores: the sum of 0 * x (0 for finite x, NaN otherwise) is added.
+template <typename XT, typename YT, bool ADD>
+__device__ __attribute__((noinline)) void exact_tile(const uint8_t *__restrict__ w, int64_t row_bytes,
+                                                    const XT *__restrict__ x, int64_t k,
+                           int m, YT *__restrict__ y, int64_t n, int64_t row0, int64_t row1, int sb0, int sb1,
+                           int wave, int nwaves) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;             // 64-weight group of the lane's four weights
+    const int r = 4 * (lane & 15);       // their place inside the group
+    const int j = 2 * g + (r >> 5);      // sub-block
+    const int shift = r >= 32 ? 4 : 0;   // high nibbles for the second sub-block of the group
+    const int code_off = 16 + 32 * g + (r & 31);
+    for (int64_t row = row0 + wave; row < row1; row += nwaves) {
+        const uint8_t *wr = w + row * row_bytes;
+        for (int t0 = 0; t0 < m; t0 += 4) {
+            double acc[4] = {0.0, 0.0, 0.0, 0.0};
+            float nf[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int sb = sb0; sb < sb1; ++sb) {
+                const uint8_t *blk = wr + static_cast<int64_t>(sb) * kBlockBytes;
+                const uint4 hdr = *reinterpret_cast<const uint4 *>(blk);
+                const uint32_t q4 = (*reinterpret_cast<const uint32_t *>(blk + code_off) >> shift) & 0x0f0f0f0fu;
+                int sc, mn;
+                scale_min(hdr.y, hdr.z, hdr.w, j, sc, mn);
+                const float dl = half_bits_to_float(hdr.x) * static_cast<float>(sc);
+                const float ml = half_bits_to_float(hdr.x >> 16) * static_cast<float>(mn);
+                float wv[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) wv[b] = fmaf(dl, static_cast<float>((q4 >> (8 * b)) & 0xffu), -ml);
+                const int64_t col = static_cast<int64_t>(sb) * kBlockWeights + 4 * lane;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (t0 + u < m) {
+                        const XT *xp = x + static_cast<int64_t>(t0 + u) * k + col;
+                        float part = 0.0f;
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            const float xv = static_cast<float>(xp[b]);
+                            part = fmaf(wv[b], xv, part);
+                            nf[u] = fmaf(xv, 0.0f, nf[u]);
+                        }
+                        acc[u] += static_cast<double>(part);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float v = lane_group_sum<64>(static_cast<float>(acc[u]) + nf[u]);
+                if (lane == 0 && t0 + u < m) {
+                    YT *dst = y + static_cast<int64_t>(t0 + u) * n + row;
+                    if constexpr (ADD) unsafeAtomicAdd(dst, v);
+                    else *dst = static_cast<YT>(v);
+                }
+            }
+        }
+    }
+}
+
+// The OR of this thread's share of the flag bytes [off, off + count) of the
+// scratch (whole dwords: off and count are multiples of 16).  Issued before
+// a kernel's first weight loads, so that waiting for it (in issue order)
+// leaves those loads in flight.
+__device__ __forceinline__ uint32_t load_flags(__amdgpu_buffer_rsrc_t ar, int64_t off, int64_t count) {
+    uint32_t any = 0;
+    for (int64_t i = 4 * static_cast<int64_t>(threadIdx.x); i < count; i += 4 * static_cast<int64_t>(blockDim.x))
+        any |= __builtin_amdgcn_raw_buffer_load_b32(ar, static_cast<int>(off + i), 0, 0);
+    return any;
+}
+
+// Whether any wave of the workgroup saw a set flag: each wave's lane 0 writes
+// its ballot to wflag[wave], then a barrier.  The barrier is bare (no fence),
+// with only the LDS write waited for, so weight loads in flight stay in
+// flight.
+__device__ __forceinline__ bool workgroup_any(uint32_t any, int *wflag, int nw) {
+    const bool wave_any = __builtin_amdgcn_ballot_w64(any != 0) != 0;
+    if ((threadIdx.x & 63) == 0) wflag[threadIdx.x >> 6] = wave_any ? 1 : 0;
+    // lgkmcnt(0) only (vmcnt and expcnt at their maxima, gfx9 encoding)
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    int all = 0;
+    for (int v = 0; v < nw; ++v) all |= wflag[v];
+    return all != 0;
 }
 
 // ---- the matrix-core kernel ---------------------------------------------------
@@ -266,12 +389,15 @@ struct StageGeom {
 };
 
 // YT: float or _Float16 output (f16 only with ksplit == 1: the atomics add f32).
-template <int NT, int MT, int S, typename YT>
+// x: the activations themselves (the f32 path's input); the flag bytes start
+// at flag_off in xc.
+template <int NT, int MT, int S, typename YT, typename XT>
 __global__ __launch_bounds__(128 * S, 1) void batched_mfma_kernel(const uint8_t *__restrict__ w,
                                                                   const uint8_t *__restrict__ xc,
                                                                   YT *__restrict__ y, int m, int64_t n,
                                                                   int64_t k, int64_t row_bytes, int ksplit,
-                                                                  int64_t xc_bytes) {
+                                                                  int64_t xc_bytes, const XT *__restrict__ x,
+                                                                  int64_t flag_off) {
     using G = StageGeom<NT, S>;
     constexpr int W = 2 * S;
     constexpr int P = weight_stages_ahead<MT>();
@@ -294,6 +420,9 @@ __global__ __launch_bounds__(128 * S, 1) void batched_mfma_kernel(const uint8_t 
     // rows past n read as zeros; their results are not stored
     const __amdgpu_buffer_rsrc_t wr = stream_rsrc(w + row0 * row_bytes, static_cast<int>(rows_here * row_bytes));
     const __amdgpu_buffer_rsrc_t ar = stream_rsrc(xc, static_cast<int>(xc_bytes));
+    // flags of this workgroup's halves, all token tiles: loaded first
+    const uint32_t flag_bits = load_flags(ar, flag_off + 2 * static_cast<int64_t>(sb0) * 16 * MT,
+                                          2 * static_cast<int64_t>(sb1 - sb0) * 16 * MT);
 
     // ---- this thread's pieces of every stage copy
     uint32_t g_off[G::kLoads];   // byte offset in the row block, stage base excluded
@@ -382,6 +511,18 @@ __global__ __launch_bounds__(128 * S, 1) void batched_mfma_kernel(const uint8_t 
 #pragma unroll
     for (int q = 0; q < P; ++q) issue_stage(ring[q], q);
     load_a(abuf[0], half_of(0), 0);
+    // a flagged block in the range: the whole tile on the f32 path instead
+    {
+        __shared__ int wflag[W];
+        if (workgroup_any(flag_bits, wflag, W)) {
+            if (ksplit == 1) {
+                exact_tile<XT, YT, false>(w, row_bytes, x, k, m, y, n, row0, row0 + rows_here, sb0, sb1, wave, W);
+            } else if constexpr (std::is_same_v<YT, float>) {
+                exact_tile<XT, float, true>(w, row_bytes, x, k, m, y, n, row0, row0 + rows_here, sb0, sb1, wave, W);
+            }
+            return;
+        }
+    }
     write_stage(ring[0], 0);
     issue_stage(ring[0], P);
     for (int s0 = 0; s0 < nstages; s0 += P) {
@@ -474,10 +615,10 @@ constexpr int64_t kStreamMaxK = kStreamMaxHalves * kStageK;
 template <int H>
 constexpr int stream_max_waves() { return H <= 2 ? 16 : 8; }
 
-template <int H, int NB, typename YT>
+template <int H, int NB, typename YT, typename XT>
 __global__ __launch_bounds__(64 * stream_max_waves<H>(), 1) void stream_mfma_kernel(
     const uint8_t *__restrict__ w, const uint8_t *__restrict__ xc, YT *__restrict__ y, int m, int64_t n, int64_t k,
-    int64_t row_bytes, int64_t xc_bytes) {
+    int64_t row_bytes, int64_t xc_bytes, const XT *__restrict__ x, int64_t flag_off) {
     static_assert(H == 1 || H == 2 || H == 4, "a wave's halves start a super-block (H even) or are one half");
     constexpr int NH = (H + 1) / 2;  // super-blocks (headers) per wave
     __shared__ __align__(16) float4_t part[2][kStreamFlush][stream_max_waves<H>()][64];
@@ -495,8 +636,10 @@ __global__ __launch_bounds__(64 * stream_max_waves<H>(), 1) void stream_mfma_ker
     const int sb = hw0 >> 1;   // its first super-block
 
     // activations of the wave's halves (a lane whose token is past m reads
-    // zeros; a half past the row reads the last one and is skipped)
+    // zeros; a half past the row reads the last one and is skipped); the
+    // flags of every half first
     const __amdgpu_buffer_rsrc_t ar = stream_rsrc(xc, static_cast<int>(xc_bytes));
+    const uint32_t flag_bits = load_flags(ar, flag_off, static_cast<int64_t>(nhalf) * 16);
     const uint32_t a_off = col < m ? 0u : 0x40000000u;
     uint4 af[H][8];
     PairSelect ps[H];
@@ -512,11 +655,23 @@ __global__ __launch_bounds__(64 * stream_max_waves<H>(), 1) void stream_mfma_ker
         if (lane < kTail) tails[hl[h]][lane] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(ar, kSubOff + lane * 16, soff, 0));
         ps[h] = pair_select(2 * ((hw0 + h) & 1) + (kq >> 1));
     }
+    __shared__ int wflag[stream_max_waves<H>()];
+    const bool exact = workgroup_any(flag_bits, wflag, nw);
     __syncthreads();
 
     // the host keeps gridDim.x <= the number of tiles: every workgroup has one
     const int64_t ntiles = (n + 15) / 16;
     const int my_tiles = static_cast<int>((ntiles - 1 - blockIdx.x) / gridDim.x) + 1;
+    if (exact) {
+        // a flagged block: the workgroup's tiles on the f32 path
+        for (int c = 0; c < my_tiles; ++c) {
+            const int64_t r0 = (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(c) * gridDim.x) * 16;
+            const int64_t r1 = r0 + 16 < n ? r0 + 16 : n;
+            exact_tile<XT, YT, false>(w, row_bytes, x, k, m, y, n, r0, r1, 0, static_cast<int>(k / kBlockWeights),
+                                      wave, nw);
+        }
+        return;
+    }
     // byte offset of the lane's header inside a tile (< 16 * 2304 + 2304)
     const uint32_t lane_off = static_cast<uint32_t>(col * row_bytes + sb * kBlockBytes);
     struct TileLoads {
@@ -614,7 +769,8 @@ hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, i
                        hipStream_t stream) {
     constexpr int S = Q4K_BATCH_STAGE_SB;
     const int64_t nst = k / kStageK;
-    const int64_t bytes = nst * MT * kTileStageBytes;
+    const int64_t flag_off = nst * MT * kTileStageBytes;
+    const int64_t bytes = flag_off + flag_bytes(nst, MT);
     constexpr bool kF32Out = std::is_same_v<YT, float>;
     const bool staged = !kF32Out && ksplit > 1;
     const int64_t ny = ksplit > 1 ? static_cast<int64_t>(m) * n : 0;
@@ -633,15 +789,15 @@ hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, i
     const int64_t prep_threads = nst * 16 * MT * 32;
     const int64_t prep_blocks = (prep_threads + 255) / 256;
     hipLaunchKernelGGL(x_prep_kernel<XT>, dim3(static_cast<unsigned>(prep_blocks)), dim3(256), 0, stream, x, xc,
-                       reinterpret_cast<uint32_t *>(acc_y), m, MT, k, ny);
+                       xc + flag_off, reinterpret_cast<uint32_t *>(acc_y), m, MT, k, ny);
     e = hipGetLastError();
     if (e == hipSuccess) {
         const int64_t nrb = (n + 16 * NT - 1) / (16 * NT);
         const dim3 grid(static_cast<unsigned>(nrb * ksplit));
         const int64_t rb = (k / kBlockWeights) * kBlockBytes;
         if (staged) {
-            hipLaunchKernelGGL((batched_mfma_kernel<NT, MT, S, float>), grid, dim3(128 * S), 0, stream, w, xc, acc_y,
-                               m, n, k, rb, ksplit, bytes);
+            hipLaunchKernelGGL((batched_mfma_kernel<NT, MT, S, float, XT>), grid, dim3(128 * S), 0, stream, w, xc,
+                               acc_y, m, n, k, rb, ksplit, bytes, x, flag_off);
             e = hipGetLastError();
             if (e == hipSuccess) {
                 const int64_t need = (ny + 255) / 256;
@@ -650,8 +806,8 @@ hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, i
                 e = hipGetLastError();
             }
         } else {
-            hipLaunchKernelGGL((batched_mfma_kernel<NT, MT, S, YT>), grid, dim3(128 * S), 0, stream, w, xc, y, m, n, k,
-                               rb, ksplit, bytes);
+            hipLaunchKernelGGL((batched_mfma_kernel<NT, MT, S, YT, XT>), grid, dim3(128 * S), 0, stream, w, xc, y, m,
+                               n, k, rb, ksplit, bytes, x, flag_off);
             e = hipGetLastError();
         }
     }
@@ -669,7 +825,8 @@ template <typename XT, typename YT>
 hipError_t launch_stream(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, Workspace &ws,
                          hipStream_t stream) {
     const int64_t nhalf = k / kStageK;
-    const int64_t bytes = nhalf * kTileStageBytes;
+    const int64_t flag_off = nhalf * kTileStageBytes;
+    const int64_t bytes = flag_off + flag_bytes(nhalf, 1);
     if (ws.query) {
         if (bytes > ws.need) ws.need = bytes;
         return hipSuccess;
@@ -680,7 +837,7 @@ hipError_t launch_stream(const uint8_t *w, const XT *x, YT *y, int m, int64_t n,
     if (e != hipSuccess) return e;
     const int64_t prep_blocks = (nhalf * 16 * 32 + 255) / 256;
     hipLaunchKernelGGL(x_prep_kernel<XT>, dim3(static_cast<unsigned>(prep_blocks)), dim3(256), 0, stream, x, xc,
-                       static_cast<uint32_t *>(nullptr), m, 1, k, int64_t{0});
+                       xc + flag_off, static_cast<uint32_t *>(nullptr), m, 1, k, int64_t{0});
     e = hipGetLastError();
     if (e == hipSuccess) {
         // halves per wave: one up to 16 halves (K = 2048), then four (eight
@@ -693,11 +850,11 @@ hipError_t launch_stream(const uint8_t *w, const XT *x, YT *y, int m, int64_t n,
         const int64_t rb = (k / kBlockWeights) * kBlockBytes;
         constexpr int NB = Q4K_STREAM_NB;
         if (H == 1) {
-            hipLaunchKernelGGL((stream_mfma_kernel<1, NB, YT>), grid, dim3(64 * nw), 0, stream, w, xc, y, m, n, k, rb,
-                               bytes);
+            hipLaunchKernelGGL((stream_mfma_kernel<1, NB, YT, XT>), grid, dim3(64 * nw), 0, stream, w, xc, y, m, n, k,
+                               rb, bytes, x, flag_off);
         } else {
-            hipLaunchKernelGGL((stream_mfma_kernel<4, NB, YT>), grid, dim3(64 * nw), 0, stream, w, xc, y, m, n, k, rb,
-                               bytes);
+            hipLaunchKernelGGL((stream_mfma_kernel<4, NB, YT, XT>), grid, dim3(64 * nw), 0, stream, w, xc, y, m, n, k,
+                               rb, bytes, x, flag_off);
         }
         e = hipGetLastError();
     }

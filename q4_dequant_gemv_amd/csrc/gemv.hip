@@ -102,6 +102,26 @@ struct Q4KFormat {
             if (active) acc[t] = xr[t].scale * group_dot(c, xr[t]);
         }
     }
+    // sum over the group of w * x in f32, each weight on its own (the f32
+    // path); xs: the group's 64 activations (registers or memory)
+    // (after: see exact_group_dot)
+    template <typename T>
+    static __device__ __forceinline__ float dot_exact(const Loads &l, const Lane &g, const T *xs, float after) {
+        GroupCodes c;
+        decode_group(l.hdr, l.qa, l.qb, g.ps, c);
+        return exact_group_dot(c, xs, after);
+    }
+    template <int MT, typename T>
+    static __device__ __forceinline__ void dot_tokens_exact(const Loads &l, const Lane &g, const T *const (&xs)[MT],
+                                                            bool active, float after, float (&acc)[MT]) {
+        GroupCodes c;
+        decode_group(l.hdr, l.qa, l.qb, g.ps, c);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            acc[t] = 0.0f;
+            if (active) acc[t] = exact_group_dot(c, xs[t], t == 0 ? after : acc[t - 1]);
+        }
+    }
 };
 
 // Q8_0: 34-byte blocks of 32 weights, an f16 scale d then 32 signed bytes q,
@@ -166,6 +186,40 @@ struct Q8_0Format {
                                                                         static_cast<float>(a10)));
         return d0 * s0 + d1 * s1;
     }
+    // the f32 path: w = d * q (exact in f32) times x, each product rounded once
+    template <typename T>
+    static __device__ __forceinline__ float dot_exact(const Loads &l, const Lane &, const T *xs, float after) {
+        const uint32_t dw[17] = {l.a.x, l.a.y, l.a.z, l.a.w, l.b.x, l.b.y, l.b.z, l.b.w, l.c.x,
+                                 l.c.y, l.c.z, l.c.w, l.d.x, l.d.y, l.d.z, l.d.w, l.e};
+        const float d0 = half_bits_to_float(dw[0]);
+        const float d1 = half_bits_to_float(dw[8] >> 16);
+        float a0 = 0.0f, a1 = 0.0f, nf = 0.0f;
+        // a quarter of the activations at a time, each quarter summed on its
+        // own, and NaN for a non-finite activation, as exact_group_dot
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const global_ptr<T> p = opaque_after(xs, h == 0 ? after : a0, a1);
+            float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+            for (int i = 2 * h; i < 2 * h + 2; ++i) {
+                const uint32_t q0 = __builtin_amdgcn_alignbyte(dw[i + 1], dw[i], 2);
+                const uint32_t q1 = dw[9 + i];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const float w0 = d0 * static_cast<float>(static_cast<int8_t>((q0 >> (8 * b)) & 0xffu));
+                    const float w1 = d1 * static_cast<float>(static_cast<int8_t>((q1 >> (8 * b)) & 0xffu));
+                    const float x0 = static_cast<float>(p[4 * i + b]);
+                    const float x1 = static_cast<float>(p[32 + 4 * i + b]);
+                    s0 = fmaf(w0, x0, s0);
+                    s1 = fmaf(w1, x1, s1);
+                    nf = fmaf(x0, 0.0f, fmaf(x1, 0.0f, nf));
+                }
+            }
+            a0 += s0;
+            a1 += s1;
+        }
+        return (a0 + a1) + nf;
+    }
 };
 
 // One row's weight bytes for one lane, per matrix.
@@ -192,6 +246,18 @@ __device__ __forceinline__ void lane_dot(const RowLoads<F, NMAT> &b, const typen
     for (int mt = 0; mt < NMAT; ++mt) {
         acc[mt] = 0.0f;
         if (active) acc[mt] = xr.scale * F::dot(b.m[mt], g, xr);
+    }
+}
+
+// The same on the f32 path: xs is the lane's group of the activations.
+// after: see exact_group_dot.
+template <class F, int NMAT, typename T>
+__device__ __forceinline__ void lane_dot_exact(const RowLoads<F, NMAT> &b, const typename F::Lane &g, const T *xs,
+                                               bool active, float after, float (&acc)[NMAT]) {
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+        acc[mt] = 0.0f;
+        if (active) acc[mt] = F::dot_exact(b.m[mt], g, xs, mt == 0 ? after : acc[mt - 1]);
     }
 }
 
@@ -362,111 +428,140 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
         if (kTok == 1 || t < ntok) prepare_x<BLOCK, kXChunks>(xl[t], ngroups, xg + t * ngroups);
     }
     __syncthreads();
-    XRegs xr[MT];
+    // the tokens of this wave (tokens past ntok repeat the last)
+    int tok[MT];
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
-        int tok = 0;
+        tok[j] = 0;
         if constexpr (kTok > 1) {
-            tok = tile * MT + j;
-            tok = tok < ntok ? tok : ntok - 1;
+            tok[j] = tile * MT + j;
+            tok[j] = tok[j] < ntok ? tok[j] : ntok - 1;
         }
-        load_xregs(xg[tok * ngroups + g.j], xr[j]);
     }
     // token tiles: outputs of token tile*MT + j sit j*ystride after the
     // tile's first; nvalid of the tile's tokens exist
     const int64_t ystride = mt.n[0];
     const int nvalid = ntok - tile * MT;
-
-    // The loads are never inside a branch: at a control-flow join the wait
-    // counters would have to assume the fewest loads in flight and drain the
-    // prefetch.  Iterations past the end load nothing (0-byte descriptor).
-    //
-    // Results are not stored row by row: gfx9 counts stores with the loads,
-    // and a store on some paths through the loop but not others makes the
-    // wait counters drain loads still in flight.  Lane k of a row's lane group
-    // keeps the group's k-th result of the current window of LPR rows (and
-    // where it goes); the window is stored in one go when it is full (a wave
-    // streaming fewer than LPR rows per group stores only after the loop).
-    float yv[MT];
-#pragma unroll
-    for (int j = 0; j < MT; ++j) yv[j] = 0.0f;
-    YT *yp = nullptr;
-    const float *rp = nullptr;
-    int win = 0;
-    auto flush = [&]() {
-        if (yp != nullptr) {
-            if constexpr (RES) {
-                *yp = static_cast<YT>(rp != nullptr ? yv[0] + *rp : yv[0]);
-            } else {
-                *yp = static_cast<YT>(yv[0]);
-#pragma unroll
-                for (int j = 1; j < MT; ++j) {
-                    if (j < nvalid) yp[j * ystride] = static_cast<YT>(yv[j]);
-                }
-            }
-        }
-        yp = nullptr;
-        win = 0;
-    };
-    // The last iteration leaves both loops at once (goto): a break that fell
-    // back to the outer loop's test would join the loop head with loads of
-    // the unfinished unrolled pass still in flight, and the wait counters
-    // would have to drain them there.
-    // The sequencer issues from the oldest wave first, so with equal shares
-    // the younger waves of a CU fall behind and finish alone, long after the
-    // others.  Each wave therefore lowers its own priority as the share of its
-    // iterations still to do drops (1/2, 1/4, 1/8): a wave that is behind
-    // outranks the ones ahead of it, and the finish times close up.
     const int my_iters = (niters - it0 + nwaves - 1) / nwaves;
-    if (it0 < niters) {
-        for (int it = it0;; it += NB * nwaves) {
+
+    // The row stream, on the integer path (EXACT false: src is the MT
+    // tokens' activation registers) or the f32 path (EXACT true: src holds
+    // MT pointers to the lane's group of activations, in registers or in
+    // memory, and every weight is multiplied on its own).
+    auto stream_rows = [&](auto exact_tag, const auto &src) {
+        constexpr bool EXACT = decltype(exact_tag)::value;
+        // The loads are never inside a branch: at a control-flow join the wait
+        // counters would have to assume the fewest loads in flight and drain the
+        // prefetch.  Iterations past the end load nothing (0-byte descriptor).
+        //
+        // Results are not stored row by row: gfx9 counts stores with the loads,
+        // and a store on some paths through the loop but not others makes the
+        // wait counters drain loads still in flight.  Lane k of a row's lane group
+        // keeps the group's k-th result of the current window of LPR rows (and
+        // where it goes); the window is stored in one go when it is full (a wave
+        // streaming fewer than LPR rows per group stores only after the loop).
+        float yv[MT];
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const int cur = it + b * nwaves;
-                {
-                    const int left = (niters - cur + nwaves - 1) / nwaves;
-                    if (2 * left > my_iters) __builtin_amdgcn_s_setprio(3);
-                    else if (4 * left > my_iters) __builtin_amdgcn_s_setprio(2);
-                    else if (8 * left > my_iters) __builtin_amdgcn_s_setprio(1);
-                    else __builtin_amdgcn_s_setprio(0);
-                }
-                issue(buf[(b + NB - 1) % NB], cur + (NB - 1) * nwaves);
-                row_cursor(cur);
+        for (int j = 0; j < MT; ++j) yv[j] = 0.0f;
+        YT *yp = nullptr;
+        const float *rp = nullptr;
+        int win = 0;
+        auto flush = [&]() {
+            if (yp != nullptr) {
+                if constexpr (RES) {
+                    *yp = static_cast<YT>(rp != nullptr ? yv[0] + *rp : yv[0]);
+                } else {
+                    *yp = static_cast<YT>(yv[0]);
 #pragma unroll
-                for (int q = 0; q < RPG; ++q) {
-                    const int64_t row =
-                        static_cast<int64_t>(cur - rc.begin) * kRowsPerWave + q * kRowsPerGroup + slot;
-                    const bool rok = row < rc.n;
-                    const bool mine = sub == win;
-                    if constexpr (MT == 1) {
-                        float acc[NMAT];
-                        lane_dot(buf[b][q], g, xr[0], rok && g.ok, acc);
-#pragma unroll
-                        for (int m2 = 0; m2 < NMAT; ++m2) acc[m2] = lane_group_sum<LPR>(acc[m2]);
-                        const float out = SWIGLU ? silu(acc[0]) * acc[1] : acc[0];
-                        yv[0] = mine ? out : yv[0];
-                    } else {
-                        // one decode of the group for the wave's MT tokens
-                        float acc[MT];
-                        F::dot_tokens(buf[b][q].m[0], g, xr, rok && g.ok, acc);
-#pragma unroll
-                        for (int j = 0; j < MT; ++j) {
-                            acc[j] = lane_group_sum<LPR>(acc[j]);
-                            yv[j] = mine ? acc[j] : yv[j];
-                        }
+                    for (int j = 1; j < MT; ++j) {
+                        if (j < nvalid) yp[j * ystride] = static_cast<YT>(yv[j]);
                     }
-                    if constexpr (QG) yp = mine ? (rok ? dest(row) : nullptr) : yp;
-                    else if constexpr (kTok > 1) yp = mine ? (rok ? rc.y + tile * MT * ystride + row : nullptr) : yp;
-                    else yp = mine ? (rok ? rc.y + row : nullptr) : yp;
-                    if constexpr (RES) rp = mine ? (rc.r != nullptr ? rc.r + row : nullptr) : rp;
-                    if (++win == LPR) flush();
                 }
-                if (cur + nwaves >= niters) goto done;
+            }
+            yp = nullptr;
+            win = 0;
+        };
+        // The last iteration leaves both loops at once (goto): a break that fell
+        // back to the outer loop's test would join the loop head with loads of
+        // the unfinished unrolled pass still in flight, and the wait counters
+        // would have to drain them there.
+        // The sequencer issues from the oldest wave first, so with equal shares
+        // the younger waves of a CU fall behind and finish alone, long after the
+        // others.  Each wave therefore lowers its own priority as the share of its
+        // iterations still to do drops (1/2, 1/4, 1/8): a wave that is behind
+        // outranks the ones ahead of it, and the finish times close up.
+        if (it0 < niters) {
+            for (int it = it0;; it += NB * nwaves) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int cur = it + b * nwaves;
+                    {
+                        const int left = (niters - cur + nwaves - 1) / nwaves;
+                        if (2 * left > my_iters) __builtin_amdgcn_s_setprio(3);
+                        else if (4 * left > my_iters) __builtin_amdgcn_s_setprio(2);
+                        else if (8 * left > my_iters) __builtin_amdgcn_s_setprio(1);
+                        else __builtin_amdgcn_s_setprio(0);
+                    }
+                    issue(buf[(b + NB - 1) % NB], cur + (NB - 1) * nwaves);
+                    row_cursor(cur);
+#pragma unroll
+                    for (int q = 0; q < RPG; ++q) {
+                        const int64_t row =
+                            static_cast<int64_t>(cur - rc.begin) * kRowsPerWave + q * kRowsPerGroup + slot;
+                        const bool rok = row < rc.n;
+                        const bool mine = sub == win;
+                        if constexpr (MT == 1) {
+                            float acc[NMAT];
+                            if constexpr (EXACT) lane_dot_exact(buf[b][q], g, src[0], rok && g.ok, 0.0f, acc);
+                            else lane_dot(buf[b][q], g, src[0], rok && g.ok, acc);
+#pragma unroll
+                            for (int m2 = 0; m2 < NMAT; ++m2) acc[m2] = lane_group_sum<LPR>(acc[m2]);
+                            const float out = SWIGLU ? silu(acc[0]) * acc[NMAT - 1] : acc[0];
+                            yv[0] = mine ? out : yv[0];
+                        } else {
+                            // one decode of the group for the wave's MT tokens
+                            float acc[MT];
+                            if constexpr (EXACT) F::dot_tokens_exact(buf[b][q].m[0], g, src, rok && g.ok, 0.0f, acc);
+                            else F::dot_tokens(buf[b][q].m[0], g, src, rok && g.ok, acc);
+#pragma unroll
+                            for (int j = 0; j < MT; ++j) {
+                                acc[j] = lane_group_sum<LPR>(acc[j]);
+                                yv[j] = mine ? acc[j] : yv[j];
+                            }
+                        }
+                        if constexpr (QG) yp = mine ? (rok ? dest(row) : nullptr) : yp;
+                        else if constexpr (kTok > 1) yp = mine ? (rok ? rc.y + tile * MT * ystride + row : nullptr) : yp;
+                        else yp = mine ? (rok ? rc.y + row : nullptr) : yp;
+                        if constexpr (RES) rp = mine ? (rc.r != nullptr ? rc.r + row : nullptr) : rp;
+                        if (++win == LPR) flush();
+                    }
+                    if (cur + nwaves >= niters) goto done;
+                }
             }
         }
+    done:
+        flush();
+    };
+
+    XRegs xr[MT];
+    uint32_t flagged = 0;
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+        load_xregs(xg[tok[j] * ngroups + g.j], xr[j]);
+        flagged |= xr[j].inexact;
     }
-done:
-    flush();
+    // A wave whose groups include a flagged one takes the f32 path for all
+    // of them (the choice is per wave, so its loop has no branch on it).
+    if (__builtin_amdgcn_ballot_w64(flagged != 0) == 0) {
+        stream_rows(std::false_type{}, xr);
+    } else {
+        // the f32 path reads the lane's group of activations from memory
+        // (the caches) for every row
+        const XT *src[MT];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) src[j] = x + tok[j] * xstride + 64 * g.j;
+        stream_rows(std::true_type{}, src);
+    }
 }
 
 // ------------------------------------------------------ 4096 < K <= 16384
@@ -533,79 +628,112 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
 #pragma unroll
     for (int b = 0; b + 1 < NB; ++b) issue(buf[b], b);
 
+    __shared__ int inexact;
+    if (threadIdx.x == 0) inexact = 0;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         if (MT == 1 || t < ntok) prepare_x<BLOCK, kXChunks>(xl[t], ngroups, xg + t * ngroups);
     }
     __syncthreads();
-    XRegs xr[MT];
+    int tok[MT];
+    uint32_t flagged = 0;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        const int tok = MT == 1 ? 0 : (t < ntok ? t : ntok - 1);
-        load_xregs(xg[tok * ngroups + g.j], xr[t]);
+        tok[t] = MT == 1 ? 0 : (t < ntok ? t : ntok - 1);
+        flagged |= g.ok ? xg[tok[t] * ngroups + g.j].inexact : 0u;
     }
+    // The loop below has barriers, so the choice of path is made once for the
+    // whole workgroup: the f32 path if any wave's slice holds a flagged group.
+    if (__builtin_amdgcn_ballot_w64(flagged != 0) != 0 && lane == 0) inexact = 1;
+    __syncthreads();
 
-    for (int c = 0; c < my_iters; c += NB) {
-        {
-            // priority falls with the share of iterations left, as in gemv_kernel
-            const int left = my_iters - c;
-            if (4 * left > 3 * my_iters) __builtin_amdgcn_s_setprio(3);
-            else if (4 * left > 2 * my_iters) __builtin_amdgcn_s_setprio(2);
-            else if (4 * left > my_iters) __builtin_amdgcn_s_setprio(1);
-            else __builtin_amdgcn_s_setprio(0);
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const int cur = c + b;
-            issue(buf[(b + NB - 1) % NB], cur + NB - 1);
-            float acc[NV];
-            if constexpr (MT == 1) {
-                lane_dot(buf[b], g, xr[0], g.ok, acc);
-            } else {
-                float at[MT];
-                F::dot_tokens(buf[b].m[0], g, xr, g.ok, at);
-#pragma unroll
-                for (int t = 0; t < MT; ++t) acc[t] = at[t];
+    // EXACT false: src is the MT tokens' activation registers; EXACT true:
+    // MT pointers to the lane's group of activations (registers or memory).
+    auto stream_rows = [&](auto exact_tag, const auto &src) {
+        constexpr bool EXACT = decltype(exact_tag)::value;
+        // f32 path: each row's reads wait for the previous row's sums (the
+        // unrolled rows would otherwise all hold their activations at once)
+        float chain = 0.0f;
+        for (int c = 0; c < my_iters; c += NB) {
+            {
+                // priority falls with the share of iterations left, as in gemv_kernel
+                const int left = my_iters - c;
+                if (4 * left > 3 * my_iters) __builtin_amdgcn_s_setprio(3);
+                else if (4 * left > 2 * my_iters) __builtin_amdgcn_s_setprio(2);
+                else if (4 * left > my_iters) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
             }
-            const int d = cur % kFlush;
-            const int half = (cur / kFlush) & 1;
-            float *pp = part + (((half * kFlush + d) * R + rslot) * S + slice) * NV;
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                acc[v] = lane_group_sum<kWave>(acc[v]);
-                if (lane == 0) pp[v] = acc[v];
-            }
-            if (d == kFlush - 1 || cur + 1 == my_iters) {
-                __syncthreads();
-                const int t = static_cast<int>(threadIdx.x);
-                if (t < (d + 1) * R) {
-                    const int dd = t / R;
-                    const int r = t % R;
-                    const int64_t row = row_of(cur - d + dd, r);
-                    if (row < n) {
-                        const float *q = part + ((half * kFlush + dd) * R + r) * S * NV;
-                        float sum[NV];
+            for (int b = 0; b < NB; ++b) {
+                const int cur = c + b;
+                // the f32 path loads each row just before it is used, after the
+                // previous row's result (few registers: it is a fallback)
+                if constexpr (EXACT) issue(buf[b], opaque_int_after(cur, chain));
+                else issue(buf[(b + NB - 1) % NB], cur + NB - 1);
+                float acc[NV];
+                if constexpr (MT == 1) {
+                    if constexpr (EXACT) lane_dot_exact(buf[b], g, src[0], g.ok, chain, acc);
+                    else lane_dot(buf[b], g, src[0], g.ok, acc);
+                } else {
+                    float at[MT];
+                    if constexpr (EXACT) F::dot_tokens_exact(buf[b].m[0], g, src, g.ok, chain, at);
+                    else F::dot_tokens(buf[b].m[0], g, src, g.ok, at);
 #pragma unroll
-                        for (int v = 0; v < NV; ++v) sum[v] = q[v];
+                    for (int t = 0; t < MT; ++t) acc[t] = at[t];
+                }
+                if constexpr (EXACT) chain = acc[NV - 1];
+                const int d = cur % kFlush;
+                const int half = (cur / kFlush) & 1;
+                float *pp = part + (((half * kFlush + d) * R + rslot) * S + slice) * NV;
 #pragma unroll
-                        for (int s = 1; s < S; ++s) {
+                for (int v = 0; v < NV; ++v) {
+                    acc[v] = lane_group_sum<kWave>(acc[v]);
+                    if (lane == 0) pp[v] = acc[v];
+                }
+                if (d == kFlush - 1 || cur + 1 == my_iters) {
+                    __syncthreads();
+                    const int t = static_cast<int>(threadIdx.x);
+                    if (t < (d + 1) * R) {
+                        const int dd = t / R;
+                        const int r = t % R;
+                        const int64_t row = row_of(cur - d + dd, r);
+                        if (row < n) {
+                            const float *q = part + ((half * kFlush + dd) * R + r) * S * NV;
+                            float sum[NV];
 #pragma unroll
-                            for (int v = 0; v < NV; ++v) sum[v] += q[s * NV + v];
-                        }
-                        if constexpr (MT == 1) {
-                            const float v = SWIGLU ? silu(sum[0]) * sum[1] : sum[0];
-                            y[row] = static_cast<YT>(res != nullptr ? v + res[row] : v);
-                        } else {
+                            for (int v = 0; v < NV; ++v) sum[v] = q[v];
 #pragma unroll
-                            for (int j = 0; j < MT; ++j) {
-                                if (j < ntok) y[j * n + row] = static_cast<YT>(sum[j]);
+                            for (int s = 1; s < S; ++s) {
+#pragma unroll
+                                for (int v = 0; v < NV; ++v) sum[v] += q[s * NV + v];
+                            }
+                            if constexpr (MT == 1) {
+                                const float v = SWIGLU ? silu(sum[0]) * sum[NV - 1] : sum[0];
+                                y[row] = static_cast<YT>(res != nullptr ? v + res[row] : v);
+                            } else {
+#pragma unroll
+                                for (int j = 0; j < MT; ++j) {
+                                    if (j < ntok) y[j * n + row] = static_cast<YT>(sum[j]);
+                                }
                             }
                         }
                     }
                 }
+                if (cur + 1 >= my_iters) break;
             }
-            if (cur + 1 >= my_iters) break;
         }
+    };
+
+    if (inexact == 0) {
+        XRegs xr[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) load_xregs(xg[tok[t] * ngroups + g.j], xr[t]);
+        stream_rows(std::false_type{}, xr);
+    } else {
+        const XT *src[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) src[t] = x + tok[t] * xstride + 64 * g.j;
+        stream_rows(std::true_type{}, src);
     }
 }
 

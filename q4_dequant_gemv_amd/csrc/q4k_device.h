@@ -243,4 +243,50 @@ __device__ __forceinline__ float lane_group_max(float v) {
     return v;
 }
 
+// ---- a lower bound on a group's magnitude without its four largest values
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+
+// (t1, t2) becomes the two largest of (t1, t2) and (u1, u2), both descending.
+__device__ __forceinline__ void merge_top2(float &t1, float &t2, float u1, float u2) {
+    const float n2 = fmaxf(fminf(t1, u1), fmaxf(t2, u2));
+    t1 = fmaxf(t1, u1);
+    t2 = n2;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void merge_top2_dpp(float &t1, float &t2) {
+    merge_top2(t1, t2, dpp_mov<CTRL>(t1), dpp_mov<CTRL>(t2));
+}
+
+// For the non-negative values v (4 per lane) of an aligned group of W lanes
+// (W = 16 or 32): a lower bound on the sum of the group's values other than
+// its four largest, formed from non-negative terms only (no cancellation,
+// whatever the spread).  T is the second largest, over the lanes, of each
+// lane's second largest value: two lanes hold two values >= T each, so the
+// group's four largest are all >= T, and the sum of the values below T
+// leaves them all out.  Every lane of the group gets the bound.  (The lane
+// pairings are those of lane_group_sum; after each step both partners hold
+// the same pair, so the next step merges disjoint sets.)
+template <int W>
+__device__ __forceinline__ float lane_group_rest_bound(const float (&v)[4]) {
+    static_assert(W == 16 || W == 32, "group width");
+    const float p = fmaxf(v[0], v[1]), q = fminf(v[0], v[1]);
+    const float r = fmaxf(v[2], v[3]), s = fminf(v[2], v[3]);
+    float t1 = fmaxf(fminf(p, r), fmaxf(q, s));  // the lane's second largest
+    float t2 = 0.0f;
+    merge_top2_dpp<0xb1>(t1, t2);   // quad_perm [1,0,3,2]
+    merge_top2_dpp<0x4e>(t1, t2);   // quad_perm [2,3,0,1]
+    merge_top2_dpp<0x141>(t1, t2);  // row_half_mirror
+    merge_top2_dpp<0x140>(t1, t2);  // row_mirror
+    if constexpr (W == 32) merge_top2(t1, t2, __shfl_xor(t1, 16, kWave), __shfl_xor(t2, 16, kWave));
+    float below = 0.0f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) below += v[b] < t2 ? v[b] : 0.0f;
+    if constexpr (W == 16) return lane_group_sum<16>(below);
+    else return lane_group_sum<32>(below);
+}
+
 }  // namespace q4k

@@ -14,6 +14,23 @@
 // stay within 32*15*128 = 61440 (|X2| sums within 30720), so the recombined
 // S = sum q*X is below 30720*2^16 + 61440*2^8 + 61440 < 2^31: all integer
 // arithmetic is exact.
+//
+// That representation is accurate relative to the group's largest |x|, not
+// to each activation: every activation is rounded to a step of 2^(e-21).  A
+// few outliers far above the rest of their group would make that step coarse
+// for all the others, and an outlier's weight may be zero.  prepare_x
+// therefore compares, per group, the total rounding E = sum_k |x_k - X_k
+// 2^(e-21)| with S4, the sum of the group's |x| other than its four largest
+// (what is left of sum |w x| if the weights of up to four outliers are zero),
+// through a lower bound formed without cancellation (lane_group_rest_bound).
+// A group with E > 2^-15 times that bound is flagged, and a wave that meets a
+// flagged group
+// multiplies every weight in f32 instead (exact_group_dot): the weight is
+// dequantized as the dequant kernel does and each product w * x is rounded
+// once, so every activation keeps its full precision.  On the integer path a
+// group's rounding therefore adds at most 2^-15 * max_k |w_k| * S4 to a row's
+// result (S4 is at least the bound).  Both sums are formed from terms exact
+// in f32 (their own rounding is a few 2^-24).
 #pragma once
 
 #include <float.h>
@@ -28,7 +45,7 @@ struct XGroup {
     uint32_t limb[2][3][8];  // [sub-block of the pair][limb][dword], 4 signed bytes per dword
     int32_t sx[2];           // sum of X over each 32-weight sub-block
     float scale;             // x ~= X * scale (power of two); 0 if all x are 0; NaN if any is not finite
-    uint32_t pad;
+    uint32_t inexact;        // 1: the group needs the f32 path (rounding above 2^-15 of its magnitude bar the top 4)
 };
 static_assert(sizeof(XGroup) == 208, "XGroup layout");
 
@@ -61,6 +78,10 @@ __device__ __forceinline__ XLoaded<NCH> load_x(const T *x, int ngroups) {
     return f;
 }
 
+// Converts the loaded activations to XGroups.  A group's `inexact` is 1 if
+// its total rounding exceeds 2^-15 of its magnitude without its four largest
+// (see above).
+// Non-finite groups are not flagged (their results are NaN on either path).
 template <int BLOCK, int NCH>
 __device__ __forceinline__ void prepare_x(const XLoaded<NCH> &f, int ngroups, XGroup *__restrict__ xg) {
     const int total = ngroups * 16;
@@ -99,12 +120,22 @@ __device__ __forceinline__ void prepare_x(const XLoaded<NCH> &f, int ngroups, XG
         // gives the four Xj as signed bytes.
         uint32_t bx[4];
         int s = 0;
+        // rounding and magnitudes in units of 2^(e-21)
+        float round_sum = 0.0f;
+        float mag[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const int X = (finite && !zero) ? static_cast<int>(rintf(ldexpf(v[b], sexp))) : 0;
+            // v * 2^sexp and its distance to the nearest integer are exact in f32
+            const float sv = (finite && !zero) ? ldexpf(v[b], sexp) : 0.0f;
+            const float r = rintf(sv);
+            const int X = static_cast<int>(r);
+            round_sum += fabsf(sv - r);
+            mag[b] = fabsf(sv);
             s += X;
             bx[b] = static_cast<uint32_t>(X + 0x808080);
         }
+        round_sum = lane_group_sum<16>(round_sum);
+        const float rest = lane_group_rest_bound<16>(mag);
         // v_perm_b32: byte i of the result is byte sel_i of {first (bytes 4-7), second (bytes 0-3)}
         const uint32_t t01 = __builtin_amdgcn_perm(bx[1], bx[0], 0x05010400u);  // bytes 0 and 1 of values 0, 1
         const uint32_t t23 = __builtin_amdgcn_perm(bx[3], bx[2], 0x05010400u);
@@ -118,17 +149,10 @@ __device__ __forceinline__ void prepare_x(const XLoaded<NCH> &f, int ngroups, XG
         xg[j].limb[half][1][i] = l1;
         xg[j].limb[half][2][i] = l2;
         if (i == 0) xg[j].sx[half] = s;
-        if ((it & 15) == 0) xg[j].scale = scale;
-    }
-}
-
-// The general form for any number of groups (loads inside the loop).
-template <int BLOCK>
-__device__ __forceinline__ void prepare_x(const float *__restrict__ x, int ngroups, XGroup *__restrict__ xg) {
-    const int total = ngroups * 16;
-    for (int base = 0; base < total; base += BLOCK) {
-        const XLoaded<1> f = load_x<BLOCK, 1, float>(x + 4 * base, (total - base + 15) / 16);
-        prepare_x<BLOCK, 1>(f, (total - base + 15) / 16, xg + base / 16);
+        if ((it & 15) == 0) {
+            xg[j].scale = scale;
+            xg[j].inexact = round_sum * 32768.0f > rest ? 1u : 0u;
+        }
     }
 }
 
@@ -137,6 +161,7 @@ struct XRegs {
     uint32_t limb[2][3][8];
     int32_t sx[2];
     float scale;
+    uint32_t inexact;
 };
 
 __device__ __forceinline__ void load_xregs(const XGroup &g, XRegs &r) {
@@ -150,6 +175,7 @@ __device__ __forceinline__ void load_xregs(const XGroup &g, XRegs &r) {
         r.sx[h] = g.sx[h];
     }
     r.scale = g.scale;
+    r.inexact = g.inexact;
 }
 
 // The weights of one group, decoded: codes as bytes 0..15 (four per dword) for
@@ -202,6 +228,72 @@ __device__ __forceinline__ float group_dot(const GroupCodes &c, const XS &xs) {
     const float t0 = c.dl0 * static_cast<float>(s0) - c.ml0 * static_cast<float>(xs.sx[0]);
     const float t1 = c.dl1 * static_cast<float>(s1) - c.ml1 * static_cast<float>(xs.sx[1]);
     return t0 + t1;
+}
+
+// A pointer the optimiser cannot follow, and that it takes to depend on
+// a0 and a1: the f32 path reads its activations from memory for every row.
+// Without this the loop-invariant loads would be hoisted out of the row loop,
+// or all 64 issued at once, into 64 or more registers per token, which would
+// raise the register budget of the whole kernel, integer path included.  No
+// instruction is emitted.
+// The result is a global-memory pointer (the activations are device memory),
+// so its reads are global loads, counted on the vector-memory counter only.
+template <typename T>
+using global_ptr = const __attribute__((address_space(1))) T *;
+
+template <typename T>
+__device__ __forceinline__ global_ptr<T> opaque_after(const T *p, float a0, float a1) {
+    uint64_t u = reinterpret_cast<uint64_t>(p);
+    asm volatile("" : "+v"(u) : "v"(a0), "v"(a1));
+    return (global_ptr<T>)u;
+}
+
+// A wave-uniform int the optimiser takes to depend on `after` (no
+// instruction): orders a row's loads after the previous row's result.
+__device__ __forceinline__ int opaque_int_after(int v, float after) {
+    asm volatile("" : "+s"(v) : "v"(after));
+    return v;
+}
+
+// sum over the group of w * x in f32 with every weight dequantized on its
+// own, w = fma(d*sc, q, -dmin*m) (d*sc*q is exact in f32, so this is the
+// correctly rounded weight the dequant kernel produces), and each product
+// rounded once (FMA).  xs: the group's 64 activations in memory, float or
+// _Float16 (weight 64g+l of the super-block pairs with xs[l] for the low
+// nibbles, xs[32+l] for the high).  The activations are read a quarter at a
+// time, each quarter's address depending on the sums so far (opaque_after),
+// so at most 16 of them are in registers at once; the first quarter's
+// address depends on `after` (a caller's previous result, to keep several
+// rows' reads from being issued together, or a constant).
+//
+// A non-finite activation makes the result NaN, as on the integer path: the
+// sum of 0 * x over the group (0 for finite x, NaN otherwise) is added.
+template <typename T>
+__device__ __forceinline__ float exact_group_dot(const GroupCodes &c, const T *xs, float after = 0.0f) {
+    // each quarter's eight products per sub-block are summed on their own,
+    // then added to the running sums: no chain of roundings is longer than 12
+    float a0 = 0.0f, a1 = 0.0f, nf = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const global_ptr<T> p = opaque_after(xs, h == 0 ? after : a0, a1);
+        float q0 = 0.0f, q1 = 0.0f;
+#pragma unroll
+        for (int i = 2 * h; i < 2 * h + 2; ++i) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float ql = static_cast<float>((c.lo[i] >> (8 * b)) & 0xffu);
+                const float qh = static_cast<float>((c.hi[i] >> (8 * b)) & 0xffu);
+                const float xl = static_cast<float>(p[4 * i + b]);
+                const float xh = static_cast<float>(p[32 + 4 * i + b]);
+                q0 = fmaf(fmaf(c.dl0, ql, -c.ml0), xl, q0);
+                q1 = fmaf(fmaf(c.dl1, qh, -c.ml1), xh, q1);
+                nf = fmaf(xl, 0.0f, fmaf(xh, 0.0f, nf));
+            }
+        }
+        a0 += q0;
+        a1 += q1;
+    }
+    return (a0 + a1) + nf;
 }
 
 }  // namespace q4k
