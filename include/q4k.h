@@ -244,6 +244,26 @@ Q4K_API q4k_status q4k_gemv_batched_dt(const void *w, const void *x, q4k_dtype x
                                        int64_t m, int64_t n, int64_t k, void *stream);
 
 /*
+ * q4k_gemv_batched_dt for callers that cannot allocate device memory: code
+ * recorded under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Computes exactly what q4k_gemv_batched_dt computes (the
+ * same kernels, the same order of sums) and calls no allocator: the scratch
+ * the call needs (q4k_gemv_batched_workspace_size) comes from one array of
+ * Q4K_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on,
+ * from its first such call until the process ends.  A call that needs more
+ * is refused with Q4K_ERR_UNSUPPORTED_SHAPE and launches nothing (at k = 4096
+ * up to 64 tokens need about 1.1 MB; prefill sizes with f16 activations can
+ * exceed the array).  Every call on one GPU shares that GPU's array: calls on
+ * one GPU whose work overlaps in time (on different streams without
+ * ordering between them) race; calls ordered on one stream do not.  Its
+ * contents are garbage before and after each call.  Errors and aliasing as
+ * q4k_gemv_batched_dt.
+ */
+#define Q4K_NOALLOC_SCRATCH_BYTES (16 << 20)
+Q4K_API q4k_status q4k_gemv_batched_noalloc(const void *w, const void *x, q4k_dtype x_dtype, void *y,
+                                            q4k_dtype y_dtype, int64_t m, int64_t n, int64_t k, void *stream);
+
+/*
  * Prefill-size GEMM with f16 activations (W4A16): the prefill side of
  * resolveMatmulPhase / selectQ4KFusedVariant ("@simulatte/doppler 0.1.7 ->
  * 0.1.8", matmul-selection.js), for hundreds of tokens at once.
@@ -318,7 +338,7 @@ Q4K_API const char *q4k_status_string(q4k_status s);
 
 /* ABI version of this header (major*100 + minor); q4k_abi_version() of the
  * library it was built with returns the same number. */
-#define Q4K_ABI_VERSION 108
+#define Q4K_ABI_VERSION 109
 Q4K_API int q4k_abi_version(void);
 
 #ifdef __cplusplus

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "q4k.h"
 #include "launch.h"
@@ -113,6 +114,45 @@ hipError_t launch_copy(float *y, const float *src, int64_t count, hipStream_t st
     return hipGetLastError();
 }
 
+}  // namespace q4k
+
+// Scratch of q4k_gemv_batched_noalloc: one array per GPU, held from the
+// library's load until the process ends.  Host code never uses this name as
+// an address (on the host it is only a handle of the symbol): the device
+// address comes from hipGetSymbolAddress, once per device.
+static constexpr int64_t kStaticScratchBytes = int64_t{16} << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace q4k {
+namespace {
+
+std::mutex g_scratch_mutex;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up with that
+// device current on its first use and kept.
+hipError_t static_scratch(void **out) {
+    *out = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (p == nullptr) return hipErrorInvalidSymbol;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+}  // namespace
 }  // namespace q4k
 
 using q4k::aligned;
@@ -383,6 +423,27 @@ q4k_status q4k_gemv_batched_ws(const void *w, const void *x, q4k_dtype x_dtype, 
                                                 y_dtype == Q4K_F16, m, n, k, ws, static_cast<hipStream_t>(stream)));
 }
 
+q4k_status q4k_gemv_batched_noalloc(const void *w, const void *x, q4k_dtype x_dtype, void *y, q4k_dtype y_dtype,
+                                    int64_t m, int64_t n, int64_t k, void *stream) {
+    bool run = false;
+    uint64_t wb = 0;
+    q4k_status s = check_batched(w, x, x_dtype, y, y_dtype, m, n, k, &run, &wb);
+    if (s != Q4K_OK || !run) return s;
+    int64_t need = 0;
+    s = q4k_gemv_batched_workspace_size(x_dtype, y_dtype, m, n, k, &need);
+    if (s != Q4K_OK) return s;
+    if (need > kStaticScratchBytes) return Q4K_ERR_UNSUPPORTED_SHAPE;
+    q4k::Workspace ws;
+    if (need > 0) {
+        void *p = nullptr;
+        if (q4k::static_scratch(&p) != hipSuccess) return Q4K_ERR_LAUNCH;
+        ws.ptr = static_cast<uint8_t *>(p);
+        ws.bytes = kStaticScratchBytes;
+    }
+    return from_hip(q4k::launch_gemv_batched_dt(static_cast<const uint8_t *>(w), x, x_dtype == Q4K_F16, y,
+                                                y_dtype == Q4K_F16, m, n, k, ws, static_cast<hipStream_t>(stream)));
+}
+
 q4k_status q4k_prefill_gemm(const void *w, const void *x, void *y, q4k_dtype y_dtype, int64_t m, int64_t n,
                             int64_t k, void *stream) {
     bool run = false;
@@ -464,7 +525,8 @@ const char *q4k_status_string(q4k_status s) {
         case Q4K_OK: return "ok";
         case Q4K_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size, overlapping buffers or size overflow)";
         case Q4K_ERR_UNSUPPORTED_SHAPE:
-            return "unsupported shape (k not a multiple of 256, or of 32 for Q8_0, or beyond a call's stated limits)";
+            return "unsupported shape (k not a multiple of 256, or of 32 for Q8_0, or beyond a call's stated limits, "
+                   "such as the 16 MiB of scratch of q4k_gemv_batched_noalloc)";
         case Q4K_ERR_MISALIGNED:
             return "misaligned pointer (w needs 16-byte alignment, activations/outputs their element size; dequant "
                    "output and workspaces as documented)";

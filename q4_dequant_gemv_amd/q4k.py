@@ -24,7 +24,8 @@ STATUS = {0: "Q4K_OK", 1: "Q4K_ERR_INVALID_ARG", 2: "Q4K_ERR_UNSUPPORTED_SHAPE",
 
 # exported symbols, in the order include/q4k.h declares them
 EXPORTS = ("q4k_gemv", "q4k_gemv_dt", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_q8_0_gemv", "q4k_gemv_batched",
-           "q4k_gemv_batched_dt", "q4k_prefill_gemm", "q4k_gemv_batched_workspace_size", "q4k_gemv_batched_ws",
+           "q4k_gemv_batched_dt", "q4k_gemv_batched_noalloc", "q4k_prefill_gemm", "q4k_gemv_batched_workspace_size",
+           "q4k_gemv_batched_ws",
            "q4k_prefill_workspace_size", "q4k_prefill_gemm_ws", "q4k_fused_swiglu", "q4k_dequant",
            "q4k_status_string", "q4k_abi_version")
 
@@ -71,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L.q4k_q8_0_gemv.argtypes = [p, p, p, i64, i64, p]
         L.q4k_gemv_dt.argtypes = [p, p, ctypes.c_int, p, ctypes.c_int, i64, i64, p]
         L.q4k_gemv_batched_dt.argtypes = [p, p, ctypes.c_int, p, ctypes.c_int, i64, i64, i64, p]
+        L.q4k_gemv_batched_noalloc.argtypes = [p, p, ctypes.c_int, p, ctypes.c_int, i64, i64, i64, p]
         L.q4k_prefill_gemm.argtypes = [p, p, p, ctypes.c_int, i64, i64, i64, p]
         L.q4k_gemv_batched.argtypes = [p, p, p, i64, i64, i64, p]
         pi64 = ctypes.POINTER(i64)
@@ -81,8 +83,8 @@ def lib() -> ctypes.CDLL:
         L.q4k_fused_swiglu.argtypes = [p, p, p, p, i64, i64, p]
         L.q4k_dequant.argtypes = [p, p, i64, i64, p]
         for f in (L.q4k_gemv, L.q4k_gemv_dt, L.q4k_gemv_residual, L.q4k_gemv_multi, L.q4k_q8_0_gemv,
-                  L.q4k_gemv_batched, L.q4k_gemv_batched_dt, L.q4k_prefill_gemm, L.q4k_fused_swiglu,
-                  L.q4k_dequant):
+                  L.q4k_gemv_batched, L.q4k_gemv_batched_dt, L.q4k_gemv_batched_noalloc, L.q4k_prefill_gemm,
+                  L.q4k_fused_swiglu, L.q4k_dequant):
             f.restype = st
         L.q4k_status_string.argtypes = [st]
         L.q4k_status_string.restype = ctypes.c_char_p
@@ -232,6 +234,29 @@ def gemv_batched_dt(w, x, y=None, n: int | None = None, out_dtype=None, stream=N
     _check(lib().q4k_gemv_batched_dt(_dev(w, "w", torch.uint8), _dev_any(x, "x"), _dtype_code(x, "x"),
                                      _dev_any(y, "y"), _dtype_code(y, "y"), m, n, k, _stream(stream)),
            "q4k_gemv_batched_dt")
+    return y
+
+
+# bytes of the per-GPU scratch array of gemv_batched_noalloc (Q4K_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def gemv_batched_noalloc(w, x, y=None, n: int | None = None, out_dtype=None, stream=None):
+    """``gemv_batched_dt`` with its scratch in the library's per-GPU array:
+    the library allocates nothing (``y`` must be given to allocate nothing at
+    all on this side either)."""
+    import torch
+
+    if _tensor(x, "x").dim() != 2:
+        raise ValueError("x must be [m, k]")
+    m, k = x.shape
+    n = rows_of(w, k) if n is None else n
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype or x.dtype, device=x.device)
+    _sizes(x.device, [(w, "w", _q4k_bytes(n, k))], [(y, "y", m * n)])
+    _check(lib().q4k_gemv_batched_noalloc(_dev(w, "w", torch.uint8), _dev_any(x, "x"), _dtype_code(x, "x"),
+                                          _dev_any(y, "y"), _dtype_code(y, "y"), m, n, k, _stream(stream)),
+           "q4k_gemv_batched_noalloc")
     return y
 
 

@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
         ["q4k_gemv", "q4k_gemv_dt", "q4k_gemv_residual", "q4k_gemv_multi", "q4k_q8_0_gemv", "q4k_gemv_batched",
-         "q4k_gemv_batched_dt", "q4k_prefill_gemm", "q4k_gemv_batched_workspace_size", "q4k_gemv_batched_ws",
+         "q4k_gemv_batched_dt", "q4k_gemv_batched_noalloc", "q4k_prefill_gemm", "q4k_gemv_batched_workspace_size",
+         "q4k_gemv_batched_ws",
          "q4k_prefill_workspace_size", "q4k_prefill_gemm_ws", "q4k_fused_swiglu", "q4k_dequant",
          "q4k_status_string", "q4k_abi_version"])
 
@@ -57,8 +58,8 @@ def test_only_the_abi_is_exported():
 
 
 def test_status_strings(L):
-    assert L.q4k_abi_version() == 108
-    assert re.search(r"#define Q4K_ABI_VERSION (\d+)", open(HEADER).read()).group(1) == "108"
+    assert L.q4k_abi_version() == 109
+    assert re.search(r"#define Q4K_ABI_VERSION (\d+)", open(HEADER).read()).group(1) == "109"
     for s in range(5):
         assert len(L.q4k_status_string(s)) > 0
     assert L.q4k_status_string(99) == b"unknown status"
@@ -160,6 +161,24 @@ def test_batched_dt_validation(L, args, status):
     w, x, xd, y, yd, m, n, k = args
     assert L.q4k_gemv_batched_dt(ctypes.c_void_p(w), ctypes.c_void_p(x), xd, ctypes.c_void_p(y), yd, m, n, k,
                                  None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((W, X, 1, Y, 1, 4, 16, 300), SHAPE),
+    ((W, X, 3, Y, 1, 4, 16, 256), INVALID),
+    ((W, X + 2, 0, Y, 1, 4, 16, 256), MISALIGNED),
+    ((W, X, 1, Y + 2, 0, 4, 16, 256), MISALIGNED),
+    ((W, X, 1, X + 4 * 256 * 2 - 2, 1, 4, 16, 256), INVALID),  # y starts inside f16 x[4, 256]
+    ((W, X, 1, Y, 1, 0, 16, 256), OK),
+    ((W, X, 1, Y, 1, -1, 16, 256), INVALID),
+    # scratch beyond the per-GPU array (4096 f16 tokens at k = 4096: the
+    # prefill GEMM's 32 MiB of activation operands alone)
+    ((W, X, 1, Y, 0, 4096, 4096, 4096), SHAPE),
+])
+def test_batched_noalloc_validation(L, args, status):
+    w, x, xd, y, yd, m, n, k = args
+    assert L.q4k_gemv_batched_noalloc(ctypes.c_void_p(w), ctypes.c_void_p(x), xd, ctypes.c_void_p(y), yd, m, n, k,
+                                      None) == status
 
 
 @pytest.mark.parametrize("args,status", [
