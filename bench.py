@@ -10,15 +10,20 @@ One step is one pass of the decode hot path over resident weights:
 every step streams its weights from HBM).  Inputs are seeded synthetic data of
 the pages' value distributions (q4_dequant_gemv_amd/inputs.py).
 
-Prints ONE JSON line.  `value` is step weight bytes / mean step time over K
-steps bracketed by HIP events on the launch stream; by default the K steps
-are captured once into a HIP graph and the timed region is one replay of it
-(`--eager` times plain launches; both rates are in the line).  `roofline` covers the
-dominant kernel (the lm_head GEMV): algorithmic bytes per launch / mean launch
-time over K back-to-back launches, again between events on the launch stream.  `traffic` comes from the
-committed rocprofv3 counter summary (profiles/traffic_lm_head_9b.json) when it
-was taken from the kernel sources as they are now, else null.  `cpu_baseline`
-times the CPU oracle on one full step.
+Prints ONE JSON line.  `value` is step weight bytes / mean step time.  The K
+steps are captured once into a HIP graph; after one untimed replay the graph
+is replayed R times back to back (R >= 5, R * K >= 200), each replay -- K
+steps -- between its own pair of HIP events on the launch stream, and the step
+time is the mean over the R replays (`--eager` times R back-to-back regions of
+K plain launches instead; both rates are in the line, with every region's
+figure).  A single region of a few steps (K = 20 is 2.4 ms) moves by several
+per cent from one region to the next; the mean over R regions does not.
+`roofline` covers the dominant kernel (the lm_head GEMV): algorithmic bytes
+per launch / mean launch time over R * K back-to-back launches, again between
+two events on the launch stream.  `traffic` comes from the committed rocprofv3
+counter summary (profiles/traffic_lm_head_9b.json) when it was taken from the
+kernel sources as they are now, else null.  `cpu_baseline` times the CPU
+oracle on full steps.
 """
 
 from __future__ import annotations
@@ -132,48 +137,51 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    def time_eager():
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
+    replays = max(5, -(-200 // args.steps))
+
+    def time_regions(run_region):
+        """Per-step times (us) of `replays` back-to-back regions, each between
+        its own pair of events on the launch stream, after one untimed region."""
+        run_region()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
+        evs[0].record(stream)
+        for r in range(replays):
+            run_region()
+            evs[r + 1].record(stream)
         torch.cuda.synchronize()
-        start.record(stream)
+        return [evs[r].elapsed_time(evs[r + 1]) * 1e3 / args.steps for r in range(replays)]
+
+    def eager_region():
         for _ in range(args.steps):
             step()
-        end.record(stream)
-        torch.cuda.synchronize()
-        return start.elapsed_time(end) / args.steps
 
-    # Timed region 1: K whole steps between two events on the launch stream
-    # (no events between the kernels).  By default the K steps are captured
-    # once into a HIP graph (the way a decode loop is deployed) and the timed
-    # region is one replay of it; the eager rate is reported beside it.
-    log(f"[bench] timing {args.steps} steps")
-    eager_ms = time_eager()
+    # Timed region: K whole steps between two events on the launch stream (no
+    # events between the kernels), R times.  By default the K steps are
+    # captured once into a HIP graph (the way a decode loop is deployed) and
+    # each region is one replay of it; the eager rate is reported beside it.
+    log(f"[bench] timing {replays} regions of {args.steps} steps")
+    torch.cuda.synchronize()
+    eager_us = time_regions(eager_region)
+    eager_ms = sum(eager_us) / len(eager_us) * 1e-3
     t0 = time.perf_counter()
     if args.eager:
-        ms_per_step = eager_ms
-        launch = "eager launches"
+        region_us = eager_us
+        launch = f"eager launches, {replays} regions of {args.steps} steps"
     else:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for _ in range(args.steps):
                 step(None)  # the capture stream
-        graph.replay()  # warm replay
         torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        graph.replay()
-        end.record(stream)
-        torch.cuda.synchronize()
-        ms_per_step = start.elapsed_time(end) / args.steps
-        launch = f"one HIP graph of {args.steps} steps, replayed once"
+        region_us = time_regions(graph.replay)
+        launch = f"one HIP graph of {args.steps} steps, replayed {replays} times back to back"
         del graph
+    ms_per_step = sum(region_us) / len(region_us) * 1e-3
     wall = time.perf_counter() - t0
     value = step_weight_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # Timed region 2, per kernel: K launches of that kernel alone, back to
-    # back on the launch stream between two events.  The FFN matrices (85 MB
+    # Per kernel: R * K launches of that kernel alone, back to back on the
+    # launch stream between two events.  The FFN matrices (85 MB
     # together) would stay in the 256 MB Infinity Cache when repeated, so
     # those launches rotate over copies totalling >= 512 MiB, as in the step
     # where the lm_head evicts them; the lm_head (572 MB) streams from HBM.
@@ -196,6 +204,7 @@ def main():
         "gemv_lm_head": lambda i: q4k.gemv(W["lm_head_9b"], y, y=logits, stream=stream),
     }
     kernels = {}
+    n_launch = replays * args.steps
     for nm, fn in launches.items():
         for i in range(args.warmup):
             fn(i)
@@ -203,11 +212,11 @@ def main():
         b = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record(stream)
-        for i in range(args.steps):
+        for i in range(n_launch):
             fn(i)
         b.record(stream)
         torch.cuda.synchronize()
-        mean_s = a.elapsed_time(b) / args.steps * 1e-3
+        mean_s = a.elapsed_time(b) / n_launch * 1e-3
         gbs = kernel_bytes[nm] / mean_s / 1e9
         kernels[nm] = {"mean_us": round(mean_s * 1e6, 3), "GB/s": round(gbs, 1),
                        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "calls_per_s": round(1.0 / mean_s, 1),
@@ -313,6 +322,8 @@ def main():
             "weight_bytes_per_step": step_weight_bytes,
             "launch": launch,
             "eager_ms_per_step": round(eager_ms, 5),
+            "regions_us_per_step": [round(v, 2) for v in region_us],
+            "eager_regions_us_per_step": [round(v, 2) for v in eager_us],
             "frac_hbm_peak_step": round(value / HBM_PEAK_GBS, 4),
             "kernels": kernels,
             "batched_9b_ffn": batched,

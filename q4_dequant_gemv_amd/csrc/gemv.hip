@@ -59,6 +59,12 @@ namespace q4k {
 // Q4_K: the group is sub-block pair (2g, 2g+1) of a 144-byte super-block; the
 // lane loads the super-block's 16-byte header and the group's 32 code bytes.
 struct Q4KFormat {
+    // Single-token kernels stage the weight stream through LDS: a wave's
+    // iteration (whole rows, contiguous bytes) arrives by 16-byte loads that
+    // each cover a contiguous kilobyte, and each lane then reads its header
+    // and code chunks from LDS (fetch).
+    static constexpr bool kStaged = true;
+    static constexpr int kGroupBytes = 36;  // 144 bytes per 4 groups of 64 weights
     struct Lane {
         uint32_t off_hdr;  // byte offset of the super-block header
         uint32_t off_qa;   // byte offset of the group's first 16 code bytes
@@ -83,6 +89,13 @@ struct Q4KFormat {
         l.hdr = buffer_load16(r, g.off_hdr);
         l.qa = buffer_load16(r, g.off_qa);
         l.qb = buffer_load16(r, g.off_qa + 16u);
+    }
+    // the same bytes from a staged copy of the iteration in LDS (16-byte
+    // aligned: headers and code chunks sit at multiples of 16)
+    static __device__ __forceinline__ void fetch(Loads &l, const uint8_t *stage, const Lane &g) {
+        l.hdr = *reinterpret_cast<const uint4 *>(stage + g.off_hdr);
+        l.qa = *reinterpret_cast<const uint4 *>(stage + g.off_qa);
+        l.qb = *reinterpret_cast<const uint4 *>(stage + g.off_qa + 16u);
     }
     // sum over the group of w * x in units of the group's activation scale
     static __device__ __forceinline__ float dot(const Loads &l, const Lane &g, const XRegs &xr) {
@@ -136,6 +149,9 @@ struct Q4KFormat {
 // (exactly) and combined with two FMAs, one rounding each (a relative 2^-24
 // of the block's sum).
 struct Q8_0Format {
+    // groups start at multiples of 68 bytes, not of 16: no LDS staging
+    static constexpr bool kStaged = false;
+    static constexpr int kGroupBytes = 68;
     static constexpr int kBlockWeights = 32;
     static constexpr int kBlockBytes = 34;
     struct Lane {
@@ -272,6 +288,12 @@ __device__ __forceinline__ void lane_dot_exact(const RowLoads<F, NMAT> &b, const
 // q, k and v projections of a decode step, say).  Matrix i owns the wave
 // iterations [it_begin[i], it_begin[i+1]); its last iteration covers
 // tail_bytes of weights.  r[i], if set, is added to each output (a residual).
+// 1: single-token Q4_K streams read their weights through LDS (see
+// gemv_kernel); 0: straight into registers, as the other streams do.
+#ifndef Q4K_STAGE
+#define Q4K_STAGE 1
+#endif
+
 constexpr int kMaxMats = 8;
 struct MatTable {
     const uint8_t *w[kMaxMats];
@@ -316,6 +338,13 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     constexpr int kTok = MT * TP;
     extern __shared__ __align__(16) unsigned char smem[];
     XGroup *xg = reinterpret_cast<XGroup *>(smem);
+    // Single-token Q4_K streams stage the weights through LDS: one slot per
+    // wave and matrix holds the wave's current iteration (kDma kilobyte loads,
+    // the last one partly past the iteration's bytes, which reads zeros).
+    constexpr bool kStage = F::kStaged && kTok == 1 && Q4K_STAGE != 0;
+    constexpr int kDma = (RPG * kWave * F::kGroupBytes + 1023) / 1024;
+    __shared__ __align__(16) uint8_t stage[kStage ? NMAT : 1][kStage ? kWavesPerBlock : 1][kStage ? kDma * 1024 : 16];
+    const int swave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
 
     const int lane = threadIdx.x & (kWave - 1);
     const int sub = lane % LPR;
@@ -351,7 +380,9 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     LoadCursor lc{0, 0, mt.it_begin[1], mt.tail_bytes[0], mt.w[0]};
     RowCursor rc{0, 0, mt.it_begin[1], mt.n[0], static_cast<YT *>(mt.y[0]), mt.r[0], static_cast<YT *>(mt.y_gate[0]),
                  mt.head_log2[0]};
-    auto issue = [&](RowLoads<F, NMAT> (&b)[RPG], int it) {
+    // moves the load cursor to iteration `it`: its byte offset in the
+    // matrix, its byte count (0 past the end) and the matrix
+    auto load_cursor = [&](int it, int64_t &off, int &nrec) -> const uint8_t * {
         while (it >= lc.end && lc.mi + 1 < count) {
             ++lc.mi;
             lc.begin = lc.end;
@@ -360,11 +391,28 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
             lc.w = mt.w[lc.mi];
         }
         const int left = lc.end - it;
-        const int64_t off = static_cast<int64_t>(it - lc.begin) * iter_bytes;
-        const int nrec = __builtin_amdgcn_readfirstlane(left > 1 ? iter_bytes : (left == 1 ? lc.tail : 0));
+        off = static_cast<int64_t>(it - lc.begin) * iter_bytes;
+        nrec = __builtin_amdgcn_readfirstlane(left > 1 ? iter_bytes : (left == 1 ? lc.tail : 0));
         // uniform by construction; said again so that the descriptor is built
         // in scalar registers whatever the compiler concluded across the joins
-        const uint8_t *wbase = reinterpret_cast<const uint8_t *>(wave_uniform(reinterpret_cast<int64_t>(lc.w)));
+        return reinterpret_cast<const uint8_t *>(wave_uniform(reinterpret_cast<int64_t>(lc.w)));
+    };
+    // staged stream: iteration `it` into the wave's slots
+    auto issue_stage = [&](int it) {
+        int64_t off;
+        int nrec;
+        const uint8_t *wbase = load_cursor(it, off, nrec);
+#pragma unroll
+        for (int m2 = 0; m2 < NMAT; ++m2) {
+            const __amdgpu_buffer_rsrc_t r = stream_rsrc((m2 == 0 ? wbase : wu) + off, nrec);
+#pragma unroll
+            for (int i = 0; i < kDma; ++i) buffer_load16_lds(r, &stage[m2][swave][i * 1024], i * 1024u + lane * 16u);
+        }
+    };
+    auto issue = [&](RowLoads<F, NMAT> (&b)[RPG], int it) {
+        int64_t off;
+        int nrec;
+        const uint8_t *wbase = load_cursor(it, off, nrec);
 #pragma unroll
         for (int q = 0; q < RPG; ++q) {
             const int sh = q * kRowsPerGroup * static_cast<int>(row_bytes);
@@ -419,9 +467,13 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     // memory clobber: no instruction, only an ordering point for the compiler;
     // x is deliberately not __restrict__ so its loads cannot move across it)
     asm volatile("" ::: "memory");
-    RowLoads<F, NMAT> buf[NB][RPG];
+    RowLoads<F, NMAT> buf[kStage ? 1 : NB][RPG];
+    if constexpr (kStage) {
+        issue_stage(it0);
+    } else {
 #pragma unroll
-    for (int b = 0; b + 1 < NB; ++b) issue(buf[b], it0 + b * nwaves);
+        for (int b = 0; b + 1 < NB; ++b) issue(buf[b], it0 + b * nwaves);
+    }
 
 #pragma unroll
     for (int t = 0; t < kTok; ++t) {
@@ -481,60 +533,88 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
             yp = nullptr;
             win = 0;
         };
-        // The last iteration leaves both loops at once (goto): a break that fell
-        // back to the outer loop's test would join the loop head with loads of
-        // the unfinished unrolled pass still in flight, and the wait counters
-        // would have to drain them there.
+        // Finishes one wave iteration whose weights are in `rows`: the lane
+        // group's dot products, reduced, kept for the window's store.
+        auto finish = [&](const RowLoads<F, NMAT> (&rows)[RPG], int cur) {
+            row_cursor(cur);
+#pragma unroll
+            for (int q = 0; q < RPG; ++q) {
+                const int64_t row = static_cast<int64_t>(cur - rc.begin) * kRowsPerWave + q * kRowsPerGroup + slot;
+                const bool rok = row < rc.n;
+                const bool mine = sub == win;
+                if constexpr (MT == 1) {
+                    float acc[NMAT];
+                    if constexpr (EXACT) lane_dot_exact(rows[q], g, src[0], rok && g.ok, 0.0f, acc);
+                    else lane_dot(rows[q], g, src[0], rok && g.ok, acc);
+#pragma unroll
+                    for (int m2 = 0; m2 < NMAT; ++m2) acc[m2] = lane_group_sum<LPR>(acc[m2]);
+                    const float out = SWIGLU ? silu(acc[0]) * acc[NMAT - 1] : acc[0];
+                    yv[0] = mine ? out : yv[0];
+                } else {
+                    // one decode of the group for the wave's MT tokens
+                    float acc[MT];
+                    if constexpr (EXACT) F::dot_tokens_exact(rows[q].m[0], g, src, rok && g.ok, 0.0f, acc);
+                    else F::dot_tokens(rows[q].m[0], g, src, rok && g.ok, acc);
+#pragma unroll
+                    for (int j = 0; j < MT; ++j) {
+                        acc[j] = lane_group_sum<LPR>(acc[j]);
+                        yv[j] = mine ? acc[j] : yv[j];
+                    }
+                }
+                if constexpr (QG) yp = mine ? (rok ? dest(row) : nullptr) : yp;
+                else if constexpr (kTok > 1) yp = mine ? (rok ? rc.y + tile * MT * ystride + row : nullptr) : yp;
+                else yp = mine ? (rok ? rc.y + row : nullptr) : yp;
+                if constexpr (RES) rp = mine ? (rc.r != nullptr ? rc.r + row : nullptr) : rp;
+                if (++win == LPR) flush();
+            }
+        };
         // The sequencer issues from the oldest wave first, so with equal shares
         // the younger waves of a CU fall behind and finish alone, long after the
         // others.  Each wave therefore lowers its own priority as the share of its
         // iterations still to do drops (1/2, 1/4, 1/8): a wave that is behind
         // outranks the ones ahead of it, and the finish times close up.
-        if (it0 < niters) {
+        auto set_priority = [&](int cur) {
+            const int left = (niters - cur + nwaves - 1) / nwaves;
+            if (2 * left > my_iters) __builtin_amdgcn_s_setprio(3);
+            else if (4 * left > my_iters) __builtin_amdgcn_s_setprio(2);
+            else if (8 * left > my_iters) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        };
+        if constexpr (kStage) {
+            // Staged: the iteration's bytes are read from the slot into
+            // registers, the slot is refilled with the wave's next iteration,
+            // and the registers are decoded while those loads are in flight.
+            // (The read waits for the slot's loads; the compiler places that
+            // wait.  The refill waits for the reads: wait_lds_reads.)
+            if (it0 < niters) {
+                for (int cur = it0;; cur += nwaves) {
+                    set_priority(cur);
+                    RowLoads<F, NMAT> rows[RPG];
+#pragma unroll
+                    for (int q = 0; q < RPG; ++q) {
+#pragma unroll
+                        for (int m2 = 0; m2 < NMAT; ++m2)
+                            F::fetch(rows[q].m[m2], &stage[m2][swave][q * kRowsPerGroup * static_cast<int>(row_bytes)],
+                                     g);
+                    }
+                    wait_lds_reads();
+                    issue_stage(cur + nwaves);
+                    finish(rows, cur);
+                    if (cur + nwaves >= niters) break;
+                }
+            }
+        } else if (it0 < niters) {
+            // The last iteration leaves both loops at once (goto): a break that
+            // fell back to the outer loop's test would join the loop head with
+            // loads of the unfinished unrolled pass still in flight, and the
+            // wait counters would have to drain them there.
             for (int it = it0;; it += NB * nwaves) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     const int cur = it + b * nwaves;
-                    {
-                        const int left = (niters - cur + nwaves - 1) / nwaves;
-                        if (2 * left > my_iters) __builtin_amdgcn_s_setprio(3);
-                        else if (4 * left > my_iters) __builtin_amdgcn_s_setprio(2);
-                        else if (8 * left > my_iters) __builtin_amdgcn_s_setprio(1);
-                        else __builtin_amdgcn_s_setprio(0);
-                    }
+                    set_priority(cur);
                     issue(buf[(b + NB - 1) % NB], cur + (NB - 1) * nwaves);
-                    row_cursor(cur);
-#pragma unroll
-                    for (int q = 0; q < RPG; ++q) {
-                        const int64_t row =
-                            static_cast<int64_t>(cur - rc.begin) * kRowsPerWave + q * kRowsPerGroup + slot;
-                        const bool rok = row < rc.n;
-                        const bool mine = sub == win;
-                        if constexpr (MT == 1) {
-                            float acc[NMAT];
-                            if constexpr (EXACT) lane_dot_exact(buf[b][q], g, src[0], rok && g.ok, 0.0f, acc);
-                            else lane_dot(buf[b][q], g, src[0], rok && g.ok, acc);
-#pragma unroll
-                            for (int m2 = 0; m2 < NMAT; ++m2) acc[m2] = lane_group_sum<LPR>(acc[m2]);
-                            const float out = SWIGLU ? silu(acc[0]) * acc[NMAT - 1] : acc[0];
-                            yv[0] = mine ? out : yv[0];
-                        } else {
-                            // one decode of the group for the wave's MT tokens
-                            float acc[MT];
-                            if constexpr (EXACT) F::dot_tokens_exact(buf[b][q].m[0], g, src, rok && g.ok, 0.0f, acc);
-                            else F::dot_tokens(buf[b][q].m[0], g, src, rok && g.ok, acc);
-#pragma unroll
-                            for (int j = 0; j < MT; ++j) {
-                                acc[j] = lane_group_sum<LPR>(acc[j]);
-                                yv[j] = mine ? acc[j] : yv[j];
-                            }
-                        }
-                        if constexpr (QG) yp = mine ? (rok ? dest(row) : nullptr) : yp;
-                        else if constexpr (kTok > 1) yp = mine ? (rok ? rc.y + tile * MT * ystride + row : nullptr) : yp;
-                        else yp = mine ? (rok ? rc.y + row : nullptr) : yp;
-                        if constexpr (RES) rp = mine ? (rc.r != nullptr ? rc.r + row : nullptr) : rp;
-                        if (++win == LPR) flush();
-                    }
+                    finish(buf[b], cur);
                     if (cur + nwaves >= niters) goto done;
                 }
             }

@@ -48,6 +48,29 @@ __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint3
     return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, Q4K_WEIGHT_CPOL);
 }
 
+// Weight loads that go straight to LDS (no registers): lane l's 16 bytes at
+// descriptor offset voff land at dst + 16 l, dst being wave-uniform (it goes
+// to M0).  Such loads read whole lines in one instruction, so they take the
+// non-temporal policy, which streams faster than the default one when every
+// line is consumed by a single load (and slower when several loads share a
+// line, as the register loads above do).
+#ifndef Q4K_STAGE_CPOL
+#define Q4K_STAGE_CPOL 2
+#endif
+
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, 0, 0,
+                                             Q4K_STAGE_CPOL);
+}
+
+// Waits for this wave's LDS reads (and scalar loads), nothing else; the empty
+// asm statements keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void wait_lds_reads() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+    asm volatile("" ::: "memory");
+}
+
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 // f16 bit patterns of 1024 + sc*q for the two codes of a nibble pair (the

@@ -70,8 +70,8 @@ def test_gemv_dt_all_combinations(q4k, n, k):
 
 
 def test_gemv_dt_full_size_lm_head_9b(q4k):
-    """The 9B lm_head with f16 activations and f16 logits, whole on the GPU,
-    sampled rows against the oracle."""
+    """The 9B lm_head with f16 activations and f16 logits, every row against
+    the oracle."""
     import torch
 
     n, k = inputs.SHAPES["lm_head_9b"]
@@ -81,9 +81,8 @@ def test_gemv_dt_full_size_lm_head_9b(q4k):
     q4k.gemv_dt(to_dev(w.reshape(-1)), to_dev(x16), y=y)
     got = to_host(y.float())
     assert np.isfinite(got).all()
-    rows = np.unique(np.r_[0:64, n - 64:n, np.random.default_rng(61).choice(n, 2000, replace=False)])
-    yr, ar = oracle.gemv(w[rows], x16.astype(np.float32), threads=THREADS)
-    check_bound_f16(got[rows], yr, ar, "lm_head 9b f16->f16")
+    yr, ar = oracle.gemv(w, x16.astype(np.float32), threads=THREADS)
+    check_bound_f16(got, yr, ar, "lm_head 9b f16->f16")
 
 
 def test_gemv_dt_two_byte_aligned_f16_and_overflow(q4k):

@@ -73,7 +73,7 @@ def test_full_size_9b_step_in_a_graph():
     benchmark times (a HIP graph of whole steps): fused gate+up SwiGLU
     (2 x 12288 x 4096), down (4096 x 12288), lm_head (248320 x 4096).
     Replays equal the eager step bit for bit; each stage is checked against
-    the oracle on the GPU's own input to that stage (h, y), on sampled rows."""
+    the oracle on the GPU's own input to that stage (h, y), every output."""
     import torch
 
     import oracle
@@ -118,11 +118,9 @@ def test_full_size_9b_step_in_a_graph():
         step()
         torch.cuda.synchronize()
     hh, yy, lg = (to_host(t) for t in ref)
-    rows = np.unique(np.r_[0:64, nff - 64:nff, np.random.default_rng(1).choice(nff, 1500, replace=False)])
-    sw = oracle.fused_swiglu(wg_h[rows], wu_h[rows], x_h, threads=THREADS)
-    check_swiglu_bound(hh[rows], sw, "9B step: SwiGLU")
+    sw = oracle.fused_swiglu(wg_h, wu_h, x_h, threads=THREADS)
+    check_swiglu_bound(hh, sw, "9B step: SwiGLU")
     yr, ar = oracle.gemv(wd_h, hh, threads=THREADS)
     check_bound(yy, yr, ar, "9B step: down")
-    rows = np.unique(np.r_[0:64, nv - 64:nv, np.random.default_rng(2).choice(nv, 3000, replace=False)])
-    lr, la = oracle.gemv(wl_h[rows], yy, threads=THREADS)
-    check_bound(lg[rows], lr, la, "9B step: lm_head")
+    lr, la = oracle.gemv(wl_h, yy, threads=THREADS)
+    check_bound(lg, lr, la, "9B step: lm_head")

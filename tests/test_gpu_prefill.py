@@ -3,7 +3,7 @@ of tokens, matrix cores) through the C ABI against the CPU oracle's batched
 GEMM on the same activations (widened exactly to f32): every output within
 2e-4 * sum|w x| (f32 output), plus the output rounding for f16 outputs.
 Shapes cover ragged token and row tiles (m, n not multiples of 128), several
-super-blocks, the 9B FFN shapes at prefill sizes (sampled), special weight
+super-blocks, the 9B FFN shapes at prefill sizes (whole), special weight
 values, and bitwise reruns.
 """
 
@@ -36,7 +36,7 @@ def _report(name, worst):
     print(f"[parity] {name}: worst |err|/bound = {worst:.3e}", flush=True)
 
 
-def _case(q4k, w, x16, label, rows=None, toks=None):
+def _case(q4k, w, x16, label):
     import torch
 
     n = w.shape[0]
@@ -52,11 +52,9 @@ def _case(q4k, w, x16, label, rows=None, toks=None):
     assert torch.equal(y16, y.half()), f"{label}: f16 output is not the rounded f32 result"
     got = to_host(y)
     assert np.isfinite(got).all(), f"{label}: {int((~np.isfinite(got)).sum())} outputs not written"
-    rows = np.arange(n) if rows is None else rows
-    toks = np.arange(m) if toks is None else toks
-    yr, ar = oracle.gemv_batched(w[rows], x16[toks].astype(np.float32), threads=THREADS)
-    _report(label, check_bound(got[np.ix_(toks, rows)], yr, ar, label))
-    check_bound_f16(to_host(y16.float())[np.ix_(toks, rows)], yr, ar, label + " f16")
+    yr, ar = oracle.gemv_batched(w, x16.astype(np.float32), threads=THREADS)
+    _report(label, check_bound(got, yr, ar, label))
+    check_bound_f16(to_host(y16.float()), yr, ar, label + " f16")
 
 
 @pytest.mark.parametrize("m,n,k", [(128, 128, 256), (130, 300, 512), (1, 64, 256), (127, 129, 1024), (256, 1024, 4096),
@@ -68,17 +66,14 @@ def test_prefill_shapes(q4k, m, n, k):
 
 
 @pytest.mark.parametrize("name,tid", [("gate_9b", 0), ("down_9b", 2)])
-def test_prefill_9b_ffn_sampled(q4k, name, tid):
-    """512 tokens through the 9B gate and down projections, whole on the GPU,
-    sampled rows and tokens against the oracle."""
+def test_prefill_9b_ffn_whole(q4k, name, tid):
+    """512 tokens through the 9B gate and down projections, every output
+    against the oracle."""
     n, k = inputs.SHAPES[name]
     m = 512
     w = inputs.make_q4k(n, k, config_id=71, tensor_id=tid)
     x16 = inputs.make_x(m, k, config_id=71, tensor_id=100 + tid).astype(np.float16)
-    g = np.random.default_rng(tid)
-    rows = np.unique(np.r_[0:16, n - 16:n, g.choice(n, 200, replace=False)])
-    toks = np.unique(np.r_[0:4, m - 4:m, g.choice(m, 24, replace=False)])
-    _case(q4k, w, x16, name, rows=rows, toks=toks)
+    _case(q4k, w, x16, name)
 
 
 def test_prefill_special_values(q4k):

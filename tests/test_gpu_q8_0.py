@@ -1,8 +1,7 @@
 """GPU parity of the Q8_0 GEMV (q4k_q8_0_gemv) through the C ABI against the
 CPU oracle on the same seeded inputs: every output within
-2e-4 * sum_k |w_k x_k|, at small shapes whole and at the 9B shapes on sampled
-rows (the whole matrix computed on the GPU in the configuration the benchmark
-times).  Shapes cover the streaming kernel (K % 64 == 0, K <= 4096), the
+2e-4 * sum_k |w_k x_k|, every output, at small shapes and at the 9B shapes
+(computed on the GPU in the configuration the benchmark times).  Shapes cover the streaming kernel (K % 64 == 0, K <= 4096), the
 K-split kernel (K up to 16384) and the one-wave-per-row kernel (an odd number
 of blocks per row, a matrix that is only 2-byte aligned, K > 16384).
 """
@@ -35,7 +34,7 @@ def _report(name, worst):
     print(f"[parity] {name}: worst |err|/sum|wx| = {worst:.3e}", flush=True)
 
 
-def _case(q4k, w, x, label, rows=None):
+def _case(q4k, w, x, label):
     import torch
 
     n = w.shape[0]
@@ -44,12 +43,8 @@ def _case(q4k, w, x, label, rows=None):
     q4k.q8_0_gemv(to_dev(w.reshape(-1)), to_dev(x), y=y, n=n)
     got = to_host(y)
     assert np.isfinite(got).all() or not np.isfinite(x).all(), f"{label}: rows not written"
-    if rows is None:
-        yr, ar = oracle.q8_0_gemv(w, x, threads=THREADS)
-        _report(f"q8_0 {label}", check_bound(got, yr, ar, label))
-    else:
-        yr, ar = oracle.q8_0_gemv(w[rows], x, threads=THREADS)
-        _report(f"q8_0 {label}", check_bound(got[rows], yr, ar, label))
+    yr, ar = oracle.q8_0_gemv(w, x, threads=THREADS)
+    _report(f"q8_0 {label}", check_bound(got, yr, ar, label))
     return got
 
 
@@ -71,13 +66,11 @@ def test_q8_0_0p8b_projections(q4k, name, tid):
 
 
 @pytest.mark.parametrize("name,tid", [("lm_head_9b", 0), ("gate_9b", 1), ("down_9b", 2)])
-def test_q8_0_9b_sampled(q4k, name, tid):
+def test_q8_0_9b_whole(q4k, name, tid):
     n, k = inputs.SHAPES[name]
     w = inputs.make_q8_0(n, k, config_id=52, tensor_id=tid)
     x = inputs.make_x(1, k, config_id=52, tensor_id=100 + tid)[0]
-    g = np.random.default_rng(tid)
-    rows = np.unique(np.r_[0:64, n - 64:n, g.choice(n, 2000, replace=False)])
-    _case(q4k, w, x, name, rows=rows)
+    _case(q4k, w, x, name)
 
 
 def test_q8_0_two_byte_aligned_matrix(q4k):
