@@ -16,8 +16,11 @@ is replayed R times back to back (R >= 5, R * K >= 200), each replay -- K
 steps -- between its own pair of HIP events on the launch stream, and the step
 time is the mean over the R replays (`--eager` times R back-to-back regions of
 K plain launches instead; both rates are in the line, with every region's
-figure).  A single region of a few steps (K = 20 is 2.4 ms) moves by several
-per cent from one region to the next; the mean over R regions does not.
+figure).  Every timed section is preceded by >= 100 ms of the same work,
+untimed and back to back (warm_up): after a few milliseconds of idle GPU the
+same steps run up to a fifth slower and speed up over tens of milliseconds of
+load, so a single short region timed right after a synchronize or a graph
+capture measures that ramp, not the kernels.
 `roofline` covers the dominant kernel (the lm_head GEMV): algorithmic bytes
 per launch / mean launch time over R * K back-to-back launches, again between
 two events on the launch stream.  `traffic` comes from the committed rocprofv3
@@ -141,8 +144,9 @@ def main():
 
     def time_regions(run_region):
         """Per-step times (us) of `replays` back-to-back regions, each between
-        its own pair of events on the launch stream, after one untimed region."""
-        run_region()
+        its own pair of events on the launch stream, after >= 100 ms of the
+        same regions untimed (see warm_up)."""
+        warm_up(run_region, torch, stream)
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
         evs[0].record(stream)
         for r in range(replays):
@@ -210,7 +214,7 @@ def main():
             fn(i)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
+        warm_up(lambda: [fn(i) for i in range(args.steps)], torch, stream)
         a.record(stream)
         for i in range(n_launch):
             fn(i)
@@ -401,9 +405,8 @@ def graph_timed_calls(q4k, inputs, torch, dev, stream, cases):
         with torch.cuda.graph(graph):
             for i in range(nl):
                 fn(i, None)  # the capture stream
-        graph.replay()
-        torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        warm_up(graph.replay, torch, stream)
         a.record(stream)
         graph.replay()
         b.record(stream)
@@ -421,7 +424,8 @@ def graph_timed_calls(q4k, inputs, torch, dev, stream, cases):
 def stream_read_ceiling(torch, dev, stream, lm_head_gbs):
     """The device's achievable HBM read rate, for context: the read-only
     streaming kernel (libq4k_stream.so) over 1 GiB, the best of a few grid
-    sizes and load depths.  None if that library is not built."""
+    sizes, load depths and the two cache policies.  None if that library is
+    not built."""
     import ctypes
 
     from q4_dequant_gemv_amd import build as hip_build
@@ -432,27 +436,28 @@ def stream_read_ceiling(torch, dev, stream, lm_head_gbs):
     lib = ctypes.CDLL(hip_build.STREAM_LIB)
     lib.q4k_stream_read.restype = ctypes.c_int
     lib.q4k_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
-                                    ctypes.c_void_p]
+                                    ctypes.c_int, ctypes.c_void_p]
     nbytes = 1 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(7)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    grids = [cus * g for g in (2, 4, 8, 16)]
+    grids = [cus * g for g in (1, 2, 3, 4, 8)]
     out = torch.empty(max(grids) * 256, dtype=torch.int32, device=dev)
     s = ctypes.c_void_p(stream.cuda_stream)
     best = None
-    for grid in grids:
-        for unroll in (4, 8):
-            def call(i):
-                rc = lib.q4k_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
-                                         grid, unroll, s)
-                if rc != 0:
-                    raise RuntimeError(f"q4k_stream_read: hip error {rc}")
+    for policy in (0, 2):
+        for grid in grids:
+            for unroll in (4, 8):
+                def call(i):
+                    rc = lib.q4k_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
+                                             grid, unroll, policy, s)
+                    if rc != 0:
+                        raise RuntimeError(f"q4k_stream_read: hip error {rc}")
 
-            t = _time_launches(call, torch, stream, 20, 3)
-            gbs = nbytes / t / 1e9
-            if best is None or gbs > best["GB/s"]:
-                best = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "grid": grid,
-                        "loads_in_flight_per_thread": unroll}
+                t = _time_launches(call, torch, stream, 20, 3)
+                gbs = nbytes / t / 1e9
+                if best is None or gbs > best["GB/s"]:
+                    best = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "grid": grid,
+                            "loads_in_flight_per_thread": unroll, "cache_policy": "non-temporal" if policy else "default"}
     best["lm_head_gemv_frac_of_it"] = round(lm_head_gbs / best["GB/s"], 4)
     del buf, out
     return best
@@ -475,14 +480,34 @@ def _per_launch(fn, torch, stream, reps):
             "p90": round(float(np.percentile(t, 90)), 3), "n": reps}
 
 
+def warm_up(run_region, torch, stream, seconds=0.1):
+    """Runs `run_region` back to back for at least `seconds` of GPU time and
+    returns without synchronizing, so that the timed work queued next starts
+    on a busy GPU.  After the host has kept the GPU idle for a few
+    milliseconds (a synchronize, a graph capture) the device runs the same
+    work up to a fifth slower at first and speeds up over some tens of
+    milliseconds of load (per-step times of back-to-back 20-step replays
+    falling from 130 to 109 us); timing starts past that."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    run_region()
+    b.record(stream)
+    torch.cuda.synchronize()
+    one = max(a.elapsed_time(b) * 1e-3, 1e-6)
+    for _ in range(int(seconds / one) + 1):
+        run_region()
+
+
 def _time_launches(fn, torch, stream, steps, warmup):
     """Mean time of one fn(i) over `steps` back-to-back calls between two
-    events on the launch stream."""
+    events on the launch stream, after a warm-up (warm_up)."""
     for i in range(warmup):
         fn(i)
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    warm_up(lambda: [fn(i) for i in range(steps)], torch, stream)
     a.record(stream)
     for i in range(steps):
         fn(i)

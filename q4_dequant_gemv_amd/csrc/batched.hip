@@ -156,7 +156,14 @@ __global__ __launch_bounds__(256) void x_prep_kernel(const XT *x, uint8_t *__res
     const float sub8 = lane_group_sum<8>(part);
     const float tot = lane_group_sum<32>(part);
     round_sum = lane_group_sum<32>(round_sum);
-    const float rest = lane_group_rest_bound<32>(mag);
+    // a lower bound of the magnitude without the four largest: the sum of all
+    // minus four times the largest (here 1 <= largest < 2); the tighter one
+    // only where that does not clear the rounding
+    const float abs_sum = lane_group_sum<32>((mag[0] + mag[1]) + (mag[2] + mag[3]));
+    const float amax_s = nz ? ldexpf(amax, -e) : 0.0f;
+    float rest = abs_sum - 4.0f * amax_s;
+    const bool clear = round_sum * 32768.0f <= rest;
+    if (__builtin_amdgcn_ballot_w64(!clear) != 0) rest = clear ? rest : lane_group_rest_bound<32>(mag);
     if (!live) return;
     if (c == 0) flags[st * tpad + tok] = round_sum * 32768.0f > rest ? 1 : 0;
     uint8_t *blk = xc + (st * mt + tok / 16) * kTileStageBytes;

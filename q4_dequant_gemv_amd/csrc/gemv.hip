@@ -90,12 +90,10 @@ struct Q4KFormat {
         l.qa = buffer_load16(r, g.off_qa);
         l.qb = buffer_load16(r, g.off_qa + 16u);
     }
-    // the same bytes from a staged copy of the iteration in LDS (16-byte
-    // aligned: headers and code chunks sit at multiples of 16)
-    static __device__ __forceinline__ void fetch(Loads &l, const uint8_t *stage, const Lane &g) {
-        l.hdr = *reinterpret_cast<const uint4 *>(stage + g.off_hdr);
-        l.qa = *reinterpret_cast<const uint4 *>(stage + g.off_qa);
-        l.qb = *reinterpret_cast<const uint4 *>(stage + g.off_qa + 16u);
+    // the same bytes from a staged copy of the iteration at LDS byte address
+    // `stage` (headers and code chunks sit at multiples of 16 bytes)
+    static __device__ __forceinline__ void fetch(Loads &l, uint32_t stage, const Lane &g) {
+        lds_read_3x16(stage + g.off_hdr, stage + g.off_qa, l.hdr, l.qa, l.qb);
     }
     // sum over the group of w * x in units of the group's activation scale
     static __device__ __forceinline__ float dot(const Loads &l, const Lane &g, const XRegs &xr) {
@@ -338,12 +336,15 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     constexpr int kTok = MT * TP;
     extern __shared__ __align__(16) unsigned char smem[];
     XGroup *xg = reinterpret_cast<XGroup *>(smem);
-    // Single-token Q4_K streams stage the weights through LDS: one slot per
-    // wave and matrix holds the wave's current iteration (kDma kilobyte loads,
-    // the last one partly past the iteration's bytes, which reads zeros).
+    // Single-token Q4_K streams stage the weights through LDS: a ring of
+    // kSlots = NB - 1 slots per wave (one per matrix each) holds the wave's
+    // next iterations (kIterBytes at most: RPG * 64 groups).
     constexpr bool kStage = F::kStaged && kTok == 1 && Q4K_STAGE != 0;
-    constexpr int kDma = (RPG * kWave * F::kGroupBytes + 1023) / 1024;
-    __shared__ __align__(16) uint8_t stage[kStage ? NMAT : 1][kStage ? kWavesPerBlock : 1][kStage ? kDma * 1024 : 16];
+    constexpr int kSlots = kStage ? NB - 1 : 1;
+    constexpr int kIterBytes = RPG * kWave * F::kGroupBytes;
+    constexpr int kDma = stage_loads<kIterBytes>();
+    __shared__ __align__(16)
+        uint8_t stage[kSlots][kStage ? NMAT : 1][kStage ? kWavesPerBlock : 1][kStage ? kIterBytes : 16];
     const int swave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -397,16 +398,14 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
         // in scalar registers whatever the compiler concluded across the joins
         return reinterpret_cast<const uint8_t *>(wave_uniform(reinterpret_cast<int64_t>(lc.w)));
     };
-    // staged stream: iteration `it` into the wave's slots
-    auto issue_stage = [&](int it) {
+    // staged stream: iteration `it` into slot b of the wave's ring
+    auto issue_stage = [&](int b, int it) {
         int64_t off;
         int nrec;
         const uint8_t *wbase = load_cursor(it, off, nrec);
 #pragma unroll
         for (int m2 = 0; m2 < NMAT; ++m2) {
-            const __amdgpu_buffer_rsrc_t r = stream_rsrc((m2 == 0 ? wbase : wu) + off, nrec);
-#pragma unroll
-            for (int i = 0; i < kDma; ++i) buffer_load16_lds(r, &stage[m2][swave][i * 1024], i * 1024u + lane * 16u);
+            stage_bytes<kIterBytes>(stream_rsrc((m2 == 0 ? wbase : wu) + off, nrec), &stage[b][m2][swave][0], lane);
         }
     };
     auto issue = [&](RowLoads<F, NMAT> (&b)[RPG], int it) {
@@ -469,7 +468,8 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     asm volatile("" ::: "memory");
     RowLoads<F, NMAT> buf[kStage ? 1 : NB][RPG];
     if constexpr (kStage) {
-        issue_stage(it0);
+#pragma unroll
+        for (int b = 0; b < kSlots; ++b) issue_stage(b, it0 + b * nwaves);
     } else {
 #pragma unroll
         for (int b = 0; b + 1 < NB; ++b) issue(buf[b], it0 + b * nwaves);
@@ -479,7 +479,8 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
     for (int t = 0; t < kTok; ++t) {
         if (kTok == 1 || t < ntok) prepare_x<BLOCK, kXChunks>(xl[t], ngroups, xg + t * ngroups);
     }
-    __syncthreads();
+    if constexpr (kStage) lds_barrier();  // the first iteration's loads stay in flight
+    else __syncthreads();
     // the tokens of this wave (tokens past ntok repeat the last)
     int tok[MT];
 #pragma unroll
@@ -581,26 +582,32 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
             else __builtin_amdgcn_s_setprio(0);
         };
         if constexpr (kStage) {
-            // Staged: the iteration's bytes are read from the slot into
-            // registers, the slot is refilled with the wave's next iteration,
-            // and the registers are decoded while those loads are in flight.
-            // (The read waits for the slot's loads; the compiler places that
-            // wait.  The refill waits for the reads: wait_lds_reads.)
+            // Staged: slot b of the ring holds iterations b, b + kSlots, ...
+            // (in units of nwaves).  Each step waits for its slot's loads
+            // (the other slots' kSlots - 1 iterations of loads, issued later,
+            // stay in flight), reads the slot into registers, refills it with
+            // the iteration kSlots ahead and decodes the registers meanwhile.
             if (it0 < niters) {
-                for (int cur = it0;; cur += nwaves) {
-                    set_priority(cur);
-                    RowLoads<F, NMAT> rows[RPG];
+                for (int it = it0;; it += kSlots * nwaves) {
 #pragma unroll
-                    for (int q = 0; q < RPG; ++q) {
+                    for (int b = 0; b < kSlots; ++b) {
+                        const int cur = it + b * nwaves;
+                        set_priority(cur);
+                        wait_vm<kDma * NMAT * (kSlots - 1)>();
+                        RowLoads<F, NMAT> rows[RPG];
 #pragma unroll
-                        for (int m2 = 0; m2 < NMAT; ++m2)
-                            F::fetch(rows[q].m[m2], &stage[m2][swave][q * kRowsPerGroup * static_cast<int>(row_bytes)],
-                                     g);
+                        for (int q = 0; q < RPG; ++q) {
+#pragma unroll
+                            for (int m2 = 0; m2 < NMAT; ++m2)
+                                F::fetch(rows[q].m[m2],
+                                         lds_addr(&stage[b][m2][swave][0]) +
+                                             static_cast<uint32_t>(q * kRowsPerGroup) * static_cast<uint32_t>(row_bytes),
+                                         g);
+                        }
+                        issue_stage(b, cur + kSlots * nwaves);
+                        finish(rows, cur);
+                        if (cur + nwaves >= niters) goto done;
                     }
-                    wait_lds_reads();
-                    issue_stage(cur + nwaves);
-                    finish(rows, cur);
-                    if (cur + nwaves >= niters) break;
                 }
             }
         } else if (it0 < niters) {
@@ -675,6 +682,16 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
     XGroup *xg = reinterpret_cast<XGroup *>(smem);
     // [2][kFlush][R][S][NV]
     float *part = reinterpret_cast<float *>(smem + static_cast<size_t>(MT) * ngroups * sizeof(XGroup));
+    // Single-token Q4_K rows stage each wave's slice (64 groups, 2304
+    // contiguous bytes) through LDS, as gemv_kernel does: a ring of
+    // kSlots = NB - 1 slices in flight per wave.
+    constexpr bool kStage = F::kStaged && MT == 1 && !SWIGLU && Q4K_STAGE != 0;
+    constexpr int kSlots = kStage ? NB - 1 : 1;
+    constexpr int kSliceBytes = kWave * F::kGroupBytes;
+    constexpr int kDma = stage_loads<kSliceBytes>();
+    constexpr int kStageWaves = kStage ? S * R : 1;
+    constexpr int kStageBytes = kStage ? kSliceBytes : 16;
+    __shared__ __align__(16) uint8_t stage[kSlots][kStageWaves][kStageBytes];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -693,6 +710,22 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
         const bool live = c < my_iters && row < n;
         issue_row(b, w, wu, live ? row * row_bytes : 0, live ? static_cast<int>(row_bytes) : 0, g);
     };
+    // staged: the wave's slice of iteration c into slot b of its ring
+    auto slot = [&](int b) -> uint8_t * { return &stage[b][wave][0]; };
+    auto issue_stage = [&](int b, int c) {
+        const int64_t row = row_of(c, rslot);
+        const bool live = c < my_iters && row < n;
+        const int64_t sb = static_cast<int64_t>(slice) * kSliceBytes;
+        const int64_t left = row_bytes - sb;
+        const int nrec = __builtin_amdgcn_readfirstlane(
+            live ? static_cast<int>(left < kSliceBytes ? (left > 0 ? left : 0) : kSliceBytes) : 0);
+        const uint8_t *base =
+            reinterpret_cast<const uint8_t *>(wave_uniform(reinterpret_cast<int64_t>(w + (live ? row * row_bytes + sb : 0))));
+        stage_bytes<kSliceBytes>(stream_rsrc(base, nrec), slot(b), lane);
+    };
+    // the lane's byte offsets inside its slice (its validity and pair
+    // selection come from g)
+    const typename F::Lane gs = F::lane(lane, kWave, 0u);
 
     constexpr int kXChunks = (S * kWave * 16 + BLOCK - 1) / BLOCK;
     const int64_t xstride = static_cast<int64_t>(ngroups) * 64;
@@ -704,9 +737,18 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
         xl[t] = load_x<BLOCK, kXChunks, XT>(xt, ngroups);
     }
     asm volatile("" ::: "memory");
-    RowLoads<F, NMAT> buf[NB];
+    RowLoads<F, NMAT> buf[kStage ? 1 : NB];
+    if constexpr (kStage) {
 #pragma unroll
-    for (int b = 0; b + 1 < NB; ++b) issue(buf[b], b);
+        for (int b = 0; b < kSlots; ++b) issue_stage(b, b);
+    } else {
+#pragma unroll
+        for (int b = 0; b + 1 < NB; ++b) issue(buf[b], b);
+    }
+    auto barrier = [&]() {
+        if constexpr (kStage) lds_barrier();
+        else __syncthreads();
+    };
 
     __shared__ int inexact;
     if (threadIdx.x == 0) inexact = 0;
@@ -714,7 +756,7 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
     for (int t = 0; t < MT; ++t) {
         if (MT == 1 || t < ntok) prepare_x<BLOCK, kXChunks>(xl[t], ngroups, xg + t * ngroups);
     }
-    __syncthreads();
+    barrier();
     int tok[MT];
     uint32_t flagged = 0;
 #pragma unroll
@@ -725,7 +767,7 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
     // The loop below has barriers, so the choice of path is made once for the
     // whole workgroup: the f32 path if any wave's slice holds a flagged group.
     if (__builtin_amdgcn_ballot_w64(flagged != 0) != 0 && lane == 0) inexact = 1;
-    __syncthreads();
+    barrier();
 
     // EXACT false: src is the MT tokens' activation registers; EXACT true:
     // MT pointers to the lane's group of activations (registers or memory).
@@ -734,72 +776,97 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
         // f32 path: each row's reads wait for the previous row's sums (the
         // unrolled rows would otherwise all hold their activations at once)
         float chain = 0.0f;
-        for (int c = 0; c < my_iters; c += NB) {
-            {
-                // priority falls with the share of iterations left, as in gemv_kernel
-                const int left = my_iters - c;
-                if (4 * left > 3 * my_iters) __builtin_amdgcn_s_setprio(3);
-                else if (4 * left > 2 * my_iters) __builtin_amdgcn_s_setprio(2);
-                else if (4 * left > my_iters) __builtin_amdgcn_s_setprio(1);
-                else __builtin_amdgcn_s_setprio(0);
+        // the lane's share of iteration cur, reduced into LDS; every kFlush
+        // iterations (and at the end) the rows' slices are added and stored
+        auto finish = [&](const RowLoads<F, NMAT> &rows, int cur) {
+            float acc[NV];
+            if constexpr (MT == 1) {
+                if constexpr (EXACT) lane_dot_exact(rows, g, src[0], g.ok, chain, acc);
+                else lane_dot(rows, g, src[0], g.ok, acc);
+            } else {
+                float at[MT];
+                if constexpr (EXACT) F::dot_tokens_exact(rows.m[0], g, src, g.ok, chain, at);
+                else F::dot_tokens(rows.m[0], g, src, g.ok, at);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[t] = at[t];
             }
+            if constexpr (EXACT) chain = acc[NV - 1];
+            const int d = cur % kFlush;
+            const int half = (cur / kFlush) & 1;
+            float *pp = part + (((half * kFlush + d) * R + rslot) * S + slice) * NV;
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const int cur = c + b;
-                // the f32 path loads each row just before it is used, after the
-                // previous row's result (few registers: it is a fallback)
-                if constexpr (EXACT) issue(buf[b], opaque_int_after(cur, chain));
-                else issue(buf[(b + NB - 1) % NB], cur + NB - 1);
-                float acc[NV];
-                if constexpr (MT == 1) {
-                    if constexpr (EXACT) lane_dot_exact(buf[b], g, src[0], g.ok, chain, acc);
-                    else lane_dot(buf[b], g, src[0], g.ok, acc);
-                } else {
-                    float at[MT];
-                    if constexpr (EXACT) F::dot_tokens_exact(buf[b].m[0], g, src, g.ok, chain, at);
-                    else F::dot_tokens(buf[b].m[0], g, src, g.ok, at);
+            for (int v = 0; v < NV; ++v) {
+                acc[v] = lane_group_sum<kWave>(acc[v]);
+                if (lane == 0) pp[v] = acc[v];
+            }
+            if (d == kFlush - 1 || cur + 1 == my_iters) {
+                barrier();
+                const int t = static_cast<int>(threadIdx.x);
+                if (t < (d + 1) * R) {
+                    const int dd = t / R;
+                    const int r = t % R;
+                    const int64_t row = row_of(cur - d + dd, r);
+                    if (row < n) {
+                        const float *q = part + ((half * kFlush + dd) * R + r) * S * NV;
+                        float sum[NV];
 #pragma unroll
-                    for (int t = 0; t < MT; ++t) acc[t] = at[t];
-                }
-                if constexpr (EXACT) chain = acc[NV - 1];
-                const int d = cur % kFlush;
-                const int half = (cur / kFlush) & 1;
-                float *pp = part + (((half * kFlush + d) * R + rslot) * S + slice) * NV;
+                        for (int v = 0; v < NV; ++v) sum[v] = q[v];
 #pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    acc[v] = lane_group_sum<kWave>(acc[v]);
-                    if (lane == 0) pp[v] = acc[v];
-                }
-                if (d == kFlush - 1 || cur + 1 == my_iters) {
-                    __syncthreads();
-                    const int t = static_cast<int>(threadIdx.x);
-                    if (t < (d + 1) * R) {
-                        const int dd = t / R;
-                        const int r = t % R;
-                        const int64_t row = row_of(cur - d + dd, r);
-                        if (row < n) {
-                            const float *q = part + ((half * kFlush + dd) * R + r) * S * NV;
-                            float sum[NV];
+                        for (int s = 1; s < S; ++s) {
 #pragma unroll
-                            for (int v = 0; v < NV; ++v) sum[v] = q[v];
+                            for (int v = 0; v < NV; ++v) sum[v] += q[s * NV + v];
+                        }
+                        if constexpr (MT == 1) {
+                            const float v = SWIGLU ? silu(sum[0]) * sum[NV - 1] : sum[0];
+                            y[row] = static_cast<YT>(res != nullptr ? v + res[row] : v);
+                        } else {
 #pragma unroll
-                            for (int s = 1; s < S; ++s) {
-#pragma unroll
-                                for (int v = 0; v < NV; ++v) sum[v] += q[s * NV + v];
-                            }
-                            if constexpr (MT == 1) {
-                                const float v = SWIGLU ? silu(sum[0]) * sum[NV - 1] : sum[0];
-                                y[row] = static_cast<YT>(res != nullptr ? v + res[row] : v);
-                            } else {
-#pragma unroll
-                                for (int j = 0; j < MT; ++j) {
-                                    if (j < ntok) y[j * n + row] = static_cast<YT>(sum[j]);
-                                }
+                            for (int j = 0; j < MT; ++j) {
+                                if (j < ntok) y[j * n + row] = static_cast<YT>(sum[j]);
                             }
                         }
                     }
                 }
-                if (cur + 1 >= my_iters) break;
+            }
+        };
+        // priority falls with the share of iterations left, as in gemv_kernel
+        auto set_priority = [&](int c) {
+            const int left = my_iters - c;
+            if (4 * left > 3 * my_iters) __builtin_amdgcn_s_setprio(3);
+            else if (4 * left > 2 * my_iters) __builtin_amdgcn_s_setprio(2);
+            else if (4 * left > my_iters) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        };
+        if constexpr (kStage) {
+            // slot b holds iterations b, b + kSlots, ...: wait for its loads
+            // (the other slots' stay in flight), read it, refill it with the
+            // wave's iteration kSlots ahead, decode the registers meanwhile
+            for (int c = 0; c < my_iters; c += kSlots) {
+                set_priority(c);
+#pragma unroll
+                for (int b = 0; b < kSlots; ++b) {
+                    const int cur = c + b;
+                    wait_vm<kDma * (kSlots - 1)>();
+                    RowLoads<F, NMAT> rows;
+                    F::fetch(rows.m[0], lds_addr(slot(b)), gs);
+                    issue_stage(b, cur + kSlots);
+                    finish(rows, cur);
+                    if (cur + 1 >= my_iters) break;
+                }
+            }
+        } else {
+            for (int c = 0; c < my_iters; c += NB) {
+                set_priority(c);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int cur = c + b;
+                    // the f32 path loads each row just before it is used, after the
+                    // previous row's result (few registers: it is a fallback)
+                    if constexpr (EXACT) issue(buf[b], opaque_int_after(cur, chain));
+                    else issue(buf[(b + NB - 1) % NB], cur + NB - 1);
+                    finish(buf[b], cur);
+                    if (cur + 1 >= my_iters) break;
+                }
             }
         }
     };
@@ -1134,6 +1201,32 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const void *x, co
 #ifndef Q4K_SPLIT_NB
 #define Q4K_SPLIT_NB 3
 #endif
+// Single-token Q4_K streams read through an LDS ring of this many iterations
+// per wave (one slot per matrix each, 2304 bytes per 64 groups); Q8_0 keeps
+// the register buffers above.  Deeper rings measured slower wherever they fit
+// (the 9B lm_head: 85.3, 87.9, 88.9 us for 1, 2, 3 slots; the 9B down: 8.9 us
+// with 2 slots, 9.6 with 3, 11.0 with 4): more loads queued per CU do not
+// stream faster.  The K-split ring and the activation groups must fit the 160
+// KB of LDS: two slices per row (16 waves, K <= 8192), three (12 waves,
+// K <= 12288) and four (16 waves, K <= 16384).
+#ifndef Q4K_LARGE_SLOTS
+#define Q4K_LARGE_SLOTS 1
+#endif
+#ifndef Q4K_SMALL_SLOTS
+#define Q4K_SMALL_SLOTS 1
+#endif
+#ifndef Q4K_SWIGLU_SLOTS
+#define Q4K_SWIGLU_SLOTS 1
+#endif
+#ifndef Q4K_SPLIT2_SLOTS
+#define Q4K_SPLIT2_SLOTS 3
+#endif
+#ifndef Q4K_SPLIT3_SLOTS
+#define Q4K_SPLIT3_SLOTS 2
+#endif
+#ifndef Q4K_SPLIT4_SLOTS
+#define Q4K_SPLIT4_SLOTS 2
+#endif
 // matrices below this many bytes use the small launch shape
 #ifndef Q4K_SMALL_BYTES
 #define Q4K_SMALL_BYTES (8 << 20)
@@ -1142,20 +1235,23 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const void *x, co
 template <class F, typename XT, typename YT, int LPR, bool SWIGLU>
 hipError_t dispatch_lpr(const GemvJob *jobs, int count, const uint8_t *wu, const void *x, int64_t k,
                         hipStream_t stream) {
+    // staged streams: NB - 1 = slots of the LDS ring
+    constexpr bool kStaged = F::kStaged;
     if constexpr (SWIGLU) {
-        return launch_fast<F, XT, YT, LPR, true, Q4K_SWIGLU_NB, Q4K_SWIGLU_BLOCK, Q4K_SWIGLU_MINW>(jobs, count, wu, x, k,
-                                                                                          stream);
+        constexpr int NB = kStaged ? 1 + Q4K_SWIGLU_SLOTS : Q4K_SWIGLU_NB;
+        return launch_fast<F, XT, YT, LPR, true, NB, Q4K_SWIGLU_BLOCK, Q4K_SWIGLU_MINW>(jobs, count, wu, x, k, stream);
     } else {
         int64_t bytes = 0;
         for (int i = 0; i < count; ++i) bytes += jobs[i].n * F::row_bytes(k);
         if (bytes < Q4K_SMALL_BYTES) {
-            return launch_fast<F, XT, YT, LPR, false, Q4K_SMALL_NB, Q4K_SMALL_BLOCK, Q4K_SMALL_MINW>(jobs, count, wu, x, k,
-                                                                                             stream);
+            constexpr int NB = kStaged ? 1 + Q4K_SMALL_SLOTS : Q4K_SMALL_NB;
+            return launch_fast<F, XT, YT, LPR, false, NB, Q4K_SMALL_BLOCK, Q4K_SMALL_MINW>(jobs, count, wu, x, k, stream);
         }
         constexpr int kShort = std::is_same_v<F, Q8_0Format> ? Q8_0_LARGE_BLOCK_SHORT : Q4K_LARGE_BLOCK_SHORT;
         constexpr int kBlock = LPR <= 16 ? kShort : Q4K_LARGE_BLOCK;
-        return launch_fast<F, XT, YT, LPR, false, Q4K_LARGE_NB, kBlock, Q4K_LARGE_MINW, Q4K_LARGE_RPG>(jobs, count, wu, x,
-                                                                                                 k, stream);
+        constexpr int NB = kStaged ? 1 + Q4K_LARGE_SLOTS : Q4K_LARGE_NB;
+        return launch_fast<F, XT, YT, LPR, false, NB, kBlock, Q4K_LARGE_MINW, Q4K_LARGE_RPG>(jobs, count, wu, x, k,
+                                                                                           stream);
     }
 }
 
@@ -1171,9 +1267,13 @@ hipError_t dispatch_wide(const GemvJob &j, const uint8_t *wu, const void *x, int
         if (ngroups <= 192) return launch_split<F, XT, YT, 3, 4, true, NB, 3>(j.w, wu, x, j.r, j.y, j.n, k, stream);
         if (ngroups <= 256) return launch_split<F, XT, YT, 4, 2, true, NB, 2>(j.w, wu, x, j.r, j.y, j.n, k, stream);
     } else {
-        if (ngroups <= 128) return launch_split<F, XT, YT, 2, 8, false, NB, 4>(j.w, wu, x, j.r, j.y, j.n, k, stream);
-        if (ngroups <= 192) return launch_split<F, XT, YT, 3, 4, false, NB, 3>(j.w, wu, x, j.r, j.y, j.n, k, stream);
-        if (ngroups <= 256) return launch_split<F, XT, YT, 4, 4, false, NB, 4>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        constexpr bool kStaged = F::kStaged;
+        constexpr int NB2 = kStaged ? 1 + Q4K_SPLIT2_SLOTS : NB;
+        constexpr int NB3 = kStaged ? 1 + Q4K_SPLIT3_SLOTS : NB;
+        constexpr int NB4 = kStaged ? 1 + Q4K_SPLIT4_SLOTS : NB;
+        if (ngroups <= 128) return launch_split<F, XT, YT, 2, 8, false, NB2, 4>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 192) return launch_split<F, XT, YT, 3, 4, false, NB3, 3>(j.w, wu, x, j.r, j.y, j.n, k, stream);
+        if (ngroups <= 256) return launch_split<F, XT, YT, 4, 4, false, NB4, 4>(j.w, wu, x, j.r, j.y, j.n, k, stream);
     }
     // beyond K = 16384: the plain kernel
     return launch_generic<F, XT, YT, SWIGLU>(j.w, wu, x, j.r, j.y, j.n, k, stream);

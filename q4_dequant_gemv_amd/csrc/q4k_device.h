@@ -63,11 +63,100 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint
                                              Q4K_STAGE_CPOL);
 }
 
+// The same with 4 bytes per lane (256 bytes per wave).
+__device__ __forceinline__ void buffer_load4_lds(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 4, voff, 0, 0,
+                                             Q4K_STAGE_CPOL);
+}
+
+// BYTES (a multiple of 256) contiguous bytes from descriptor offset 0 to LDS
+// at dst (wave-uniform): whole kilobytes by 16-byte loads, the rest by 4-byte
+// loads.  stage_loads<BYTES> is the number of load instructions, for wait_vm.
+template <int BYTES>
+constexpr int stage_loads() {
+    return BYTES / 1024 + (BYTES % 1024) / 256;
+}
+
+template <int BYTES>
+__device__ __forceinline__ void stage_bytes(__amdgpu_buffer_rsrc_t r, uint8_t *dst, int lane) {
+    static_assert(BYTES % 256 == 0, "whole 256-byte pieces");
+    constexpr int kFull = BYTES / 1024;
+    constexpr int kTail = (BYTES % 1024) / 256;
+#pragma unroll
+    for (int i = 0; i < kFull; ++i) buffer_load16_lds(r, dst + i * 1024, i * 1024u + static_cast<uint32_t>(lane) * 16u);
+#pragma unroll
+    for (int i = 0; i < kTail; ++i)
+        buffer_load4_lds(r, dst + kFull * 1024 + i * 256, kFull * 1024u + i * 256u + static_cast<uint32_t>(lane) * 4u);
+}
+
 // Waits for this wave's LDS reads (and scalar loads), nothing else; the empty
 // asm statements keep the compiler from moving memory operations across it.
 __device__ __forceinline__ void wait_lds_reads() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+    asm volatile("" ::: "memory");
+}
+
+// Waits until at most N vector memory operations of this wave are in flight.
+// Loads complete in issue order, so this waits for everything issued before
+// the last N operations.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    asm volatile("" ::: "memory");
+    // vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) at their maxima
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
+// The 32-bit LDS byte address of a pointer into LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
+}
+
+// Three 16-byte LDS reads, at LDS byte addresses a, b and b + 16 (each a
+// multiple of 16), complete on return.  Written as one asm statement with its
+// own lgkmcnt wait: the compiler then sees no LDS read and adds no wait for
+// the staged weight loads still in flight to other slots (it cannot tell
+// them apart and would wait for all of them); the caller waits for the
+// slot's own loads (wait_vm).
+__device__ __forceinline__ void lds_read_3x16(uint32_t a, uint32_t b, uint4 &ra, uint4 &rb, uint4 &rc) {
+    u32x4_t x, y, z;
+    asm volatile(
+        "ds_read_b128 %0, %3\n\t"
+        "ds_read_b128 %1, %4\n\t"
+        "ds_read_b128 %2, %4 offset:16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x), "=&v"(y), "=&v"(z)
+        : "v"(a), "v"(b)
+        : "memory");
+    ra = make_uint4(x.x, x.y, x.z, x.w);
+    rb = make_uint4(y.x, y.y, y.z, y.w);
+    rc = make_uint4(z.x, z.y, z.z, z.w);
+}
+
+// One 16-byte LDS read at LDS byte address a (a multiple of 16), complete on
+// return (see lds_read_3x16).
+__device__ __forceinline__ uint4 lds_read_16(uint32_t a) {
+    u32x4_t x;
+    asm volatile(
+        "ds_read_b128 %0, %1\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x)
+        : "v"(a)
+        : "memory");
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+
+// Workgroup barrier for data exchanged through LDS only: this wave's LDS
+// operations complete, then s_barrier.  Unlike __syncthreads() it does not
+// wait for loads still in flight to LDS (a workgroup release fence waits for
+// those), so the weight stream keeps running across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
 

@@ -135,7 +135,15 @@ __device__ __forceinline__ void prepare_x(const XLoaded<NCH> &f, int ngroups, XG
             bx[b] = static_cast<uint32_t>(X + 0x808080);
         }
         round_sum = lane_group_sum<16>(round_sum);
-        const float rest = lane_group_rest_bound<16>(mag);
+        // The magnitude without the four largest is at least the sum of all
+        // minus four times the largest (here 2^21 <= largest < 2^22): when
+        // that already clears the rounding, the tighter bound is not needed;
+        // otherwise the waves holding such a group compute it.
+        const float abs_sum = lane_group_sum<16>((mag[0] + mag[1]) + (mag[2] + mag[3]));
+        const float amax_s = (finite && !zero) ? ldexpf(amax, sexp) : 0.0f;
+        const bool clear = round_sum * 32768.0f <= abs_sum - 4.0f * amax_s;
+        float rest = abs_sum - 4.0f * amax_s;
+        if (__builtin_amdgcn_ballot_w64(!clear) != 0) rest = clear ? rest : lane_group_rest_bound<16>(mag);
         // v_perm_b32: byte i of the result is byte sel_i of {first (bytes 4-7), second (bytes 0-3)}
         const uint32_t t01 = __builtin_amdgcn_perm(bx[1], bx[0], 0x05010400u);  // bytes 0 and 1 of values 0, 1
         const uint32_t t23 = __builtin_amdgcn_perm(bx[3], bx[2], 0x05010400u);

@@ -8,6 +8,8 @@
 // flight, so a wave reads 1 KB of consecutive bytes per load and the whole
 // grid sweeps the buffer front to back.  The loaded words are folded with
 // XOR into one word per thread, written to `out`, so that no load is dead.
+// AUX is the loads' cache policy: 0 the default, 2 non-temporal (every line
+// is read whole by one load, where the non-temporal policy streams faster).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -15,7 +17,7 @@ namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-template <int UNROLL>
+template <int UNROLL, int AUX>
 __global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t *__restrict__ p, int64_t chunks,
                                                           uint32_t *__restrict__ out) {
     const int64_t tid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -31,7 +33,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t *__restr
         for (int u = 0; u < UNROLL; ++u) {
             const int64_t c = base + u * nth;
             const uint32_t off = c < chunks ? static_cast<uint32_t>(c * 16) : 0x80000000u;
-            v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, AUX);
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
@@ -42,19 +44,24 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t *__restr
 }  // namespace
 
 // Reads `bytes` (a multiple of 16, at most 2 GiB - 16) at device pointer p
-// once on `stream` with `grid` workgroups of 256 threads and `unroll` (4 or
-// 8) loads in flight per thread; out: device buffer of grid * 256 words.
-// Returns a hipError_t value (0: launched).
+// once on `stream` with `grid` workgroups of 256 threads, `unroll` (4 or 8)
+// loads in flight per thread and cache policy `policy` (0 default, 2
+// non-temporal); out: device buffer of grid * 256 words.  Returns a
+// hipError_t value (0: launched).
 extern "C" __attribute__((visibility("default"))) int q4k_stream_read(const void *p, int64_t bytes, void *out,
-                                                                      int grid, int unroll, void *stream) {
+                                                                      int grid, int unroll, int policy,
+                                                                      void *stream) {
     if (p == nullptr || out == nullptr || bytes <= 0 || bytes % 16 != 0 || bytes >= (int64_t{1} << 31) ||
-        grid <= 0 || (unroll != 4 && unroll != 8)) {
+        grid <= 0 || (unroll != 4 && unroll != 8) || (policy != 0 && policy != 2)) {
         return static_cast<int>(hipErrorInvalidValue);
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const auto *src = static_cast<const uint8_t *>(p);
     auto *dst = static_cast<uint32_t *>(out);
-    if (unroll == 4) hipLaunchKernelGGL((stream_read_kernel<4>), dim3(grid), dim3(256), 0, s, src, bytes / 16, dst);
-    else hipLaunchKernelGGL((stream_read_kernel<8>), dim3(grid), dim3(256), 0, s, src, bytes / 16, dst);
+    const int64_t chunks = bytes / 16;
+    if (unroll == 4 && policy == 0) hipLaunchKernelGGL((stream_read_kernel<4, 0>), dim3(grid), dim3(256), 0, s, src, chunks, dst);
+    else if (unroll == 4) hipLaunchKernelGGL((stream_read_kernel<4, 2>), dim3(grid), dim3(256), 0, s, src, chunks, dst);
+    else if (policy == 0) hipLaunchKernelGGL((stream_read_kernel<8, 0>), dim3(grid), dim3(256), 0, s, src, chunks, dst);
+    else hipLaunchKernelGGL((stream_read_kernel<8, 2>), dim3(grid), dim3(256), 0, s, src, chunks, dst);
     return static_cast<int>(hipGetLastError());
 }

@@ -392,7 +392,8 @@ def test_stream_read_probe_library():
     L = ctypes.CDLL(hip_build.STREAM_LIB)
     L.q4k_stream_read.restype = ctypes.c_int
     L.q4k_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
-                                  ctypes.c_void_p]
-    for args in ((0, 1024, Y, 8, 4), (X, 1000, Y, 8, 4), (X, 1 << 31, Y, 8, 4), (X, 1024, 0, 8, 4),
-                 (X, 1024, Y, 0, 4), (X, 1024, Y, 8, 5), (X, -16, Y, 8, 8)):
+                                  ctypes.c_int, ctypes.c_void_p]
+    for args in ((0, 1024, Y, 8, 4, 0), (X, 1000, Y, 8, 4, 0), (X, 1 << 31, Y, 8, 4, 2), (X, 1024, 0, 8, 4, 0),
+                 (X, 1024, Y, 0, 4, 2), (X, 1024, Y, 8, 5, 0), (X, -16, Y, 8, 8, 0), (X, 1024, Y, 8, 4, 1),
+                 (X, 1024, Y, 8, 8, 3)):
         assert L.q4k_stream_read(*args, None) != 0, args
