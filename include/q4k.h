@@ -333,7 +333,13 @@ Q4K_API q4k_status q4k_fused_swiglu(const void *w_gate, const void *w_up, const 
  */
 Q4K_API q4k_status q4k_dequant(const void *w, float *out, int64_t n, int64_t k, void *stream);
 
-/* Static, NUL-terminated description of a status code. */
+/*
+ * Static, NUL-terminated description of a status code (never NULL; codes the
+ * library does not define give "unknown status").  No page defines this
+ * call: it is the C form of the fallible entry points of the cuda_lane module
+ * docs (try_q4k_soa_gemv and its siblings return an error value that a
+ * caller can print), which this ABI's status codes stand for.
+ */
 Q4K_API const char *q4k_status_string(q4k_status s);
 
 /* ABI version of this header (major*100 + minor); q4k_abi_version() of the

@@ -534,14 +534,16 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
             yp = nullptr;
             win = 0;
         };
-        // Finishes one wave iteration whose weights are in `rows`: the lane
-        // group's dot products, reduced, kept for the window's store.
-        auto finish = [&](const RowLoads<F, NMAT> (&rows)[RPG], int cur) {
-            row_cursor(cur);
+        // Finishes one wave iteration whose weights are in `rows` and whose
+        // lane slot's first row is row0 of a matrix of nrows rows (output
+        // ybase, residual rbase): the lane group's dot products, reduced, kept
+        // for the window's store.
+        auto finish_rows = [&](const RowLoads<F, NMAT> (&rows)[RPG], int64_t row0, int64_t nrows, YT *ybase,
+                               const float *rbase) {
 #pragma unroll
             for (int q = 0; q < RPG; ++q) {
-                const int64_t row = static_cast<int64_t>(cur - rc.begin) * kRowsPerWave + q * kRowsPerGroup + slot;
-                const bool rok = row < rc.n;
+                const int64_t row = row0 + q * kRowsPerGroup;
+                const bool rok = row < nrows;
                 const bool mine = sub == win;
                 if constexpr (MT == 1) {
                     float acc[NMAT];
@@ -563,19 +565,25 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
                     }
                 }
                 if constexpr (QG) yp = mine ? (rok ? dest(row) : nullptr) : yp;
-                else if constexpr (kTok > 1) yp = mine ? (rok ? rc.y + tile * MT * ystride + row : nullptr) : yp;
-                else yp = mine ? (rok ? rc.y + row : nullptr) : yp;
-                if constexpr (RES) rp = mine ? (rc.r != nullptr ? rc.r + row : nullptr) : rp;
+                else if constexpr (kTok > 1) yp = mine ? (rok ? ybase + tile * MT * ystride + row : nullptr) : yp;
+                else yp = mine ? (rok ? ybase + row : nullptr) : yp;
+                if constexpr (RES) rp = mine ? (rbase != nullptr ? rbase + row : nullptr) : rp;
                 if (++win == LPR) flush();
             }
+        };
+        // the same for iteration `cur` of the whole table (cursor over the matrices)
+        auto finish = [&](const RowLoads<F, NMAT> (&rows)[RPG], int cur) {
+            row_cursor(cur);
+            finish_rows(rows, static_cast<int64_t>(cur - rc.begin) * kRowsPerWave + slot, rc.n, rc.y, rc.r);
         };
         // The sequencer issues from the oldest wave first, so with equal shares
         // the younger waves of a CU fall behind and finish alone, long after the
         // others.  Each wave therefore lowers its own priority as the share of its
         // iterations still to do drops (1/2, 1/4, 1/8): a wave that is behind
-        // outranks the ones ahead of it, and the finish times close up.
-        auto set_priority = [&](int cur) {
-            const int left = (niters - cur + nwaves - 1) / nwaves;
+        // outranks the ones ahead of it, and the finish times close up.  kdone:
+        // the wave's iterations finished so far.
+        auto set_priority = [&](int kdone) {
+            const int left = my_iters - kdone;
             if (2 * left > my_iters) __builtin_amdgcn_s_setprio(3);
             else if (4 * left > my_iters) __builtin_amdgcn_s_setprio(2);
             else if (8 * left > my_iters) __builtin_amdgcn_s_setprio(1);
@@ -587,23 +595,63 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
             // (the other slots' kSlots - 1 iterations of loads, issued later,
             // stay in flight), reads the slot into registers, refills it with
             // the iteration kSlots ahead and decodes the registers meanwhile.
-            if (it0 < niters) {
+            auto fetch_slot = [&](RowLoads<F, NMAT> (&rows)[RPG], int b) {
+    #pragma unroll
+                for (int q = 0; q < RPG; ++q) {
+    #pragma unroll
+                    for (int m2 = 0; m2 < NMAT; ++m2)
+                        F::fetch(rows[q].m[m2],
+                                 lds_addr(&stage[b][m2][swave][0]) +
+                                     static_cast<uint32_t>(q * kRowsPerGroup) * static_cast<uint32_t>(row_bytes),
+                                 g);
+                }
+            };
+            if (it0 < niters && !QG && count == 1) {
+                // One matrix (the common call): the next load's byte offset
+                // and the lane's row advance by constant strides, so a step
+                // costs few scalar instructions (a vector instruction occupies
+                // a SIMD for 4 cycles, and the scalar unit takes one
+                // instruction per 4 cycles for all waves of a SIMD).
+                const int64_t n0 = mt.n[0];
+                YT *const y0 = static_cast<YT *>(mt.y[0]);
+                const float *const r0 = mt.r[0];
+                const uint8_t *const w0 = mt.w[0];
+                const int tail = mt.tail_bytes[0];
+                const int64_t lstep = static_cast<int64_t>(nwaves) * iter_bytes;
+                int lit = it0 + kSlots * nwaves;  // iteration of the next load
+                int64_t loff = static_cast<int64_t>(lit) * iter_bytes;
+                int64_t row0 = static_cast<int64_t>(it0) * kRowsPerWave + slot;
+                const int64_t rstep = static_cast<int64_t>(nwaves) * kRowsPerWave;
+                int kdone = 0;
+                for (;;) {
+#pragma unroll
+                    for (int b = 0; b < kSlots; ++b) {
+                        set_priority(kdone);
+                        wait_vm<kDma * NMAT * (kSlots - 1)>();
+                        RowLoads<F, NMAT> rows[RPG];
+                        fetch_slot(rows, b);
+                        const int nrec = lit < niters - 1 ? iter_bytes : (lit == niters - 1 ? tail : 0);
+#pragma unroll
+                        for (int m2 = 0; m2 < NMAT; ++m2)
+                            stage_bytes<kIterBytes>(stream_rsrc((m2 == 0 ? w0 : wu) + loff, nrec),
+                                                    &stage[b][m2][swave][0], lane);
+                        lit += nwaves;
+                        loff += lstep;
+                        finish_rows(rows, row0, n0, y0, r0);
+                        row0 += rstep;
+                        if (++kdone == my_iters) goto done;
+                    }
+                }
+            } else if (it0 < niters) {
+                int kdone = 0;
                 for (int it = it0;; it += kSlots * nwaves) {
 #pragma unroll
                     for (int b = 0; b < kSlots; ++b) {
                         const int cur = it + b * nwaves;
-                        set_priority(cur);
+                        set_priority(kdone++);
                         wait_vm<kDma * NMAT * (kSlots - 1)>();
                         RowLoads<F, NMAT> rows[RPG];
-#pragma unroll
-                        for (int q = 0; q < RPG; ++q) {
-#pragma unroll
-                            for (int m2 = 0; m2 < NMAT; ++m2)
-                                F::fetch(rows[q].m[m2],
-                                         lds_addr(&stage[b][m2][swave][0]) +
-                                             static_cast<uint32_t>(q * kRowsPerGroup) * static_cast<uint32_t>(row_bytes),
-                                         g);
-                        }
+                        fetch_slot(rows, b);
                         issue_stage(b, cur + kSlots * nwaves);
                         finish(rows, cur);
                         if (cur + nwaves >= niters) goto done;
@@ -615,11 +663,12 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
             // fell back to the outer loop's test would join the loop head with
             // loads of the unfinished unrolled pass still in flight, and the
             // wait counters would have to drain them there.
+            int kdone = 0;
             for (int it = it0;; it += NB * nwaves) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     const int cur = it + b * nwaves;
-                    set_priority(cur);
+                    set_priority(kdone++);
                     issue(buf[(b + NB - 1) % NB], cur + (NB - 1) * nwaves);
                     finish(buf[b], cur);
                     if (cur + nwaves >= niters) goto done;
