@@ -27,12 +27,18 @@
  *    void*; NULL means the null stream) and returns; it never synchronises.
  *    Results are ready when the stream is.  Only the batched calls on the
  *    matrix cores (see q4k_gemv_batched) and the prefill GEMM need device
- *    scratch: they take it stream-ordered from the device's default memory
- *    pool (hipMallocAsync / hipFreeAsync on `stream`), about 67 *
- *    ceil(m'/16) * k bytes for the batched call with m' = min(m, 64) tokens
- *    (about 1.1 MB at m = 64, k = 4096; the size queries below give it
- *    exactly), or, through their *_ws forms, from a workspace the caller
- *    passes in.
+ *    scratch, about 67 * ceil(m'/16) * k bytes for the batched call with
+ *    m' = min(m, 64) tokens (about 1.1 MB at m = 64, k = 4096; the size
+ *    queries below give it exactly).  Called plainly they use a buffer the
+ *    library keeps per (device, stream), allocated stream-ordered from the
+ *    device's default memory pool (hipMallocAsync on `stream`) the first time
+ *    a stream needs it and grown the same way when a call needs more; calls
+ *    on one stream run in order and calls on different streams use different
+ *    buffers.  The buffers are held until the process ends (up to 64 MiB
+ *    per stream, 64 streams); beyond that, and while `stream` is being
+ *    captured into a graph, a call allocates and frees its own scratch
+ *    stream-ordered.  Through their *_ws forms the scratch is a workspace
+ *    the caller passes in, and q4k_gemv_batched_noalloc uses a static array.
  *  - Arguments are validated on the host before anything is enqueued; on any
  *    error nothing is launched and the status says why.  Launch failures are
  *    reported as Q4K_ERR_LAUNCH.
@@ -276,8 +282,8 @@ Q4K_API q4k_status q4k_gemv_batched_noalloc(const void *w, const void *x, q4k_dt
  *       even.
  * Any m >= 1 is accepted; the kernel works in 128-token tiles, so it is
  * meant for m >= 128 (q4k_gemv_batched_dt covers fewer tokens).  Takes
- * stream-ordered scratch (hipMallocAsync / hipFreeAsync) of
- * 2*m'*k + 32*(m'/128)*(k/256)*128 bytes, m' = m rounded up to 128.
+ * scratch (as described at the top) of 2*m'*k + 32*(m'/128)*(k/256)*128
+ * bytes, m' = m rounded up to 128.
  * k > 2^24 -> Q4K_ERR_UNSUPPORTED_SHAPE.  Other errors and aliasing as
  * q4k_gemv_batched.
  */
@@ -300,7 +306,7 @@ Q4K_API q4k_status q4k_prefill_gemm(const void *w, const void *x, void *y, q4k_d
  * q4k_gemv_batched_ws / q4k_prefill_gemm_ws compute exactly what
  * q4k_gemv_batched_dt / q4k_prefill_gemm compute (the same kernels, the same
  * order of sums) with `workspace`, a device buffer of workspace_bytes owned by
- * the caller, in place of the stream-ordered allocation.  The workspace must
+ * the caller, in place of the library's scratch.  The workspace must
  * be 256-byte aligned (else Q4K_ERR_MISALIGNED), hold at least the queried
  * size (else Q4K_ERR_INVALID_ARG; it may be NULL when that size is 0) and
  * overlap none of w, x, y (Q4K_ERR_INVALID_ARG).  Its contents are garbage before and after

@@ -89,6 +89,79 @@ hipError_t launch_fill_zero_f16(_Float16 *y, int64_t count, hipStream_t stream) 
     return hipGetLastError();
 }
 
+namespace {
+
+// Scratch of the calls made without a workspace, kept per (device, stream)
+// and reused: a call takes its stream's buffer (grown, stream-ordered, when it
+// needs more), so back-to-back calls allocate nothing.  Calls on one stream
+// run in order, and calls on different streams get different buffers, so no
+// two calls in flight share one.  Buffers live until the process ends (at
+// most kStreamScratchMax bytes per stream and kStreamScratchSlots streams);
+// larger needs, a full table and calls recorded into a graph (whose
+// allocations the graph must own) allocate and free per call as before.
+constexpr int kStreamScratchSlots = 64;
+constexpr int64_t kStreamScratchMax = int64_t{64} << 20;
+
+struct StreamScratch {
+    int dev;
+    hipStream_t stream;
+    uint8_t *ptr;
+    int64_t bytes;
+};
+
+std::mutex g_stream_scratch_mutex;
+StreamScratch g_stream_scratch[kStreamScratchSlots];
+int g_stream_scratch_count = 0;
+
+// *out = the stream's cached buffer of at least `total` bytes, or nullptr if
+// the call should allocate for itself.
+hipError_t stream_scratch(int64_t total, hipStream_t stream, uint8_t **out) {
+    *out = nullptr;
+    if (total > kStreamScratchMax) return hipSuccess;
+    hipStreamCaptureStatus status = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &status) != hipSuccess || status != hipStreamCaptureStatusNone) {
+        (void)hipGetLastError();
+        return hipSuccess;
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_stream_scratch_mutex);
+    StreamScratch *slot = nullptr;
+    for (int i = 0; i < g_stream_scratch_count; ++i) {
+        if (g_stream_scratch[i].dev == dev && g_stream_scratch[i].stream == stream) slot = &g_stream_scratch[i];
+    }
+    if (slot != nullptr && slot->bytes >= total) {
+        *out = slot->ptr;
+        return hipSuccess;
+    }
+    if (slot == nullptr) {
+        if (g_stream_scratch_count == kStreamScratchSlots) return hipSuccess;
+        slot = &g_stream_scratch[g_stream_scratch_count];
+        *slot = StreamScratch{dev, stream, nullptr, 0};
+        ++g_stream_scratch_count;
+    }
+    // grow: at least double, so a stream settles after a few calls
+    int64_t bytes = slot->bytes * 2 > total ? slot->bytes * 2 : total;
+    bytes = bytes < kStreamScratchMax ? bytes : kStreamScratchMax;
+    uint8_t *p = nullptr;
+    e = hipMallocAsync(reinterpret_cast<void **>(&p), static_cast<size_t>(bytes), stream);
+    if (e != hipSuccess) return e;
+    if (slot->ptr != nullptr) {
+        e = hipFreeAsync(slot->ptr, stream);
+        if (e != hipSuccess) {
+            (void)hipFreeAsync(p, stream);
+            return e;
+        }
+    }
+    slot->ptr = p;
+    slot->bytes = bytes;
+    *out = p;
+    return hipSuccess;
+}
+
+}  // namespace
+
 hipError_t ws_acquire(Workspace &ws, int64_t total, hipStream_t stream, uint8_t **out, bool *owned) {
     *owned = false;
     *out = nullptr;
@@ -97,7 +170,9 @@ hipError_t ws_acquire(Workspace &ws, int64_t total, hipStream_t stream, uint8_t 
         *out = ws.ptr;
         return hipSuccess;
     }
-    const hipError_t e = hipMallocAsync(reinterpret_cast<void **>(out), static_cast<size_t>(total), stream);
+    hipError_t e = stream_scratch(total, stream, out);
+    if (e != hipSuccess || *out != nullptr) return e;
+    e = hipMallocAsync(reinterpret_cast<void **>(out), static_cast<size_t>(total), stream);
     *owned = e == hipSuccess;
     return e;
 }

@@ -211,3 +211,57 @@ def test_workspace_calls_in_a_graph_replay_equal_eager(q4k):
         assert torch.equal(y16, ref[3]), f"replay {rep}: sixteen-token output differs"
         step()
         torch.cuda.synchronize()
+
+
+def test_plain_calls_reuse_per_stream_scratch(q4k):
+    """The calls made without a workspace keep one scratch buffer per stream:
+    calls alternating between two streams that run at the same time, a call
+    that needs more scratch than the stream's buffer holds (it grows) and a
+    smaller one after it all give the bits of the workspace form; a plain call
+    recorded into a HIP graph (which allocates for itself there) replays to
+    the eager result."""
+    import torch
+
+    cus = _cus()
+    k = 2048
+    nb = 16 * cus
+    print(f"[case] per-stream scratch n={nb} k={k}", flush=True)
+    w = to_dev(inputs.make_q4k(nb, k, config_id=93, tensor_id=7).reshape(-1))
+    xs = [to_dev(inputs.make_x(m, k, config_id=93, tensor_id=10 + i)) for i, m in enumerate((16, 40, 16, 64))]
+
+    def ref(x):
+        y = torch.empty((x.shape[0], nb), dtype=torch.float32, device="cuda")
+        ws = _workspace(q4k.gemv_batched_workspace_size(x.shape[0], nb, k))
+        q4k.gemv_batched_ws(w, x, ws, y=y)
+        torch.cuda.synchronize()
+        return y
+
+    refs = [ref(x) for x in xs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rnd in range(6):
+        for si, st in enumerate(streams):
+            i = (rnd + si) % len(xs)   # each stream walks the sizes: 16, 40 (grows), 16, 64 (grows), ...
+            y = torch.full((xs[i].shape[0], nb), float("nan"), dtype=torch.float32, device="cuda")
+            with torch.cuda.stream(st):
+                q4k.gemv_batched(w, xs[i], y=y)
+            outs.append((i, y))
+    for st in streams:
+        torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for i, y in outs:
+        assert torch.equal(y, refs[i]), f"plain call on size {xs[i].shape[0]} differs from the workspace form"
+    # a plain call inside a graph
+    yg = torch.empty((16, nb), dtype=torch.float32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q4k.gemv_batched(w, xs[0], y=yg)
+    for rep in range(3):
+        yg.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, refs[0]), f"replay {rep} of a plain call differs"
+        q4k.gemv_batched(w, xs[2], y=torch.empty_like(yg))   # eager work between replays
+        torch.cuda.synchronize()
