@@ -500,6 +500,23 @@ def warm_up(run_region, torch, stream, seconds=0.1):
         run_region()
 
 
+def _time_graph(fn, count, torch, stream):
+    """Mean time of one fn(i, s) when `count` of them are recorded into one HIP
+    graph (s: the capture stream) and the graph is replayed after a warm-up."""
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(count):
+            fn(i, None)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    warm_up(graph.replay, torch, stream)
+    a.record(stream)
+    graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return a.elapsed_time(b) / count * 1e-3
+
+
 def _time_launches(fn, torch, stream, steps, warmup):
     """Mean time of one fn(i) over `steps` back-to-back calls between two
     events on the launch stream, after a warm-up (warm_up)."""
@@ -543,11 +560,24 @@ def decode_blocks(q4k, inputs, torch, dev, stream, steps, warmup):
             q4k.gemv(w, x, y=y, n=n, stream=stream)
 
     t_four = _time_launches(four, torch, stream, steps, warmup)
+    # the same launches recorded into HIP graphs (device time, no host cost
+    # per call): one multi node against four gemv nodes per step
+    nl = max(200, copies)
+    g_multi = _time_graph(lambda i, s: q4k.gemv_multi(sets[i % copies], x, ys=ys, ns=ns, stream=s), nl, torch,
+                          stream)
+
+    def four_g(i, s):
+        for w, y, n in zip(sets[i % copies], ys, ns):
+            q4k.gemv(w, x, y=y, n=n, stream=s)
+
+    g_four = _time_graph(four_g, nl, torch, stream)
     abytes = nbytes + 4 * k + 4 * sum(ns)
     out["gdn_in_proj_0p8b"] = {"weight_bytes": nbytes, "multi_us": round(t_multi * 1e6, 3),
                                "multi_GB/s": round(abytes / t_multi / 1e9, 1),
                                "four_calls_us": round(t_four * 1e6, 3),
-                               "four_calls_GB/s": round(abytes / t_four / 1e9, 1)}
+                               "four_calls_GB/s": round(abytes / t_four / 1e9, 1),
+                               "multi_graph_us": round(g_multi * 1e6, 3),
+                               "four_calls_graph_us": round(g_four * 1e6, 3)}
     del sets
     n, k = inputs.SHAPES["down_9b"]
     w0 = inputs.make_q4k(n, k, config_id=6, tensor_id=1).reshape(-1)
