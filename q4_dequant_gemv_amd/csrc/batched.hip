@@ -30,7 +30,7 @@
 // The preparation kernel compares, per (half, token) block, the split's total
 // remainder E = sum |x - 2^e (hi + lo)| (each remainder exact in f32) with
 // S4, the sum of the block's |x| other than its four largest (through a lower
-// bound formed without cancellation, lane_group_rest_bound), and flags the
+// bound formed without cancellation, rest_bound_tiers), and flags the
 // block if E exceeds 2^-15 times that bound.  A
 // workgroup whose range holds a flagged block computes its whole tile in f32
 // instead (exact_tile: every weight dequantized on its own, every product
@@ -157,13 +157,11 @@ __global__ __launch_bounds__(256) void x_prep_kernel(const XT *x, uint8_t *__res
     const float tot = lane_group_sum<32>(part);
     round_sum = lane_group_sum<32>(round_sum);
     // a lower bound of the magnitude without the four largest: the sum of all
-    // minus four times the largest (here 1 <= largest < 2); the tighter one
+    // minus four times the largest (here 1 <= largest < 2); the tighter ones
     // only where that does not clear the rounding
     const float abs_sum = lane_group_sum<32>((mag[0] + mag[1]) + (mag[2] + mag[3]));
     const float amax_s = nz ? ldexpf(amax, -e) : 0.0f;
-    float rest = abs_sum - 4.0f * amax_s;
-    const bool clear = round_sum * 32768.0f <= rest;
-    if (__builtin_amdgcn_ballot_w64(!clear) != 0) rest = clear ? rest : lane_group_rest_bound<32>(mag);
+    const float rest = rest_bound_tiers<32>(mag, abs_sum - 4.0f * amax_s, round_sum * 32768.0f);
     if (!live) return;
     if (c == 0) flags[st * tpad + tok] = round_sum * 32768.0f > rest ? 1 : 0;
     uint8_t *blk = xc + (st * mt + tok / 16) * kTileStageBytes;

@@ -374,16 +374,15 @@ __device__ __forceinline__ void merge_top2_dpp(float &t1, float &t2) {
 }
 
 // For the non-negative values v (4 per lane) of an aligned group of W lanes
-// (W = 16 or 32): a lower bound on the sum of the group's values other than
-// its four largest, formed from non-negative terms only (no cancellation,
-// whatever the spread).  T is the second largest, over the lanes, of each
-// lane's second largest value: two lanes hold two values >= T each, so the
-// group's four largest are all >= T, and the sum of the values below T
-// leaves them all out.  Every lane of the group gets the bound.  (The lane
-// pairings are those of lane_group_sum; after each step both partners hold
-// the same pair, so the next step merges disjoint sets.)
+// (W = 16 or 32): a quick lower bound on the sum of the group's values other
+// than its four largest, formed from non-negative terms only.  T is the
+// second largest, over the lanes, of each lane's second largest value: two
+// lanes hold two values >= T each, so the group's four largest are all >= T,
+// and the sum of the values below T leaves them all out (with up to 4 + W - 2
+// values in all, so it can fall well below the sum without the four largest;
+// lane_group_rest_bound then gives that sum).
 template <int W>
-__device__ __forceinline__ float lane_group_rest_bound(const float (&v)[4]) {
+__device__ __forceinline__ float lane_group_rest_bound_quick(const float (&v)[4]) {
     static_assert(W == 16 || W == 32, "group width");
     const float p = fmaxf(v[0], v[1]), q = fminf(v[0], v[1]);
     const float r = fmaxf(v[2], v[3]), s = fminf(v[2], v[3]);
@@ -399,6 +398,87 @@ __device__ __forceinline__ float lane_group_rest_bound(const float (&v)[4]) {
     for (int b = 0; b < 4; ++b) below += v[b] < t2 ? v[b] : 0.0f;
     if constexpr (W == 16) return lane_group_sum<16>(below);
     else return lane_group_sum<32>(below);
+}
+
+// (a, b) becomes (max, min).
+__device__ __forceinline__ void order2(float &a, float &b) {
+    const float hi = fmaxf(a, b);
+    b = fminf(a, b);
+    a = hi;
+}
+
+// t becomes the four largest of t and u, both descending.  The maxima of
+// t[i] and u[3-i] are those four (a multiset), falling then rising; two
+// rounds of compare-exchange (a bitonic merge) sort them.
+__device__ __forceinline__ void merge_top4(float (&t)[4], const float (&u)[4]) {
+    float c0 = fmaxf(t[0], u[3]), c1 = fmaxf(t[1], u[2]), c2 = fmaxf(t[2], u[1]), c3 = fmaxf(t[3], u[0]);
+    order2(c0, c2);
+    order2(c1, c3);
+    order2(c0, c1);
+    order2(c2, c3);
+    t[0] = c0;
+    t[1] = c1;
+    t[2] = c2;
+    t[3] = c3;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void merge_top4_dpp(float (&t)[4]) {
+    const float u[4] = {dpp_mov<CTRL>(t[0]), dpp_mov<CTRL>(t[1]), dpp_mov<CTRL>(t[2]), dpp_mov<CTRL>(t[3])};
+    merge_top4(t, u);
+}
+
+// For the non-negative values v (4 per lane) of an aligned group of W lanes
+// (W = 16 or 32): a lower bound on the sum of the group's values other than
+// its four largest, formed from non-negative terms only (no cancellation,
+// whatever the spread).  Every lane's four values are sorted, then merged
+// with its partner's into the four largest of both, over the lane pairings
+// of lane_group_sum (after each step both partners hold the same four, so the
+// next step merges disjoint sets); every lane ends with the group's four
+// largest.  The values below the fourth largest, T, leave out the four
+// largest (and any value tied with T), so their sum is the bound; it equals
+// the sum without the four largest when no other value equals T.
+template <int W>
+__device__ __forceinline__ float lane_group_rest_bound(const float (&v)[4]) {
+    static_assert(W == 16 || W == 32, "group width");
+    float t[4] = {v[0], v[1], v[2], v[3]};
+    order2(t[0], t[1]);
+    order2(t[2], t[3]);
+    order2(t[0], t[2]);
+    order2(t[1], t[3]);
+    order2(t[1], t[2]);
+    merge_top4_dpp<0xb1>(t);   // quad_perm [1,0,3,2]
+    merge_top4_dpp<0x4e>(t);   // quad_perm [2,3,0,1]
+    merge_top4_dpp<0x141>(t);  // row_half_mirror
+    merge_top4_dpp<0x140>(t);  // row_mirror
+    if constexpr (W == 32) {
+        const float u[4] = {__shfl_xor(t[0], 16, kWave), __shfl_xor(t[1], 16, kWave), __shfl_xor(t[2], 16, kWave),
+                            __shfl_xor(t[3], 16, kWave)};
+        merge_top4(t, u);
+    }
+    float below = 0.0f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) below += v[b] < t[3] ? v[b] : 0.0f;
+    if constexpr (W == 16) return lane_group_sum<16>(below);
+    else return lane_group_sum<32>(below);
+}
+
+// A lower bound on the magnitude of a group (W lanes, four values each)
+// without its four largest, as tight as the test needs: `first` (the sum
+// minus four times the largest) where it is at least `need`, else the quick
+// bound where that is, else the exact one.  Each tier runs only in waves that
+// hold a group the previous one did not clear; a group's lanes agree on every
+// test, so the lane exchanges inside each bound stay within active groups.
+template <int W>
+__device__ __forceinline__ float rest_bound_tiers(const float (&mag)[4], float first, float need) {
+    float rest = first;
+    if (__builtin_amdgcn_ballot_w64(need > rest) != 0) {
+        if (need > rest) rest = lane_group_rest_bound_quick<W>(mag);
+        if (__builtin_amdgcn_ballot_w64(need > rest) != 0) {
+            if (need > rest) rest = lane_group_rest_bound<W>(mag);
+        }
+    }
+    return rest;
 }
 
 }  // namespace q4k

@@ -22,7 +22,7 @@
 // therefore compares, per group, the total rounding E = sum_k |x_k - X_k
 // 2^(e-21)| with S4, the sum of the group's |x| other than its four largest
 // (what is left of sum |w x| if the weights of up to four outliers are zero),
-// through a lower bound formed without cancellation (lane_group_rest_bound).
+// through a lower bound formed without cancellation (rest_bound_tiers).
 // A group with E > 2^-15 times that bound is flagged, and a wave that meets a
 // flagged group
 // multiplies every weight in f32 instead (exact_group_dot): the weight is
@@ -32,6 +32,8 @@
 // result (S4 is at least the bound).  Both sums are formed from terms exact
 // in f32 (their own rounding is a few 2^-24).
 #pragma once
+
+#include <type_traits>
 
 #include <float.h>
 #include <math.h>
@@ -62,8 +64,11 @@ struct XLoaded {
 };
 
 // T is float or _Float16 (f16 activations are widened exactly).
-template <int BLOCK, int NCH, typename T>
+// COHERENT: device-coherent loads (agent scope), for activations that other
+// workgroups of the same launch wrote with device-coherent stores.
+template <int BLOCK, int NCH, typename T, bool COHERENT = false>
 __device__ __forceinline__ XLoaded<NCH> load_x(const T *x, int ngroups) {
+    static_assert(!COHERENT || std::is_same_v<T, float>, "coherent loads of f32 activations");
     XLoaded<NCH> f;
     const int total = ngroups * 16;
     // every load is issued (items past the end re-read item 0) so that no
@@ -73,7 +78,13 @@ __device__ __forceinline__ XLoaded<NCH> load_x(const T *x, int ngroups) {
         const int it = static_cast<int>(threadIdx.x) + c * BLOCK;
         const T *p = x + 4 * (it < total ? it : 0);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) f.v[c][b] = static_cast<float>(p[b]);
+        for (int b = 0; b < 4; ++b) {
+            if constexpr (COHERENT) {
+                f.v[c][b] = __hip_atomic_load(p + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                f.v[c][b] = static_cast<float>(p[b]);
+            }
+        }
     }
     return f;
 }
@@ -136,14 +147,13 @@ __device__ __forceinline__ void prepare_x(const XLoaded<NCH> &f, int ngroups, XG
         }
         round_sum = lane_group_sum<16>(round_sum);
         // The magnitude without the four largest is at least the sum of all
-        // minus four times the largest (here 2^21 <= largest < 2^22): when
-        // that already clears the rounding, the tighter bound is not needed;
-        // otherwise the waves holding such a group compute it.
+        // minus four times the largest (here 2^21 <= largest < 2^22); where
+        // that does not clear the rounding, the waves holding such a group
+        // form the quick bound, and where that does not either, the exact one
+        // (rest_bound_tiers).
         const float abs_sum = lane_group_sum<16>((mag[0] + mag[1]) + (mag[2] + mag[3]));
         const float amax_s = (finite && !zero) ? ldexpf(amax, sexp) : 0.0f;
-        const bool clear = round_sum * 32768.0f <= abs_sum - 4.0f * amax_s;
-        float rest = abs_sum - 4.0f * amax_s;
-        if (__builtin_amdgcn_ballot_w64(!clear) != 0) rest = clear ? rest : lane_group_rest_bound<16>(mag);
+        const float rest = rest_bound_tiers<16>(mag, abs_sum - 4.0f * amax_s, round_sum * 32768.0f);
         // v_perm_b32: byte i of the result is byte sel_i of {first (bytes 4-7), second (bytes 0-3)}
         const uint32_t t01 = __builtin_amdgcn_perm(bx[1], bx[0], 0x05010400u);  // bytes 0 and 1 of values 0, 1
         const uint32_t t23 = __builtin_amdgcn_perm(bx[3], bx[2], 0x05010400u);
