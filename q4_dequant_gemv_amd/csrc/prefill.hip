@@ -15,20 +15,21 @@
 //     codes (1024 + sc*q as an f16 bit pattern) and one packed f16 subtract.
 //   * Per super-block s the f32 tile P_s = sum_k x * sc*q (8 MFMA steps of 32
 //     weights) is finished as
-//         acc += d_s * P_s - dmin_s * Q_s,   Q_s = sum_j m_j * (sum of x over j),
+//         acc = fma(-dmin_s, Q_s, fma(d_s, P_s, acc)),   Q_s = sum_j m_j * (sum of x over j),
 //     where Q_s is one 16x16x16 MFMA: A holds the eight sub-block sums of each
 //     token (divided by 32 so they stay inside the f16 range) as hi + lo f16
 //     parts, B the eight six-bit mins (exact).
 //
 // Data flow.  A preparation kernel writes the activations once per call into
 // scratch in the lane order of the MFMA operand (and the sub-block sums).  A
-// workgroup of 4 waves owns a 128-row x 128-token tile; each wave a 64 x 64
-// quarter (4 x 4 tiles of 16 x 16).  K is walked in half super-blocks: the
-// workgroup copies the next half super-block of activations (32 KB) and, every
-// other step, the next super-block of its 128 weight rows (18 KB) into LDS
-// with direct-to-LDS buffer loads while the matrix cores work on the current
-// one (double-buffered, one barrier per step).  Every output is computed by
-// one lane in a fixed order: results are bitwise reproducible.
+// workgroup of 8 waves owns a 128-row x 128-token tile; each wave 16 rows x
+// 128 tokens (8 tiles of 16 x 16), two waves per SIMD.  K is walked in half
+// super-blocks: the workgroup copies the next half super-block of activations
+// (32 KB) and, every other step, the next super-block of its 128 weight rows
+// (18 KB) into LDS with direct-to-LDS buffer loads while the matrix cores work
+// on the current one (three buffers of each, one barrier per step).  Every
+// output is computed by one lane in a fixed order: results are bitwise
+// reproducible.
 #include <type_traits>
 
 #include "launch.h"
@@ -50,20 +51,24 @@ constexpr int kAStage = 8 * 4 * 64 * 16;      // [token tile][MFMA step][lane][8
 constexpr int kWStage = kPfTile * kBlockBytes;  // one super-block of 128 rows = 18 KB
 constexpr int kMinBlock = 8 * 64 * 8;         // [token tile][lane][4 f16] = 4 KB per super-block
 constexpr int kWPieces = kWStage / 16;        // 1152 16-byte pieces = 18 wave-wide copies
+constexpr int kWCopies = kWPieces / 64;
 #ifndef Q4K_PREFILL_RT
-#define Q4K_PREFILL_RT 2
+#define Q4K_PREFILL_RT 1
 #endif
 #ifndef Q4K_PREFILL_TT
 #define Q4K_PREFILL_TT 8
 #endif
+// waves of a workgroup: RT x TT tiles each cover the 128 x 128 tile
+template <int RT, int TT>
+constexpr int pf_waves() { return (kPfTile / (16 * RT)) * (kPfTile / (16 * TT)); }
+
 constexpr int kPfRT = Q4K_PREFILL_RT;  // row tiles per wave
 constexpr int kPfTT = Q4K_PREFILL_TT;  // token tiles per wave
+constexpr int kPfWaves = pf_waves<kPfRT, kPfTT>();
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8): wait for vector memory down to N in flight, nothing else
 constexpr int wait_vm(int nvm) { return (nvm & 15) | ((nvm >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kWaitVm0 = wait_vm(0);
-constexpr int kWaitVm8 = wait_vm(8);
-constexpr int kWStagePad = 20 * 1024;  // 18 KB of weights + the two padding copies
 
 __device__ __forceinline__ half8_t as_half8(u32x4_t v) { return __builtin_bit_cast(half8_t, v); }
 
@@ -116,25 +121,31 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(const _Float16 *__res
 
 // ---- the matrix-core kernel ---------------------------------------------------
 // Each wave owns RT row tiles x TT token tiles of 16 x 16; (128/16/RT) x
-// (128/16/TT) = 4 waves cover the 128 x 128 tile.  Building a B operand costs
-// about 20 vector instructions per 8 weights and each is used TT times; each
-// A operand is read from LDS by every wave with those tokens.  RT = 2, TT = 8
-// builds every B operand once per workgroup and keeps the vector units under
-// the matrix cores' time.  With ksplit > 1 the workgroup covers super-blocks
+// (128/16/TT) waves (4, 8 or 16) cover the 128 x 128 tile.  Building a B
+// operand costs about 16 vector instructions per 8 weights and each is used
+// TT times; each A operand is read from LDS by every wave with those tokens
+// and used RT times.  RT = 1, TT = 8 builds every B operand once per workgroup
+// and gives two waves per SIMD (160 registers each), so one wave's operand
+// building overlaps the other's matrix-core work: 12-16 % faster than four
+// waves of RT = 2 at 512 and 2048 tokens, although each activation fragment
+// is read from LDS twice as often.  With ksplit > 1 the workgroup covers super-blocks
 // [ks*nsb/ksplit, (ks+1)*nsb/ksplit) and writes its f32 partial tile to
 // part[ks] instead of y (added up in a fixed order by prefill_reduce_kernel).
 template <int V>
 using ic = std::integral_constant<int, V>;
 
 template <typename YT, int RT, int TT>
-__global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(const uint8_t *__restrict__ w,
+__global__ __launch_bounds__((64 * pf_waves<RT, TT>()), 1) void prefill_mfma_kernel(const uint8_t *__restrict__ w,
                                                               const uint8_t *__restrict__ xa,
                                                               const uint8_t *__restrict__ xs, YT *__restrict__ y,
                                                               float *__restrict__ part, int64_t m, int64_t n,
                                                               int64_t k, int64_t row_bytes, int nblocks, int nrb,
                                                               int ksplit) {
     constexpr int WR = kPfTile / (16 * RT);  // waves along the rows
-    static_assert(WR * (kPfTile / (16 * TT)) == 4, "four waves cover the tile");
+    constexpr int NW = pf_waves<RT, TT>();
+    static_assert(NW == 4 || NW == 8 || NW == 16, "4, 8 or 16 waves cover the tile");
+    constexpr int kAPer = (kAStage / 1024) / NW;      // activation copies per wave per step
+    constexpr int kWPer = (kWCopies + NW - 1) / NW;   // weight copies per wave per super-block
     // Three buffers each for the activations (one per step, copied two steps
     // ahead) and the weights (one per super-block, copied one super-block
     // ahead).  Every buffer is its own array and every access names it at
@@ -142,7 +153,9 @@ __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(const uint8_t *__r
     // compiler can tell a copy in flight into one buffer from reads of
     // another and adds no waits of its own.
     __shared__ __align__(16) uint8_t a0[kAStage], a1[kAStage], a2[kAStage];
-    __shared__ __align__(16) uint8_t w0[kWStagePad], w1[kWStagePad], w2[kWStagePad];
+    __shared__ __align__(16) uint8_t w0[kWStage], w1[kWStage], w2[kWStage];
+    // where the copies past the 18 of a super-block land (read by nobody)
+    __shared__ __align__(16) uint8_t wpad[1024];
     uint8_t *const abuf[3] = {a0, a1, a2};
     uint8_t *const wbuf[3] = {w0, w1, w2};
     const int lane = threadIdx.x & 63;
@@ -174,19 +187,19 @@ __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(const uint8_t *__r
             xa + (static_cast<int64_t>(2 * sb_begin + h) * nblocks + tbk) * kAStage, h < 2 * nsb ? kAStage : 0);
         lds_u8 *base = (lds_u8 *)dst;  // generic -> LDS address space
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = wave * 8 + i;
+        for (int i = 0; i < kAPer; ++i) {
+            const int c = wave * kAPer + i;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, reinterpret_cast<lds_void *>(base + c * 1024), 16,
                                                      c * 1024 + lane * 16, 0, 0, 0);
         }
     };
     auto dma_w = [&](int s, uint8_t *dst) {
         lds_u8 *base = (lds_u8 *)dst;
-        // 18 copies of 64 x 16 bytes per super-block, 5 per wave: the last two
-        // read past the descriptor (zeros) into the padding
+        // 18 copies of 64 x 16 bytes per super-block, kWPer per wave: the
+        // ones past the 18th read past the descriptor (zeros) into wpad
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            const int ii = wave + 4 * i;
+        for (int i = 0; i < kWPer; ++i) {
+            const int ii = wave + NW * i;
             const int p = ii * 64 + lane;
             const int row = p / 9;
             const int pc = p % 9;
@@ -195,8 +208,8 @@ __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(const uint8_t *__r
                                            static_cast<uint32_t>(sb_begin + s) * kBlockBytes +
                                            static_cast<uint32_t>(pc * 16)
                                      : 0x80000000u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, reinterpret_cast<lds_void *>(base + ii * 1024), 16, off, 0,
-                                                     0, 0);
+            lds_u8 *dst_c = ii < kWCopies ? base + ii * 1024 : (lds_u8 *)wpad;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, reinterpret_cast<lds_void *>(dst_c), 16, off, 0, 0, 0);
         }
     };
     // a barrier without a memory fence: the waits before it are explicit
@@ -301,17 +314,18 @@ __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(const uint8_t *__r
             // min-term loads and the next super-block's weights (issued a
             // super-block ago); after them only this step's copies (8 + 5).
             if (half == 0) {
-                __builtin_amdgcn_s_waitcnt(wait_vm(TT + 8));
+                __builtin_amdgcn_s_waitcnt(wait_vm(TT + kAPer));
             } else {
-                __builtin_amdgcn_s_waitcnt(wait_vm(8 + 5));
-                // finish super-block s: acc += d * P - dmin * Q
+                __builtin_amdgcn_s_waitcnt(wait_vm(kAPer + kWPer));
+                // finish super-block s: acc = fma(-dmin, Q, fma(d, P, acc))
 #pragma unroll
                 for (int tt = 0; tt < TT; ++tt) {
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) {
                         const float4_t q = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[tt], qb[rt], zero, 0, 0, 0);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[rt][tt][r] += dd[rt] * P[rt][tt][r] - dm[rt] * q[r];
+                        for (int r = 0; r < 4; ++r)
+                            acc[rt][tt][r] = fmaf(-dm[rt], q[r], fmaf(dd[rt], P[rt][tt][r], acc[rt][tt][r]));
                     }
                 }
             }
@@ -324,8 +338,8 @@ __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(const uint8_t *__r
     dma_a(0, a0);
     dma_a(1, a1);
     // step 0's activations and super-block 0's weights have landed (step 1's
-    // activations may still fly: 8 copies)
-    __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    // activations may still fly)
+    __builtin_amdgcn_s_waitcnt(wait_vm(kAPer));
     barrier();
     for (int s = 0; s < nsb; s += 3) {
         super_block(ic<0>{}, s);
@@ -408,10 +422,10 @@ hipError_t launch_prefill(const uint8_t *w, const _Float16 *x, void *y, bool y_f
         const int64_t rb = (k / kBlockWeights) * kBlockBytes;
         const int nb = static_cast<int>(nblocks), nr = static_cast<int>(nrb), ksp = static_cast<int>(ksplit);
         if (y_f16) {
-            hipLaunchKernelGGL((prefill_mfma_kernel<_Float16, kPfRT, kPfTT>), grid, dim3(256), 0, stream, w, xa, xs,
+            hipLaunchKernelGGL((prefill_mfma_kernel<_Float16, kPfRT, kPfTT>), grid, dim3(64 * kPfWaves), 0, stream, w, xa, xs,
                                static_cast<_Float16 *>(y), part, m, n, k, rb, nb, nr, ksp);
         } else {
-            hipLaunchKernelGGL((prefill_mfma_kernel<float, kPfRT, kPfTT>), grid, dim3(256), 0, stream, w, xa, xs,
+            hipLaunchKernelGGL((prefill_mfma_kernel<float, kPfRT, kPfTT>), grid, dim3(64 * kPfWaves), 0, stream, w, xa, xs,
                                static_cast<float *>(y), part, m, n, k, rb, nb, nr, ksp);
         }
         e = hipGetLastError();
