@@ -1238,6 +1238,9 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const void *x, co
 #ifndef Q4K_SMALL_NB
 #define Q4K_SMALL_NB 2
 #endif
+#ifndef Q4K_SWIGLU_WIDE_ROWS
+#define Q4K_SWIGLU_WIDE_ROWS 8192
+#endif
 #ifndef Q4K_SWIGLU_BLOCK
 #define Q4K_SWIGLU_BLOCK 512
 #endif
@@ -1288,6 +1291,16 @@ hipError_t dispatch_lpr(const GemvJob *jobs, int count, const uint8_t *wu, const
     constexpr bool kStaged = F::kStaged;
     if constexpr (SWIGLU) {
         constexpr int NB = kStaged ? 1 + Q4K_SWIGLU_SLOTS : Q4K_SWIGLU_NB;
+        if constexpr (LPR == 64) {
+            // many rows of a whole wave each: one 12-wave workgroup per CU
+            // (2 % faster at 12288 rows; slower with few rows, where more,
+            // smaller workgroups spread the rows better)
+            int64_t rows = 0;
+            for (int i = 0; i < count; ++i) rows += jobs[i].n;
+            if (rows >= Q4K_SWIGLU_WIDE_ROWS) {
+                return launch_fast<F, XT, YT, LPR, true, NB, 768, 3>(jobs, count, wu, x, k, stream);
+            }
+        }
         return launch_fast<F, XT, YT, LPR, true, NB, Q4K_SWIGLU_BLOCK, Q4K_SWIGLU_MINW>(jobs, count, wu, x, k, stream);
     } else {
         int64_t bytes = 0;
