@@ -453,7 +453,7 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
 
     // activations first, then the first rows' weights: waiting for the
     // activations (in issue order) then leaves the weight loads in flight
-    constexpr int kXChunks = (LPR * 16 + BLOCK - 1) / BLOCK;
+    constexpr int kXChunks = x_chunks(LPR, BLOCK);
     const int64_t xstride = static_cast<int64_t>(ngroups) * 64;
     XLoaded<kXChunks> xl[kTok];
 #pragma unroll
@@ -750,9 +750,12 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
     // block iterations b = blockIdx.x + c * gridDim.x cover rows b*R .. b*R+R-1;
     // the host keeps gridDim.x <= the number of block iterations
     const int64_t nbi = (n + R - 1) / R;
-    const int my_iters = static_cast<int>((nbi - 1 - blockIdx.x) / gridDim.x) + 1;
+    // the grid size once, in a scalar register (the loop would otherwise
+    // reload it from the argument segment every iteration)
+    const int nblk = __builtin_amdgcn_readfirstlane(static_cast<int>(gridDim.x));
+    const int my_iters = static_cast<int>((nbi - 1 - blockIdx.x) / nblk) + 1;
     auto row_of = [&](int c, int r) -> int64_t {
-        return (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(c) * gridDim.x) * R + r;
+        return (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(c) * nblk) * R + r;
     };
     auto issue = [&](RowLoads<F, NMAT> &b, int c) {
         const int64_t row = row_of(c, rslot);
@@ -776,7 +779,7 @@ __global__ __launch_bounds__(64 * S * R, MIN_WAVES) void gemv_split_kernel(const
     // selection come from g)
     const typename F::Lane gs = F::lane(lane, kWave, 0u);
 
-    constexpr int kXChunks = (S * kWave * 16 + BLOCK - 1) / BLOCK;
+    constexpr int kXChunks = x_chunks(S * kWave, BLOCK);
     const int64_t xstride = static_cast<int64_t>(ngroups) * 64;
     XLoaded<kXChunks> xl[MT];
 #pragma unroll

@@ -22,10 +22,9 @@
 // therefore compares, per group, the total rounding E = sum_k |x_k - X_k
 // 2^(e-21)| with S4, the sum of the group's |x| other than its four largest
 // (what is left of sum |w x| if the weights of up to four outliers are zero),
-// through a lower bound formed without cancellation (rest_bound_tiers).
-// A group with E > 2^-15 times that bound is flagged, and a wave that meets a
-// flagged group
-// multiplies every weight in f32 instead (exact_group_dot): the weight is
+// through a lower bound formed without cancellation (quad_rest_bound).  A
+// group with E > 2^-15 times that bound is flagged, and a wave that meets a
+// flagged group multiplies every weight in f32 instead (exact_group_dot): the weight is
 // dequantized as the dequant kernel does and each product w * x is rounded
 // once, so every activation keeps its full precision.  On the integer path a
 // group's rounding therefore adds at most 2^-15 * max_k |w_k| * S4 to a row's
@@ -51,16 +50,22 @@ struct XGroup {
 };
 static_assert(sizeof(XGroup) == 208, "XGroup layout");
 
-// Converts x[0 .. 64*ngroups) into XGroups, 16 threads per group, 4
-// activations per thread.  BLOCK is a multiple of 64, so the 16 threads of a
-// group are 16 aligned lanes of one wave and are either all active or all not.
-// The activations are loaded first (load_x) so that a kernel can issue them
-// ahead of its weight loads: waits are counted in issue order, so waiting for
-// the activations then leaves the weight loads in flight.  NCH covers
-// ngroups*16 <= NCH*BLOCK.
+// Converts x[0 .. 64*ngroups) into XGroups, 4 threads per group, 16
+// consecutive activations per thread (an item: item it holds activations
+// 16*it .. 16*it+15, the quarter it & 3 of group it >> 2).  BLOCK is a
+// multiple of 64, so the 4 threads of a group are 4 aligned lanes (a quad) of
+// one wave and are either all active or all not.  The activations are loaded
+// first (load_x) so that a kernel can issue them ahead of its weight loads:
+// waits are counted in issue order, so waiting for the activations then
+// leaves the weight loads in flight.  NCH covers ngroups*4 <= NCH*BLOCK
+// (x_chunks).
+constexpr int kXItem = 16;  // activations per thread and chunk
+
+constexpr int x_chunks(int max_groups, int block) { return (max_groups * 4 + block - 1) / block; }
+
 template <int NCH>
 struct XLoaded {
-    float v[NCH][4];
+    float v[NCH][kXItem];
 };
 
 // T is float or _Float16 (f16 activations are widened exactly).
@@ -70,15 +75,15 @@ template <int BLOCK, int NCH, typename T, bool COHERENT = false>
 __device__ __forceinline__ XLoaded<NCH> load_x(const T *x, int ngroups) {
     static_assert(!COHERENT || std::is_same_v<T, float>, "coherent loads of f32 activations");
     XLoaded<NCH> f;
-    const int total = ngroups * 16;
+    const int total = ngroups * 4;
     // every load is issued (items past the end re-read item 0) so that no
     // load sits in a branch; the unused values are dropped afterwards
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int it = static_cast<int>(threadIdx.x) + c * BLOCK;
-        const T *p = x + 4 * (it < total ? it : 0);
+        const T *p = x + kXItem * (it < total ? it : 0);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < kXItem; ++b) {
             if constexpr (COHERENT) {
                 f.v[c][b] = __hip_atomic_load(p + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             } else {
@@ -89,87 +94,159 @@ __device__ __forceinline__ XLoaded<NCH> load_x(const T *x, int ngroups) {
     return f;
 }
 
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Maximum over the quads of unsigned values (DPP, no LDS).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+    return umax(static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xf, 0xf, true)), v);
+}
+
+// For the 64 non-negative values of a group (16 per lane of a quad): a lower
+// bound on the sum of the values other than the four largest, formed from
+// non-negative terms only (no cancellation, whatever the spread).  Each lane
+// keeps the four largest of its values (sorted runs of four, merged), the
+// quad's lanes merge theirs over the lane pairings of lane_group_sum (after
+// each step both partners hold the same four, so the next step merges
+// disjoint sets), and every lane ends with the group's four largest.  The
+// values below the fourth largest, T, leave out the four largest (and any
+// value tied with T), so their sum is the bound; it equals the sum without
+// the four largest when no other value equals T.
+__device__ __forceinline__ float quad_rest_bound(const float (&v)[kXItem]) {
+    float t[4];
+#pragma unroll
+    for (int r = 0; r < kXItem / 4; ++r) {
+        float u[4] = {v[4 * r], v[4 * r + 1], v[4 * r + 2], v[4 * r + 3]};
+        order2(u[0], u[1]);
+        order2(u[2], u[3]);
+        order2(u[0], u[2]);
+        order2(u[1], u[3]);
+        order2(u[1], u[2]);
+        if (r == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t[i] = u[i];
+        } else {
+            merge_top4(t, u);
+        }
+    }
+    merge_top4_dpp<0xb1>(t);  // quad_perm [1,0,3,2]
+    merge_top4_dpp<0x4e>(t);  // quad_perm [2,3,0,1]
+    float below = 0.0f;
+#pragma unroll
+    for (int b = 0; b < kXItem; ++b) below += v[b] < t[3] ? v[b] : 0.0f;
+    return lane_group_sum<4>(below);
+}
+
 // Converts the loaded activations to XGroups.  A group's `inexact` is 1 if
-// its total rounding exceeds 2^-15 of its magnitude without its four largest
-// (see above).
-// Non-finite groups are not flagged (their results are NaN on either path).
+// its total rounding E exceeds 2^-15 of S4, its magnitude without its four
+// largest (see above).  Non-finite groups are not flagged (their results are
+// NaN on either path, whatever their integers).  Per chunk:
+//  - the largest magnitude is taken on the bit patterns of |x| (for
+//    non-negative floats integer order is numeric order, and every NaN
+//    pattern lies above infinity's);
+//  - X = rint(x * 2^(21-e)) comes from one addition of 1.5 * 2^23: the sum
+//    lies in [2^23, 2^24], where the spacing of floats is 1, so it is rounded
+//    to the nearest integer, ties to even, as rint does, and its bit pattern
+//    is 0x4B400000 + X;
+//  - the lower bound on S4 is first the sum of the magnitudes less four times
+//    the largest (no sort).  E is at most 64 * 1/2 = 2^5 units of 2^(e-21), so
+//    where that bound reaches 2^20 units the group passes whatever E is, and
+//    only waves holding a group below it form E and, where E * 2^15 exceeds
+//    the first bound, the exact one (quad_rest_bound).
 template <int BLOCK, int NCH>
 __device__ __forceinline__ void prepare_x(const XLoaded<NCH> &f, int ngroups, XGroup *__restrict__ xg) {
-    const int total = ngroups * 16;
+    const int total = ngroups * 4;
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int it = static_cast<int>(threadIdx.x) + c * BLOCK;
-        if (it >= total) break;
-        const int j = it >> 4;
-        const int half = (it >> 3) & 1;
-        const int i = it & 7;
-        float v[4];
-        float amax = 0.0f;
+        if (it >= total) break;  // whole quads leave together
+        uint32_t mb = 0;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            v[b] = f.v[c][b];
-            float a = fabsf(v[b]);
-            a = (a <= FLT_MAX) ? a : INFINITY;  // NaN counts as non-finite
-            amax = fmaxf(amax, a);
+        for (int b = 0; b < kXItem; ++b) mb = umax(mb, __float_as_uint(f.v[c][b]) & 0x7fffffffu);
+        mb = dpp_max_u32<0xb1>(mb);
+        mb = dpp_max_u32<0x4e>(mb);
+        const bool finite = mb < 0x7f800000u;
+        const bool zero = mb == 0u;
+        const bool live = finite && !zero;
+        const float amax = __uint_as_float(mb);
+        const int e = __builtin_amdgcn_frexp_expf(amax) - 1;  // ilogb of a finite non-zero amax
+        const int sexp = live ? 21 - e : 0;
+        const float scale = !finite ? NAN : (zero ? 0.0f : ldexpf(1.0f, e - 21));
+        const float amax_s = live ? ldexpf(amax, sexp) : 0.0f;
+        // v * 2^sexp is exact in f32 (a group that is not live keeps its
+        // values: zeros give X = 0, and a non-finite group's integers are
+        // never used, its scale being NaN)
+        float sv[kXItem];
+        uint32_t bx[kXItem];
+#pragma unroll
+        for (int b = 0; b < kXItem; ++b) {
+            sv[b] = ldexpf(f.v[c][b], sexp);
+            bx[b] = __float_as_uint(sv[b] + kMagic) - (0x4B400000u - 0x808080u);
         }
-        amax = lane_group_max<16>(amax);  // DPP inside the 16-lane row: no LDS round trip
-        const bool finite = amax <= FLT_MAX;
-        const bool zero = amax == 0.0f;
-        int sexp = 0;
-        float scale = 0.0f;
-        if (!finite) {
-            scale = NAN;
-        } else if (!zero) {
-            const int e = ilogbf(amax);
-            sexp = 21 - e;
-            scale = ldexpf(1.0f, e - 21);
+        float asum[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            asum[r] = (fabsf(sv[4 * r]) + fabsf(sv[4 * r + 1])) + (fabsf(sv[4 * r + 2]) + fabsf(sv[4 * r + 3]));
         }
+        const float first = lane_group_sum<4>((asum[0] + asum[1]) + (asum[2] + asum[3])) - 4.0f * amax_s;
+        uint32_t flag = 0u;
+        const bool quick = !live || first >= 1048576.0f;
+        if (__builtin_amdgcn_ballot_w64(!quick) != 0) {
+            // rounding and magnitudes in units of 2^(e-21)
+            float round_sum = 0.0f;
+            float mag[kXItem];
+#pragma unroll
+            for (int b = 0; b < kXItem; ++b) {
+                const float r = (sv[b] + kMagic) - kMagic;  // rint(sv), exactly
+                round_sum += fabsf(sv[b] - r);
+                mag[b] = fabsf(sv[b]);
+            }
+            const float need = lane_group_sum<4>(round_sum) * 32768.0f;
+            float rest = first;
+            if (__builtin_amdgcn_ballot_w64(live && need > rest) != 0) {
+                const float exact = quad_rest_bound(mag);
+                if (need > rest) rest = exact;
+            }
+            flag = live && need > rest ? 1u : 0u;
+        }
+        const int j = it >> 2;
+        const int q = it & 3;
+        const int half = q >> 1;
         // Balanced digits by a bias: with X = X2*2^16 + X1*2^8 + X0 and every
         // Xj in [-128, 127], byte j of B = X + 0x808080 is Xj + 128 (B stays
-        // below 2^24), so gathering byte j of the four values into one dword
-        // (two rounds of byte permutes) and flipping each byte's top bit
-        // gives the four Xj as signed bytes.
-        uint32_t bx[4];
-        int s = 0;
-        // rounding and magnitudes in units of 2^(e-21)
-        float round_sum = 0.0f;
-        float mag[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            // v * 2^sexp and its distance to the nearest integer are exact in f32
-            const float sv = (finite && !zero) ? ldexpf(v[b], sexp) : 0.0f;
-            const float r = rintf(sv);
-            const int X = static_cast<int>(r);
-            round_sum += fabsf(sv - r);
-            mag[b] = fabsf(sv);
-            s += X;
-            bx[b] = static_cast<uint32_t>(X + 0x808080);
-        }
-        round_sum = lane_group_sum<16>(round_sum);
-        // The magnitude without the four largest is at least the sum of all
-        // minus four times the largest (here 2^21 <= largest < 2^22); where
-        // that does not clear the rounding, the waves holding such a group
-        // form the quick bound, and where that does not either, the exact one
-        // (rest_bound_tiers).
-        const float abs_sum = lane_group_sum<16>((mag[0] + mag[1]) + (mag[2] + mag[3]));
-        const float amax_s = (finite && !zero) ? ldexpf(amax, sexp) : 0.0f;
-        const float rest = rest_bound_tiers<16>(mag, abs_sum - 4.0f * amax_s, round_sum * 32768.0f);
+        // below 2^24), so gathering byte j of four values into one dword (two
+        // rounds of byte permutes) and flipping each byte's top bit gives the
+        // four Xj as signed bytes.
         // v_perm_b32: byte i of the result is byte sel_i of {first (bytes 4-7), second (bytes 0-3)}
-        const uint32_t t01 = __builtin_amdgcn_perm(bx[1], bx[0], 0x05010400u);  // bytes 0 and 1 of values 0, 1
-        const uint32_t t23 = __builtin_amdgcn_perm(bx[3], bx[2], 0x05010400u);
-        const uint32_t u01 = __builtin_amdgcn_perm(bx[1], bx[0], 0x07030602u);  // bytes 2 and 3 of values 0, 1
-        const uint32_t u23 = __builtin_amdgcn_perm(bx[3], bx[2], 0x07030602u);
-        const uint32_t l0 = __builtin_amdgcn_perm(t23, t01, 0x05040100u) ^ 0x80808080u;
-        const uint32_t l1 = __builtin_amdgcn_perm(t23, t01, 0x07060302u) ^ 0x80808080u;
-        const uint32_t l2 = __builtin_amdgcn_perm(u23, u01, 0x05040100u) ^ 0x80808080u;
-        s = lane_group_sum_int<8>(s);
-        xg[j].limb[half][0][i] = l0;
-        xg[j].limb[half][1][i] = l1;
-        xg[j].limb[half][2][i] = l2;
-        if (i == 0) xg[j].sx[half] = s;
-        if ((it & 15) == 0) {
+        uint4 limb[3];
+        uint32_t *l0 = &limb[0].x, *l1 = &limb[1].x, *l2 = &limb[2].x;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t *b4 = &bx[4 * d];
+            const uint32_t t01 = __builtin_amdgcn_perm(b4[1], b4[0], 0x05010400u);  // bytes 0, 1 of values 0, 1
+            const uint32_t t23 = __builtin_amdgcn_perm(b4[3], b4[2], 0x05010400u);
+            const uint32_t u01 = __builtin_amdgcn_perm(b4[1], b4[0], 0x07030602u);  // bytes 2, 3 of values 0, 1
+            const uint32_t u23 = __builtin_amdgcn_perm(b4[3], b4[2], 0x07030602u);
+            l0[d] = __builtin_amdgcn_perm(t23, t01, 0x05040100u) ^ 0x80808080u;
+            l1[d] = __builtin_amdgcn_perm(t23, t01, 0x07060302u) ^ 0x80808080u;
+            l2[d] = __builtin_amdgcn_perm(u23, u01, 0x05040100u) ^ 0x80808080u;
+        }
+        // sum of the sixteen X (the biases removed; exact in 32-bit arithmetic),
+        // then over the two lanes of the sub-block
+        uint32_t bsum = 0u;
+#pragma unroll
+        for (int b = 0; b < kXItem; ++b) bsum += bx[b];
+        bsum -= static_cast<uint32_t>(kXItem) * 0x808080u;
+        const int s = dpp_add_int<0xb1>(static_cast<int>(bsum));
+        uint4 *dst = reinterpret_cast<uint4 *>(&xg[j].limb[half][0][4 * (q & 1)]);
+        dst[0] = limb[0];  // limb l of the half starts 8 dwords after limb l-1
+        dst[2] = limb[1];
+        dst[4] = limb[2];
+        if ((q & 1) == 0) xg[j].sx[half] = s;
+        if (q == 0) {
             xg[j].scale = scale;
-            xg[j].inexact = round_sum * 32768.0f > rest ? 1u : 0u;
+            xg[j].inexact = flag;
         }
     }
 }
@@ -224,14 +301,29 @@ __device__ __forceinline__ void decode_group(const uint4 &hdr, const uint4 &qa, 
 
 // sum over the group of w*x, in units of the activation scale (multiply the
 // result by the group's `scale`).  XS is XGroup (LDS) or XRegs (registers).
+// v_dot4_i32_i8 with a zero accumulator (for the first product of a chain:
+// the builtin with 0 becomes a move of 0 and the accumulate-in-place form)
+__device__ __forceinline__ int sdot4_first(int a, int b) {
+    int r;
+    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 template <typename XS>
 __device__ __forceinline__ float group_dot(const GroupCodes &c, const XS &xs) {
     // The code and min products are rounded separately (no FMA), so a
     // sub-block whose weights all cancel (d*sc*q == dmin*m) gives exactly 0.
 #pragma clang fp contract(off)
-    int a00 = 0, a01 = 0, a02 = 0, a10 = 0, a11 = 0, a12 = 0;
+    const int lo0 = static_cast<int>(c.lo[0]);
+    const int hi0 = static_cast<int>(c.hi[0]);
+    int a00 = sdot4_first(lo0, static_cast<int>(xs.limb[0][0][0]));
+    int a01 = sdot4_first(lo0, static_cast<int>(xs.limb[0][1][0]));
+    int a02 = sdot4_first(lo0, static_cast<int>(xs.limb[0][2][0]));
+    int a10 = sdot4_first(hi0, static_cast<int>(xs.limb[1][0][0]));
+    int a11 = sdot4_first(hi0, static_cast<int>(xs.limb[1][1][0]));
+    int a12 = sdot4_first(hi0, static_cast<int>(xs.limb[1][2][0]));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 1; i < 8; ++i) {
         const int lo = static_cast<int>(c.lo[i]);
         const int hi = static_cast<int>(c.hi[i]);
         a00 = __builtin_amdgcn_sdot4(lo, static_cast<int>(xs.limb[0][0][i]), a00, false);
