@@ -549,8 +549,12 @@ __global__ __launch_bounds__(BLOCK, MIN_WAVES) void gemv_kernel(const MatTable m
                     float acc[NMAT];
                     if constexpr (EXACT) lane_dot_exact(rows[q], g, src[0], rok && g.ok, 0.0f, acc);
                     else lane_dot(rows[q], g, src[0], rok && g.ok, acc);
+                    if constexpr (SWIGLU && LPR == kWave) {
+                        wave_sum_pair(acc[0], acc[1]);
+                    } else {
 #pragma unroll
-                    for (int m2 = 0; m2 < NMAT; ++m2) acc[m2] = lane_group_sum<LPR>(acc[m2]);
+                        for (int m2 = 0; m2 < NMAT; ++m2) acc[m2] = lane_group_sum<LPR>(acc[m2]);
+                    }
                     const float out = SWIGLU ? silu(acc[0]) * acc[NMAT - 1] : acc[0];
                     yv[0] = mine ? out : yv[0];
                 } else {
@@ -1244,6 +1248,12 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const void *x, co
 #ifndef Q4K_SWIGLU_WIDE_ROWS
 #define Q4K_SWIGLU_WIDE_ROWS 8192
 #endif
+#ifndef Q4K_SWIGLU_WIDE_BLOCK
+#define Q4K_SWIGLU_WIDE_BLOCK 768
+#endif
+#ifndef Q4K_SWIGLU_WIDE_MINW
+#define Q4K_SWIGLU_WIDE_MINW 3
+#endif
 #ifndef Q4K_SWIGLU_BLOCK
 #define Q4K_SWIGLU_BLOCK 512
 #endif
@@ -1259,8 +1269,8 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const void *x, co
 // Single-token Q4_K streams read through an LDS ring of this many iterations
 // per wave (one slot per matrix each, 2304 bytes per 64 groups); Q8_0 keeps
 // the register buffers above.  Deeper rings measured slower wherever they fit
-// (the 9B lm_head: 85.3, 87.9, 88.9 us for 1, 2, 3 slots; the 9B down: 8.9 us
-// with 2 slots, 9.6 with 3, 11.0 with 4): more loads queued per CU do not
+// (the 9B lm_head: 85.3, 87.9, 88.9 us for 1, 2, 3 slots; the 9B down: 8.4 us
+// with 1 slot, 8.6 with 2, 9.3 with 3): more loads queued per CU do not
 // stream faster.  The K-split ring and the activation groups must fit the 160
 // KB of LDS: two slices per row (16 waves, K <= 8192), three (12 waves,
 // K <= 12288) and four (16 waves, K <= 16384).
@@ -1277,7 +1287,7 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const void *x, co
 #define Q4K_SPLIT2_SLOTS 3
 #endif
 #ifndef Q4K_SPLIT3_SLOTS
-#define Q4K_SPLIT3_SLOTS 2
+#define Q4K_SPLIT3_SLOTS 1
 #endif
 #ifndef Q4K_SPLIT4_SLOTS
 #define Q4K_SPLIT4_SLOTS 2
@@ -1301,7 +1311,8 @@ hipError_t dispatch_lpr(const GemvJob *jobs, int count, const uint8_t *wu, const
             int64_t rows = 0;
             for (int i = 0; i < count; ++i) rows += jobs[i].n;
             if (rows >= Q4K_SWIGLU_WIDE_ROWS) {
-                return launch_fast<F, XT, YT, LPR, true, NB, 768, 3>(jobs, count, wu, x, k, stream);
+                return launch_fast<F, XT, YT, LPR, true, NB, Q4K_SWIGLU_WIDE_BLOCK, Q4K_SWIGLU_WIDE_MINW>(
+                    jobs, count, wu, x, k, stream);
             }
         }
         return launch_fast<F, XT, YT, LPR, true, NB, Q4K_SWIGLU_BLOCK, Q4K_SWIGLU_MINW>(jobs, count, wu, x, k, stream);

@@ -312,6 +312,27 @@ __device__ __forceinline__ float lane_group_sum(float v) {
     return v;
 }
 
+// The sums over the whole wave of two values at once, each the same bits as
+// lane_group_sum<64> of it: one permlane32 swap of a and b leaves lanes 0-31
+// with a's lane pairs (i, i+32) and lanes 32-63 with b's, added in the order
+// swap32_sum adds them; the rest of the reduction then runs once for both
+// halves, and a last swap hands every lane both totals.
+__device__ __forceinline__ void wave_sum_pair(float &a, float &b) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    const unsigned r0 = s[0];
+    const unsigned r1 = opaque_copy(s[1]);
+    float v = __uint_as_float(r0) + __uint_as_float(r1);
+    v = swap16_sum(v);
+    v = dpp_add<0xb1>(v);
+    v = dpp_add<0x4e>(v);
+    v = dpp_add<0x141>(v);
+    v = dpp_add<0x140>(v);
+    const unsigned u = __float_as_uint(v);
+    const auto t = __builtin_amdgcn_permlane32_swap(u, opaque_copy(u), false, false);
+    a = __uint_as_float(t[0]);              // lanes 0-31 of v everywhere: a's sum
+    b = __uint_as_float(opaque_copy(t[1]));  // lanes 32-63 of v everywhere: b's sum
+}
+
 // Integer sum over aligned groups of W lanes, W in {4, 8, 16} (inside one
 // 16-lane row, so DPP alone reaches every partner).
 template <int CTRL>
