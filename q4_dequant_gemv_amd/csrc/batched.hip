@@ -762,17 +762,27 @@ __global__ __launch_bounds__(256) void f32_to_f16_kernel(const float *__restrict
 // ------------------------------------------------------------- launchers
 namespace {
 
-// Super-blocks per stage (the workgroup has 2 waves per super-block).
+// Super-blocks per stage (the workgroup has 2 waves per super-block).  More
+// than 16 tokens at K <= 4096 take two (4 waves, one per SIMD): the kernel
+// then has the whole register file of its SIMD and keeps its token tiles
+// without spilling (at four super-blocks, 8 waves of 256 registers, the 32-
+// and 48-row shapes of 2-4 token tiles spill 48-64 bytes per lane to scratch,
+// and the spill stores reach HBM).  Measured on the 9B gate: m = 32 24.6 ->
+// 22.2 us, m = 64 43.9 -> 41.8 us; the 9B down (K = 12288) is unchanged at
+// m = 32 and 64 and 3 % slower at m = 16 with two.
 #ifndef Q4K_BATCH_STAGE_SB
 #define Q4K_BATCH_STAGE_SB 4
 #endif
+#ifndef Q4K_BATCH_STAGE_SB_SHORT
+#define Q4K_BATCH_STAGE_SB_SHORT 2
+#endif
+constexpr int64_t kBatchShortK = 4096;
 
 // x: [m, k] of XT; y: [m, n] of YT.  An f16 output with K split across
 // workgroups is accumulated in f32 in the call's scratch, then converted.
-template <int NT, int MT, typename XT, typename YT>
-hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, int ksplit, Workspace &ws,
-                       hipStream_t stream) {
-    constexpr int S = Q4K_BATCH_STAGE_SB;
+template <int NT, int MT, int S, typename XT, typename YT>
+hipError_t launch_mfma_s(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, int ksplit, Workspace &ws,
+                         hipStream_t stream) {
     const int64_t nst = k / kStageK;
     const int64_t flag_off = nst * MT * kTileStageBytes;
     const int64_t bytes = flag_off + flag_bytes(nst, MT);
@@ -818,6 +828,15 @@ hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, i
     }
     const hipError_t f = ws_release(xc, owned, stream);
     return e != hipSuccess ? e : f;
+}
+
+template <int NT, int MT, typename XT, typename YT>
+hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, int ksplit, Workspace &ws,
+                       hipStream_t stream) {
+    if (MT > 1 && k <= kBatchShortK) {
+        return launch_mfma_s<NT, MT, Q4K_BATCH_STAGE_SB_SHORT, XT, YT>(w, x, y, m, n, k, ksplit, ws, stream);
+    }
+    return launch_mfma_s<NT, MT, Q4K_BATCH_STAGE_SB, XT, YT>(w, x, y, m, n, k, ksplit, ws, stream);
 }
 
 #ifndef Q4K_STREAM_NB
