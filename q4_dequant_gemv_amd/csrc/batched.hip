@@ -776,6 +776,9 @@ namespace {
 #ifndef Q4K_BATCH_STAGE_SB_SHORT
 #define Q4K_BATCH_STAGE_SB_SHORT 2
 #endif
+#ifndef Q4K_BATCH_NT_SHORT
+#define Q4K_BATCH_NT_SHORT 3
+#endif
 constexpr int64_t kBatchShortK = 4096;
 
 // x: [m, k] of XT; y: [m, n] of YT.  An f16 output with K split across
@@ -830,15 +833,6 @@ hipError_t launch_mfma_s(const uint8_t *w, const XT *x, YT *y, int m, int64_t n,
     return e != hipSuccess ? e : f;
 }
 
-template <int NT, int MT, typename XT, typename YT>
-hipError_t launch_mfma(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, int ksplit, Workspace &ws,
-                       hipStream_t stream) {
-    if (MT > 1 && k <= kBatchShortK) {
-        return launch_mfma_s<NT, MT, Q4K_BATCH_STAGE_SB_SHORT, XT, YT>(w, x, y, m, n, k, ksplit, ws, stream);
-    }
-    return launch_mfma_s<NT, MT, Q4K_BATCH_STAGE_SB, XT, YT>(w, x, y, m, n, k, ksplit, ws, stream);
-}
-
 #ifndef Q4K_STREAM_NB
 #define Q4K_STREAM_NB 2
 #endif
@@ -891,37 +885,53 @@ hipError_t launch_stream(const uint8_t *w, const XT *x, YT *y, int m, int64_t n,
 // per activation) besides its weights (0.5625 bytes per weight), so when
 // there are too few rows for every CU to get several, rows are grouped into
 // larger blocks and K is split across workgroups instead (their partial tiles
-// are then added into y with atomics).  The register budget caps the rows per
-// workgroup at 64 / 48 / 32 / 32 for 1 / 2 / 3 / 4 token tiles (the 48-row
-// shape of 2 tiles and the 32-row shape of 4 spill a few registers and are
-// still the faster ones: each row block re-reads fewer activations).
+// are then added into y with atomics).  With four super-blocks per stage (8
+// waves of 256 registers) the register budget caps the rows per workgroup at
+// 64 / 48 / 32 / 32 for 1 / 2 / 3 / 4 token tiles (the 48-row shape of 2
+// tiles and the 32-row shape of 4 spill a few registers and are still the
+// faster ones: each row block re-reads fewer activations); with two (4 waves
+// of 512 registers, more than 16 tokens at K <= 4096) 48 rows fit 2-4 token
+// tiles, and a 12,288-row matrix is then one row block per CU instead of 1.5.
 #ifndef Q4K_BATCH_NT_CAP
 #define Q4K_BATCH_NT_CAP 4
 #endif
-template <int MT, typename XT, typename YT>
-hipError_t dispatch_mt(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, Workspace &ws,
-                       hipStream_t stream) {
-    constexpr int kNtMax0 = MT == 1 ? 4 : (MT == 2 ? 3 : 2);
-    constexpr int kNtMax = kNtMax0 < Q4K_BATCH_NT_CAP ? kNtMax0 : Q4K_BATCH_NT_CAP;
+template <int MT, int S, int kNtMax, typename XT, typename YT>
+hipError_t dispatch_rows(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, Workspace &ws,
+                         hipStream_t stream) {
     const int64_t cus = device_cu_count();
-    if constexpr (MT == 1) {
-        // a row tile for every CU: the weight-streaming kernel
-        if (k <= kStreamMaxK && (n + 15) / 16 >= cus) return launch_stream(w, x, y, m, n, k, ws, stream);
-    }
     const int64_t nsb = k / kBlockWeights;
     const int64_t per = n / (16 * cus);  // row tiles per CU with one row block each
     if (per >= 1 || nsb < 2) {
         const int64_t nt = per < 1 ? 1 : (per > kNtMax ? kNtMax : per);
-        if (nt >= 4) return launch_mfma<kNtMax, MT, XT, YT>(w, x, y, m, n, k, 1, ws, stream);
-        if (nt == 3) return launch_mfma<(kNtMax < 3 ? kNtMax : 3), MT, XT, YT>(w, x, y, m, n, k, 1, ws, stream);
-        if (nt == 2) return launch_mfma<(kNtMax < 2 ? kNtMax : 2), MT, XT, YT>(w, x, y, m, n, k, 1, ws, stream);
-        return launch_mfma<1, MT, XT, YT>(w, x, y, m, n, k, 1, ws, stream);
+        if (nt >= 4) return launch_mfma_s<kNtMax, MT, S, XT, YT>(w, x, y, m, n, k, 1, ws, stream);
+        if (nt == 3) return launch_mfma_s<(kNtMax < 3 ? kNtMax : 3), MT, S, XT, YT>(w, x, y, m, n, k, 1, ws, stream);
+        if (nt == 2) return launch_mfma_s<(kNtMax < 2 ? kNtMax : 2), MT, S, XT, YT>(w, x, y, m, n, k, 1, ws, stream);
+        return launch_mfma_s<1, MT, S, XT, YT>(w, x, y, m, n, k, 1, ws, stream);
     }
     // fewer than 16 rows per CU: the largest row blocks, K split to fill the CUs
     const int64_t nrb = (n + 16 * kNtMax - 1) / (16 * kNtMax);
     int64_t ksplit = (cus + nrb - 1) / nrb;
     if (ksplit > nsb) ksplit = nsb;
-    return launch_mfma<kNtMax, MT, XT, YT>(w, x, y, m, n, k, static_cast<int>(ksplit), ws, stream);
+    return launch_mfma_s<kNtMax, MT, S, XT, YT>(w, x, y, m, n, k, static_cast<int>(ksplit), ws, stream);
+}
+
+template <int MT, typename XT, typename YT>
+hipError_t dispatch_mt(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, int64_t k, Workspace &ws,
+                       hipStream_t stream) {
+    constexpr int kNtMax0 = MT == 1 ? 4 : (MT == 2 ? 3 : 2);
+    constexpr int kNtMax = kNtMax0 < Q4K_BATCH_NT_CAP ? kNtMax0 : Q4K_BATCH_NT_CAP;
+    constexpr int kNtShort0 = MT == 1 ? kNtMax0 : Q4K_BATCH_NT_SHORT;
+    constexpr int kNtShort = kNtShort0 < Q4K_BATCH_NT_CAP ? kNtShort0 : Q4K_BATCH_NT_CAP;
+    if constexpr (MT == 1) {
+        // a row tile for every CU: the weight-streaming kernel
+        if (k <= kStreamMaxK && (n + 15) / 16 >= device_cu_count()) return launch_stream(w, x, y, m, n, k, ws, stream);
+        return dispatch_rows<MT, Q4K_BATCH_STAGE_SB, kNtMax>(w, x, y, m, n, k, ws, stream);
+    } else {
+        if (k <= kBatchShortK) {
+            return dispatch_rows<MT, Q4K_BATCH_STAGE_SB_SHORT, kNtShort>(w, x, y, m, n, k, ws, stream);
+        }
+        return dispatch_rows<MT, Q4K_BATCH_STAGE_SB, kNtMax>(w, x, y, m, n, k, ws, stream);
+    }
 }
 
 }  // namespace
