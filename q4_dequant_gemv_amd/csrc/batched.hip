@@ -776,6 +776,9 @@ namespace {
 #ifndef Q4K_BATCH_STAGE_SB_SHORT
 #define Q4K_BATCH_STAGE_SB_SHORT 2
 #endif
+#ifndef Q4K_BATCH_HALVE_K
+#define Q4K_BATCH_HALVE_K 1
+#endif
 #ifndef Q4K_BATCH_NT_SHORT
 #define Q4K_BATCH_NT_SHORT 3
 #endif
@@ -922,14 +925,27 @@ hipError_t dispatch_mt(const uint8_t *w, const XT *x, YT *y, int m, int64_t n, i
     constexpr int kNtMax = kNtMax0 < Q4K_BATCH_NT_CAP ? kNtMax0 : Q4K_BATCH_NT_CAP;
     constexpr int kNtShort0 = MT == 1 ? kNtMax0 : Q4K_BATCH_NT_SHORT;
     constexpr int kNtShort = kNtShort0 < Q4K_BATCH_NT_CAP ? kNtShort0 : Q4K_BATCH_NT_CAP;
+    const int64_t cus = device_cu_count();
+    // Long rows with exactly one 16-row tile per CU (the 9B down: 4096 rows,
+    // K = 12288): every workgroup would read its whole K range of
+    // activations for 16 rows.  32-row workgroups with K halved between two
+    // of them read half as much per row for the same number of workgroups;
+    // the two partial tiles are added into y (zeroed first) with f32 atomics,
+    // and with exactly two addends (0 + a, then + b, or the other way round)
+    // the sum is the same whatever their order, so the result stays
+    // reproducible.
+    const bool halve_k = Q4K_BATCH_HALVE_K && k > kBatchShortK && n / (16 * cus) == 1 &&
+                         2 * ((n + 31) / 32) <= cus && k / kBlockWeights >= 2;
     if constexpr (MT == 1) {
         // a row tile for every CU: the weight-streaming kernel
-        if (k <= kStreamMaxK && (n + 15) / 16 >= device_cu_count()) return launch_stream(w, x, y, m, n, k, ws, stream);
+        if (k <= kStreamMaxK && (n + 15) / 16 >= cus) return launch_stream(w, x, y, m, n, k, ws, stream);
+        if (halve_k) return launch_mfma_s<2, MT, Q4K_BATCH_STAGE_SB, XT, YT>(w, x, y, m, n, k, 2, ws, stream);
         return dispatch_rows<MT, Q4K_BATCH_STAGE_SB, kNtMax>(w, x, y, m, n, k, ws, stream);
     } else {
         if (k <= kBatchShortK) {
             return dispatch_rows<MT, Q4K_BATCH_STAGE_SB_SHORT, kNtShort>(w, x, y, m, n, k, ws, stream);
         }
+        if (halve_k) return launch_mfma_s<2, MT, Q4K_BATCH_STAGE_SB_SHORT, XT, YT>(w, x, y, m, n, k, 2, ws, stream);
         return dispatch_rows<MT, Q4K_BATCH_STAGE_SB, kNtMax>(w, x, y, m, n, k, ws, stream);
     }
 }

@@ -474,12 +474,18 @@ def _boundary_cases():
     # the batched call's kernel choice switches at m = 2 | 3..4 | 5..16 | 17+,
     # at K = 4096 (token pairs, streamed tiles) and 16384 (two-token K split),
     # and at 16 and 64 rows per CU (rows as multiples of 16 * CUs, here for up
-    # to 256 CUs: each side of each switch appears for any CU count <= 256)
+    # to 256 CUs: each side of each switch appears for any CU count <= 256);
+    # rows longer than 4096 weights halve K between two workgroups at exactly
+    # one 16-row tile per CU with no more than 32 rows per CU pair (4096 rows
+    # on 256 CUs: 4080, 4096 and 4112 rows are its two sides)
     out = []
     for m in (2, 3, 4, 5, 16, 17):
         for n in (4080, 4096, 16368, 16384):
             out.append((m, n, 4096))
         out.append((m, 16384, 4352))
+    for m in (3, 16, 17, 64):
+        for n in (4080, 4096, 4112):
+            out.append((m, n, 4352))
     out += [(2, 512, 16384), (2, 512, 16640), (3, 512, 16384)]
     return out
 
@@ -524,6 +530,35 @@ def test_batched_special_values(q4k, n):
         xs[0, 5] = np.inf
         y = to_host(q4k.gemv_batched(to_dev(w.reshape(-1)), to_dev(xs)))
         assert np.all(np.isnan(y[0])) and np.all(np.isfinite(y[1:]))
+
+
+@pytest.mark.parametrize("m", [4, 16, 40, 64])
+def test_batched_long_rows_two_k_halves_bitwise(q4k, m):
+    """One 16-row tile per compute unit with rows longer than 4096 weights (the
+    9B down's 4096 x 12288 on 256 CUs): 32-row workgroups with K halved between
+    two, the two partial tiles added into a zeroed y with f32 atomics.  Two
+    addends give the same sum in either order, so repeated calls agree bitwise,
+    also with an f16 output (summed in f32 scratch, then rounded); every output
+    inside the oracle's bound."""
+    import torch
+
+    print(f"[case] long rows m={m}", flush=True)
+    n = 16 * torch.cuda.get_device_properties(0).multi_processor_count
+    k = 12288
+    wh = inputs.make_q4k(n, k, config_id=94, tensor_id=m)
+    xh = inputs.make_x(m, k, config_id=94, tensor_id=m)
+    w, xs = to_dev(wh.reshape(-1)), to_dev(xh)
+    a = to_host(q4k.gemv_batched(w, xs))
+    b = to_host(q4k.gemv_batched(w, xs))
+    np.testing.assert_array_equal(a, b)
+    c = q4k.gemv_batched_dt(w, xs, out_dtype=torch.float16)
+    d = q4k.gemv_batched_dt(w, xs, out_dtype=torch.float16)
+    assert torch.equal(c, d)
+    yr, ar = oracle.gemv_batched(wh, xh, threads=THREADS)
+    check_bound(a, yr, ar, f"long rows m={m}")
+    # the f16 output is the f32 sum rounded once: its error adds half an f16 ulp
+    ch = to_host(c).astype(np.float64)
+    assert np.all(np.abs(ch - yr) <= 2e-4 * ar + np.abs(yr) * 2.0**-11 + 2.0**-24), "f16 output outside the bound"
 
 
 def test_batched_run_to_run(q4k):
