@@ -620,11 +620,12 @@ constexpr int64_t kStreamMaxK = kStreamMaxHalves * kStageK;
 template <int H>
 constexpr int stream_max_waves() { return H <= 2 ? 16 : 8; }
 
-template <int H, int NB, typename YT, typename XT>
-__global__ __launch_bounds__(64 * stream_max_waves<H>(), 1) void stream_mfma_kernel(
+template <int H, int NB, typename YT, typename XT, int KP = 1>
+__global__ __launch_bounds__(64 * (KP == 1 ? stream_max_waves<H>() : 8), 1) void stream_mfma_kernel(
     const uint8_t *__restrict__ w, const uint8_t *__restrict__ xc, YT *__restrict__ y, int m, int64_t n, int64_t k,
     int64_t row_bytes, int64_t xc_bytes, const XT *__restrict__ x, int64_t flag_off) {
     static_assert(H == 1 || H == 2 || H == 4, "a wave's halves start a super-block (H even) or are one half");
+    static_assert(KP == 1 || (KP == 2 && std::is_same_v<YT, float>), "K parts add f32 partial tiles");
     constexpr int NH = (H + 1) / 2;  // super-blocks (headers) per wave
     __shared__ __align__(16) float4_t part[2][kStreamFlush][stream_max_waves<H>()][64];
     // per half: the scratch block's tail from kSubOff (sub-block sums, bias,
@@ -637,7 +638,13 @@ __global__ __launch_bounds__(64 * stream_max_waves<H>(), 1) void stream_mfma_ker
     const int col = lane & 15;
     const int kq = lane >> 4;
     const int nhalf = static_cast<int>(k / kStageK);
-    const int hw0 = wave * H;  // the wave's first half (even when H >= 2)
+    // KP = 2: workgroup b takes K part b % 2 (half the halves) of the tiles
+    // b / 2, b / 2 + gridDim.x / 2, ...; its partial tiles are added into y
+    // (zeroed by the preparation kernel), two addends per output
+    const int kp = KP == 1 ? 0 : static_cast<int>(blockIdx.x % KP);
+    const int tblk = static_cast<int>(blockIdx.x / KP);
+    const int tgrid = static_cast<int>(gridDim.x / KP);
+    const int hw0 = kp * (nhalf / KP) + wave * H;  // the wave's first half (even when H >= 2)
     const int sb = hw0 >> 1;   // its first super-block
 
     // activations of the wave's halves (a lane whose token is past m reads
@@ -664,16 +671,24 @@ __global__ __launch_bounds__(64 * stream_max_waves<H>(), 1) void stream_mfma_ker
     const bool exact = workgroup_any(flag_bits, wflag, nw);
     __syncthreads();
 
-    // the host keeps gridDim.x <= the number of tiles: every workgroup has one
+    // the host keeps gridDim.x / KP <= the number of tiles: every workgroup has one
     const int64_t ntiles = (n + 15) / 16;
-    const int my_tiles = static_cast<int>((ntiles - 1 - blockIdx.x) / gridDim.x) + 1;
+    const int my_tiles = static_cast<int>((ntiles - 1 - tblk) / tgrid) + 1;
+    auto tile_row0 = [&](int c) -> int64_t {
+        return (static_cast<int64_t>(tblk) + static_cast<int64_t>(c) * tgrid) * 16;
+    };
     if (exact) {
-        // a flagged block: the workgroup's tiles on the f32 path
+        // a flagged block: the workgroup's tiles (its K part) on the f32 path
+        const int nsb = static_cast<int>(k / kBlockWeights);
         for (int c = 0; c < my_tiles; ++c) {
-            const int64_t r0 = (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(c) * gridDim.x) * 16;
+            const int64_t r0 = tile_row0(c);
             const int64_t r1 = r0 + 16 < n ? r0 + 16 : n;
-            exact_tile<XT, YT, false>(w, row_bytes, x, k, m, y, n, r0, r1, 0, static_cast<int>(k / kBlockWeights),
-                                      wave, nw);
+            if constexpr (KP == 1) {
+                exact_tile<XT, YT, false>(w, row_bytes, x, k, m, y, n, r0, r1, 0, nsb, wave, nw);
+            } else {
+                exact_tile<XT, float, true>(w, row_bytes, x, k, m, y, n, r0, r1, kp * nsb / KP, (kp + 1) * nsb / KP,
+                                            wave, nw);
+            }
         }
         return;
     }
@@ -687,7 +702,7 @@ __global__ __launch_bounds__(64 * stream_max_waves<H>(), 1) void stream_mfma_ker
     // descriptor, so the loads read zeros without a fetch)
     auto issue = [&](TileLoads &L, int c) {
         const bool live = c < my_tiles;
-        const int64_t row0 = live ? (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(c) * gridDim.x) * 16 : 0;
+        const int64_t row0 = live ? tile_row0(c) : 0;
         const int64_t rows = n - row0 < 16 ? n - row0 : 16;
         const int nrec = __builtin_amdgcn_readfirstlane(live ? static_cast<int>(rows * row_bytes) : 0);
         const uint8_t *base = reinterpret_cast<const uint8_t *>(wave_uniform(reinterpret_cast<int64_t>(w + row0 * row_bytes)));
@@ -734,14 +749,15 @@ __global__ __launch_bounds__(64 * stream_max_waves<H>(), 1) void stream_mfma_ker
                     const int ln = t & 63;
                     float4_t sum = part[half][dd][0][ln];
                     for (int v = 1; v < nw; ++v) sum += part[half][dd][v][ln];
-                    const int64_t row =
-                        (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(cur - d + dd) * gridDim.x) * 16 +
-                        (ln & 15);
+                    const int64_t row = tile_row0(cur - d + dd) + (ln & 15);
                     if (row < n) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int tok = 4 * (ln >> 4) + r;
-                            if (tok < m) y[static_cast<int64_t>(tok) * n + row] = static_cast<YT>(sum[r]);
+                            if (tok >= m) continue;
+                            YT *dst = y + static_cast<int64_t>(tok) * n + row;
+                            if constexpr (KP == 1) *dst = static_cast<YT>(sum[r]);
+                            else unsafeAtomicAdd(dst, sum[r]);
                         }
                     }
                 }
@@ -836,6 +852,12 @@ hipError_t launch_mfma_s(const uint8_t *w, const XT *x, YT *y, int m, int64_t n,
     return e != hipSuccess ? e : f;
 }
 
+#ifndef Q4K_STREAM_KP_NB
+#define Q4K_STREAM_KP_NB 2
+#endif
+#ifndef Q4K_STREAM_KPARTS
+#define Q4K_STREAM_KPARTS 1
+#endif
 #ifndef Q4K_STREAM_NB
 #define Q4K_STREAM_NB 2
 #endif
@@ -856,17 +878,37 @@ hipError_t launch_stream(const uint8_t *w, const XT *x, YT *y, int m, int64_t n,
     bool owned = false;
     hipError_t e = ws_acquire(ws, bytes, stream, &xc, &owned);
     if (e != hipSuccess) return e;
+    const int64_t ntiles = (n + 15) / 16;
+    const int64_t cus = device_cu_count();
+    // Few tiles per CU at K = 4096 (the 9B gate: 3): each workgroup's
+    // activation fragments (256 KB at 16 tokens) weigh as much as its
+    // weights, so two workgroups split K instead, each loading half of them
+    // for twice as many tiles; their partial tiles are added into y (zeroed
+    // by the preparation kernel), two addends per output, whose sum does not
+    // depend on their order.
+    const bool kparts = std::is_same_v<YT, float> && Q4K_STREAM_KPARTS && nhalf == kStreamMaxHalves &&
+                        ntiles <= 8 * cus && cus % 2 == 0;
     const int64_t prep_blocks = (nhalf * 16 * 32 + 255) / 256;
     hipLaunchKernelGGL(x_prep_kernel<XT>, dim3(static_cast<unsigned>(prep_blocks)), dim3(256), 0, stream, x, xc,
-                       xc + flag_off, static_cast<uint32_t *>(nullptr), m, 1, k, int64_t{0});
+                       xc + flag_off, kparts ? reinterpret_cast<uint32_t *>(y) : static_cast<uint32_t *>(nullptr), m,
+                       1, k, kparts ? static_cast<int64_t>(m) * n : int64_t{0});
     e = hipGetLastError();
-    if (e == hipSuccess) {
+    if (e == hipSuccess && kparts) {
+        // two halves per wave, eight waves per K part, one workgroup per CU
+        const int64_t tiles2 = 2 * ntiles;
+        const dim3 grid(static_cast<unsigned>(tiles2 < cus ? tiles2 : cus));
+        const int64_t rb = (k / kBlockWeights) * kBlockBytes;
+        if constexpr (std::is_same_v<YT, float>) {
+            hipLaunchKernelGGL((stream_mfma_kernel<2, Q4K_STREAM_KP_NB, float, XT, 2>), grid, dim3(64 * 8), 0, stream, w, xc,
+                               y, m, n, k, rb, bytes, x, flag_off);
+        }
+        e = hipGetLastError();
+    } else if (e == hipSuccess) {
         // halves per wave: one up to 16 halves (K = 2048), then four (eight
         // waves of 256 registers); two spill at the 128 registers of 16 waves
         const int H = nhalf <= kStreamMaxWaves ? 1 : 4;
         const int nw = static_cast<int>((nhalf + H - 1) / H);
-        const int64_t ntiles = (n + 15) / 16;
-        const int64_t cap = static_cast<int64_t>(device_cu_count()) * (H == 1 && nw <= 8 ? 2 : 1);
+        const int64_t cap = cus * (H == 1 && nw <= 8 ? 2 : 1);
         const dim3 grid(static_cast<unsigned>(ntiles < cap ? ntiles : cap));
         const int64_t rb = (k / kBlockWeights) * kBlockBytes;
         constexpr int NB = Q4K_STREAM_NB;

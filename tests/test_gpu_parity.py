@@ -486,6 +486,9 @@ def _boundary_cases():
     for m in (3, 16, 17, 64):
         for n in (4080, 4096, 4112):
             out.append((m, n, 4352))
+    # the streaming matrix-core kernel splits K = 4096 between two workgroups
+    # up to 8 tiles per CU (32768 rows on 256 CUs)
+    out += [(5, 32768, 4096), (16, 32784, 4096)]
     out += [(2, 512, 16384), (2, 512, 16640), (3, 512, 16384)]
     return out
 
@@ -532,19 +535,20 @@ def test_batched_special_values(q4k, n):
         assert np.all(np.isnan(y[0])) and np.all(np.isfinite(y[1:]))
 
 
-@pytest.mark.parametrize("m", [4, 16, 40, 64])
-def test_batched_long_rows_two_k_halves_bitwise(q4k, m):
-    """One 16-row tile per compute unit with rows longer than 4096 weights (the
-    9B down's 4096 x 12288 on 256 CUs): 32-row workgroups with K halved between
-    two, the two partial tiles added into a zeroed y with f32 atomics.  Two
-    addends give the same sum in either order, so repeated calls agree bitwise,
-    also with an f16 output (summed in f32 scratch, then rounded); every output
-    inside the oracle's bound."""
+@pytest.mark.parametrize("m,tiles_per_cu,k", [(4, 1, 12288), (16, 1, 12288), (40, 1, 12288), (64, 1, 12288),
+                                               (5, 3, 4096), (16, 3, 4096)])
+def test_batched_two_k_halves_bitwise(q4k, m, tiles_per_cu, k):
+    """K halved between two workgroups, the two partial tiles added into a
+    zeroed y with f32 atomics: one 16-row tile per compute unit with rows longer
+    than 4096 weights (the 9B down's 4096 x 12288 on 256 CUs: 32-row workgroups),
+    and the weight-streaming kernel with few tiles per compute unit at K = 4096
+    (the 9B gate, 3 tiles per CU).  Two addends give the same sum in either
+    order, so repeated calls agree bitwise, also with an f16 output (summed in
+    f32, then rounded); every output inside the oracle's bound."""
     import torch
 
-    print(f"[case] long rows m={m}", flush=True)
-    n = 16 * torch.cuda.get_device_properties(0).multi_processor_count
-    k = 12288
+    print(f"[case] two K halves m={m} tiles/CU={tiles_per_cu} k={k}", flush=True)
+    n = 16 * tiles_per_cu * torch.cuda.get_device_properties(0).multi_processor_count
     wh = inputs.make_q4k(n, k, config_id=94, tensor_id=m)
     xh = inputs.make_x(m, k, config_id=94, tensor_id=m)
     w, xs = to_dev(wh.reshape(-1)), to_dev(xh)
@@ -555,7 +559,7 @@ def test_batched_long_rows_two_k_halves_bitwise(q4k, m):
     d = q4k.gemv_batched_dt(w, xs, out_dtype=torch.float16)
     assert torch.equal(c, d)
     yr, ar = oracle.gemv_batched(wh, xh, threads=THREADS)
-    check_bound(a, yr, ar, f"long rows m={m}")
+    check_bound(a, yr, ar, f"two K halves m={m} k={k}")
     # the f16 output is the f32 sum rounded once: its error adds half an f16 ulp
     ch = to_host(c).astype(np.float64)
     assert np.all(np.abs(ch - yr) <= 2e-4 * ar + np.abs(yr) * 2.0**-11 + 2.0**-24), "f16 output outside the bound"
