@@ -223,11 +223,15 @@ Q4K_API q4k_status q4k_q8_0_gemv(const void *w, const float *x, float *y, int64_
  * k <= 4096 over n >= 64 * (compute units) rows, which the matrix cores do
  * faster.  Every other m >= 2 runs on the matrix cores (each weight decoded
  * once per 64 tokens).  There, with n >= 16 *
- * (compute units of the device), every output is summed by one workgroup in
- * a fixed order and the call is bitwise reproducible; with fewer rows the K
- * range is split across workgroups whose partial sums are added into y with
- * f32 atomics, so the last bits may differ between runs (every run is inside
- * the error bound).  y is overwritten, not accumulated.
+ * (compute units of the device), every output is summed in a fixed order, or
+ * from exactly two partial sums (K halved between two workgroups: k == 4096
+ * with at most 8 16-row tiles per compute unit and at most 16 tokens, or
+ * k > 4096 with exactly one 16-row tile per compute unit) added into a zeroed
+ * y, whose sum does not depend on their order: the call is bitwise
+ * reproducible.  With fewer rows the K range is split across more workgroups
+ * whose partial sums are added into y with f32 atomics, so the last bits may
+ * differ between runs (every run is inside the error bound).  y is
+ * overwritten, not accumulated.
  */
 Q4K_API q4k_status q4k_gemv_batched(const void *w, const float *x, float *y, int64_t m, int64_t n, int64_t k,
                             void *stream);
