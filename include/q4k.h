@@ -225,7 +225,7 @@ Q4K_API q4k_status q4k_q8_0_gemv(const void *w, const float *x, float *y, int64_
  * once per 64 tokens).  There, with n >= 16 *
  * (compute units of the device), every output is summed in a fixed order, or
  * from exactly two partial sums (K halved between two workgroups: k == 4096
- * with 5 to 16 tokens, an f32 y and at most 8 16-row tiles per compute unit,
+ * with at most 16 tokens, an f32 y and at most 8 16-row tiles per compute unit,
  * or k > 4096 with n == 16 * (compute units)) added into a zeroed y, whose
  * sum does not depend on their order: the call is bitwise
  * reproducible.  With fewer rows the K range is split across more workgroups
