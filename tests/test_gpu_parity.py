@@ -392,6 +392,53 @@ def test_batched_small(q4k, m):
     _report(f"batched m={m}", check_bound(y, yr, ar, f"batched m={m} {n}x{k}"))
 
 
+def _random_batched_cases(count=24, seed=2024):
+    """Seeded (m, rows, k) draws over the batched call's whole range: m from 2
+    to 80, k from 256 to 16384 and 1 to 6000 rows; and, alternately, rows a
+    multiple (1, 2, 3 or 8) of 16 * CUs give or take 16 (the kernel-choice
+    switches, scaled by the CU count at run time) at k = 1024, 4096, 4352 or
+    12288; at most about 1.6e9 multiply-adds each (on 256 CUs)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        if len(out) % 2 == 0:
+            m = int(rng.integers(2, 81))
+            k = 256 * int(rng.integers(1, 65))
+            rows = ("free", int(rng.integers(1, 6001)))
+            n_est = rows[1]
+        else:
+            m = int(rng.integers(2, 65))
+            k = int(rng.choice([1024, 4096, 4352, 12288]))
+            rows = ("cus", int(rng.choice([1, 2, 3, 8])), int(rng.choice([-16, 0, 16])))
+            n_est = 16 * 256 * rows[1]
+        if m * n_est * k > 1.6e9:
+            continue
+        out.append((m, rows, k))
+    return out
+
+
+@pytest.mark.parametrize("m,rows,k", _random_batched_cases())
+def test_batched_random_shapes(q4k, m, rows, k):
+    """Every output written and inside the oracle's bound; where the header
+    promises it (at least 16 rows per compute unit), two calls agree bitwise."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = rows[1] if rows[0] == "free" else max(1, 16 * cus * rows[1] + rows[2])
+    print(f"[case] random batched m={m} {n}x{k}", flush=True)
+    w = inputs.make_q4k(n, k, config_id=95, tensor_id=n + k)
+    xs = inputs.make_x(m, k, config_id=95, tensor_id=m)
+    wd, xd = to_dev(w.reshape(-1)), to_dev(xs)
+    yd = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    q4k.gemv_batched(wd, xd, y=yd)
+    y = to_host(yd)
+    assert np.isfinite(y).all(), f"{int((~np.isfinite(y)).sum())} outputs not written"
+    if n >= 16 * cus:
+        assert torch.equal(yd, q4k.gemv_batched(wd, xd)), "two calls differ"
+    yr, ar = oracle.gemv_batched(w, xs, threads=THREADS)
+    check_bound(y, yr, ar, f"random batched m={m} {n}x{k}")
+
+
 @pytest.mark.parametrize("m,n,k", [(4, 70, 12288), (16, 70, 12288), (64, 70, 12288), (3, 10, 256), (20, 10, 256),
                                    (7, 129, 20480), (40, 129, 1280), (2, 70, 12288), (2, 129, 8192), (2, 33, 16384),
                                    (2, 300, 4352), (4, 4097, 1024), (3, 1, 256), (2, 5, 20480)])
