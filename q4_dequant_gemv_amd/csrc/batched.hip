@@ -780,12 +780,13 @@ namespace {
 
 // Super-blocks per stage (the workgroup has 2 waves per super-block).  More
 // than 16 tokens at K <= 4096 take two (4 waves, one per SIMD): the kernel
-// then has the whole register file of its SIMD and keeps its token tiles
-// without spilling (at four super-blocks, 8 waves of 256 registers, the 32-
-// and 48-row shapes of 2-4 token tiles spill 48-64 bytes per lane to scratch,
-// and the spill stores reach HBM).  Measured on the 9B gate: m = 32 24.6 ->
-// 22.2 us, m = 64 43.9 -> 41.8 us; the 9B down (K = 12288) is unchanged at
-// m = 32 and 64 and 3 % slower at m = 16 with two.
+// then has the whole register file of its SIMD, so 48-row workgroups keep 2-4
+// token tiles without spilling to scratch (at four super-blocks, 8 waves of
+// 256 registers, the 32- and 48-row shapes of 2-4 token tiles spill 48-64
+// bytes per lane, and the spill stores reach HBM).  On the 9B gate two
+// super-blocks alone took m = 32 from 24.6 to 22.2 us and m = 64 from 43.9 to
+// 41.8 us, and the 48-row workgroups they allow m = 64 to 31.3 us; the 9B
+// down (K = 12288) gained nothing from two.
 #ifndef Q4K_BATCH_STAGE_SB
 #define Q4K_BATCH_STAGE_SB 4
 #endif
