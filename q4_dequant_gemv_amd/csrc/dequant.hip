@@ -10,6 +10,7 @@
 // Work split: one thread writes four consecutive outputs with one 16-byte
 // store, so every store instruction of a wave covers 1 KiB of contiguous
 // output; the operation is bound by those writes (4 bytes out per 0.5625 in).
+// Large outputs use non-temporal stores (launch_dequant).
 // A thread reads its super-block's 16-byte header and the one code dword
 // holding its four nibbles; neighbouring threads re-read the same lines from
 // cache.
@@ -18,6 +19,9 @@
 
 namespace q4k {
 
+// NT: non-temporal stores (outputs larger than the Infinity Cache stream
+// straight out instead of displacing it; see launch_dequant).
+template <bool NT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ w, float *__restrict__ out,
                                                       int64_t total_quads) {
 #pragma clang fp contract(off)
@@ -47,7 +51,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
         o.y = dl * static_cast<float>((nib >> 8) & 0xffu) - ml;
         o.z = dl * static_cast<float>((nib >> 16) & 0xffu) - ml;
         o.w = dl * static_cast<float>(nib >> 24) - ml;
-        *reinterpret_cast<float4 *>(out + 4 * t) = o;
+        if constexpr (NT) {
+            __builtin_nontemporal_store(o.x, out + 4 * t);
+            __builtin_nontemporal_store(o.y, out + 4 * t + 1);
+            __builtin_nontemporal_store(o.z, out + 4 * t + 2);
+            __builtin_nontemporal_store(o.w, out + 4 * t + 3);
+        } else {
+            *reinterpret_cast<float4 *>(out + 4 * t) = o;
+        }
     }
 }
 
@@ -58,7 +69,15 @@ hipError_t launch_dequant(const uint8_t *w, float *out, int64_t n, int64_t k, hi
     const int64_t want = (total_quads + threads - 1) / threads;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * 32;
     const int grid = static_cast<int>(want < cap ? want : cap);
-    hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(threads), 0, stream, w, out, total_quads);
+    // Outputs of 256 MiB or more (beyond the device's 256 MB Infinity Cache)
+    // are written with non-temporal stores: the 0.8B lm_head (1 GB of f32)
+    // went from 3.80 to 5.30 TB/s of reads and writes; a 201 MB output (the 9B
+    // gate), which the cache holds, is 2 % faster with ordinary stores.
+    if (total_quads * 16 >= (int64_t{256} << 20)) {
+        hipLaunchKernelGGL(dequant_kernel<true>, dim3(grid), dim3(threads), 0, stream, w, out, total_quads);
+    } else {
+        hipLaunchKernelGGL(dequant_kernel<false>, dim3(grid), dim3(threads), 0, stream, w, out, total_quads);
+    }
     return hipGetLastError();
 }
 

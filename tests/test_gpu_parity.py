@@ -91,6 +91,28 @@ def test_dequant_9b_ffn_whole(q4k, name, tid):
     np.testing.assert_array_equal(to_host(out).view(np.uint32), want.view(np.uint32))
 
 
+def test_dequant_lm_head_0p8b_whole(q4k):
+    """The whole 0.8B lm_head (248320 x 1024: 1 GB of f32, written with
+    non-temporal stores, the path for outputs of 256 MiB or more) bit for bit;
+    and both sides of that switch (65535 and 65536 rows of 1024 weights:
+    256 MiB less 4 KiB, and exactly 256 MiB of output)."""
+    import torch
+
+    n, k = inputs.SHAPES["lm_head_0p8b"]
+    w = inputs.make_q4k(n, k, config_id=1, tensor_id=3)
+    wd = to_dev(w.reshape(-1))
+    out = torch.full((n, k), float("nan"), dtype=torch.float32, device="cuda")
+    q4k.dequant(wd, k, out=out)
+    want = oracle.dequant(w, k, threads=THREADS)
+    np.testing.assert_array_equal(to_host(out).view(np.uint32), want.view(np.uint32))
+    del out
+    rb = inputs.row_bytes(k)
+    for cnt in (65535, 65536):
+        o = torch.full((cnt, k), float("nan"), dtype=torch.float32, device="cuda")
+        q4k.dequant(wd[:cnt * rb], k, out=o)
+        np.testing.assert_array_equal(to_host(o).view(np.uint32), want[:cnt].view(np.uint32))
+
+
 def test_dequant_row_chunks_of_lm_head_9b(q4k):
     """Rows of the 9B lm_head (248320 x 4096, 572 MB) through pointer offsets:
     the first rows, a middle range and the last rows."""
