@@ -101,6 +101,26 @@ __device__ __forceinline__ int stage_pos(int kk) {
     return kq * 32 + i * 8 + 4 * (dd & 1) + tb;
 }
 
+// Maximum of unsigned values over aligned groups of 32 lanes (the pairings of
+// lane_group_sum<32>: a permlane16 swap, then DPP inside 16-lane rows).
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_dpp_u32(uint32_t v) {
+    const uint32_t moved = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xf, 0xf, true));
+    return moved > v ? moved : v;
+}
+
+__device__ __forceinline__ uint32_t lane32_max_u32(uint32_t v) {
+    const auto s = __builtin_amdgcn_permlane16_swap(v, opaque_copy(v), false, false);
+    const uint32_t r0 = s[0];
+    const uint32_t r1 = opaque_copy(s[1]);
+    v = r0 > r1 ? r0 : r1;
+    v = max_dpp_u32<0xb1>(v);   // quad_perm [1,0,3,2]
+    v = max_dpp_u32<0x4e>(v);   // quad_perm [2,3,0,1]
+    v = max_dpp_u32<0x141>(v);  // row_half_mirror
+    v = max_dpp_u32<0x140>(v);  // row_mirror
+    return v;
+}
+
 // ---- activations, converted once per call ----------------------------------
 // One half-wave per (stage, token) of the padded token range 16*mt; each lane
 // converts four activations.  Tokens >= m are written as zeros.  The same
@@ -125,45 +145,61 @@ __global__ __launch_bounds__(256) void x_prep_kernel(const XT *x, uint8_t *__res
     const int tok = static_cast<int>(pair % tpad);
     const bool real = tok < m;
     const XT *px = x + static_cast<int64_t>(real ? tok : 0) * k + st * kStageK + 4 * c;
+    // The largest magnitude is taken on the bit patterns of |x|: integer
+    // order is numeric order for non-negative floats, and every NaN pattern
+    // lies above infinity's, so a NaN counts as non-finite.
     float v[4];
-    float amax = 0.0f;
+    uint32_t mb = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         v[b] = real ? static_cast<float>(px[b]) : 0.0f;
-        float a = fabsf(v[b]);
-        a = (a <= FLT_MAX) ? a : INFINITY;  // NaN counts as non-finite
-        amax = fmaxf(amax, a);
+        const uint32_t a = __float_as_uint(v[b]) & 0x7fffffffu;
+        mb = a > mb ? a : mb;
     }
-    amax = lane_group_max<32>(amax);
-    const bool finite = amax <= FLT_MAX;
-    const bool nz = finite && amax > 0.0f;
-    const int e = nz ? ilogbf(amax) : 0;
+    mb = lane32_max_u32(mb);
+    const bool finite = mb < 0x7f800000u;
+    const bool nz = finite && mb != 0u;
+    const float amax = __uint_as_float(mb);
+    const int e = nz ? __builtin_amdgcn_frexp_expf(amax) - 1 : 0;  // ilogb of a finite non-zero amax
     _Float16 hi[4], lo[4];
+    float sv[4];
     float part = 0.0f;
-    // remainder and magnitudes in units of 2^e
-    float round_sum = 0.0f;
+    // magnitudes in units of 2^e
     float mag[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        const float sv = nz ? ldexpf(v[b], -e) : 0.0f;
-        hi[b] = static_cast<_Float16>(sv);
-        const float rem = sv - static_cast<float>(hi[b]);  // exact in f32
+        sv[b] = nz ? ldexpf(v[b], -e) : 0.0f;
+        hi[b] = static_cast<_Float16>(sv[b]);
+        const float rem = sv[b] - static_cast<float>(hi[b]);  // exact in f32
         lo[b] = static_cast<_Float16>(rem);
-        round_sum += fabsf(rem - static_cast<float>(lo[b]));  // exact: what the split leaves out
-        mag[b] = fabsf(sv);
+        mag[b] = fabsf(sv[b]);
         part += static_cast<float>(hi[b]) + static_cast<float>(lo[b]);
     }
     const float sub8 = lane_group_sum<8>(part);
     const float tot = lane_group_sum<32>(part);
-    round_sum = lane_group_sum<32>(round_sum);
     // a lower bound of the magnitude without the four largest: the sum of all
-    // minus four times the largest (here 1 <= largest < 2); the tighter ones
-    // only where that does not clear the rounding
+    // minus four times the largest (here 1 <= largest < 2); the total
+    // remainder E and the tighter bounds only where that does not clear the
+    // test.  |sv - hi| <= 2^-11 and |sv - hi - lo| <= 2^-23, so E <= 128 *
+    // 2^-23 = 2^-16 and E * 2^15 <= 1/2: a block whose first bound reaches 1/2
+    // passes whatever E is.
     const float abs_sum = lane_group_sum<32>((mag[0] + mag[1]) + (mag[2] + mag[3]));
     const float amax_s = nz ? ldexpf(amax, -e) : 0.0f;
-    const float rest = rest_bound_tiers<32>(mag, abs_sum - 4.0f * amax_s, round_sum * 32768.0f);
+    const float first = abs_sum - 4.0f * amax_s;
+    uint8_t flag = 0;
+    if (__builtin_amdgcn_ballot_w64(nz && !(first >= 0.5f)) != 0) {
+        float round_sum = 0.0f;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float rem = sv[b] - static_cast<float>(hi[b]);
+            round_sum += fabsf(rem - static_cast<float>(lo[b]));  // exact: what the split leaves out
+        }
+        round_sum = lane_group_sum<32>(round_sum);
+        const float rest = rest_bound_tiers<32>(mag, first, round_sum * 32768.0f);
+        flag = round_sum * 32768.0f > rest ? 1 : 0;
+    }
     if (!live) return;
-    if (c == 0) flags[st * tpad + tok] = round_sum * 32768.0f > rest ? 1 : 0;
+    if (c == 0) flags[st * tpad + tok] = flag;
     uint8_t *blk = xc + (st * mt + tok / 16) * kTileStageBytes;
     const int col = tok & 15;
     // activations 4c..4c+3 land at positions pos + {0, 2, 1, 3} of one lane
