@@ -395,11 +395,21 @@ hipError_t launch_prefill(const uint8_t *w, const _Float16 *x, void *y, bool y_f
     const int64_t xa_bytes = mpad * k * 2;
     const int64_t xs_bytes = nsb * nblocks * kMinBlock;
     // Too few tiles to fill the CUs: split K across workgroups (each keeps
-    // at least 4 super-blocks), partial tiles added by a second kernel.
+    // at least 4 super-blocks), partial tiles added by a second kernel.  One
+    // workgroup fits a CU (its LDS), so a launch runs in rounds of one
+    // workgroup per CU; the split is the smallest that minimizes rounds per
+    // unit of K, ceil(tiles * s / CUs) / s (a last round half full costs a
+    // whole one).
     const int64_t tiles = nrb * nblocks;
-    const int64_t want = (2 * static_cast<int64_t>(device_cu_count()) + tiles - 1) / tiles;
-    int64_t ksplit = want < nsb / 4 ? want : nsb / 4;
-    if (ksplit < 1) ksplit = 1;
+    const int64_t cus = device_cu_count();
+    const int64_t max_split = nsb / 4 > 1 ? nsb / 4 : 1;
+    int64_t ksplit = 1;
+    for (int64_t s = 2; s <= max_split && tiles * (s - 1) < 4 * cus; ++s) {
+        // rounds(s) / s < rounds(ksplit) / ksplit, in integers
+        const int64_t r = (tiles * s + cus - 1) / cus;
+        const int64_t rb = (tiles * ksplit + cus - 1) / cus;
+        if (r * ksplit < rb * s) ksplit = s;
+    }
     const int64_t part_bytes = ksplit > 1 ? ksplit * m * n * 4 : 0;
     const int64_t total = xa_bytes + xs_bytes + part_bytes;
     if (ws.query) {
