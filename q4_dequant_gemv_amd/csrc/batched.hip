@@ -826,12 +826,16 @@ namespace {
 #ifndef Q4K_BATCH_STAGE_SB
 #define Q4K_BATCH_STAGE_SB 4
 #endif
+// super-blocks per stage for more than 16 tokens at K <= kBatchShortK
 #ifndef Q4K_BATCH_STAGE_SB_SHORT
 #define Q4K_BATCH_STAGE_SB_SHORT 2
 #endif
+// 1: long rows with one 16-row tile per CU halve K between two workgroups
+// (dispatch_mt)
 #ifndef Q4K_BATCH_HALVE_K
 #define Q4K_BATCH_HALVE_K 1
 #endif
+// row tiles per workgroup at most for 2-4 token tiles with the short stage
 #ifndef Q4K_BATCH_NT_SHORT
 #define Q4K_BATCH_NT_SHORT 3
 #endif
@@ -889,6 +893,8 @@ hipError_t launch_mfma_s(const uint8_t *w, const XT *x, YT *y, int m, int64_t n,
     return e != hipSuccess ? e : f;
 }
 
+// tiles in flight per wave (ring slots + 1) of the weight-streaming kernel
+// when two workgroups split K, and whether they do (launch_stream)
 #ifndef Q4K_STREAM_KP_NB
 #define Q4K_STREAM_KP_NB 2
 #endif
