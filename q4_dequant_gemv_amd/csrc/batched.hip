@@ -803,6 +803,196 @@ __global__ __launch_bounds__(64 * (KP == 1 ? stream_max_waves<H>() : 8), 1) void
     }
 }
 
+// ---- the same, K split in two, with the weights staged through LDS ----------
+// At K = 4096 with few tiles per CU (the two-part form above), each wave's
+// share of a tile is 16 rows x one super-block: 16 runs of 144 bytes.  Three
+// loads per wave copy them straight into LDS ([row][144 bytes], lane l of
+// load i taking 16-byte piece 64 i + l), so a ring of D tiles per wave costs
+// no registers and D tiles' weights are in flight from the start, where the
+// register ring held one.  D = 2: deeper rings put more of every
+// workgroup's loads into one burst at the start, which delays each first
+// tile (9B gate, 16 tokens, per call with the preparation: 13.4 / 13.9 /
+// 14.6 us for D = 2 / 3 / 4, the register ring 15.0).  A wave reads only its own ring
+// slots, so it waits for its own loads alone (wait_vm) and needs no barrier
+// for them; the barriers of the sums between waves wait for LDS operations
+// only, so the stream keeps running across them.  Everything else (the
+// activation fragments in registers, the B operands, the products, the fixed
+// order of the sums, two addends per output in y) is the kernel above with
+// H = 2, K parts = 2.
+#ifndef Q4K_STREAM_LDS
+#define Q4K_STREAM_LDS 1
+#endif
+#ifndef Q4K_STREAM_LDS_D
+#define Q4K_STREAM_LDS_D 2
+#endif
+// tiles between two additions of the waves' sums
+#ifndef Q4K_STREAM_LDS_FLUSH
+#define Q4K_STREAM_LDS_FLUSH 2
+#endif
+constexpr int kLdsFlush = Q4K_STREAM_LDS_FLUSH;
+constexpr int kLdsWaves = 8;
+constexpr int kLdsPieces = 16 * kBlockBytes / 16;   // 16-byte pieces of a wave's tile share: 144
+constexpr int kLdsLoads = (kLdsPieces + 63) / 64;   // load instructions per wave and tile: 3
+
+// The lane's 16-byte header at LDS byte address a and its two 16-byte code
+// pieces at b and b + 64, complete on return.  One asm statement with its
+// own wait: the compiler then sees no LDS read and adds no wait for the
+// weight loads still in flight to the other ring slots.
+__device__ __forceinline__ void lds_read_hdr_q2(uint32_t a, uint32_t b, uint4 &hdr, uint4 &q0, uint4 &q1) {
+    u32x4_t x0, x1, x2;
+    asm volatile(
+        "ds_read_b128 %0, %3\n\t"
+        "ds_read_b128 %1, %4\n\t"
+        "ds_read_b128 %2, %4 offset:64\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x0), "=&v"(x1), "=&v"(x2)
+        : "v"(a), "v"(b)
+        : "memory");
+    hdr = make_uint4(x0.x, x0.y, x0.z, x0.w);
+    q0 = make_uint4(x1.x, x1.y, x1.z, x1.w);
+    q1 = make_uint4(x2.x, x2.y, x2.z, x2.w);
+}
+
+template <int D, typename XT>
+__global__ __launch_bounds__(64 * kLdsWaves, 1) void stream_lds_kernel(
+    const uint8_t *__restrict__ w, const uint8_t *__restrict__ xc, float *__restrict__ y, int m, int64_t n, int64_t k,
+    int64_t row_bytes, int64_t xc_bytes, const XT *__restrict__ x, int64_t flag_off) {
+    constexpr int kSlot = kLdsLoads * 1024;
+    __shared__ __align__(16) uint8_t wst[D][kLdsWaves][kSlot];
+    __shared__ __align__(16) float4_t part[2][kLdsFlush][kLdsWaves][64];
+    __shared__ int wflag[kLdsWaves];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+    const int nhalf = static_cast<int>(k / kStageK);
+    // workgroup b: K part b % 2 of the tiles b / 2, b / 2 + gridDim.x / 2, ...
+    const int kp = static_cast<int>(blockIdx.x & 1);
+    const int tblk = static_cast<int>(blockIdx.x >> 1);
+    const int tgrid = static_cast<int>(gridDim.x >> 1);
+    const int hw0 = kp * (nhalf / 2) + 2 * wave;  // the wave's first half (even)
+    const int sb = hw0 >> 1;                      // its super-block
+
+    // the wave's two halves of activation fragments, sums and scales, in
+    // registers (a lane whose token is past m reads zeros); the flags of
+    // every half first
+    const __amdgpu_buffer_rsrc_t ar = stream_rsrc(xc, static_cast<int>(xc_bytes));
+    // (16 flag bytes per half: 128 dwords for 32 halves, one per thread)
+    const uint32_t flag_bits = static_cast<int>(threadIdx.x) < nhalf * 4
+                                   ? __builtin_amdgcn_raw_buffer_load_b32(ar, static_cast<int>(flag_off + 4 * threadIdx.x), 0, 0)
+                                   : 0u;
+    const uint32_t a_off = col < m ? 0u : 0x40000000u;
+    AStep as[2];
+    PairSelect ps[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int soff = (hw0 + h) * kTileStageBytes;
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+            as[h].f[f] = as_uint4(
+                __builtin_amdgcn_raw_buffer_load_b128(ar, static_cast<int>(a_off + f * 1024 + lane * 16), soff, 0));
+        as[h].sub = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(ar, kSubOff + col * 16, soff, 0));
+        as[h].bias = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, kBiasOff + kq * 16, soff, 0));
+        as[h].esc = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, kEscOff + kq * 16, soff, 0));
+        ps[h] = pair_select(2 * h + (kq >> 1));
+    }
+    const bool exact = workgroup_any(flag_bits, wflag, kLdsWaves);
+
+    // the host keeps gridDim.x / 2 <= the number of tiles: every workgroup has one
+    const int64_t ntiles = (n + 15) / 16;
+    const int my_tiles = static_cast<int>((ntiles - 1 - tblk) / tgrid) + 1;
+    auto tile_row0 = [&](int c) -> int64_t {
+        return (static_cast<int64_t>(tblk) + static_cast<int64_t>(c) * tgrid) * 16;
+    };
+    if (exact) {
+        // a flagged block: the workgroup's tiles (its K part) on the f32 path
+        const int nsb = static_cast<int>(k / kBlockWeights);
+        for (int c = 0; c < my_tiles; ++c) {
+            const int64_t r0 = tile_row0(c);
+            const int64_t r1 = r0 + 16 < n ? r0 + 16 : n;
+            exact_tile<XT, float, true>(w, row_bytes, x, k, m, y, n, r0, r1, kp * nsb / 2, (kp + 1) * nsb / 2, wave,
+                                        kLdsWaves);
+        }
+        return;
+    }
+    // the lane's descriptor offsets for the three loads of a tile: piece
+    // p = 64 i + lane is row p / 9, bytes 16 (p % 9) of its super-block sb;
+    // pieces past the 144th read past the descriptor's end (zeros)
+    uint32_t voff[kLdsLoads];
+#pragma unroll
+    for (int i = 0; i < kLdsLoads; ++i) {
+        const int p = 64 * i + lane;
+        voff[i] = p < kLdsPieces ? static_cast<uint32_t>((p / 9) * row_bytes + sb * kBlockBytes + (p % 9) * 16)
+                                 : 0x40000000u;
+    }
+    // tile c of this workgroup into ring slot b (a tile past the last: a
+    // 0-byte descriptor, so the loads read zeros without a fetch)
+    auto issue_stage = [&](int b, int c) {
+        const bool live = c < my_tiles;
+        const int64_t row0 = live ? tile_row0(c) : 0;
+        const int64_t rows = n - row0 < 16 ? n - row0 : 16;
+        const int nrec = __builtin_amdgcn_readfirstlane(live ? static_cast<int>(rows * row_bytes) : 0);
+        const uint8_t *base =
+            reinterpret_cast<const uint8_t *>(wave_uniform(reinterpret_cast<int64_t>(w + row0 * row_bytes)));
+        const __amdgpu_buffer_rsrc_t r = stream_rsrc(base, nrec);
+#pragma unroll
+        for (int i = 0; i < kLdsLoads; ++i) buffer_load16_lds(r, &wst[b][wave][i * 1024], voff[i]);
+    };
+    const uint32_t rd_hdr = static_cast<uint32_t>(col * kBlockBytes);
+    const uint32_t rd_q = rd_hdr + 16u + 16u * static_cast<uint32_t>(kq);
+
+#pragma unroll
+    for (int b = 0; b < D; ++b) issue_stage(b, b);
+    // the activation loads (issued first) done, the weights still in flight;
+    // without this the compiler waits for every load before the loop
+    wait_vm<kLdsLoads * D>();
+    for (int c = 0; c < my_tiles; c += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int cur = c + u;
+            // tile cur's loads done (the D - 1 later tiles' stay in flight)
+            wait_vm<kLdsLoads * (D - 1)>();
+            const uint32_t slot = lds_addr(&wst[u][wave][0]);
+            uint4 hdr, q[2];
+            lds_read_hdr_q2(slot + rd_hdr, slot + rd_q, hdr, q[0], q[1]);
+            issue_stage(u, cur + D);
+            float4_t out = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                BOps bo;
+                build_b_ops(bo, hdr, q[h], ps[h], kq);
+                mfma_half(bo, as[h], out, kq);
+            }
+            const int d = cur % kLdsFlush;
+            const int half = (cur / kLdsFlush) & 1;
+            part[half][d][wave][lane] = out;
+            if (d == kLdsFlush - 1 || cur + 1 == my_tiles) {
+                lds_barrier();
+                const int t = static_cast<int>(threadIdx.x);
+                if (t < (d + 1) * 64) {
+                    const int dd = t >> 6;
+                    const int ln = t & 63;
+                    float4_t sum = part[half][dd][0][ln];
+#pragma unroll
+                    for (int v = 1; v < kLdsWaves; ++v) sum += part[half][dd][v][ln];
+                    const int64_t row = tile_row0(cur - d + dd) + (ln & 15);
+                    if (row < n) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int tok = 4 * (ln >> 4) + r;
+                            if (tok < m) unsafeAtomicAdd(y + static_cast<int64_t>(tok) * n + row, sum[r]);
+                        }
+                    }
+                }
+            }
+            if (cur + 1 >= my_tiles) break;
+        }
+    }
+    // the ring's last loads (past the last tile) land before the workgroup's
+    // LDS is released
+    wait_vm<0>();
+}
+
 __global__ __launch_bounds__(256) void f32_to_f16_kernel(const float *__restrict__ src, _Float16 *__restrict__ dst,
                                                           int64_t count) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
@@ -942,8 +1132,13 @@ hipError_t launch_stream(const uint8_t *w, const XT *x, YT *y, int m, int64_t n,
         const dim3 grid(static_cast<unsigned>(tiles2 < cus ? tiles2 : cus));
         const int64_t rb = (k / kBlockWeights) * kBlockBytes;
         if constexpr (std::is_same_v<YT, float>) {
-            hipLaunchKernelGGL((stream_mfma_kernel<2, Q4K_STREAM_KP_NB, float, XT, 2>), grid, dim3(64 * 8), 0, stream, w, xc,
-                               y, m, n, k, rb, bytes, x, flag_off);
+            if (Q4K_STREAM_LDS) {
+                hipLaunchKernelGGL((stream_lds_kernel<Q4K_STREAM_LDS_D, XT>), grid, dim3(64 * kLdsWaves), 0, stream, w,
+                                   xc, y, m, n, k, rb, bytes, x, flag_off);
+            } else {
+                hipLaunchKernelGGL((stream_mfma_kernel<2, Q4K_STREAM_KP_NB, float, XT, 2>), grid, dim3(64 * 8), 0, stream,
+                                   w, xc, y, m, n, k, rb, bytes, x, flag_off);
+            }
         }
         e = hipGetLastError();
     } else if (e == hipSuccess) {
