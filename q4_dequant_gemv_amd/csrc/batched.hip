@@ -878,9 +878,10 @@ __global__ __launch_bounds__(64 * kLdsWaves, 1) void stream_lds_kernel(
     // every half first
     const __amdgpu_buffer_rsrc_t ar = stream_rsrc(xc, static_cast<int>(xc_bytes));
     // (16 flag bytes per half: 128 dwords for 32 halves, one per thread)
-    const uint32_t flag_bits = static_cast<int>(threadIdx.x) < nhalf * 4
-                                   ? __builtin_amdgcn_raw_buffer_load_b32(ar, static_cast<int>(flag_off + 4 * threadIdx.x), 0, 0)
-                                   : 0u;
+    // (threads past them read past the descriptor's end: zeros, and no
+    // branch, so that the wait for the flags comes after the loads below)
+    const uint32_t flag_bits = __builtin_amdgcn_raw_buffer_load_b32(
+        ar, static_cast<int>(threadIdx.x) < nhalf * 4 ? static_cast<int>(flag_off + 4 * threadIdx.x) : 0x40000000, 0, 0);
     const uint32_t a_off = col < m ? 0u : 0x40000000u;
     AStep as[2];
     PairSelect ps[2];
