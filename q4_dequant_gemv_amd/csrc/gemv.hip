@@ -236,6 +236,48 @@ struct Q8_0Format {
     }
 };
 
+// Q8_0 staged through LDS like Q4_K: a wave's iteration (whole rows,
+// contiguous bytes) arrives by direct-to-LDS loads, then each lane reads its
+// group's 17 dwords from LDS (dword-aligned: lane stride 68 bytes, 17 dwords,
+// an odd count, so the 64 lanes' reads fall in distinct banks).  Used where
+// every iteration starts on a 16-byte boundary: rows of a multiple of 256
+// weights (68 * K / 64 bytes, a multiple of 16) in a 16-byte aligned matrix,
+// at most 4096 weights long (longer rows' split kernels would need more LDS
+// than a CU has for their rings of 4352-byte slices).
+#ifndef Q4K_Q8_0_STAGE
+#define Q4K_Q8_0_STAGE 1
+#endif
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+struct Q8_0StagedFormat : Q8_0Format {
+    static constexpr bool kStaged = true;
+    static __device__ __forceinline__ void fetch(Loads &l, uint32_t stage, const Lane &g) {
+        const uint32_t a = stage + g.off;
+        u32x2_t p0, p1, p2, p3, p4, p5, p6, p7;
+        uint32_t e;
+        // one asm statement with its own wait: the compiler sees no LDS read
+        // and adds no wait for the loads still in flight to other slots
+        asm volatile(
+            "ds_read2_b32 %0, %9 offset1:1\n\t"
+            "ds_read2_b32 %1, %9 offset0:2 offset1:3\n\t"
+            "ds_read2_b32 %2, %9 offset0:4 offset1:5\n\t"
+            "ds_read2_b32 %3, %9 offset0:6 offset1:7\n\t"
+            "ds_read2_b32 %4, %9 offset0:8 offset1:9\n\t"
+            "ds_read2_b32 %5, %9 offset0:10 offset1:11\n\t"
+            "ds_read2_b32 %6, %9 offset0:12 offset1:13\n\t"
+            "ds_read2_b32 %7, %9 offset0:14 offset1:15\n\t"
+            "ds_read_b32 %8, %9 offset:64\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(p0), "=&v"(p1), "=&v"(p2), "=&v"(p3), "=&v"(p4), "=&v"(p5), "=&v"(p6), "=&v"(p7), "=&v"(e)
+            : "v"(a)
+            : "memory");
+        l.a = make_uint4(p0.x, p0.y, p1.x, p1.y);
+        l.b = make_uint4(p2.x, p2.y, p3.x, p3.y);
+        l.c = make_uint4(p4.x, p4.y, p5.x, p5.y);
+        l.d = make_uint4(p6.x, p6.y, p7.x, p7.y);
+        l.e = e;
+    }
+};
+
 // One row's weight bytes for one lane, per matrix.
 template <class F, int NMAT>
 struct RowLoads {
@@ -1198,7 +1240,7 @@ hipError_t launch_generic(const uint8_t *w, const uint8_t *wu, const void *x, co
     const int64_t need = (n + 3) / 4;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
     const int grid = static_cast<int>(need < cap ? need : cap);
-    if constexpr (std::is_same_v<F, Q8_0Format>) {
+    if constexpr (std::is_base_of_v<Q8_0Format, F>) {
         static_assert(!SWIGLU && std::is_same_v<XT, float> && std::is_same_v<YT, float>, "Q8_0: f32 GEMV only");
         hipLaunchKernelGGL(q8_0_generic_kernel, dim3(grid), dim3(256), 0, stream, w, static_cast<const float *>(x),
                            static_cast<float *>(y), r, n, k, F::row_bytes(k));
@@ -1323,7 +1365,7 @@ hipError_t dispatch_lpr(const GemvJob *jobs, int count, const uint8_t *wu, const
             constexpr int NB = kStaged ? 1 + Q4K_SMALL_SLOTS : Q4K_SMALL_NB;
             return launch_fast<F, XT, YT, LPR, false, NB, Q4K_SMALL_BLOCK, Q4K_SMALL_MINW>(jobs, count, wu, x, k, stream);
         }
-        constexpr int kShort = std::is_same_v<F, Q8_0Format> ? Q8_0_LARGE_BLOCK_SHORT : Q4K_LARGE_BLOCK_SHORT;
+        constexpr int kShort = std::is_base_of_v<Q8_0Format, F> ? Q8_0_LARGE_BLOCK_SHORT : Q4K_LARGE_BLOCK_SHORT;
         constexpr int kBlock = LPR <= 16 ? kShort : Q4K_LARGE_BLOCK;
         constexpr int NB = kStaged ? 1 + Q4K_LARGE_SLOTS : Q4K_LARGE_NB;
         return launch_fast<F, XT, YT, LPR, false, NB, kBlock, Q4K_LARGE_MINW, Q4K_LARGE_RPG>(jobs, count, wu, x, k,
@@ -1356,14 +1398,20 @@ hipError_t dispatch_wide(const GemvJob &j, const uint8_t *wu, const void *x, int
 }
 
 template <class F, typename XT, typename YT, bool SWIGLU>
-hipError_t dispatch(const GemvJob *jobs, int count, const uint8_t *wu, const void *x, int64_t k,
-                    hipStream_t stream) {
+hipError_t dispatch_short(const GemvJob *jobs, int count, const uint8_t *wu, const void *x, int64_t k,
+                          hipStream_t stream) {
     const int64_t ngroups = k / 64;
     if (ngroups <= 4) return dispatch_lpr<F, XT, YT, 4, SWIGLU>(jobs, count, wu, x, k, stream);
     if (ngroups <= 8) return dispatch_lpr<F, XT, YT, 8, SWIGLU>(jobs, count, wu, x, k, stream);
     if (ngroups <= 16) return dispatch_lpr<F, XT, YT, 16, SWIGLU>(jobs, count, wu, x, k, stream);
     if (ngroups <= 32) return dispatch_lpr<F, XT, YT, 32, SWIGLU>(jobs, count, wu, x, k, stream);
-    if (ngroups <= 64) return dispatch_lpr<F, XT, YT, 64, SWIGLU>(jobs, count, wu, x, k, stream);
+    return dispatch_lpr<F, XT, YT, 64, SWIGLU>(jobs, count, wu, x, k, stream);
+}
+
+template <class F, typename XT, typename YT, bool SWIGLU>
+hipError_t dispatch(const GemvJob *jobs, int count, const uint8_t *wu, const void *x, int64_t k,
+                    hipStream_t stream) {
+    if (k <= 4096) return dispatch_short<F, XT, YT, SWIGLU>(jobs, count, wu, x, k, stream);
     for (int i = 0; i < count; ++i) {
         const hipError_t e = dispatch_wide<F, XT, YT, SWIGLU>(jobs[i], wu, x, k, stream);
         if (e != hipSuccess) return e;
@@ -1442,6 +1490,8 @@ hipError_t launch_q8_0_gemv(const uint8_t *w, const float *x, const float *r, fl
     if (k % 64 != 0 || (reinterpret_cast<uintptr_t>(w) & 3) != 0) {
         return launch_generic<Q8_0Format, float, float, false>(w, nullptr, x, r, y, n, k, stream);
     }
+    if (Q4K_Q8_0_STAGE && k <= 4096 && k % 256 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0)
+        return dispatch_short<Q8_0StagedFormat, float, float, false>(&job, 1, nullptr, x, k, stream);
     return dispatch<Q8_0Format, float, float, false>(&job, 1, nullptr, x, k, stream);
 }
 
