@@ -242,8 +242,9 @@ struct Q8_0Format {
 // an odd count, so the 64 lanes' reads fall in distinct banks).  Used where
 // every iteration starts on a 16-byte boundary: rows of a multiple of 256
 // weights (68 * K / 64 bytes, a multiple of 16) in a 16-byte aligned matrix,
-// at most 4096 weights long (longer rows' split kernels would need more LDS
-// than a CU has for their rings of 4352-byte slices).
+// at most 4096 weights long, or 8193-12288 weights (the three-slice split
+// kernel; the other split shapes would need more LDS than a CU has for their
+// rings of 4352-byte slices).
 #ifndef Q4K_Q8_0_STAGE
 #define Q4K_Q8_0_STAGE 1
 #endif
@@ -1490,8 +1491,15 @@ hipError_t launch_q8_0_gemv(const uint8_t *w, const float *x, const float *r, fl
     if (k % 64 != 0 || (reinterpret_cast<uintptr_t>(w) & 3) != 0) {
         return launch_generic<Q8_0Format, float, float, false>(w, nullptr, x, r, y, n, k, stream);
     }
-    if (Q4K_Q8_0_STAGE && k <= 4096 && k % 256 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0)
-        return dispatch_short<Q8_0StagedFormat, float, float, false>(&job, 1, nullptr, x, k, stream);
+    if (Q4K_Q8_0_STAGE && k % 256 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0) {
+        if (k <= 4096) return dispatch_short<Q8_0StagedFormat, float, float, false>(&job, 1, nullptr, x, k, stream);
+        // rows of 129-192 groups: the three-slice split kernel, whose ring
+        // (one 4352-byte slice per wave, 12 waves) fits in LDS beside the
+        // activations
+        if (k > 8192 && k <= 12288)
+            return launch_split<Q8_0StagedFormat, float, float, 3, 4, false, 1 + Q4K_SPLIT3_SLOTS, 3>(w, nullptr, x, r,
+                                                                                                     y, n, k, stream);
+    }
     return dispatch<Q8_0Format, float, float, false>(&job, 1, nullptr, x, k, stream);
 }
 
