@@ -2,7 +2,7 @@
 CPU oracle on the same seeded inputs: every output within
 2e-4 * sum_k |w_k x_k|, every output, at small shapes and at the 9B shapes
 (computed on the GPU in the configuration the benchmark times).  Shapes cover the streaming kernel (K % 64 == 0, K <= 4096), the
-K-split kernel (K up to 16384) and the one-wave-per-row kernel (an odd number
+K-split kernel (K up to 16384), both with LDS-staged and register loads, and the one-wave-per-row kernel (an odd number
 of blocks per row, a matrix that is only 2-byte aligned, K > 16384).
 """
 
@@ -87,6 +87,32 @@ def test_q8_0_two_byte_aligned_matrix(q4k):
     q4k.q8_0_gemv(wd[rb:], to_dev(x), y=y, n=n - 1)
     yr, ar = oracle.q8_0_gemv(w[1:], x, threads=THREADS)
     _report("q8_0 2-byte aligned", check_bound(to_host(y), yr, ar, "2-byte aligned"))
+
+
+@pytest.mark.parametrize("n,k", [(300, 1024), (129, 4096), (17, 12288)])
+def test_q8_0_staged_equals_register_path(q4k, n, k):
+    """Rows of a multiple of 256 weights (K <= 4096, or 8192 < K <= 12288) in a
+    16-byte aligned matrix stream through LDS; the same bytes at an address
+    that is 4-byte but not 16-byte aligned stream through registers.  Both give
+    bitwise the same outputs, inside the oracle's bound."""
+    import torch
+
+    print(f"[case] q8_0 staged vs register loads {n}x{k}", flush=True)
+    w = inputs.make_q8_0(n, k, config_id=56, tensor_id=k)
+    x = inputs.make_x(1, k, config_id=56, tensor_id=k)[0]
+    flat = w.reshape(-1)
+    wa = to_dev(flat)
+    assert wa.data_ptr() % 16 == 0
+    buf = torch.zeros(flat.size + 16, dtype=torch.uint8, device="cuda")
+    buf[4:4 + flat.size].copy_(wa)
+    w4 = buf[4:4 + flat.size]
+    assert w4.data_ptr() % 16 == 4
+    xd = to_dev(x)
+    ya = q4k.q8_0_gemv(wa, xd, n=n)
+    y4 = q4k.q8_0_gemv(w4, xd, n=n)
+    assert torch.equal(ya, y4)
+    yr, ar = oracle.q8_0_gemv(w, x, threads=THREADS)
+    _report(f"q8_0 staged {n}x{k}", check_bound(to_host(ya), yr, ar, "staged"))
 
 
 def test_q8_0_special_values(q4k):
