@@ -206,8 +206,11 @@ Q4K_API q4k_status q4k_gemv_multi(const q4k_gemv_item *items, int count, const f
  *   w : Q8_0 matrix [n, k] (n*(k/32)*34 bytes), 2-byte aligned
  *   x : f32 [k];  y : f32 [n], written: y[i] = sum_c W[i,c] x[c].
  * k % 32 != 0 -> Q4K_ERR_UNSUPPORTED_SHAPE.  Rows with an even number of
- * blocks in a 4-byte aligned matrix take the streaming kernels; any other
- * layout a slower one-wave-per-row kernel.  Accuracy as q4k_gemv.
+ * blocks in a 4-byte aligned matrix take the streaming kernels (fastest with
+ * k % 256 == 0 in a 16-byte aligned matrix, k <= 4096 or 8192 < k <= 12288:
+ * the weights then pass through LDS; the results are the same bits either
+ * way); any other layout a slower one-wave-per-row kernel.  Accuracy as
+ * q4k_gemv.
  */
 Q4K_API q4k_status q4k_q8_0_gemv(const void *w, const float *x, float *y, int64_t n, int64_t k, void *stream);
 
